@@ -1,0 +1,246 @@
+"""Benchmark: compressed-KV decode attention GB/s (fraction of HBM peak) and
+quantize-append Mtok/s on one MI355X.
+
+Workload (default): batch 4, 8 KV heads, 32 query heads, head_dim 128,
+context 32768, K 3-bit / V 4-bit (3.5 bits), 36 layers.  One step is, per
+layer in order: quantize-append an 8192-token prefill chunk per sequence at
+positions [24576, 32768), then one decode step attending over all 32768
+positions.  Inputs are seeded synthetic fp16 (per-channel log-normal(0, 0.5)
+scales with 1% x8 outlier channels; q N(0, 1)); every layer has its own
+buffers.  The codebook build and the cache fill are set-up, outside the
+timed region.
+
+Prints one JSON line.  `value` is the decode GB/s over the algorithmic bytes
+(every packed code word and norm of positions [0, 32768) for K and V, plus q
+and out); quantize-append Mtok/s rides along in the same line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+WORKLOADS = {
+    "c4_tq35_32k": dict(batch=4, kv_heads=8, q_heads=32, head_dim=128, tokens=32768, layers=36,
+                        k=("packed", 3), v=("packed", 4), prefill=8192, dist="channel",
+                        outlier_frac=0.01),
+    "c2_sym4_4k": dict(batch=1, kv_heads=8, q_heads=32, head_dim=128, tokens=4096, layers=36,
+                       k=("packed", 4), v=("packed", 4), prefill=0, dist="channel", outlier_frac=0.01),
+    "c3_asym_16k": dict(batch=8, kv_heads=8, q_heads=32, head_dim=128, tokens=16384, layers=36,
+                        k=("fp16", 0), v=("packed", 4), prefill=0, append=1, dist="channel",
+                        outlier_frac=0.01),
+    "c5_delegated_64k": dict(batch=16, kv_heads=4, q_heads=32, head_dim=128, tokens=65536, layers=48,
+                             k=("fp16", 0), v=("delegated", 4), prefill=0, dist="channel",
+                             outlier_frac=0.0, hot=256),
+}
+
+
+def side_bytes_per_token(mode: str, bits: int, d: int) -> int:
+    if mode == "fp16":
+        return 2 * d
+    return 4 * ((bits * d + 31) // 32) + 4
+
+
+def decode_bytes(w) -> int:
+    """Algorithmic bytes one decode launch must move."""
+    d, T = w["head_dim"], w["tokens"]
+    units = w["batch"] * w["kv_heads"]
+    kb = side_bytes_per_token(w["k"][0], w["k"][1], d) * T
+    if w["v"][0] == "delegated":
+        hot = min(w.get("hot", 256), T)
+        vb = side_bytes_per_token("packed", w["v"][1], d) * (T - hot) + 2 * d * hot
+    else:
+        vb = side_bytes_per_token(w["v"][0], w["v"][1], d) * T
+    q = w["batch"] * w["q_heads"] * d * 2
+    out = w["batch"] * w["q_heads"] * d * 4
+    return units * (kb + vb) + q + out
+
+
+def append_bytes(w, n_new: int) -> int:
+    """Algorithmic bytes of one quantize-append launch (fp16 read + packed write)."""
+    d = w["head_dim"]
+    units = w["batch"] * w["kv_heads"]
+    per = 0
+    for mode, bits in (w["k"], w["v"]):
+        per += 2 * d + (2 * d if mode == "fp16" else side_bytes_per_token(mode, bits, d))
+    return units * n_new * per
+
+
+def cpu_baseline(w, budget_s: float = 12.0):
+    """Time the oracle (float64 NumPy) on a bounded sample of the decode:
+    whole (batch, KV head) units over the full context, until ~budget_s."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    d, T, G = w["head_dim"], w["tokens"], w["q_heads"] // w["kv_heads"]
+    kb, vb = w["k"][1], w["v"][1]
+    R = oracle.rotation_matrix(0, d)
+    units, spent, nbytes = 0, 0.0, 0
+    while spent < budget_s and units < 64:
+        k, v = synth.kv_numpy(1000 + units, 1, 1, T, d, dist=w["dist"], outlier_frac=w["outlier_frac"])
+        q = synth.q_numpy(1000 + units, 1, G, d)
+        kc, kt = oracle.lloyd_max(d, kb) if w["k"][0] != "fp16" else (None, None)
+        vc, vt = oracle.lloyd_max(d, vb)
+        # pre-quantize outside the timed part: the decode reads packed rows
+        if w["k"][0] != "fp16":
+            kcodes, kn, _ = oracle.quantize(k, R, kt)
+            kwords = oracle.pack_codes(kcodes, kb)
+        vcodes, vn, _ = oracle.quantize(v, R, vt)
+        vwords = oracle.pack_codes(vcodes, vb)
+        t0 = time.perf_counter()
+        if w["k"][0] != "fp16":
+            krows = oracle.dequantize(oracle.unpack_codes(kwords, kb, d), kn.astype(np.float32), R, kc)
+        else:
+            krows = k.astype(np.float64)
+        vrows = oracle.dequantize(oracle.unpack_codes(vwords, vb, d), vn.astype(np.float32), R, vc)
+        oracle.decode_attention(q, krows, vrows)
+        spent += time.perf_counter() - t0
+        units += 1
+        nbytes += (side_bytes_per_token(w["k"][0], kb, d) + side_bytes_per_token(w["v"][0], vb, d)) * T
+    return {"value": nbytes / spent / 1e9, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{units} of {w['batch'] * w['kv_heads']} (batch, KV head) units of one layer's "
+                      f"decode at context {T} (unpack + dequantize + float64 attention), {spent:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c4_tq35_32k", choices=sorted(WORKLOADS))
+    ap.add_argument("--layers", type=int, default=0, help="override the layer count (profiling only)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}), flush=True)
+        sys.exit(2)
+
+    import torch
+
+    import compressed_decode_attention_append_amd as tq
+    import synth
+
+    w = dict(WORKLOADS[args.workload])
+    if args.layers:
+        w["layers"] = args.layers
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    B, Hkv, Hq, d, T, Lyr = w["batch"], w["kv_heads"], w["q_heads"], w["head_dim"], w["tokens"], w["layers"]
+    pre = w.get("prefill", 0)
+    app = w.get("append", 0)
+    n_new = pre or app
+    base = T - n_new if n_new else T
+
+    kspec = tq.SideSpec(w["k"][0], w["k"][1])
+    vspec = tq.SideSpec(w["v"][0], w["v"][1], w.get("hot", 256))
+    layers = []
+    t_fill = time.time()
+    for li in range(Lyr):
+        cache = tq.TQCache(B, Hkv, d, T, kspec, vspec, seed=0, device=dev)
+        # fill positions [0, base) with the layer's own synthetic rows
+        chunk = 4096
+        for s in range(0, base, chunk):
+            n = min(chunk, base - s)
+            k, v = synth.kv_torch(7919 * li + s, B, Hkv, n, d, dist=w["dist"],
+                                  outlier_frac=w["outlier_frac"], device=dev)
+            cache.quantize_append(k, v, s)
+            del k, v
+        if n_new:
+            kn, vn = synth.kv_torch(104729 + li, B, Hkv, n_new, d, dist=w["dist"],
+                                    outlier_frac=w["outlier_frac"], device=dev)
+        else:
+            kn = vn = None
+        q = synth.q_torch(31 + li, B, Hq, d, device=dev)
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+        ws = cache.workspace(Hq, T)
+        layers.append((cache, kn, vn, q, out, ws))
+    torch.cuda.synchronize()
+    t_fill = time.time() - t_fill
+    print(f"# filled {Lyr} layers in {t_fill:.1f} s", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+
+    def step(record):
+        for cache, kn, vn, q, out, ws in layers:
+            if n_new:
+                if record is not None:
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                cache.quantize_append(kn, vn, base, stream=stream)
+                if record is not None:
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e1.record(stream)
+                    record["append"].append((e0, e1))
+            if record is not None:
+                e2 = torch.cuda.Event(enable_timing=True)
+                e2.record(stream)
+            cache.decode_attention(q, T, out=out, workspace=ws, stream=stream)
+            if record is not None:
+                e3 = torch.cuda.Event(enable_timing=True)
+                e3.record(stream)
+                record["decode"].append((e2, e3))
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    rec = {"append": [], "decode": []}
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(rec)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    dec_ms = [a.elapsed_time(b) for a, b in rec["decode"]]
+    app_ms = [a.elapsed_time(b) for a, b in rec["append"]]
+    dbytes = decode_bytes(w)
+    dec_avg_s = sum(dec_ms) / len(dec_ms) / 1e3
+    dec_gbs = dbytes / dec_avg_s / 1e9
+    res = {
+        "metric": "compressed-KV decode attention GB/s (% of HBM peak) + quantize-append Mtok/s",
+        "value": round(dec_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32+fp16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": B, "kv_heads": Hkv, "q_heads": Hq,
+                   "head_dim": d, "context": T, "layers": Lyr,
+                   "k": f"{w['k'][0]}{w['k'][1] or ''}", "v": f"{w['v'][0]}{w['v'][1]}",
+                   "append_per_layer": n_new},
+        "hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+        "decode_us_per_layer": round(dec_avg_s * 1e6, 2),
+        "decode_bytes_per_layer": dbytes,
+        "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    if n_new:
+        app_avg_s = sum(app_ms) / len(app_ms) / 1e3
+        res["quantize_append_mtok_s"] = round(B * n_new / app_avg_s / 1e6, 2)
+        res["quantize_append_us_per_layer"] = round(app_avg_s * 1e6, 2)
+        res["quantize_append_gbs"] = round(append_bytes(w, n_new) / app_avg_s / 1e9, 1)
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,293 @@
+"""Python binding of libtq (TurboQuant KV-cache quantize-append and decode
+attention from the packed cache, MI355X / gfx950).
+
+Argument marshalling only: every step of the path runs in libtq's HIP
+kernels; torch provides device memory and the current HIP stream.  The
+functions keep the names of the C ABI in ``include/tq.h``.  If ``libtq.so``
+has not been built, importing succeeds but every call raises ``TQError``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libtq.so")
+
+TQ_OK = 0
+TQ_ERR_ARG = -1
+TQ_ERR_HEAD_DIM = -2
+TQ_ERR_BITS = -3
+TQ_ERR_CAPACITY = -4
+TQ_ERR_WORKSPACE = -5
+TQ_ERR_MODE = -6
+TQ_ERR_HIP = -7
+
+SIDE_FP16 = 0
+SIDE_PACKED = 1
+SIDE_DELEGATED = 2
+_MODES = {"fp16": SIDE_FP16, "packed": SIDE_PACKED, "delegated": SIDE_DELEGATED}
+
+
+class TQError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+
+
+class tq_side(ctypes.Structure):
+    _fields_ = [
+        ("mode", ctypes.c_int),
+        ("bits", ctypes.c_int),
+        ("centroids", ctypes.c_void_p),
+        ("thresholds", ctypes.c_void_p),
+        ("codes", ctypes.c_void_p),
+        ("norms", ctypes.c_void_p),
+        ("fp16", ctypes.c_void_p),
+        ("hot", ctypes.c_int),
+    ]
+
+
+class tq_cache(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int),
+        ("kv_heads", ctypes.c_int),
+        ("head_dim", ctypes.c_int),
+        ("capacity", ctypes.c_int),
+        ("seed", ctypes.c_uint64),
+        ("k", tq_side),
+        ("v", tq_side),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libtq (raises TQError if it was never built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise TQError(TQ_ERR_HIP, f"libtq.so is not built at {LIB_PATH}")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        I = ctypes.c_int
+        L.tq_split_bits.argtypes = [ctypes.c_double, ctypes.POINTER(I), ctypes.POINTER(I)]
+        L.tq_split_bits.restype = I
+        L.tq_row_words.argtypes = [I, I]
+        L.tq_row_words.restype = I
+        L.tq_sign_words.argtypes = [ctypes.c_uint64, I, P]
+        L.tq_sign_words.restype = I
+        L.tq_build_codebook.argtypes = [I, I, P, P]
+        L.tq_build_codebook.restype = I
+        L.tq_quantize_append.argtypes = [ctypes.POINTER(tq_cache), P, P, I, I, P]
+        L.tq_quantize_append.restype = I
+        L.tq_decode_workspace_bytes.argtypes = [ctypes.POINTER(tq_cache), I, I, I]
+        L.tq_decode_workspace_bytes.restype = ctypes.c_size_t
+        L.tq_decode_attention.argtypes = [ctypes.POINTER(tq_cache), P, I, I, I, P, P, P,
+                                          ctypes.c_size_t, P]
+        L.tq_decode_attention.restype = I
+        L.tq_dequantize.argtypes = [ctypes.POINTER(tq_cache), I, I, I, P, P]
+        L.tq_dequantize.restype = I
+        L.tq_status_string.argtypes = [I]
+        L.tq_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    try:
+        return lib().tq_status_string(int(status)).decode()
+    except TQError:
+        return "libtq not built"
+
+
+def _check(status: int, what: str):
+    if status != TQ_OK:
+        raise TQError(status, what)
+
+
+def split_bits(bits: float) -> tuple[int, int]:
+    k, v = ctypes.c_int(), ctypes.c_int()
+    _check(lib().tq_split_bits(float(bits), ctypes.byref(k), ctypes.byref(v)), "tq_split_bits")
+    return k.value, v.value
+
+
+def row_words(head_dim: int, bits: int) -> int:
+    r = lib().tq_row_words(int(head_dim), int(bits))
+    if r < 0:
+        raise TQError(r, "tq_row_words")
+    return r
+
+
+def sign_words(seed: int, head_dim: int) -> np.ndarray:
+    out = np.zeros(max(1, head_dim // 32), np.uint32)
+    _check(lib().tq_sign_words(int(seed), int(head_dim), out.ctypes.data), "tq_sign_words")
+    return out
+
+
+def build_codebook(head_dim: int, bits: int) -> tuple[np.ndarray, np.ndarray]:
+    """Lloyd-Max codebook (float64 centroids[2^bits], thresholds[2^bits - 1])."""
+    L = 1 << int(bits) if 1 <= int(bits) <= 8 else 2
+    c = np.zeros(L, np.float64)
+    t = np.zeros(L - 1, np.float64)
+    _check(lib().tq_build_codebook(int(head_dim), int(bits), c.ctypes.data, t.ctypes.data),
+           "tq_build_codebook")
+    return c, t
+
+
+_CODEBOOKS: dict = {}
+
+
+class Codebook:
+    """Host codebook of one (head_dim, bits), built once by tq_build_codebook
+    and kept as the fp32 arrays the cache descriptor points at."""
+
+    def __init__(self, head_dim: int, bits: int):
+        self.head_dim, self.bits = int(head_dim), int(bits)
+        self.centroids64, self.thresholds64 = build_codebook(head_dim, bits)
+        self.centroids = np.ascontiguousarray(self.centroids64.astype(np.float32))
+        self.thresholds = np.ascontiguousarray(self.thresholds64.astype(np.float32))
+
+    @classmethod
+    def get(cls, head_dim: int, bits: int) -> "Codebook":
+        key = (int(head_dim), int(bits))
+        if key not in _CODEBOOKS:
+            _CODEBOOKS[key] = cls(*key)
+        return _CODEBOOKS[key]
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def _stream_handle(stream) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+@dataclass
+class SideSpec:
+    mode: str = "packed"   # "fp16" | "packed" | "delegated"
+    bits: int = 4
+    hot: int = 256
+
+
+class TQCache:
+    """One layer's cache in device memory plus its C descriptor.
+
+    Layouts (all contiguous): codes [B][Hkv][cap][W] int32 (uint32 bits),
+    norms [B][Hkv][cap] fp32, fp16 rows [B][Hkv][cap][d], delegated ring
+    [B][Hkv][hot][d].  Buffers start zeroed.
+    """
+
+    def __init__(self, batch, kv_heads, head_dim, capacity, k: SideSpec, v: SideSpec,
+                 seed: int = 0, device="cuda"):
+        import torch
+        self.batch, self.kv_heads, self.head_dim = int(batch), int(kv_heads), int(head_dim)
+        self.capacity, self.seed = int(capacity), int(seed)
+        self.k_spec, self.v_spec = k, v
+        self.device = device
+        self._keep = []
+        self.desc = tq_cache()
+        self.desc.batch, self.desc.kv_heads = self.batch, self.kv_heads
+        self.desc.head_dim, self.desc.capacity = self.head_dim, self.capacity
+        self.desc.seed = self.seed
+        self.tensors = {}
+        for name, spec, side in (("k", k, self.desc.k), ("v", v, self.desc.v)):
+            side.mode = _MODES[spec.mode]
+            side.bits = int(spec.bits) if spec.mode != "fp16" else 0
+            side.hot = int(spec.hot) if spec.mode == "delegated" else 0
+            B, H, cap, d = self.batch, self.kv_heads, self.capacity, self.head_dim
+            if spec.mode in ("packed", "delegated"):
+                cb = Codebook.get(d, spec.bits)
+                self._keep.append(cb)
+                side.centroids = cb.centroids.ctypes.data
+                side.thresholds = cb.thresholds.ctypes.data
+                W = row_words(d, spec.bits)
+                codes = torch.zeros((B, H, cap, W), dtype=torch.int32, device=device)
+                norms = torch.zeros((B, H, cap), dtype=torch.float32, device=device)
+                side.codes, side.norms = _ptr(codes), _ptr(norms)
+                self.tensors[name + "_codes"] = codes
+                self.tensors[name + "_norms"] = norms
+            if spec.mode == "fp16":
+                rows = torch.zeros((B, H, cap, d), dtype=torch.float16, device=device)
+                side.fp16 = _ptr(rows)
+                self.tensors[name + "_fp16"] = rows
+            if spec.mode == "delegated":
+                ring = torch.zeros((B, H, spec.hot, d), dtype=torch.float16, device=device)
+                side.fp16 = _ptr(ring)
+                self.tensors[name + "_ring"] = ring
+        self._ws = None
+
+    # -- the four operations ------------------------------------------------
+    def quantize_append(self, k_new, v_new, offset: int, stream=None):
+        """k_new, v_new: fp16 [B][Hkv][n][d] on the device."""
+        for x in (k_new, v_new):
+            self._check_rows(x)
+        n = int(k_new.shape[2])
+        if int(v_new.shape[2]) != n:
+            raise ValueError("k_new and v_new differ in length")
+        _check(lib().tq_quantize_append(ctypes.byref(self.desc), _ptr(k_new), _ptr(v_new), n,
+                                        int(offset), _stream_handle(stream)),
+               "tq_quantize_append")
+
+    def workspace_bytes(self, q_heads: int, length: int, n_splits: int = 0) -> int:
+        return int(lib().tq_decode_workspace_bytes(ctypes.byref(self.desc), int(q_heads),
+                                                   int(length), int(n_splits)))
+
+    def workspace(self, q_heads: int, length: int, n_splits: int = 0):
+        import torch
+        need = self.workspace_bytes(q_heads, length, n_splits)
+        if need == 0:
+            raise TQError(TQ_ERR_ARG, "tq_decode_workspace_bytes")
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.zeros(need, dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def decode_attention(self, q, length: int, n_splits: int = 0, out=None, scores=False,
+                         workspace=None, stream=None):
+        """q: fp16 [B][Hq][d].  Returns out fp32 [B][Hq][d] (and scores
+        fp32 [B][Hq][length] when ``scores`` is true)."""
+        import torch
+        if q.dtype != torch.float16 or not q.is_contiguous() or q.dim() != 3:
+            raise ValueError("q must be contiguous fp16 [B, Hq, d]")
+        B, Hq, d = q.shape
+        if B != self.batch or d != self.head_dim:
+            raise ValueError("q shape does not match the cache")
+        if out is None:
+            out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+        sc = torch.empty((B, Hq, max(int(length), 1)), dtype=torch.float32, device=q.device) if scores else None
+        ws = workspace if workspace is not None else self.workspace(Hq, length, n_splits)
+        _check(lib().tq_decode_attention(ctypes.byref(self.desc), _ptr(q), int(Hq), int(length),
+                                         int(n_splits), _ptr(out), _ptr(sc), _ptr(ws),
+                                         ws.numel() * ws.element_size(), _stream_handle(stream)),
+               "tq_decode_attention")
+        return (out, sc[:, :, :length]) if scores else out
+
+    def dequantize(self, side: str, start: int, count: int, stream=None):
+        import torch
+        out = torch.empty((self.batch, self.kv_heads, max(int(count), 1), self.head_dim),
+                          dtype=torch.float32, device=self.device)
+        _check(lib().tq_dequantize(ctypes.byref(self.desc), 0 if side == "k" else 1, int(start),
+                                   int(count), _ptr(out), _stream_handle(stream)),
+               "tq_dequantize")
+        return out[:, :, :count]
+
+    def _check_rows(self, x):
+        import torch
+        if x.dtype != torch.float16 or not x.is_contiguous() or x.dim() != 4:
+            raise ValueError("new rows must be contiguous fp16 [B, Hkv, n, d]")
+        if (x.shape[0], x.shape[1], x.shape[3]) != (self.batch, self.kv_heads, self.head_dim):
+            raise ValueError("new rows do not match the cache shape")
+
+
+__all__ = [
+    "TQError", "tq_side", "tq_cache", "lib", "status_string", "split_bits", "row_words",
+    "sign_words", "build_codebook", "Codebook", "SideSpec", "TQCache", "SIDE_FP16",
+    "SIDE_PACKED", "SIDE_DELEGATED",
+]

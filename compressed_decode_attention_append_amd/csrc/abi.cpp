@@ -1,0 +1,258 @@
+// C ABI of libtq: argument validation, rotation signs, parameter blocks and
+// kernel dispatch.  Every check runs on the host before any HIP call, so an
+// invalid call launches nothing and writes nothing.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "tq.h"
+#include "tq_common.h"
+
+namespace tq {
+hipError_t launch_decode_ref(const DecodeParams &p, hipStream_t stream);
+}
+
+namespace {
+
+bool head_dim_ok(int d) { return d == 32 || d == 64 || d == 128 || d == 256; }
+
+int words_of(int d, int bits) { return (bits * d + 31) / 32; }
+
+// SplitMix64 (Steele, Lea and Flood, OOPSLA 2014): add the golden-ratio
+// increment to the state, then two xor-shift-multiply rounds and a final
+// xor-shift give the output.
+uint64_t splitmix64_next(uint64_t &state) {
+  state += 0x9E3779B97F4A7C15ull;
+  uint64_t z = state;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+void fill_signs(uint64_t seed, int d, uint32_t *words) {
+  uint64_t state = seed;
+  for (int w = 0; w < tq::kMaxSignWords; ++w) words[w] = 0;
+  for (int j = 0; j < d; ++j) {
+    if (splitmix64_next(state) >> 63) words[j >> 5] |= 1u << (j & 31);
+  }
+}
+
+int check_side(const tq_side &s, bool is_v) {
+  switch (s.mode) {
+    case TQ_SIDE_FP16:
+      return s.fp16 ? TQ_OK : TQ_ERR_ARG;
+    case TQ_SIDE_PACKED:
+    case TQ_SIDE_DELEGATED:
+      if (s.mode == TQ_SIDE_DELEGATED && !is_v) return TQ_ERR_MODE;
+      if (s.bits < TQ_MIN_BITS || s.bits > TQ_MAX_BITS) return TQ_ERR_BITS;
+      if (!s.codes || !s.norms || !s.centroids || !s.thresholds) return TQ_ERR_ARG;
+      if (s.mode == TQ_SIDE_DELEGATED && (s.hot < 1 || !s.fp16)) return TQ_ERR_ARG;
+      return TQ_OK;
+    default:
+      return TQ_ERR_MODE;
+  }
+}
+
+int check_cache(const tq_cache *c) {
+  if (!c) return TQ_ERR_ARG;
+  if (!head_dim_ok(c->head_dim)) return TQ_ERR_HEAD_DIM;
+  if (c->batch < 1 || c->kv_heads < 1 || c->capacity < 0) return TQ_ERR_ARG;
+  if (static_cast<long long>(c->batch) * c->kv_heads > 65535) return TQ_ERR_ARG;
+  int r = check_side(c->k, false);
+  if (r != TQ_OK) return r;
+  return check_side(c->v, true);
+}
+
+tq::SideDev side_dev(const tq_side &s, int d) {
+  tq::SideDev o;
+  o.mode = s.mode;
+  o.bits = (s.mode == TQ_SIDE_FP16) ? 0 : s.bits;
+  o.words = (s.mode == TQ_SIDE_FP16) ? 0 : words_of(d, s.bits);
+  o.hot = s.hot;
+  o.codes = s.codes;
+  o.norms = s.norms;
+  o.fp16 = s.fp16;
+  return o;
+}
+
+void copy_levels(const tq_side &s, const float *src, int n, float *dst) {
+  for (int i = 0; i < tq::kMaxLevels; ++i) dst[i] = 0.0f;
+  if (s.mode != TQ_SIDE_FP16 && src) memcpy(dst, src, sizeof(float) * n);
+}
+
+// Context split of the plain decode: the block keeps G * (d + split) floats
+// in LDS, so the split length shrinks as the query group grows.
+int ref_max_split(int G, int d) {
+  const int budget = 16384 - 2 * tq::kMaxLevels - 4;
+  return budget / G - d;
+}
+
+bool choose_split(const tq_cache *c, int q_heads, int length, int n_splits, int *ns, int *sl) {
+  const int G = q_heads / c->kv_heads;
+  const int cap = ref_max_split(G, c->head_dim);
+  if (cap < 1) return false;
+  int split;
+  if (n_splits > 0) {
+    split = length > 0 ? (length + n_splits - 1) / n_splits : 1;
+    if (split > cap) return false;
+    *ns = n_splits;
+  } else {
+    split = std::min(cap, 1024);
+    split = split >= 64 ? split / 64 * 64 : split;
+    *ns = length > 0 ? (length + split - 1) / split : 1;
+  }
+  *sl = std::max(split, 1);
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *tq_status_string(int status) {
+  switch (status) {
+    case TQ_OK: return "ok";
+    case TQ_ERR_ARG: return "invalid argument";
+    case TQ_ERR_HEAD_DIM: return "head_dim must be a power of two in [32, 256]";
+    case TQ_ERR_BITS: return "bits must be in [1, 8]";
+    case TQ_ERR_CAPACITY: return "rows outside the cache capacity";
+    case TQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case TQ_ERR_MODE: return "unsupported side mode";
+    case TQ_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int tq_split_bits(double bits, int *k_bits, int *v_bits) {
+  if (!k_bits || !v_bits) return TQ_ERR_ARG;
+  if (!(bits == bits)) return TQ_ERR_BITS;
+  const double lo = floor(bits), hi = ceil(bits);
+  if (lo < TQ_MIN_BITS || hi > TQ_MAX_BITS) return TQ_ERR_BITS;
+  *k_bits = static_cast<int>(lo);
+  *v_bits = static_cast<int>(hi);
+  return TQ_OK;
+}
+
+int tq_row_words(int head_dim, int bits) {
+  if (!head_dim_ok(head_dim)) return TQ_ERR_HEAD_DIM;
+  if (bits < TQ_MIN_BITS || bits > TQ_MAX_BITS) return TQ_ERR_BITS;
+  return words_of(head_dim, bits);
+}
+
+int tq_sign_words(uint64_t seed, int head_dim, uint32_t *sign_words) {
+  if (!sign_words) return TQ_ERR_ARG;
+  if (!head_dim_ok(head_dim)) return TQ_ERR_HEAD_DIM;
+  uint32_t w[tq::kMaxSignWords];
+  fill_signs(seed, head_dim, w);
+  memcpy(sign_words, w, sizeof(uint32_t) * (head_dim / 32));
+  return TQ_OK;
+}
+
+int tq_quantize_append(const tq_cache *cache, const void *k_new, const void *v_new, int n_new,
+                       int offset, void *hip_stream) {
+  int r = check_cache(cache);
+  if (r != TQ_OK) return r;
+  if (n_new < 0) return TQ_ERR_ARG;
+  if (offset < 0 || static_cast<long long>(offset) + n_new > cache->capacity) return TQ_ERR_CAPACITY;
+  if (n_new == 0) return TQ_OK;
+  if (!k_new || !v_new) return TQ_ERR_ARG;
+
+  tq::QuantizeParams p;
+  memset(&p, 0, sizeof(p));
+  const int d = cache->head_dim;
+  p.k = side_dev(cache->k, d);
+  p.v = side_dev(cache->v, d);
+  p.k_new = static_cast<const uint16_t *>(k_new);
+  p.v_new = static_cast<const uint16_t *>(v_new);
+  p.batch = cache->batch;
+  p.heads = cache->kv_heads;
+  p.head_dim = d;
+  p.capacity = cache->capacity;
+  p.n_new = n_new;
+  p.offset = offset;
+  fill_signs(cache->seed, d, p.sign);
+  copy_levels(cache->k, cache->k.thresholds, (1 << cache->k.bits) - 1, p.k_thr);
+  copy_levels(cache->v, cache->v.thresholds, (1 << cache->v.bits) - 1, p.v_thr);
+  const hipError_t e = tq::launch_quantize_append(p, static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
+size_t tq_decode_workspace_bytes(const tq_cache *cache, int q_heads, int length, int n_splits) {
+  if (check_cache(cache) != TQ_OK) return 0;
+  if (q_heads < cache->kv_heads || q_heads % cache->kv_heads) return 0;
+  if (length < 0 || length > cache->capacity || n_splits < 0) return 0;
+  int ns = 0, sl = 0;
+  if (!choose_split(cache, q_heads, length, n_splits, &ns, &sl)) return 0;
+  return tq::decode_workspace_layout(cache->batch, q_heads, ns, cache->head_dim).total;
+}
+
+int tq_decode_attention(const tq_cache *cache, const void *q, int q_heads, int length, int n_splits,
+                        float *out, float *scores, void *workspace, size_t workspace_bytes,
+                        void *hip_stream) {
+  int r = check_cache(cache);
+  if (r != TQ_OK) return r;
+  if (!q || !out) return TQ_ERR_ARG;
+  if (q_heads < cache->kv_heads || q_heads % cache->kv_heads) return TQ_ERR_ARG;
+  if (n_splits < 0) return TQ_ERR_ARG;
+  if (length < 0 || length > cache->capacity) return TQ_ERR_CAPACITY;
+  int ns = 0, sl = 0;
+  if (!choose_split(cache, q_heads, length, n_splits, &ns, &sl)) return TQ_ERR_ARG;
+  const tq::DecodeWorkspace lay = tq::decode_workspace_layout(cache->batch, q_heads, ns, cache->head_dim);
+  if (!workspace || workspace_bytes < lay.total ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return TQ_ERR_WORKSPACE;
+
+  tq::DecodeParams p;
+  memset(&p, 0, sizeof(p));
+  const int d = cache->head_dim;
+  p.k = side_dev(cache->k, d);
+  p.v = side_dev(cache->v, d);
+  p.q = static_cast<const uint16_t *>(q);
+  p.out = out;
+  p.scores = scores;
+  p.ws = static_cast<float *>(workspace);
+  p.batch = cache->batch;
+  p.kv_heads = cache->kv_heads;
+  p.q_heads = q_heads;
+  p.head_dim = d;
+  p.capacity = cache->capacity;
+  p.length = length;
+  p.n_splits = ns;
+  p.split_len = sl;
+  fill_signs(cache->seed, d, p.sign);
+  copy_levels(cache->k, cache->k.centroids, 1 << cache->k.bits, p.k_cent);
+  copy_levels(cache->v, cache->v.centroids, 1 << cache->v.bits, p.v_cent);
+  const hipError_t e = tq::launch_decode_ref(p, static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
+int tq_dequantize(const tq_cache *cache, int side, int start, int count, float *out,
+                  void *hip_stream) {
+  int r = check_cache(cache);
+  if (r != TQ_OK) return r;
+  if (side != 0 && side != 1) return TQ_ERR_ARG;
+  const tq_side &s = side ? cache->v : cache->k;
+  if (s.mode == TQ_SIDE_FP16) return TQ_ERR_MODE;
+  if (start < 0 || count < 0 || static_cast<long long>(start) + count > cache->capacity)
+    return TQ_ERR_CAPACITY;
+  if (count == 0) return TQ_OK;
+  if (!out) return TQ_ERR_ARG;
+  tq::DequantParams p;
+  memset(&p, 0, sizeof(p));
+  const int d = cache->head_dim;
+  p.s = side_dev(s, d);
+  p.out = out;
+  p.batch = cache->batch;
+  p.heads = cache->kv_heads;
+  p.head_dim = d;
+  p.capacity = cache->capacity;
+  p.start = start;
+  p.count = count;
+  fill_signs(cache->seed, d, p.sign);
+  copy_levels(s, s.centroids, 1 << s.bits, p.cent);
+  const hipError_t e = tq::launch_dequantize(p, static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,83 @@
+// Shared host/device definitions of libtq: kernel parameter blocks and the
+// launchers each kernel file provides.  Internal; the public ABI is tq.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tq.h"
+
+namespace tq {
+
+constexpr int kMaxLevels = 1 << TQ_MAX_BITS;   // 256 centroids, 255 thresholds
+constexpr int kMaxSignWords = TQ_MAX_HEAD_DIM / 32;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Device view of one side of a cache.
+struct SideDev {
+  int mode;        // TQ_SIDE_*
+  int bits;        // code width (packed / delegated)
+  int words;       // uint32 words per packed row
+  int hot;         // delegated ring length
+  uint32_t *codes; // [B][H][cap][words]
+  float *norms;    // [B][H][cap]
+  uint16_t *fp16;  // fp16 rows (FP16) or hot ring (DELEGATED)
+};
+
+struct QuantizeParams {
+  SideDev k, v;
+  const uint16_t *k_new;  // [B][H][n_new][d] fp16
+  const uint16_t *v_new;
+  int batch, heads, head_dim, capacity, n_new, offset;
+  uint32_t sign[kMaxSignWords];  // bit j set: s_j = -1
+  float k_thr[kMaxLevels];       // thresholds (L-1 used)
+  float v_thr[kMaxLevels];
+};
+
+struct DequantParams {
+  SideDev s;
+  float *out;  // [B][H][count][d]
+  int batch, heads, head_dim, capacity, start, count;
+  uint32_t sign[kMaxSignWords];
+  float cent[kMaxLevels];
+};
+
+struct DecodeParams {
+  SideDev k, v;
+  const uint16_t *q;  // [B][Hq][d] fp16
+  float *out;         // [B][Hq][d]
+  float *scores;      // [B][Hq][length] or null
+  float *ws;          // workspace (partials)
+  int batch, kv_heads, q_heads, head_dim, capacity, length, n_splits, split_len;
+  uint32_t sign[kMaxSignWords];
+  float k_cent[kMaxLevels];
+  float v_cent[kMaxLevels];
+};
+
+// Workspace layout of the decode (floats, each region 256-byte aligned):
+//   ml   [B*Hq][n_splits][2]   running max (log2 domain) and sum
+//   orot [B*Hq][n_splits][d]   rotated-domain value accumulator (packed V)
+//   ohot [B*Hq][n_splits][d]   original-domain accumulator (fp16 V rows)
+struct DecodeWorkspace {
+  size_t ml_off, orot_off, ohot_off, total;  // in bytes
+};
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+__host__ __device__ inline DecodeWorkspace decode_workspace_layout(int batch, int q_heads,
+                                               int n_splits, int head_dim) {
+  DecodeWorkspace w;
+  const size_t units = size_t(batch) * q_heads * n_splits;
+  w.ml_off = 0;
+  w.orot_off = align256(units * 2 * sizeof(float));
+  w.ohot_off = w.orot_off + align256(units * head_dim * sizeof(float));
+  w.total = w.ohot_off + align256(units * head_dim * sizeof(float));
+  return w;
+}
+
+hipError_t launch_quantize_append(const QuantizeParams &p, hipStream_t stream);
+hipError_t launch_dequantize(const DequantParams &p, hipStream_t stream);
+hipError_t launch_decode_ref(const DecodeParams &p, hipStream_t stream);
+
+}  // namespace tq

@@ -1,0 +1,75 @@
+// Device helpers shared by the libtq kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tq {
+
+__device__ __forceinline__ float h2f(uint16_t bits) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, bits));
+}
+
+__device__ __forceinline__ uint16_t f2h(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+}
+
+// Sign s_j of the rotation (+1 / -1) from the packed sign words.
+__device__ __forceinline__ float sign_of(const uint32_t *sign, int j) {
+  return ((sign[j >> 5] >> (j & 31)) & 1u) ? -1.0f : 1.0f;
+}
+
+// Walsh-Hadamard butterflies over one row held by a group of TPR lanes, four
+// consecutive elements per lane (lane t of the group holds elements
+// 4t .. 4t+3).  Strides 1 and 2 are inside the lane, strides 4, 8, ... pair
+// lane t with lane t ^ (stride / 4).  Butterfly (a, b) -> (a + b, a - b),
+// strides in increasing order: the natural-order Sylvester transform.
+template <int TPR>
+__device__ __forceinline__ void fwht_group4(float (&v)[4], int t) {
+  const float a0 = v[0] + v[1], a1 = v[0] - v[1];
+  const float a2 = v[2] + v[3], a3 = v[2] - v[3];
+  v[0] = a0 + a2;
+  v[2] = a0 - a2;
+  v[1] = a1 + a3;
+  v[3] = a1 - a3;
+#pragma unroll
+  for (int m = 1; m < TPR; m <<= 1) {
+    const bool upper = (t & m) != 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float o = __shfl_xor(v[e], m);
+      v[e] = upper ? (o - v[e]) : (v[e] + o);
+    }
+  }
+}
+
+// Sum over the TPR lanes of a group (all lanes receive the total).
+template <int TPR>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+  for (int m = 1; m < TPR; m <<= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+// Number of thresholds strictly below y: branch-free binary search over the
+// ascending array thr[0 .. 2^bits - 2].
+__device__ __forceinline__ int count_below(const float *thr, int bits, float y) {
+  int code = 0;
+  for (int s = bits - 1; s >= 0; --s) {
+    const int cand = code + (1 << s);
+    code = (y > thr[cand - 1]) ? cand : code;
+  }
+  return code;
+}
+
+// Extract code j (bits wide) from a packed LSB-first row.
+__device__ __forceinline__ uint32_t extract_code(const uint32_t *row, int bits, int j) {
+  const int o = bits * j;
+  const int w = o >> 5;
+  const int sh = o & 31;
+  uint32_t v = row[w] >> sh;
+  if (sh + bits > 32) v |= row[w + 1] << (32 - sh);
+  return v & ((1u << bits) - 1u);
+}
+
+}  // namespace tq

@@ -1,0 +1,184 @@
+/*
+ * tq.h -- C ABI of libtq: TurboQuant KV-cache quantize-append and decode
+ * attention computed from the packed cache, for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (source pages: "TurboQuant KV Cache Quantization
+ * in MLX-VLM", sections "The TurboQuantKVCache Class", "Quantization Codecs
+ * and Bit Splitting", "How TurboQuant KV Cache Quantization Works" and the FAQ
+ * on dequantization; "How to Use TurboQuant with the MLX-VLM CLI", section
+ * "What Is TurboQuant?"; mlxcel "TurboQuant KV cache", sections "Available
+ * modes" and "WHT head-dimension constraint"):
+ *
+ *   quantize   x (fp16, d values) -> n = ||x||_2 (fp32, one per token-head),
+ *              y = H diag(s) x / (n sqrt(d)) with H the Sylvester Hadamard
+ *              matrix and s a seeded sign vector, code_j = #{k : y_j > t_k}
+ *              for the Lloyd-Max thresholds t of the coordinate pdf, packed
+ *              LSB-first into uint32 words (code j at bits [b j, b j + b) of
+ *              the row; word w holds bits [32 w, 32 w + 32)).
+ *   dequantize x~ = n diag(s) H c[code] / sqrt(d).
+ *   decode     out_h = softmax(q_h . K~^T / sqrt(d)) V~ for one query token
+ *              per sequence, query head h reading KV head floor(h / G).
+ *
+ * Readings where the pages are silent: signs from SplitMix64 (sign j is
+ * negative when the top bit of output j is set); one rotation per cache,
+ * shared by K and V; ties go to the lower code; a zero row stores n = 0 and
+ * codes L/2 - 1; no causal mask inside the attended length.
+ *
+ * Conventions for every entry point:
+ *   - Status: 0 (TQ_OK) or a negative TQ_ERR_* code, returned synchronously.
+ *     On any error nothing is launched and no caller memory is written.
+ *   - Device pointers are caller-owned HIP device memory; the library never
+ *     allocates, frees or synchronises.  Host pointers are read during the
+ *     call only.
+ *   - Work is enqueued on `hip_stream` (a hipStream_t; NULL = the null
+ *     stream).  Results are visible after the caller synchronises the stream.
+ *   - Layouts are dense, row-major, innermost index last.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+  TQ_OK = 0,
+  TQ_ERR_ARG = -1,       /* null pointer, negative size, bad q_heads, ...  */
+  TQ_ERR_HEAD_DIM = -2,  /* head_dim not a power of two in [32, 256]
+                            ("WHT head-dimension constraint": no padding)   */
+  TQ_ERR_BITS = -3,      /* packed side with bits outside [1, 8]            */
+  TQ_ERR_CAPACITY = -4,  /* rows outside [0, capacity)                      */
+  TQ_ERR_WORKSPACE = -5, /* workspace missing or smaller than required      */
+  TQ_ERR_MODE = -6,      /* unsupported side mode or mode combination       */
+  TQ_ERR_HIP = -7        /* the HIP runtime reported a launch error         */
+};
+
+/* How one side (K or V) of a cache is stored ("Available modes": fp16 K with
+ * TurboQuant V, TurboQuant K and V, and the delegated hot/cold V split). */
+enum {
+  TQ_SIDE_FP16 = 0,      /* plain fp16 rows                                 */
+  TQ_SIDE_PACKED = 1,    /* TurboQuant codes + fp32 norms                   */
+  TQ_SIDE_DELEGATED = 2  /* V only: newest `hot` tokens fp16 in a ring
+                            (slot = position mod hot), older tokens packed  */
+};
+
+#define TQ_MIN_BITS 1
+#define TQ_MAX_BITS 8
+#define TQ_MIN_HEAD_DIM 32
+#define TQ_MAX_HEAD_DIM 256
+
+/* Bit split of a (possibly fractional) budget: keys get floor(bits), values
+ * ceil(bits) ("Quantization Codecs and Bit Splitting").  Returns TQ_ERR_BITS
+ * unless 1 <= floor(bits) and ceil(bits) <= 8; TQ_ERR_ARG on null outputs. */
+int tq_split_bits(double bits, int *k_bits, int *v_bits);
+
+/* uint32 words per packed row: ceil(bits * head_dim / 32).  Returns the count
+ * (> 0), or TQ_ERR_HEAD_DIM / TQ_ERR_BITS. */
+int tq_row_words(int head_dim, int bits);
+
+/* Sign vector of the rotation for `seed`: bit j of sign_words[j / 32] is set
+ * when s_j = -1.  sign_words must hold head_dim / 32 words (host memory).
+ * ("How TurboQuant KV Cache Quantization Works": random Hadamard transform;
+ * SplitMix64 of Steele, Lea and Flood (2014) is the sign source.) */
+int tq_sign_words(uint64_t seed, int head_dim, uint32_t *sign_words);
+
+/* Lloyd-Max codebook for one coordinate of a uniform unit vector in
+ * R^head_dim, whose density is proportional to (1 - x^2)^((head_dim - 3)/2)
+ * (the "Beta-PDF Lloyd-Max quantizer").  Host only, deterministic, double
+ * precision; takes milliseconds for bits <= 5 and up to seconds for 8 bits,
+ * so build once per (head_dim, bits) and keep the result.
+ *   centroids:  [1 << bits], ascending, antisymmetric (c_k = -c_{L-1-k}).
+ *   thresholds: [(1 << bits) - 1], midpoints of neighbouring centroids; the
+ *               middle one is exactly 0.
+ * head_dim must be a power of two in [2, 65536] here (the quantizer itself
+ * only accepts [32, 256]). */
+int tq_build_codebook(int head_dim, int bits, double *centroids,
+                      double *thresholds);
+
+/* One side of one layer's cache.  All buffers are caller-owned. */
+typedef struct tq_side {
+  int mode;                /* TQ_SIDE_*                                       */
+  int bits;                /* PACKED / DELEGATED: code width in [1, 8]        */
+  const float *centroids;  /* HOST fp32 [1 << bits]: the side's codebook,
+                              normally tq_build_codebook rounded to fp32      */
+  const float *thresholds; /* HOST fp32 [(1 << bits) - 1]                     */
+  uint32_t *codes;         /* DEVICE [B][Hkv][capacity][row_words]           */
+  float *norms;            /* DEVICE [B][Hkv][capacity]                      */
+  uint16_t *fp16;          /* DEVICE fp16 bits: FP16 -> [B][Hkv][capacity][d];
+                              DELEGATED -> hot ring [B][Hkv][hot][d]          */
+  int hot;                 /* DELEGATED: ring length (>= 1)                   */
+} tq_side;
+
+/* One layer's cache.  K may be FP16 or PACKED; V may be FP16, PACKED or
+ * DELEGATED.  `seed` selects the rotation shared by both sides. */
+typedef struct tq_cache {
+  int batch;
+  int kv_heads;
+  int head_dim;
+  int capacity;  /* positions per (batch, kv head) */
+  uint64_t seed;
+  tq_side k;
+  tq_side v;
+} tq_cache;
+
+/* Quantize-append ("update_and_fetch" of the TurboQuantKVCache; one launch
+ * handles K and V, as the fused quantize path does).
+ * k_new, v_new: DEVICE fp16 [B][Hkv][n_new][d].  Writes positions
+ * [offset, offset + n_new) of each side and nothing else:
+ *   PACKED    -> codes/norms rows at those positions;
+ *   FP16      -> fp16 rows at those positions;
+ *   DELEGATED -> for each new position p, the ring slot p mod hot is first
+ *                evicted (its previous occupant, position p - hot, is
+ *                quantized into the packed cold rows) and then overwritten;
+ *                new positions that are already older than the newest `hot`
+ *                go straight to the cold rows.  Positions must be appended
+ *                in order (offset = current length) for the ring to hold the
+ *                newest tokens.
+ * Errors: TQ_ERR_CAPACITY if offset < 0 or offset + n_new > capacity.
+ * n_new = 0 is a no-op returning TQ_OK. */
+int tq_quantize_append(const tq_cache *cache, const void *k_new,
+                       const void *v_new, int n_new, int offset,
+                       void *hip_stream);
+
+/* Bytes of workspace tq_decode_attention needs for this shape (0 on invalid
+ * arguments).  n_splits = 0 picks the library's split of the context. */
+size_t tq_decode_workspace_bytes(const tq_cache *cache, int q_heads,
+                                 int length, int n_splits);
+
+/* Decode attention over positions [0, length) straight from the packed cache
+ * ("How TurboQuant KV Cache Quantization Works": scores from the compressed
+ * representation).  Packed K is scored as n_i <R q, c[code_i]>; packed V is
+ * accumulated in the rotated domain and rotated back once per output head.
+ *   q:      DEVICE fp16 [B][q_heads][d]; q_heads a multiple of kv_heads.
+ *   out:    DEVICE fp32 [B][q_heads][d].
+ *   scores: DEVICE fp32 [B][q_heads][length] or NULL; when given, receives
+ *           the scaled logits q . k~ / sqrt(d).
+ *   workspace: DEVICE, >= tq_decode_workspace_bytes(...), 256-byte aligned.
+ *           It holds per-split partial results; calls that share a workspace
+ *           must not overlap.
+ *   n_splits: 0 = automatic, else the number of context splits (>= 1).
+ * length = 0 writes zeros to out. */
+int tq_decode_attention(const tq_cache *cache, const void *q, int q_heads,
+                        int length, int n_splits, float *out, float *scores,
+                        void *workspace, size_t workspace_bytes,
+                        void *hip_stream);
+
+/* Dequantize packed rows [start, start + count) of one side (0 = K, 1 = V;
+ * for a DELEGATED V this reads the packed cold rows) into DEVICE fp32
+ * out[B][Hkv][count][d] (the FAQ's "dequantize" back to float32).  A check
+ * path; FP16 sides return TQ_ERR_MODE. */
+int tq_dequantize(const tq_cache *cache, int side, int start, int count,
+                  float *out, void *hip_stream);
+
+/* Static description of a status code. */
+const char *tq_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

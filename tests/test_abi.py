@@ -1,0 +1,188 @@
+"""Host-side tests of the C ABI (no GPU needed): every symbol the header
+declares is exported, the host helpers agree with the oracle, and every
+error path is taken before anything is launched."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import compressed_decode_attention_append_amd as tq
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "tq.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(tq_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert len(names) >= 9
+    L = tq.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    for s in range(0, -8, -1):
+        assert tq.status_string(s) not in ("", "unknown status")
+    assert tq.status_string(-99) == "unknown status"
+
+
+def test_split_bits_and_row_words():
+    assert tq.split_bits(3.5) == oracle.split_bits(3.5) == (3, 4)
+    assert tq.split_bits(4.2) == (4, 5)
+    assert tq.split_bits(8) == (8, 8)
+    for bad in (0.5, 8.5, 9, float("nan")):
+        with pytest.raises(tq.TQError):
+            tq.split_bits(bad)
+    for d in (32, 64, 128, 256):
+        for b in range(1, 9):
+            assert tq.row_words(d, b) == oracle.row_words(d, b)
+    with pytest.raises(tq.TQError):
+        tq.row_words(80, 4)
+    with pytest.raises(tq.TQError):
+        tq.row_words(128, 9)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 12345, 2**63 + 17])
+@pytest.mark.parametrize("d", [32, 64, 128, 256])
+def test_sign_words_match_oracle(seed, d):
+    w = tq.sign_words(seed, d)
+    bits = np.array([(int(w[j // 32]) >> (j % 32)) & 1 for j in range(d)])
+    want = (oracle.sign_vector(seed, d) < 0).astype(int)
+    assert np.array_equal(bits, want)
+
+
+@pytest.mark.parametrize("d", [32, 64, 128, 256, 1024])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5])
+def test_codebook_builder_matches_oracle(d, bits):
+    c, t = tq.build_codebook(d, bits)
+    co, to = oracle.lloyd_max(d, bits)
+    tol = 2e-12 if (d <= 256 and bits <= 4) else 1e-10
+    assert np.max(np.abs(c - co)) <= tol * max(1.0, np.max(np.abs(co)) * 0 + 1.0)
+    assert np.max(np.abs(t - to)) <= tol
+    assert t[(1 << bits) // 2 - 1] == 0.0
+    assert np.array_equal(c, -c[::-1])
+    # the fp32 copies the kernels use agree to within one fp32 ulp
+    assert np.all(np.abs(c.astype(np.float32) - co.astype(np.float32)) <= np.spacing(np.abs(co).astype(np.float32)))
+
+
+def test_codebook_builder_six_bits():
+    c, t = tq.build_codebook(128, 6)
+    co, to = oracle.lloyd_max(128, 6)
+    assert np.max(np.abs(c - co)) <= 1e-10
+
+
+def test_codebook_builder_rejects():
+    with pytest.raises(tq.TQError):
+        tq.build_codebook(128, 0)
+    with pytest.raises(tq.TQError):
+        tq.build_codebook(96, 3)
+
+
+# ---- error paths: nothing is launched ------------------------------------
+
+class _Fake:
+    """Host buffers standing in for device pointers; never dereferenced on
+    the error paths exercised here."""
+
+    def __init__(self):
+        self.buf = np.zeros(1 << 16, np.uint8)
+        self.c = np.zeros(256, np.float32)
+
+    def p(self, off=0):
+        return self.buf.ctypes.data + off
+
+
+def _desc(f, d=128, kmode=1, vmode=1, kb=3, vb=4, hot=256, cap=1024, B=2, H=4):
+    c = tq.tq_cache()
+    c.batch, c.kv_heads, c.head_dim, c.capacity, c.seed = B, H, d, cap, 0
+    for side, mode, bits in ((c.k, kmode, kb), (c.v, vmode, vb)):
+        side.mode, side.bits, side.hot = mode, bits, hot
+        side.centroids = f.c.ctypes.data
+        side.thresholds = f.c.ctypes.data
+        side.codes, side.norms, side.fp16 = f.p(0), f.p(256), f.p(512)
+    return c
+
+
+def _qa(c, f, n=4, off=0):
+    return tq.lib().tq_quantize_append(ctypes.byref(c), f.p(1024), f.p(2048), n, off, None)
+
+
+def _dec(c, f, Hq=8, length=100, ns=0, ws_bytes=1 << 30, ws_off=0, q=True, out=True):
+    return tq.lib().tq_decode_attention(ctypes.byref(c), f.p(4096) if q else None, Hq, length, ns,
+                                        f.p(8192) if out else None, None, f.p(ws_off) if ws_bytes else None,
+                                        ws_bytes, None)
+
+
+def test_quantize_append_errors():
+    f = _Fake()
+    assert _qa(_desc(f, d=96), f) == tq.TQ_ERR_HEAD_DIM
+    assert _qa(_desc(f, d=512), f) == tq.TQ_ERR_HEAD_DIM
+    assert _qa(_desc(f, kb=0), f) == tq.TQ_ERR_BITS
+    assert _qa(_desc(f, vb=9), f) == tq.TQ_ERR_BITS
+    assert _qa(_desc(f, kmode=2), f) == tq.TQ_ERR_MODE   # delegated K
+    assert _qa(_desc(f, vmode=7), f) == tq.TQ_ERR_MODE
+    assert _qa(_desc(f, vmode=2, hot=0), f) == tq.TQ_ERR_ARG
+    assert _qa(_desc(f), f, n=-1) == tq.TQ_ERR_ARG
+    assert _qa(_desc(f, cap=10), f, n=8, off=3) == tq.TQ_ERR_CAPACITY
+    assert _qa(_desc(f), f, n=1, off=-1) == tq.TQ_ERR_CAPACITY
+    c = _desc(f)
+    c.k.codes = None
+    assert _qa(c, f) == tq.TQ_ERR_ARG
+    c = _desc(f, kmode=0)
+    c.k.fp16 = None
+    assert _qa(c, f) == tq.TQ_ERR_ARG
+    c = _desc(f)
+    c.v.centroids = None
+    assert _qa(c, f) == tq.TQ_ERR_ARG
+    c = _desc(f)
+    c.batch = 0
+    assert _qa(c, f) == tq.TQ_ERR_ARG
+    assert tq.lib().tq_quantize_append(None, f.p(), f.p(), 1, 0, None) == tq.TQ_ERR_ARG
+    assert tq.lib().tq_quantize_append(ctypes.byref(_desc(f)), None, f.p(), 1, 0, None) == tq.TQ_ERR_ARG
+    # n_new = 0 is a no-op, even with null rows
+    assert tq.lib().tq_quantize_append(ctypes.byref(_desc(f)), None, None, 0, 0, None) == tq.TQ_OK
+
+
+def test_decode_errors():
+    f = _Fake()
+    c = _desc(f)
+    assert _dec(c, f, Hq=6) == tq.TQ_ERR_ARG          # not a multiple of Hkv
+    assert _dec(c, f, Hq=2) == tq.TQ_ERR_ARG          # fewer than Hkv
+    assert _dec(c, f, length=2000) == tq.TQ_ERR_CAPACITY
+    assert _dec(c, f, length=-1) == tq.TQ_ERR_CAPACITY
+    assert _dec(c, f, ns=-1) == tq.TQ_ERR_ARG
+    assert _dec(c, f, q=False) == tq.TQ_ERR_ARG
+    assert _dec(c, f, out=False) == tq.TQ_ERR_ARG
+    need = tq.lib().tq_decode_workspace_bytes(ctypes.byref(c), 8, 100, 0)
+    assert need > 0
+    assert _dec(c, f, ws_bytes=need - 1) == tq.TQ_ERR_WORKSPACE
+    assert _dec(c, f, ws_bytes=0) == tq.TQ_ERR_WORKSPACE
+    assert tq.lib().tq_decode_workspace_bytes(ctypes.byref(c), 6, 100, 0) == 0
+    assert tq.lib().tq_decode_workspace_bytes(ctypes.byref(c), 8, 5000, 0) == 0
+    assert _dec(_desc(f, d=100), f) == tq.TQ_ERR_HEAD_DIM
+
+
+def test_decode_workspace_grows_with_splits():
+    f = _Fake()
+    c = _desc(f)
+    a = tq.lib().tq_decode_workspace_bytes(ctypes.byref(c), 8, 1000, 1)
+    b = tq.lib().tq_decode_workspace_bytes(ctypes.byref(c), 8, 1000, 4)
+    assert 0 < a < b
+    assert a % 256 == 0 and b % 256 == 0
+
+
+def test_dequantize_errors():
+    f = _Fake()
+    L = tq.lib()
+    assert L.tq_dequantize(ctypes.byref(_desc(f)), 2, 0, 1, f.p(), None) == tq.TQ_ERR_ARG
+    assert L.tq_dequantize(ctypes.byref(_desc(f, kmode=0)), 0, 0, 1, f.p(), None) == tq.TQ_ERR_MODE
+    assert L.tq_dequantize(ctypes.byref(_desc(f, cap=10)), 1, 5, 6, f.p(), None) == tq.TQ_ERR_CAPACITY
+    assert L.tq_dequantize(ctypes.byref(_desc(f)), 1, 0, 1, None, None) == tq.TQ_ERR_ARG
+    assert L.tq_dequantize(ctypes.byref(_desc(f)), 1, 0, 0, None, None) == tq.TQ_OK
