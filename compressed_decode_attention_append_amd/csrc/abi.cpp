@@ -2,16 +2,13 @@
 // kernel dispatch.  Every check runs on the host before any HIP call, so an
 // invalid call launches nothing and writes nothing.
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
 
 #include "tq.h"
 #include "tq_common.h"
-
-namespace tq {
-hipError_t launch_decode_ref(const DecodeParams &p, hipStream_t stream);
-}
 
 namespace {
 
@@ -106,6 +103,86 @@ bool choose_split(const tq_cache *c, int q_heads, int length, int n_splits, int 
   return true;
 }
 
+// Which decode runs: the matrix-core kernel when it supports the shape,
+// else the plain one.  TQ_DECODE_VARIANT=ref|mfma forces one (for A/B
+// measurements); forcing mfma on an unsupported shape falls back to ref.
+enum Variant { kRef, kMfma };
+
+Variant pick_variant(const tq::DecodeParams &p) {
+  const char *env = getenv("TQ_DECODE_VARIANT");
+  if (env && strcmp(env, "ref") == 0) return kRef;
+  return tq::decode_mfma_supported(p) ? kMfma : kRef;
+}
+
+// Splits of the matrix-core kernel: packed positions in n_cold splits of a
+// multiple of 128 positions (4 waves x 32), aiming at ~1024 blocks; the
+// fp16 hot window of a delegated V in one split of its own.
+void mfma_splits(const tq_cache *c, int length, int n_splits, tq::DecodeParams *p) {
+  const int units = c->batch * c->kv_heads;
+  const int cold = (c->v.mode == TQ_SIDE_DELEGATED) ? std::max(0, length - c->v.hot) : length;
+  const int hot = length - cold;
+  const int cap = tq::decode_mfma_max_splits() - (hot > 0 ? 1 : 0);
+  int ncold = 0, clen = 0;
+  if (cold > 0) {
+    if (n_splits > 0) {
+      ncold = std::min(std::min(n_splits, cold), cap);
+      clen = (cold + ncold - 1) / ncold;
+    } else {
+      const int want = std::max(1, std::min(std::min((1024 + units - 1) / units, (cold + 127) / 128), cap));
+      clen = ((cold + want - 1) / want + 127) / 128 * 128;
+    }
+    ncold = (cold + clen - 1) / clen;
+  }
+  p->cold_len = cold;
+  p->n_cold_splits = ncold;
+  p->cold_split_len = clen;
+  p->n_hot_splits = hot > 0 ? 1 : 0;
+  p->hot_split_len = hot;
+  if (ncold + p->n_hot_splits == 0) {
+    p->n_cold_splits = 1;  // empty context: one split that writes zeros
+    p->cold_split_len = 1;
+  }
+}
+
+void fill_decode_params(const tq_cache *cache, const void *q, int q_heads, int length,
+                        tq::DecodeParams *p) {
+  memset(p, 0, sizeof(*p));
+  const int d = cache->head_dim;
+  p->k = side_dev(cache->k, d);
+  p->v = side_dev(cache->v, d);
+  p->q = static_cast<const uint16_t *>(q);
+  p->batch = cache->batch;
+  p->kv_heads = cache->kv_heads;
+  p->q_heads = q_heads;
+  p->head_dim = d;
+  p->capacity = cache->capacity;
+  p->length = length;
+  fill_signs(cache->seed, d, p->sign);
+  copy_levels(cache->k, cache->k.centroids, 1 << cache->k.bits, p->k_cent);
+  copy_levels(cache->v, cache->v.centroids, 1 << cache->v.bits, p->v_cent);
+  p->share_lut = (cache->k.mode == TQ_SIDE_PACKED && cache->k.bits == 4 && cache->v.bits == 4 &&
+                  memcmp(p->k_cent, p->v_cent, sizeof(float) * 16) == 0)
+                     ? 1
+                     : 0;
+}
+
+// Workspace bytes the chosen variant needs (0 if the shape is invalid).
+size_t workspace_need(const tq_cache *cache, int q_heads, int length, int n_splits,
+                      tq::DecodeParams *p, Variant *v) {
+  fill_decode_params(cache, reinterpret_cast<const void *>(1), q_heads, length, p);
+  *v = pick_variant(*p);
+  if (*v == kMfma) {
+    mfma_splits(cache, length, n_splits, p);
+    return tq::decode_mfma_workspace_bytes(cache->batch, cache->kv_heads, q_heads,
+                                           p->n_cold_splits + p->n_hot_splits, cache->head_dim);
+  }
+  int ns = 0, sl = 0;
+  if (!choose_split(cache, q_heads, length, n_splits, &ns, &sl)) return 0;
+  p->n_splits = ns;
+  p->split_len = sl;
+  return tq::decode_workspace_layout(cache->batch, q_heads, ns, cache->head_dim).total;
+}
+
 }  // namespace
 
 extern "C" {
@@ -182,9 +259,9 @@ size_t tq_decode_workspace_bytes(const tq_cache *cache, int q_heads, int length,
   if (check_cache(cache) != TQ_OK) return 0;
   if (q_heads < cache->kv_heads || q_heads % cache->kv_heads) return 0;
   if (length < 0 || length > cache->capacity || n_splits < 0) return 0;
-  int ns = 0, sl = 0;
-  if (!choose_split(cache, q_heads, length, n_splits, &ns, &sl)) return 0;
-  return tq::decode_workspace_layout(cache->batch, q_heads, ns, cache->head_dim).total;
+  tq::DecodeParams p;
+  Variant v;
+  return workspace_need(cache, q_heads, length, n_splits, &p, &v);
 }
 
 int tq_decode_attention(const tq_cache *cache, const void *q, int q_heads, int length, int n_splits,
@@ -196,34 +273,20 @@ int tq_decode_attention(const tq_cache *cache, const void *q, int q_heads, int l
   if (q_heads < cache->kv_heads || q_heads % cache->kv_heads) return TQ_ERR_ARG;
   if (n_splits < 0) return TQ_ERR_ARG;
   if (length < 0 || length > cache->capacity) return TQ_ERR_CAPACITY;
-  int ns = 0, sl = 0;
-  if (!choose_split(cache, q_heads, length, n_splits, &ns, &sl)) return TQ_ERR_ARG;
-  const tq::DecodeWorkspace lay = tq::decode_workspace_layout(cache->batch, q_heads, ns, cache->head_dim);
-  if (!workspace || workspace_bytes < lay.total ||
-      (reinterpret_cast<uintptr_t>(workspace) & 255u))
-    return TQ_ERR_WORKSPACE;
-
   tq::DecodeParams p;
-  memset(&p, 0, sizeof(p));
-  const int d = cache->head_dim;
-  p.k = side_dev(cache->k, d);
-  p.v = side_dev(cache->v, d);
+  Variant v;
+  const size_t need = workspace_need(cache, q_heads, length, n_splits, &p, &v);
+  if (need == 0) return TQ_ERR_ARG;
+  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return TQ_ERR_WORKSPACE;
   p.q = static_cast<const uint16_t *>(q);
   p.out = out;
   p.scores = scores;
   p.ws = static_cast<float *>(workspace);
-  p.batch = cache->batch;
-  p.kv_heads = cache->kv_heads;
-  p.q_heads = q_heads;
-  p.head_dim = d;
-  p.capacity = cache->capacity;
-  p.length = length;
-  p.n_splits = ns;
-  p.split_len = sl;
-  fill_signs(cache->seed, d, p.sign);
-  copy_levels(cache->k, cache->k.centroids, 1 << cache->k.bits, p.k_cent);
-  copy_levels(cache->v, cache->v.centroids, 1 << cache->v.bits, p.v_cent);
-  const hipError_t e = tq::launch_decode_ref(p, static_cast<hipStream_t>(hip_stream));
+  p.counters = static_cast<unsigned *>(workspace);
+  p.ws_part_off = tq::kCounterBytes;
+  const hipError_t e = (v == kMfma) ? tq::launch_decode_mfma(p, static_cast<hipStream_t>(hip_stream))
+                                    : tq::launch_decode_ref(p, static_cast<hipStream_t>(hip_stream));
   return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
 

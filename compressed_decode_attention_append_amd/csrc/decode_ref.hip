@@ -113,7 +113,8 @@ __global__ __launch_bounds__(kBlock) void decode_split_kernel(const DecodeParams
   }
   __syncthreads();
 
-  float *ml = p.ws;  // [B*Hq][n_splits][2]
+  const DecodeWorkspace lay = decode_workspace_layout(p.batch, p.q_heads, p.n_splits, D);
+  float *ml = reinterpret_cast<float *>(reinterpret_cast<char *>(p.ws) + lay.ml_off);
   for (int h = 0; h < G; ++h) {
     float m = -INFINITY;
     for (int tok = threadIdx.x; tok < n; tok += kBlock) m = fmaxf(m, sc[h * SL + tok]);
@@ -132,7 +133,6 @@ __global__ __launch_bounds__(kBlock) void decode_split_kernel(const DecodeParams
   }
   __syncthreads();
 
-  const DecodeWorkspace lay = decode_workspace_layout(p.batch, p.q_heads, p.n_splits, D);
   float *orot = reinterpret_cast<float *>(reinterpret_cast<char *>(p.ws) + lay.orot_off);
   float *ohot = reinterpret_cast<float *>(reinterpret_cast<char *>(p.ws) + lay.ohot_off);
   for (int o = threadIdx.x; o < G * D; o += kBlock) {
@@ -160,8 +160,8 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const DecodeParams p)
   __shared__ float buf[D];
   const long bh = blockIdx.x;
   const int j = threadIdx.x;
-  const float *ml = p.ws;
   const DecodeWorkspace lay = decode_workspace_layout(p.batch, p.q_heads, p.n_splits, D);
+  const float *ml = reinterpret_cast<const float *>(reinterpret_cast<const char *>(p.ws) + lay.ml_off);
   const float *orot = reinterpret_cast<const float *>(reinterpret_cast<const char *>(p.ws) + lay.orot_off);
   const float *ohot = reinterpret_cast<const float *>(reinterpret_cast<const char *>(p.ws) + lay.ohot_off);
   float M = -INFINITY;

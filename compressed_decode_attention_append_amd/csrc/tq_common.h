@@ -48,14 +48,27 @@ struct DecodeParams {
   const uint16_t *q;  // [B][Hq][d] fp16
   float *out;         // [B][Hq][d]
   float *scores;      // [B][Hq][length] or null
-  float *ws;          // workspace (partials)
-  int batch, kv_heads, q_heads, head_dim, capacity, length, n_splits, split_len;
+  float *ws;          // workspace base
+  unsigned *counters; // per-unit arrival counters (start of the workspace)
+  size_t ws_part_off; // byte offset of the partial results
+  int batch, kv_heads, q_heads, head_dim, capacity, length;
+  // plain split-context variant
+  int n_splits, split_len;
+  // matrix-core variant: packed (cold) positions [0, cold_len) in
+  // n_cold_splits splits, fp16 hot positions [cold_len, length) in
+  // n_hot_splits splits
+  int cold_len, n_cold_splits, cold_split_len, n_hot_splits, hot_split_len;
+  int share_lut;      // K and V use the same 4-bit codebook
   uint32_t sign[kMaxSignWords];
   float k_cent[kMaxLevels];
   float v_cent[kMaxLevels];
 };
 
-// Workspace layout of the decode (floats, each region 256-byte aligned):
+// Workspace: a fixed region of per-unit counters (zero on entry, left zero
+// on exit), then the partial results of whichever variant runs.
+constexpr size_t kCounterBytes = size_t(65536) * sizeof(unsigned);
+
+// Plain variant's partials (floats, each region 256-byte aligned):
 //   ml   [B*Hq][n_splits][2]   running max (log2 domain) and sum
 //   orot [B*Hq][n_splits][d]   rotated-domain value accumulator (packed V)
 //   ohot [B*Hq][n_splits][d]   original-domain accumulator (fp16 V rows)
@@ -66,18 +79,30 @@ struct DecodeWorkspace {
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 __host__ __device__ inline DecodeWorkspace decode_workspace_layout(int batch, int q_heads,
-                                               int n_splits, int head_dim) {
+                                                                   int n_splits, int head_dim) {
   DecodeWorkspace w;
   const size_t units = size_t(batch) * q_heads * n_splits;
-  w.ml_off = 0;
-  w.orot_off = align256(units * 2 * sizeof(float));
+  w.ml_off = kCounterBytes;
+  w.orot_off = w.ml_off + align256(units * 2 * sizeof(float));
   w.ohot_off = w.orot_off + align256(units * head_dim * sizeof(float));
   w.total = w.ohot_off + align256(units * head_dim * sizeof(float));
   return w;
 }
 
+// Matrix-core variant's partials: [B*Hkv][splits][G][d + 2] floats holding
+// (max, sum, accumulator[d]) per query head.
+inline size_t decode_mfma_workspace_bytes(int batch, int kv_heads, int q_heads, int splits,
+                                          int head_dim) {
+  const size_t G = size_t(q_heads / kv_heads);
+  return kCounterBytes + align256(size_t(batch) * kv_heads * splits * G * (head_dim + 2) * sizeof(float));
+}
+
 hipError_t launch_quantize_append(const QuantizeParams &p, hipStream_t stream);
 hipError_t launch_dequantize(const DequantParams &p, hipStream_t stream);
 hipError_t launch_decode_ref(const DecodeParams &p, hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodeParams &p, hipStream_t stream);
+bool decode_mfma_supported(const DecodeParams &p);
+size_t decode_mfma_lds_bytes(int k_bits, bool share_lut, int G);
+int decode_mfma_max_splits();
 
 }  // namespace tq

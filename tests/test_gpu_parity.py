@@ -2,6 +2,7 @@
 synthetic inputs at sizes the oracle finishes in seconds (several tiles and a
 ragged tail).  Every call goes through the C ABI."""
 import math
+import os
 import zlib
 
 import numpy as np
@@ -188,8 +189,21 @@ def _build(case, extra=0, seed=0):
     return cache, k, v, q
 
 
+@pytest.fixture(params=["auto", "ref"])
+def variant(request):
+    """Runs a test with the library's own choice of decode kernel and again
+    with the plain split kernel forced (TQ_DECODE_VARIANT=ref)."""
+    old = os.environ.get("TQ_DECODE_VARIANT")
+    os.environ["TQ_DECODE_VARIANT"] = request.param
+    yield request.param
+    if old is None:
+        os.environ.pop("TQ_DECODE_VARIANT", None)
+    else:
+        os.environ["TQ_DECODE_VARIANT"] = old
+
+
 @pytest.mark.parametrize("case", DECODE_CASES, ids=[c[0] for c in DECODE_CASES])
-def test_decode_attention(case):
+def test_decode_attention(case, variant):
     cache, k, v, q = _build(case, extra=5)
     T = k.shape[2]
     out, sc = cache.decode_attention(_dev(q), T, scores=True)
@@ -203,8 +217,8 @@ def test_decode_attention(case):
     assert ok, f"out: worst {worst}"
 
 
-@pytest.mark.parametrize("case", DECODE_CASES[1:4], ids=[c[0] for c in DECODE_CASES[1:4]])
-def test_decode_split_counts_agree(case):
+@pytest.mark.parametrize("case", DECODE_CASES[1:5], ids=[c[0] for c in DECODE_CASES[1:5]])
+def test_decode_split_counts_agree(case, variant):
     cache, k, v, q = _build(case)
     T = k.shape[2]
     outs = [cache.decode_attention(_dev(q), T, n_splits=ns).cpu().numpy() for ns in (1, 3, 7, 16)]
@@ -213,7 +227,38 @@ def test_decode_split_counts_agree(case):
         assert ok, worst
 
 
-def test_decode_prefix_lengths():
+@pytest.mark.parametrize("case", DECODE_CASES[1:5], ids=[c[0] for c in DECODE_CASES[1:5]])
+def test_decode_variants_agree(case):
+    cache, k, v, q = _build(case)
+    T = k.shape[2]
+    outs = {}
+    for var in ("auto", "ref"):
+        os.environ["TQ_DECODE_VARIANT"] = var
+        outs[var] = cache.decode_attention(_dev(q), T).cpu().numpy()
+    os.environ.pop("TQ_DECODE_VARIANT", None)
+    ok, worst = rows_close(outs["auto"], outs["ref"], 1e-3)
+    assert ok, worst
+
+
+def test_decode_workspace_reuse_across_shapes():
+    """The counter region left zero by one call serves the next call, even
+    when the next call has a different shape or split count."""
+    case = DECODE_CASES[3]
+    cache, k, v, q = _build(case)
+    T = k.shape[2]
+    plan = ((3, T), (16, T), (0, 700), (0, T))
+    need = max(cache.workspace_bytes(q.shape[1], length, ns) for ns, length in plan + ((16, T),))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    ref = cache.decode_attention(_dev(q), T, n_splits=16, workspace=ws).cpu().numpy()
+    for ns, length in plan:
+        out = cache.decode_attention(_dev(q), length, n_splits=ns, workspace=ws).cpu().numpy()
+        if length == T:
+            ok, worst = rows_close(out, ref, 1e-5)
+            assert ok, (ns, worst)
+    assert int(ws[: 65536 * 4].view(torch.int32).abs().sum()) == 0
+
+
+def test_decode_prefix_lengths(variant):
     case = DECODE_CASES[3]
     cache, k, v, q = _build(case)
     for length in (1, 2, 63, 64, 65, 1000):
@@ -227,7 +272,7 @@ def test_decode_prefix_lengths():
     assert np.all(out == 0)
 
 
-def test_decode_deterministic():
+def test_decode_deterministic(variant):
     cache, k, v, q = _build(DECODE_CASES[3])
     T = k.shape[2]
     a = cache.decode_attention(_dev(q), T).cpu().numpy()
