@@ -59,22 +59,32 @@ constexpr int kRep = 32;          // pair-table replicas, one per LDS bank
 constexpr int kMaxSplits = 256;   // splits per unit the merge can stage
 constexpr float kRescale = 8.0f;  // lazy rescaling threshold (log2 units)
 
-// Static LDS layout (32-bit words) per K width.
+// Static LDS layout (32-bit words) per K width.  Tables hold fp16 pairs for
+// a code pair index e (first code in the low bits); replica r of entry e sits
+// at word e * reps + r, so lane r of each 32-lane half reads its own bank.
+// The lo tables start one word past a 64-word boundary so the compiler cannot
+// fuse a hi and a lo read into one two-address instruction (which would land
+// hi and lo in adjacent registers and cost register copies).
 //   KB = 3: K hi [64 x 32] | K lo [64 x 32] | V hi [256 x 32] | codebooks | work
-//   KB = 4: K/V hi [256 x 32] (one codebook) | K lo [256 x 16] | ... (the lo
-//           reads then see 2-way bank conflicts; the table would not fit
-//           otherwise)
+//   KB = 4: K/V hi [256 x 32] (one codebook) | K lo [256 x 16] | ... (2-way
+//           bank conflicts on the lo reads; a 32-replica lo table would not
+//           fit in 64 KB)
 //   KB = 0: V hi [256 x 32] | ...
 template <int KB>
 struct Lay {
+  static constexpr int max_g = KB == 0 ? 8 : 4;  // query heads per KV head that fit
   static constexpr int klo_rep = KB == 4 ? 16 : kRep;
   static constexpr int khi = 0;
-  static constexpr int klo = KB == 3 ? 64 * kRep : (KB == 4 ? 256 * kRep : 0);
-  static constexpr int vhi = KB == 3 ? 2 * 64 * kRep : 0;
-  static constexpr int end_tables = KB == 3 ? 2 * 64 * kRep + 256 * kRep
-                                            : (KB == 4 ? 256 * kRep + 256 * 16 : 256 * kRep);
-  static constexpr int cent = end_tables;
+  static constexpr int klo = KB == 3 ? 64 * kRep + 1 : (KB == 4 ? 256 * kRep + 1 : 0);
+  static constexpr int vhi = KB == 3 ? 2 * 64 * kRep + 2 : 0;
+  static constexpr int end_tables = KB == 3 ? vhi + 256 * kRep
+                                            : (KB == 4 ? klo + 256 * 16 : 256 * kRep);
+  static constexpr int cent = (end_tables + 3) & ~3;
   static constexpr int work = cent + 2 * kMaxLevels;
+  static constexpr int merge_words = kWaves * max_g * (D + 2);
+  static constexpr int combine_words = 2 * max_g * D + max_g;
+  static constexpr int work_words = merge_words > combine_words ? merge_words : combine_words;
+  static constexpr int total = work + work_words + 4 + 1;  // + reductions, flag
 };
 
 __device__ __forceinline__ float4_t mma(const half8_t a, const half8_t b, float4_t c) {
@@ -101,44 +111,19 @@ struct Frag {
   half8_t hi, lo;
 };
 
-__device__ __forceinline__ uint32_t ld(const uint32_t *lds, int word) { return lds[word]; }
+// LDS word at byte address `addr` plus a compile-time byte offset.
+template <int OFF>
+__device__ __forceinline__ uint32_t lds_at(const uint32_t *lds, uint32_t addr) {
+  return *reinterpret_cast<const uint32_t *>(reinterpret_cast<const char *>(lds) + addr + OFF);
+}
 
-// Decode the 32 coordinates [32 g, 32 g + 32) of one position into four K
-// fragments (octet c -> fragment c) from the pair tables.
-template <int KB>
-__device__ __forceinline__ void decode_k(const uint32_t (&w)[4], const uint32_t *lds, int rep_hi,
-                                         int rep_lo, Frag (&a)[4]) {
-  using L = Lay<KB>;
-  uint32_t idx[16];
-  if (KB == 4) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) idx[4 * c + k] = (w[c] >> (8 * k)) & 0xffu;
-    }
-  } else {
-    // 96 bits = 16 six-bit pairs; pairs 5 and 10 straddle a word boundary.
-#pragma unroll
-    for (int k = 0; k < 5; ++k) idx[k] = (w[0] >> (6 * k)) & 63u;
-    idx[5] = ((w[0] >> 30) | (w[1] << 2)) & 63u;
-#pragma unroll
-    for (int k = 6; k < 10; ++k) idx[k] = (w[1] >> (6 * k - 32)) & 63u;
-    idx[10] = ((w[1] >> 28) | (w[2] << 4)) & 63u;
-#pragma unroll
-    for (int k = 11; k < 16; ++k) idx[k] = (w[2] >> (6 * k - 64)) & 63u;
-  }
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    uint32_t h[4], l[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int e = static_cast<int>(idx[4 * c + k]);
-      h[k] = ld(lds, L::khi + e * kRep + rep_hi);
-      l[k] = ld(lds, L::klo + e * L::klo_rep + rep_lo);
-    }
-    a[c].hi = as_half8(h[0], h[1], h[2], h[3]);
-    a[c].lo = as_half8(l[0], l[1], l[2], l[3]);
-  }
+// Byte address of table entry (v >> sh) & mask for a table with 32
+// replicas: ((v >> sh) & mask) * 128 + rep * 4, i.e. shift so the index
+// lands at bit 7, mask, and OR the lane's replica offset.
+template <int SH, uint32_t MASK>
+__device__ __forceinline__ uint32_t taddr(uint32_t v, uint32_t rep4) {
+  const uint32_t x = (SH >= 7) ? (v >> (SH - 7)) : (v << (7 - SH));
+  return (x & (MASK << 7)) | rep4;
 }
 
 // 8 x 8 nibble transpose: x[s] holds codes 8w .. 8w+7 of position s; after
@@ -207,100 +192,146 @@ __device__ __forceinline__ float load_coherent(const float *p) {
   return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Buffer resource over [base, base + bytes): loads past the end read 0.
+constexpr int kBufFlags = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes > 0 ? bytes : 0, kBufFlags);
+}
+
+__device__ __forceinline__ float4 bload4f(__amdgpu_buffer_rsrc_t r, uint32_t voff, int imm) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff + imm, 0, 0);
+  return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]));
+}
+
+// Global-memory data of one chunk of 32 positions for one lane.
+template <int KB>
+struct ChunkData {
+  static constexpr int kw = KB == 0 ? 16 : (KB == 4 ? 4 : 3);  // K dwords per M-tile
+  uint32_t k[2][kw];   // K words (packed) or fp16 row piece, M-tiles 0 and 1
+  float4 kn[2];        // K norms of positions t0 + 16 m + 4 grp .. + 3
+  uint32_t v[8];       // V code word `col` of the 8 positions of this K group
+  float4 vn[2];        // V norms, same positions as kn
+};
+
 template <int KB>
 struct Wave {
   // per-lane constants
-  int col, grp, rep, rep_lo;
+  int col, grp;
+  uint32_t rep4, rep4lo;
+  uint32_t koff, knoff, voff;   // lane byte offsets inside a chunk
   const uint32_t *lds;
   Frag bq[4];
   // per-unit bases
-  const uint32_t *kcodes;
-  const uint16_t *k16;
-  const float *knorm;
-  const uint32_t *vcodes;
-  const float *vnorm;
+  const char *kbase;   // K codes or fp16 rows of this unit
+  const char *knbase;  // K norms
+  const char *vbase;   // V codes
+  const char *vnbase;  // V norms
   const uint16_t *ring;
-  int hot_len, G;
+  int capacity, hot_len, G;
   float vscale;
   // running state
   float m_run, l_run;
   float4_t accv[8];
 
-  // One chunk of 32 positions starting at t0; positions >= we are masked
-  // (only in the tail chunk).
-  template <bool TAIL, bool HOT>
-  __device__ __forceinline__ void chunk(int t0, int we, float *scores, long score_row, int length) {
-    // ---- scores: A rows are positions t0 + 16 m + col
-    float4_t acc[2];
+  static constexpr int kRowBytes = KB == 0 ? 2 * D : (KB == 4 ? 64 : 48);
+
+  __device__ __forceinline__ void load(int t0, ChunkData<KB> &c) const {
+    // rows [t0, t0 + 32) at most; rows past the unit's capacity read 0
+    const int rows = min(capacity - t0, kChunk);
+    const auto rk = rsrc(kbase + static_cast<long>(t0) * kRowBytes, rows * kRowBytes);
+    const auto rkn = rsrc(knbase + static_cast<long>(t0) * 4, rows * 4);
+    const auto rv = rsrc(vbase + static_cast<long>(t0) * 64, rows * 64);
+    const auto rvn = rsrc(vnbase + static_cast<long>(t0) * 4, rows * 4);
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      const int tr = TAIL ? min(t0 + 16 * m + col, we - 1) : t0 + 16 * m + col;
-      acc[m] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-      if (KB) {
-        uint32_t w[4];
-        if (KB == 4) {
-          const uint4 w4 = *reinterpret_cast<const uint4 *>(kcodes + tr * 16 + 4 * grp);
-          w[0] = w4.x; w[1] = w4.y; w[2] = w4.z; w[3] = w4.w;
+      const int mo = m * 16 * kRowBytes;
+      if (KB == 3) {
+        typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
+        const u32x3_t w = __builtin_amdgcn_raw_buffer_load_b96(rk, koff + mo, 0, 0);
+        c.k[m][0] = w[0]; c.k[m][1] = w[1]; c.k[m][2] = w[2];
+      } else {
+#pragma unroll
+        for (int i = 0; i < ChunkData<KB>::kw; i += 4) {
+          const u32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(rk, koff + mo + 4 * i, 0, 0);
+          c.k[m][i] = w[0]; c.k[m][i + 1] = w[1]; c.k[m][i + 2] = w[2]; c.k[m][i + 3] = w[3];
+        }
+      }
+      if (KB) c.kn[m] = bload4f(rkn, knoff, 64 * m);
+      c.vn[m] = bload4f(rvn, knoff, 64 * m);
+    }
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8)
+      c.v[s8] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff + (16 * (s8 >> 2) + (s8 & 3)) * 64, 0, 0);
+  }
+
+  // Scores of the chunk (lane: positions t0 + 16 m + 4 grp + r, head col).
+  __device__ __forceinline__ void score(const ChunkData<KB> &c, float (&s)[8]) const {
+    using L = Lay<KB>;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      float4_t acc = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      if (KB == 0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const half8_t a = as_half8(c.k[m][4 * q], c.k[m][4 * q + 1], c.k[m][4 * q + 2], c.k[m][4 * q + 3]);
+          acc = mma(a, bq[q].hi, acc);
+          acc = mma(a, bq[q].lo, acc);
+        }
+      } else {
+        uint32_t ad[16];   // byte addresses of the 16 code pairs
+        uint32_t adl[16];  // same in the lo table (KB = 4 uses 16 replicas)
+        if (KB == 3) {
+          const uint32_t w0 = c.k[m][0], w1 = c.k[m][1], w2 = c.k[m][2];
+          ad[0] = taddr<0, 63>(w0, rep4);
+          ad[1] = taddr<6, 63>(w0, rep4);
+          ad[2] = taddr<12, 63>(w0, rep4);
+          ad[3] = taddr<18, 63>(w0, rep4);
+          ad[4] = taddr<24, 63>(w0, rep4);
+          ad[5] = taddr<0, 63>(__builtin_amdgcn_alignbit(w1, w0, 30), rep4);
+          ad[6] = taddr<4, 63>(w1, rep4);
+          ad[7] = taddr<10, 63>(w1, rep4);
+          ad[8] = taddr<16, 63>(w1, rep4);
+          ad[9] = taddr<22, 63>(w1, rep4);
+          ad[10] = taddr<0, 63>(__builtin_amdgcn_alignbit(w2, w1, 28), rep4);
+          ad[11] = taddr<2, 63>(w2, rep4);
+          ad[12] = taddr<8, 63>(w2, rep4);
+          ad[13] = taddr<14, 63>(w2, rep4);
+          ad[14] = taddr<20, 63>(w2, rep4);
+          ad[15] = taddr<26, 63>(w2, rep4);
+#pragma unroll
+          for (int k = 0; k < 16; ++k) adl[k] = ad[k];
         } else {
-          const uint32_t *src = kcodes + tr * 12 + 3 * grp;
-          w[0] = src[0]; w[1] = src[1]; w[2] = src[2]; w[3] = 0u;
-        }
-        Frag a[4];
-        decode_k<KB>(w, lds, rep, rep_lo, a);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          acc[m] = mma(a[c].hi, bq[c].hi, acc[m]);
-          acc[m] = mma(a[c].lo, bq[c].hi, acc[m]);
-          acc[m] = mma(a[c].hi, bq[c].lo, acc[m]);
-        }
-      } else {
-        const uint4 *src = reinterpret_cast<const uint4 *>(k16 + tr * D + 32 * grp);
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t w = c.k[m][q];
+            ad[4 * q + 0] = taddr<0, 255>(w, rep4);
+            ad[4 * q + 1] = taddr<8, 255>(w, rep4);
+            ad[4 * q + 2] = taddr<16, 255>(w, rep4);
+            ad[4 * q + 3] = taddr<24, 255>(w, rep4);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const uint4 v = src[c];
-          const half8_t a = as_half8(v.x, v.y, v.z, v.w);
-          acc[m] = mma(a, bq[c].hi, acc[m]);
-          acc[m] = mma(a, bq[c].lo, acc[m]);
+            for (int k = 0; k < 4; ++k) adl[4 * q + k] = ((ad[4 * q + k] >> 1) & 0x3fc0u) | rep4lo;
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const half8_t ah = as_half8(lds_at<4 * L::khi>(lds, ad[4 * q]), lds_at<4 * L::khi>(lds, ad[4 * q + 1]),
+                                      lds_at<4 * L::khi>(lds, ad[4 * q + 2]), lds_at<4 * L::khi>(lds, ad[4 * q + 3]));
+          const half8_t al = as_half8(lds_at<4 * L::klo>(lds, adl[4 * q]), lds_at<4 * L::klo>(lds, adl[4 * q + 1]),
+                                      lds_at<4 * L::klo>(lds, adl[4 * q + 2]), lds_at<4 * L::klo>(lds, adl[4 * q + 3]));
+          acc = mma(ah, bq[q].hi, acc);
+          acc = mma(al, bq[q].hi, acc);
+          acc = mma(ah, bq[q].lo, acc);
         }
       }
+      const float nk[4] = {c.kn[m].x, c.kn[m].y, c.kn[m].z, c.kn[m].w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s[4 * m + r] = KB ? acc[r] * nk[r] : acc[r];
     }
-    // ---- lane holds positions t0 + 16 m + 4 grp + r for head col
-    float s[8], vn[8];
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int base = t0 + 16 * m + 4 * grp;
-      float4 nk = make_float4(1.0f, 1.0f, 1.0f, 1.0f), nv = nk;
-      if (TAIL) {
-        float kk[4], vv[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int tc = min(base + r, we - 1);
-          kk[r] = KB ? knorm[tc] : 1.0f;
-          vv[r] = HOT ? 1.0f : vnorm[tc];
-        }
-        nk = make_float4(kk[0], kk[1], kk[2], kk[3]);
-        nv = make_float4(vv[0], vv[1], vv[2], vv[3]);
-      } else {
-        if (KB) nk = *reinterpret_cast<const float4 *>(knorm + base);
-        if (!HOT) nv = *reinterpret_cast<const float4 *>(vnorm + base);
-      }
-      const float nks[4] = {nk.x, nk.y, nk.z, nk.w};
-      const float nvs[4] = {nv.x, nv.y, nv.z, nv.w};
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float x = acc[m][r] * nks[r];
-        s[4 * m + r] = (TAIL && base + r >= we) ? -INFINITY : x;
-        vn[4 * m + r] = HOT ? 1.0f : nvs[r] * vscale;
-      }
-    }
-    if (scores && col < G) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int t = t0 + 16 * (i >> 2) + 4 * grp + (i & 3);
-        if (!TAIL || t < we) scores[score_row * length + t] = s[i] * kLn2;
-      }
-    }
-    // ---- online softmax with lazy rescaling
+  }
+
+  // Online softmax update; returns the value-MFMA B operands (p n, hi/lo).
+  template <bool TAIL>
+  __device__ __forceinline__ void softmax(float (&s)[8], const float (&vn)[8], half8_t &bvh, half8_t &bvl) {
     float cmax = s[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) cmax = fmaxf(cmax, s[i]);
@@ -328,66 +359,107 @@ struct Wave {
       split_pair(p0 * vn[i], p1 * vn[i + 1], bh[i / 2], bl[i / 2]);
     }
     l_run += lsum;
-    const half8_t bvh = as_half8(bh[0], bh[1], bh[2], bh[3]);
-    const half8_t bvl = as_half8(bl[0], bl[1], bl[2], bl[3]);
+    bvh = as_half8(bh[0], bh[1], bh[2], bh[3]);
+    bvl = as_half8(bl[0], bl[1], bl[2], bl[3]);
+  }
 
-    // ---- values
-    if (!HOT) {
-      // code word `col` of positions t0 + 4 grp + r and t0 + 16 + 4 grp + r
-      uint32_t x[8];
+  // Packed values: transpose the 8 code words and accumulate 8 tiles.
+  __device__ __forceinline__ void values(const ChunkData<KB> &c, const half8_t bvh, const half8_t bvl) {
+    using L = Lay<KB>;
+    uint32_t x[8];
 #pragma unroll
-      for (int s8 = 0; s8 < 8; ++s8) {
-        int t = t0 + 16 * (s8 >> 2) + 4 * grp + (s8 & 3);
-        if (TAIL) t = min(t, we - 1);
-        x[s8] = vcodes[t * 16 + col];
+    for (int i = 0; i < 8; ++i) x[i] = c.v[i];
+    transpose8(x);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint32_t y = x[q];
+      const half8_t a = as_half8(lds_at<4 * L::vhi>(lds, taddr<0, 255>(y, rep4)),
+                                 lds_at<4 * L::vhi>(lds, taddr<8, 255>(y, rep4)),
+                                 lds_at<4 * L::vhi>(lds, taddr<16, 255>(y, rep4)),
+                                 lds_at<4 * L::vhi>(lds, taddr<24, 255>(y, rep4)));
+      accv[q] = mma(a, bvh, accv[q]);
+      accv[q] = mma(a, bvl, accv[q]);
+    }
+  }
+
+  // One chunk of packed positions [t0, t0 + 32); positions >= we are masked.
+  template <bool TAIL>
+  __device__ __forceinline__ void cold_chunk(int t0, int we, const ChunkData<KB> &c, float *scores,
+                                             long score_row, int length) {
+    float s[8], vn[8];
+    score(c, s);
+    const float v4[8] = {c.vn[0].x, c.vn[0].y, c.vn[0].z, c.vn[0].w, c.vn[1].x, c.vn[1].y, c.vn[1].z, c.vn[1].w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      vn[i] = v4[i] * vscale;
+      if (TAIL && t0 + 16 * (i >> 2) + 4 * grp + (i & 3) >= we) s[i] = -INFINITY;
+    }
+    if (scores && col < G) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int t = t0 + 16 * (i >> 2) + 4 * grp + (i & 3);
+        if (!TAIL || t < we) scores[score_row * length + t] = s[i] * kLn2;
       }
-      transpose8(x);
-      using L = Lay<KB>;
+    }
+    half8_t bvh, bvl;
+    softmax<TAIL>(s, vn, bvh, bvl);
+    values(c, bvh, bvl);
+  }
+
+  // One chunk of the fp16 hot window (delegated V), positions >= we masked.
+  __device__ __forceinline__ void hot_chunk(int t0, int we, const ChunkData<KB> &c, float *scores,
+                                            long score_row, int length) {
+    float s[8];
+    const float vn[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
+    score(c, s);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const uint32_t y = x[q];
-        const half8_t a = as_half8(ld(lds, L::vhi + static_cast<int>(y & 0xffu) * kRep + rep),
-                                   ld(lds, L::vhi + static_cast<int>((y >> 8) & 0xffu) * kRep + rep),
-                                   ld(lds, L::vhi + static_cast<int>((y >> 16) & 0xffu) * kRep + rep),
-                                   ld(lds, L::vhi + static_cast<int>(y >> 24) * kRep + rep));
-        accv[q] = mma(a, bvh, accv[q]);
-        accv[q] = mma(a, bvl, accv[q]);
+    for (int i = 0; i < 8; ++i)
+      if (t0 + 16 * (i >> 2) + 4 * grp + (i & 3) >= we) s[i] = -INFINITY;
+    if (scores && col < G) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int t = t0 + 16 * (i >> 2) + 4 * grp + (i & 3);
+        if (t < we) scores[score_row * length + t] = s[i] * kLn2;
       }
-    } else {
-      // fp16 ring rows: tile q covers coordinates 16 q + col
+    }
+    half8_t bvh, bvl;
+    softmax<true>(s, vn, bvh, bvl);
+    // fp16 ring rows: tile q covers coordinates 16 q + col
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        uint32_t u[4];
+    for (int q = 0; q < 8; ++q) {
+      uint32_t u[4];
 #pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) {
-          uint32_t h2[2];
+      for (int s2 = 0; s2 < 4; ++s2) {
+        uint32_t h2[2];
 #pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int s8 = 2 * s2 + e;
-            const int t = min(t0 + 16 * (s8 >> 2) + 4 * grp + (s8 & 3), we - 1);
-            h2[e] = ring[(t % hot_len) * D + 16 * q + col];
-          }
-          u[s2] = h2[0] | (h2[1] << 16);
+        for (int e = 0; e < 2; ++e) {
+          const int s8 = 2 * s2 + e;
+          const int t = min(t0 + 16 * (s8 >> 2) + 4 * grp + (s8 & 3), we - 1);
+          h2[e] = ring[(t % hot_len) * D + 16 * q + col];
         }
-        const half8_t a = as_half8(u[0], u[1], u[2], u[3]);
-        accv[q] = mma(a, bvh, accv[q]);
-        accv[q] = mma(a, bvl, accv[q]);
+        u[s2] = h2[0] | (h2[1] << 16);
       }
+      const half8_t a = as_half8(u[0], u[1], u[2], u[3]);
+      accv[q] = mma(a, bvh, accv[q]);
+      accv[q] = mma(a, bvl, accv[q]);
     }
   }
 };
 
 template <int KB>
-__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodeParams p) {
   using L = Lay<KB>;
-  extern __shared__ uint32_t lds[];
+  // Static LDS: its base address is a compile-time constant, so table reads
+  // fold the table offset into the instruction.
+  __shared__ uint32_t lds[L::total];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave index as a scalar: everything derived from it (the wave's range of
+  // positions, the buffer descriptors) then stays in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = p.q_heads / p.kv_heads;
   float *cent = reinterpret_cast<float *>(lds + L::cent);
   float *work = reinterpret_cast<float *>(lds + L::work);  // rotation; merge scratch
-  const int wmax = max(kWaves * G * (D + 2), G * kMaxSplits + 2 * G * D + G);
-  float *red = work + wmax;                                   // [4] block reductions
+  float *red = work + L::work_words;                         // [4] block reductions
   int *flag = reinterpret_cast<int *>(red + 4);
 
   const int nsplit = p.n_cold_splits + p.n_hot_splits;
@@ -459,8 +531,8 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(const DecodeParam
   Wave<KB> W;
   W.col = lane & 15;
   W.grp = lane >> 4;
-  W.rep = lane & (kRep - 1);
-  W.rep_lo = lane & (L::klo_rep - 1);
+  W.rep4 = (lane & (kRep - 1)) * 4u;
+  W.rep4lo = (lane & (L::klo_rep - 1)) * 4u;
   W.lds = lds;
   W.G = G;
   {
@@ -479,11 +551,17 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(const DecodeParam
     }
   }
   const long rowbase = static_cast<long>(unit) * p.capacity;
-  W.kcodes = KB ? p.k.codes + rowbase * (KB == 4 ? 16 : 12) : nullptr;
-  W.k16 = KB ? nullptr : p.k.fp16 + rowbase * D;
-  W.knorm = KB ? p.k.norms + rowbase : nullptr;
-  W.vcodes = p.v.codes + rowbase * 16;
-  W.vnorm = p.v.norms + rowbase;
+  constexpr int kRowBytes = Wave<KB>::kRowBytes;
+  constexpr int kGroupBytes = kRowBytes / 4;
+  W.kbase = KB ? reinterpret_cast<const char *>(p.k.codes) + rowbase * kRowBytes
+               : reinterpret_cast<const char *>(p.k.fp16) + rowbase * kRowBytes;
+  W.knbase = KB ? reinterpret_cast<const char *>(p.k.norms + rowbase) : W.kbase;
+  W.vbase = reinterpret_cast<const char *>(p.v.codes) + rowbase * 64;
+  W.vnbase = reinterpret_cast<const char *>(p.v.norms + rowbase);
+  W.koff = static_cast<uint32_t>(W.col * kRowBytes + W.grp * kGroupBytes);
+  W.knoff = static_cast<uint32_t>(16 * W.grp);
+  W.voff = static_cast<uint32_t>(W.grp * 4 * 64 + W.col * 4);
+  W.capacity = p.capacity;
   W.hot_len = p.v.hot > 0 ? p.v.hot : 1;
   W.ring = (p.v.mode == TQ_SIDE_DELEGATED) ? p.v.fp16 + static_cast<long>(unit) * p.v.hot * D : nullptr;
   W.m_run = -INFINITY;
@@ -494,20 +572,48 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(const DecodeParam
   // V norm scale of this wave: a power of two that keeps p n below 2^9.
   W.vscale = 1.0f;
   if (!hot) {
+    const float *vn = p.v.norms + rowbase;
     float nmax = 0.0f;
-    for (int t = ws + lane; t < we; t += 64) nmax = fmaxf(nmax, W.vnorm[t]);
+    for (int t = ws + lane; t < we; t += 64) nmax = fmaxf(nmax, vn[t]);
     for (int m = 32; m >= 1; m >>= 1) nmax = fmaxf(nmax, __shfl_xor(nmax, m));
     W.vscale = 1.0f / pow2_ceil(nmax);
   }
 
-  // ---- main loop ------------------------------------------------------
+  // ---- main loop: chunk t0 is processed while chunk t0 + 32 loads into the
+  // other of two register buffers (ping-pong, so nothing is copied) --------
   const long score_row = hq0 + W.col;
-  const int full_end = ws + (max(0, we - ws) / kChunk) * kChunk;
   if (!hot) {
-    for (int t0 = ws; t0 < full_end; t0 += kChunk) W.template chunk<false, false>(t0, we, p.scores, score_row, p.length);
-    if (full_end < we) W.template chunk<true, false>(full_end, we, p.scores, score_row, p.length);
+    if (ws < we) {
+      ChunkData<KB> A, B;
+      W.load(ws, A);
+      int t0 = ws;
+      for (;;) {
+        const bool nb = t0 + kChunk < we;
+        if (nb) W.load(t0 + kChunk, B);
+        if (t0 + kChunk <= we) {
+          W.template cold_chunk<false>(t0, we, A, p.scores, score_row, p.length);
+        } else {
+          W.template cold_chunk<true>(t0, we, A, p.scores, score_row, p.length);
+        }
+        t0 += kChunk;
+        if (!nb) break;
+        const bool na = t0 + kChunk < we;
+        if (na) W.load(t0 + kChunk, A);
+        if (t0 + kChunk <= we) {
+          W.template cold_chunk<false>(t0, we, B, p.scores, score_row, p.length);
+        } else {
+          W.template cold_chunk<true>(t0, we, B, p.scores, score_row, p.length);
+        }
+        t0 += kChunk;
+        if (!na) break;
+      }
+    }
   } else {
-    for (int t0 = ws; t0 < we; t0 += kChunk) W.template chunk<true, true>(t0, we, p.scores, score_row, p.length);
+    for (int t0 = ws; t0 < we; t0 += kChunk) {
+      ChunkData<KB> cur;
+      W.load(t0, cur);
+      W.hot_chunk(t0, we, cur, p.scores, score_row, p.length);
+    }
   }
 
   // ---- merge the waves of this block ------------------------------------
@@ -568,35 +674,53 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(const DecodeParam
   __syncthreads();
   if (*flag == 0) return;
 
+  // Every load below is independent of the others, so each thread has all of
+  // its partial results in flight at once (one memory round trip instead of
+  // one per split).  Thread (h, j4) owns head h, coordinates 4 j4 .. 4 j4 + 3.
   const float *up = part + static_cast<long>(unit) * nsplit * G * (D + 2);
-  float *wts = work;                   // [G][kMaxSplits] split weights 2^(m_s - M)
-  float *rot = work + G * kMaxSplits;  // [G][D] rotated-domain sum
-  float *pln = rot + G * D;            // [G][D] plain (hot) sum
-  float *Ls = pln + G * D;             // [G] total sums
-  for (int h = 0; h < G; ++h) {
-    float m = -INFINITY;
-    for (int sp = threadIdx.x; sp < nsplit; sp += kThreads) m = fmaxf(m, load_coherent(up + (sp * G + h) * (D + 2)));
-    const float M = block_max(m, red);
-    float l = 0.0f;
-    for (int sp = threadIdx.x; sp < nsplit; sp += kThreads) {
-      const float ms = load_coherent(up + (sp * G + h) * (D + 2));
-      const float w = (ms == -INFINITY || M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
-      wts[h * kMaxSplits + sp] = w;
-      l += w * load_coherent(up + (sp * G + h) * (D + 2) + 1);
+  float *rot = work;          // [G][D] rotated-domain sum
+  float *pln = work + G * D;  // [G][D] plain (hot) sum
+  float *Ls = pln + G * D;    // [G] total sums
+  for (int i = threadIdx.x; i < G * (D / 4); i += kThreads) {
+    const int h = i / (D / 4), j = 4 * (i % (D / 4));
+    // one pass, 16 splits per round trip, with a running maximum
+    float M = -INFINITY, L = 0.0f;
+    float4 r = make_float4(0.0f, 0.0f, 0.0f, 0.0f), q = r;
+    for (int sp0 = 0; sp0 < nsplit; sp0 += 16) {
+      float mv[16], lv[16];
+      float4 ov[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int sp = min(sp0 + k, nsplit - 1);
+        const float *src = up + (sp * G + h) * (D + 2);
+        mv[k] = (sp0 + k < nsplit) ? load_coherent(src) : -INFINITY;
+        lv[k] = load_coherent(src + 1);
+        ov[k] = make_float4(load_coherent(src + 2 + j), load_coherent(src + 3 + j),
+                            load_coherent(src + 4 + j), load_coherent(src + 5 + j));
+      }
+      float mg = M;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) mg = fmaxf(mg, mv[k]);
+      if (mg == -INFINITY) continue;
+      const float a = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - mg);
+      M = mg;
+      L *= a;
+      r.x *= a; r.y *= a; r.z *= a; r.w *= a;
+      q.x *= a; q.y *= a; q.z *= a; q.w *= a;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const float w = (mv[k] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mv[k] - M);
+        L += w * lv[k];
+        if (sp0 + k < p.n_cold_splits) {
+          r.x += w * ov[k].x; r.y += w * ov[k].y; r.z += w * ov[k].z; r.w += w * ov[k].w;
+        } else {
+          q.x += w * ov[k].x; q.y += w * ov[k].y; q.z += w * ov[k].z; q.w += w * ov[k].w;
+        }
+      }
     }
-    const float Lh = block_sum(l, red);
-    if (threadIdx.x == 0) Ls[h] = Lh;
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < G * D; i += kThreads) {
-    const int h = i / D, j = i % D;
-    float r = 0.0f, q = 0.0f;
-    for (int sp = 0; sp < p.n_cold_splits; ++sp)
-      r += wts[h * kMaxSplits + sp] * load_coherent(up + (sp * G + h) * (D + 2) + 2 + j);
-    for (int sp = p.n_cold_splits; sp < nsplit; ++sp)
-      q += wts[h * kMaxSplits + sp] * load_coherent(up + (sp * G + h) * (D + 2) + 2 + j);
-    rot[i] = r;
-    pln[i] = q;
+    rot[h * D + j] = r.x; rot[h * D + j + 1] = r.y; rot[h * D + j + 2] = r.z; rot[h * D + j + 3] = r.w;
+    pln[h * D + j] = q.x; pln[h * D + j + 1] = q.y; pln[h * D + j + 2] = q.z; pln[h * D + j + 3] = q.w;
+    if (j == 0) Ls[h] = L;
   }
   __syncthreads();
   for (int s = 1; s < D; s <<= 1) {
@@ -621,10 +745,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(const DecodeParam
 
 template <int KB>
 size_t lds_bytes(int G) {
-  using L = Lay<KB>;
-  const size_t merge = size_t(kWaves) * G * (D + 2);
-  const size_t combine = size_t(G) * kMaxSplits + 2 * size_t(G) * D + G;
-  return 4 * (L::work + std::max(merge, combine) + 4 + 1);
+  return G <= Lay<KB>::max_g ? 4 * size_t(Lay<KB>::total) : ~size_t(0);
 }
 
 }  // namespace
@@ -661,14 +782,14 @@ int decode_mfma_max_splits() { return kMaxSplits; }
 hipError_t launch_decode_mfma(const DecodeParams &p, hipStream_t stream) {
   const int G = p.q_heads / p.kv_heads;
   const int kb = p.k.mode == TQ_SIDE_PACKED ? p.k.bits : 0;
-  const size_t lds = decode_mfma_lds_bytes(kb, p.share_lut != 0, G);
+  if (decode_mfma_lds_bytes(kb, p.share_lut != 0, G) > 65536) return hipErrorInvalidValue;
   const int nsplit = p.n_cold_splits + p.n_hot_splits;
   if (nsplit > kMaxSplits) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(p.batch * p.kv_heads * nsplit));
   switch (kb) {
-    case 0: hipLaunchKernelGGL(decode_mfma_kernel<0>, grid, dim3(kThreads), lds, stream, p); break;
-    case 3: hipLaunchKernelGGL(decode_mfma_kernel<3>, grid, dim3(kThreads), lds, stream, p); break;
-    case 4: hipLaunchKernelGGL(decode_mfma_kernel<4>, grid, dim3(kThreads), lds, stream, p); break;
+    case 0: hipLaunchKernelGGL(decode_mfma_kernel<0>, grid, dim3(kThreads), 0, stream, p); break;
+    case 3: hipLaunchKernelGGL(decode_mfma_kernel<3>, grid, dim3(kThreads), 0, stream, p); break;
+    case 4: hipLaunchKernelGGL(decode_mfma_kernel<4>, grid, dim3(kThreads), 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
