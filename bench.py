@@ -123,6 +123,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c4_tq35_32k", choices=sorted(WORKLOADS))
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (profiling only)")
+    ap.add_argument("--splits", type=int, default=0,
+                    help="context splits per (batch, KV head); 0 = the library's choice")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -166,7 +168,7 @@ def main():
             kn = vn = None
         q = synth.q_torch(31 + li, B, Hq, d, device=dev)
         out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
-        ws = cache.workspace(Hq, T)
+        ws = cache.workspace(Hq, T, args.splits)
         layers.append((cache, kn, vn, q, out, ws))
     torch.cuda.synchronize()
     t_fill = time.time() - t_fill
@@ -188,7 +190,7 @@ def main():
             if record is not None:
                 e2 = torch.cuda.Event(enable_timing=True)
                 e2.record(stream)
-            cache.decode_attention(q, T, out=out, workspace=ws, stream=stream)
+            cache.decode_attention(q, T, n_splits=args.splits, out=out, workspace=ws, stream=stream)
             if record is not None:
                 e3 = torch.cuda.Event(enable_timing=True)
                 e3.record(stream)

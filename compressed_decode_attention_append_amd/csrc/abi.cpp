@@ -114,34 +114,36 @@ Variant pick_variant(const tq::DecodeParams &p) {
   return tq::decode_mfma_supported(p) ? kMfma : kRef;
 }
 
-// Splits of the matrix-core kernel: packed positions in n_cold splits of a
-// multiple of 128 positions (4 waves x 32), aiming at ~1024 blocks; the
-// fp16 hot window of a delegated V in one split of its own.
+// Splits of the matrix-core kernel: the packed positions of a unit in
+// n_cold splits of a multiple of 256 positions (8 waves x 32), aiming at one
+// block per compute unit (256 blocks) with at least 512 positions per block.
+// The fp16 hot window of a delegated V is attended by the block that
+// finishes its unit last, so it needs no split of its own.
 void mfma_splits(const tq_cache *c, int length, int n_splits, tq::DecodeParams *p) {
+  constexpr int kTargetBlocks = 256, kMinPerBlock = 512, kQuantum = 256;
   const int units = c->batch * c->kv_heads;
   const int cold = (c->v.mode == TQ_SIDE_DELEGATED) ? std::max(0, length - c->v.hot) : length;
-  const int hot = length - cold;
-  const int cap = tq::decode_mfma_max_splits() - (hot > 0 ? 1 : 0);
-  int ncold = 0, clen = 0;
+  const int cap = tq::decode_mfma_max_splits();
+  int ncold = 1, clen = 1;
   if (cold > 0) {
     if (n_splits > 0) {
       ncold = std::min(std::min(n_splits, cold), cap);
       clen = (cold + ncold - 1) / ncold;
     } else {
-      const int want = std::max(1, std::min(std::min((1024 + units - 1) / units, (cold + 127) / 128), cap));
-      clen = ((cold + want - 1) / want + 127) / 128 * 128;
+      const int want = std::max(1, std::min(std::min((kTargetBlocks + units - 1) / units,
+                                                     (cold + kMinPerBlock - 1) / kMinPerBlock),
+                                            cap));
+      clen = ((cold + want - 1) / want + kQuantum - 1) / kQuantum * kQuantum;
     }
     ncold = (cold + clen - 1) / clen;
   }
+  // an empty packed range still takes one split: it writes an empty partial
+  // and, as the unit's last block, the hot window or the zero output
   p->cold_len = cold;
   p->n_cold_splits = ncold;
   p->cold_split_len = clen;
-  p->n_hot_splits = hot > 0 ? 1 : 0;
-  p->hot_split_len = hot;
-  if (ncold + p->n_hot_splits == 0) {
-    p->n_cold_splits = 1;  // empty context: one split that writes zeros
-    p->cold_split_len = 1;
-  }
+  p->n_hot_splits = 0;
+  p->hot_split_len = length - cold;
 }
 
 void fill_decode_params(const tq_cache *cache, const void *q, int q_heads, int length,
@@ -173,8 +175,8 @@ size_t workspace_need(const tq_cache *cache, int q_heads, int length, int n_spli
   *v = pick_variant(*p);
   if (*v == kMfma) {
     mfma_splits(cache, length, n_splits, p);
-    return tq::decode_mfma_workspace_bytes(cache->batch, cache->kv_heads, q_heads,
-                                           p->n_cold_splits + p->n_hot_splits, cache->head_dim);
+    return tq::decode_mfma_workspace_bytes(cache->batch, cache->kv_heads, q_heads, p->n_cold_splits,
+                                           cache->head_dim);
   }
   int ns = 0, sl = 0;
   if (!choose_split(cache, q_heads, length, n_splits, &ns, &sl)) return 0;

@@ -5,9 +5,12 @@
 // "TurboQuant KV cache", "Available modes": fp16 K with TurboQuant V and the
 // delegated hot/cold V split).
 //
-// head_dim 128, 4-bit V codes, K packed (3 or 4 bits) or fp16, up to 16
-// query heads per KV head.  Block = 4 waves; grid = (B * Hkv units) x splits.
-// Each wave walks its share of the split in chunks of 32 positions:
+// head_dim 128, 4-bit V codes, K packed (3 or 4 bits) or fp16, up to 8 (fp16
+// K) or 4 (packed K) query heads per KV head.  Grid = (B * Hkv units) x
+// splits, about one 8-wave block per compute unit.  A block issues its first
+// loads, builds its lookup tables and rotated query while they are in
+// flight, then each wave walks its share of the split in chunks of 32
+// positions, loading chunk i + 1 while it computes chunk i:
 //
 //   score   v_mfma_f32_16x16x32_f16 with M = 16 positions, N = 16 (the G
 //           query heads, rest padding), K = 32 coordinates.  A holds the
@@ -21,10 +24,9 @@
 //   value   the same MFMA with M = 16 coordinates, N = 16 heads, K = 32
 //           positions.  Each lane loads one code word of 8 positions and
 //           transposes the 8 x 8 nibbles in registers, so it then holds one
-//           coordinate of 8 positions; B holds p_i n_i (scaled by a power of
-//           two so fp16 cannot overflow).  The sum stays in the rotated
-//           domain; the fp16 hot window of a delegated V is a split of its
-//           own that sums in the original domain.
+//           coordinate of 8 positions; B holds p_i n_i times a power of two
+//           that keeps fp16 in range (lowered lazily when a larger norm
+//           arrives).  The sum stays in the rotated domain.
 //   precision  fp16 operands carry 11 bits, and the output of a diffuse
 //           softmax is much smaller than the rows it averages, so plain fp16
 //           leaves output errors near 1e-3.  Each fp16 operand that is not
@@ -32,11 +34,12 @@
 //           remainder): the score takes A_hi B_hi + A_lo B_hi + A_hi B_lo,
 //           the value sum takes A_hi (P_hi + P_lo); fp16 K rows are exact.
 //
-// The 4 waves merge in LDS and write one partial (max, sum, accumulator) per
-// query head with L2-coherent stores; the last block of a unit to arrive
-// (atomic counter) merges the splits with L2-coherent loads, applies the
-// inverse rotation diag(s) H / sqrt(d) once per head, adds the hot part and
-// divides by the sum.
+// The 8 waves merge in LDS (over the dead tables) and write one partial
+// (max, sum, accumulator) per query head with L2-coherent stores; the last
+// block of a unit to arrive (atomic counter) attends over the fp16 hot window
+// of a delegated V (original domain), merges the splits with L2-coherent
+// loads, applies the inverse rotation diag(s) H / sqrt(d) once per head, adds
+// the hot part and divides by the sum.
 #include <math.h>
 
 #include <algorithm>
@@ -52,12 +55,13 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int D = 128;
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kChunk = 32;
 constexpr int kRep = 32;          // pair-table replicas, one per LDS bank
-constexpr int kMaxSplits = 256;   // splits per unit the merge can stage
+constexpr int kMaxSplits = 256;   // splits per unit (bounded by the host)
 constexpr float kRescale = 8.0f;  // lazy rescaling threshold (log2 units)
+constexpr float kVscaleMax = 1099511627776.0f;  // 2^40: start and ceiling of the V scale
 
 // Static LDS layout (32-bit words) per K width.  Tables hold fp16 pairs for
 // a code pair index e (first code in the low bits); replica r of entry e sits
@@ -65,14 +69,15 @@ constexpr float kRescale = 8.0f;  // lazy rescaling threshold (log2 units)
 // The lo tables start one word past a 64-word boundary so the compiler cannot
 // fuse a hi and a lo read into one two-address instruction (which would land
 // hi and lo in adjacent registers and cost register copies).
-//   KB = 3: K hi [64 x 32] | K lo [64 x 32] | V hi [256 x 32] | codebooks | work
+//   KB = 3: K hi [64 x 32] | K lo [64 x 32] | V hi [256 x 32] | codebooks | q
 //   KB = 4: K/V hi [256 x 32] (one codebook) | K lo [256 x 16] | ... (2-way
 //           bank conflicts on the lo reads; a 32-replica lo table would not
 //           fit in 64 KB)
-//   KB = 0: V hi [256 x 32] | ...
+//   KB = 0: V hi [256 x 32] | codebooks | q
+// After the main loop the whole area is reused for the merges.
 template <int KB>
 struct Lay {
-  static constexpr int max_g = KB == 0 ? 8 : 4;  // query heads per KV head that fit
+  static constexpr int max_g = KB == 0 ? 8 : 4;  // query heads per KV head supported
   static constexpr int klo_rep = KB == 4 ? 16 : kRep;
   static constexpr int khi = 0;
   static constexpr int klo = KB == 3 ? 64 * kRep + 1 : (KB == 4 ? 256 * kRep + 1 : 0);
@@ -80,11 +85,12 @@ struct Lay {
   static constexpr int end_tables = KB == 3 ? vhi + 256 * kRep
                                             : (KB == 4 ? klo + 256 * 16 : 256 * kRep);
   static constexpr int cent = (end_tables + 3) & ~3;
-  static constexpr int work = cent + 2 * kMaxLevels;
-  static constexpr int merge_words = kWaves * max_g * (D + 2);
-  static constexpr int combine_words = 2 * max_g * D + max_g;
-  static constexpr int work_words = merge_words > combine_words ? merge_words : combine_words;
-  static constexpr int total = work + work_words + 4 + 1;  // + reductions, flag
+  static constexpr int qwork = cent + 2 * kMaxLevels;           // [G][D] rotated query
+  static constexpr int red = qwork + max_g * D;                  // [16] reductions, flag
+  static constexpr int total = red + 16;
+  static constexpr int merge_words = kWaves * max_g * (D + 2);  // reuses [0, red)
+  static_assert(merge_words + max_g * (D + 2) <= red, "wave slots + hot partial must fit in the tables");
+  static_assert(4 * total <= 65536, "LDS budget");
 };
 
 __device__ __forceinline__ float4_t mma(const half8_t a, const half8_t b, float4_t c) {
@@ -160,22 +166,6 @@ __device__ __forceinline__ float sum16_32(float x) {
   return x + __shfl_xor(x, 32);
 }
 
-__device__ __forceinline__ float block_max(float x, float *red) {
-  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
-  __syncthreads();
-  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-}
-
-__device__ __forceinline__ float block_sum(float x, float *red) {
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
-  __syncthreads();
-  return (red[0] + red[1]) + (red[2] + red[3]);
-}
-
 // Smallest power of two >= x (x > 0), as a float; 1 for x <= 0.
 __device__ __forceinline__ float pow2_ceil(float x) {
   if (!(x > 0.0f)) return 1.0f;
@@ -228,12 +218,20 @@ struct Wave {
   const char *vnbase;  // V norms
   const uint16_t *ring;
   int capacity, hot_len, G;
-  float vscale;
+  float vscale;        // power of two, n vscale <= 32 for every norm seen, so
+                       // p n vscale < 2^13 fits fp16 (lowered as norms grow)
   // running state
   float m_run, l_run;
   float4_t accv[8];
 
   static constexpr int kRowBytes = KB == 0 ? 2 * D : (KB == 4 ? 64 : 48);
+
+  __device__ __forceinline__ void reset() {
+    m_run = -INFINITY;
+    l_run = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) accv[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
 
   __device__ __forceinline__ void load(int t0, ChunkData<KB> &c) const {
     // rows [t0, t0 + 32) at most; rows past the unit's capacity read 0
@@ -278,8 +276,8 @@ struct Wave {
           acc = mma(a, bq[q].lo, acc);
         }
       } else {
-        uint32_t ad[16];   // byte addresses of the 16 code pairs
-        uint32_t adl[16];  // same in the lo table (KB = 4 uses 16 replicas)
+        uint32_t ad[16];   // byte addresses of the 16 code pairs (32-replica tables)
+        uint32_t adl[16];  // same in the lo table
         if (KB == 3) {
           const uint32_t w0 = c.k[m][0], w1 = c.k[m][1], w2 = c.k[m][2];
           ad[0] = taddr<0, 63>(w0, rep4);
@@ -329,7 +327,9 @@ struct Wave {
     }
   }
 
-  // Online softmax update; returns the value-MFMA B operands (p n, hi/lo).
+  // Online softmax update (lazy: accumulators are rescaled only when the
+  // running maximum grows by more than 2^8); returns the value-MFMA B
+  // operands p n vscale as hi/lo fp16.
   template <bool TAIL>
   __device__ __forceinline__ void softmax(float (&s)[8], const float (&vn)[8], half8_t &bvh, half8_t &bvl) {
     float cmax = s[0];
@@ -363,6 +363,22 @@ struct Wave {
     bvl = as_half8(bl[0], bl[1], bl[2], bl[3]);
   }
 
+  // Keep n vscale <= 32 for the norms of this chunk: if a larger norm shows
+  // up, lower vscale (a power of two) and the accumulators with it.
+  __device__ __forceinline__ void fit_vscale(const float (&v4)[8]) {
+    float lm = v4[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) lm = fmaxf(lm, v4[i]);
+    if (__ballot(lm * vscale > 32.0f)) {
+      for (int m = 32; m >= 1; m >>= 1) lm = fmaxf(lm, __shfl_xor(lm, m));
+      const float nv = fminf(32.0f / pow2_ceil(lm), kVscaleMax);
+      const float f = nv / vscale;
+      vscale = nv;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) accv[i] *= f;
+    }
+  }
+
   // Packed values: transpose the 8 code words and accumulate 8 tiles.
   __device__ __forceinline__ void values(const ChunkData<KB> &c, const half8_t bvh, const half8_t bvl) {
     using L = Lay<KB>;
@@ -389,6 +405,7 @@ struct Wave {
     float s[8], vn[8];
     score(c, s);
     const float v4[8] = {c.vn[0].x, c.vn[0].y, c.vn[0].z, c.vn[0].w, c.vn[1].x, c.vn[1].y, c.vn[1].z, c.vn[1].w};
+    fit_vscale(v4);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       vn[i] = v4[i] * vscale;
@@ -444,10 +461,50 @@ struct Wave {
       accv[q] = mma(a, bvl, accv[q]);
     }
   }
+
+  // Write this wave's (max, sum, accumulator / vscale) for lanes col < G to
+  // the merge slot [G][D + 2]; `hot_layout` selects the coordinate order.
+  __device__ __forceinline__ void to_slot(float *slot_base, bool hot_layout) const {
+    const float l_wave = sum16_32(l_run);
+    if (col < G) {
+      float *slot = slot_base + col * (D + 2);
+      if (grp == 0) {
+        slot[0] = m_run;
+        slot[1] = l_wave;
+      }
+      const float inv = 1.0f / vscale;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int coord = hot_layout ? 16 * q + 4 * grp + r : 8 * (4 * grp + r) + q;
+          slot[2 + coord] = accv[q][r] * inv;
+        }
+      }
+    }
+  }
 };
 
+// Merge kWaves slots [w][G][D + 2] into one (max, sum, accumulator) per head
+// element i of [G][D + 2].
+__device__ __forceinline__ float merge_waves(const float *slots, int G, int i) {
+  const int h = i / (D + 2), j = i % (D + 2);
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, slots[(w * G + h) * (D + 2)]);
+  if (M == -INFINITY) return (j == 0) ? -INFINITY : 0.0f;
+  if (j == 0) return M;
+  float v = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const float mw = slots[(w * G + h) * (D + 2)];
+    if (mw != -INFINITY) v += __builtin_amdgcn_exp2f(mw - M) * slots[(w * G + h) * (D + 2) + j];
+  }
+  return v;
+}
+
 template <int KB>
-__global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(const DecodeParams p) {
   using L = Lay<KB>;
   // Static LDS: its base address is a compile-time constant, so table reads
   // fold the table offset into the instruction.
@@ -458,39 +515,59 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodePa
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = p.q_heads / p.kv_heads;
   float *cent = reinterpret_cast<float *>(lds + L::cent);
-  float *work = reinterpret_cast<float *>(lds + L::work);  // rotation; merge scratch
-  float *red = work + L::work_words;                         // [4] block reductions
-  int *flag = reinterpret_cast<int *>(red + 4);
+  float *qw = reinterpret_cast<float *>(lds + L::qwork);
+  float *red = reinterpret_cast<float *>(lds + L::red);
+  int *flag = reinterpret_cast<int *>(red + 8);
+  float *work = reinterpret_cast<float *>(lds);  // merge area after the main loop
 
-  const int nsplit = p.n_cold_splits + p.n_hot_splits;
+  const int nsplit = p.n_cold_splits;
   const int unit = blockIdx.x / nsplit;
   const int split = blockIdx.x % nsplit;
   const int b = unit / p.kv_heads;
   const int kv = unit % p.kv_heads;
   const long hq0 = static_cast<long>(b) * p.q_heads + static_cast<long>(kv) * G;
-  const bool hot = split >= p.n_cold_splits;
-  int s0, s1;
-  if (!hot) {
-    s0 = split * p.cold_split_len;
-    s1 = min(p.cold_len, s0 + p.cold_split_len);
-  } else {
-    s0 = p.cold_len + (split - p.n_cold_splits) * p.hot_split_len;
-    s1 = min(p.length, s0 + p.hot_split_len);
-  }
+  const int s0 = split * p.cold_split_len;
+  const int s1 = min(p.cold_len, s0 + p.cold_split_len);
   const int span = max(0, s1 - s0);
   const int per = ((span + kWaves - 1) / kWaves + kChunk - 1) / kChunk * kChunk;
   const int ws = s0 + wave * per;
   const int we = min(s1, ws + per);
 
-  // ---- prologue: codebooks, pair tables, rotated query ------------------
+  constexpr bool k_packed = KB != 0;
+  constexpr int kRowBytes = Wave<KB>::kRowBytes;
+  Wave<KB> W;
+  W.col = lane & 15;
+  W.grp = lane >> 4;
+  W.rep4 = (lane & (kRep - 1)) * 4u;
+  W.rep4lo = (lane & (L::klo_rep - 1)) * 4u;
+  W.lds = lds;
+  W.G = G;
+  const long rowbase = static_cast<long>(unit) * p.capacity;
+  W.kbase = KB ? reinterpret_cast<const char *>(p.k.codes) + rowbase * kRowBytes
+               : reinterpret_cast<const char *>(p.k.fp16) + rowbase * kRowBytes;
+  W.knbase = KB ? reinterpret_cast<const char *>(p.k.norms + rowbase) : W.kbase;
+  W.vbase = reinterpret_cast<const char *>(p.v.codes) + rowbase * 64;
+  W.vnbase = reinterpret_cast<const char *>(p.v.norms + rowbase);
+  W.koff = static_cast<uint32_t>(W.col * kRowBytes + W.grp * (kRowBytes / 4));
+  W.knoff = static_cast<uint32_t>(16 * W.grp);
+  W.voff = static_cast<uint32_t>(W.grp * 4 * 64 + W.col * 4);
+  W.capacity = p.capacity;
+  W.hot_len = p.v.hot > 0 ? p.v.hot : 1;
+  W.ring = (p.v.mode == TQ_SIDE_DELEGATED) ? p.v.fp16 + static_cast<long>(unit) * p.v.hot * D : nullptr;
+  W.vscale = kVscaleMax;
+  W.reset();
+
+  // ---- first chunk in flight while the block builds its tables --------
+  ChunkData<KB> A, B;
+  if (ws < we) W.load(ws, A);
+
   for (int i = threadIdx.x; i < kMaxLevels; i += kThreads) {
     cent[i] = p.k_cent[i];
     cent[kMaxLevels + i] = p.v_cent[i];
   }
-  constexpr bool k_packed = KB != 0;
   for (int i = threadIdx.x; i < G * D; i += kThreads) {
     const float x = h2f(p.q[hq0 * D + i]);
-    work[i] = k_packed ? x * sign_of(p.sign, i % D) : x;
+    qw[i] = k_packed ? x * sign_of(p.sign, i % D) : x;
   }
   __syncthreads();
   // value table (for KB = 4 also the K hi table: one codebook)
@@ -519,22 +596,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodePa
       for (int i = threadIdx.x; i < G * D / 2; i += kThreads) {
         const int h = i / (D / 2), r = i % (D / 2);
         const int j = (r / s) * 2 * s + (r % s);
-        const float a = work[h * D + j], c = work[h * D + j + s];
-        work[h * D + j] = a + c;
-        work[h * D + j + s] = a - c;
+        const float a = qw[h * D + j], c = qw[h * D + j + s];
+        qw[h * D + j] = a + c;
+        qw[h * D + j + s] = a - c;
       }
       __syncthreads();
     }
   }
   __syncthreads();
-
-  Wave<KB> W;
-  W.col = lane & 15;
-  W.grp = lane >> 4;
-  W.rep4 = (lane & (kRep - 1)) * 4u;
-  W.rep4lo = (lane & (L::klo_rep - 1)) * 4u;
-  W.lds = lds;
-  W.G = G;
   {
     const float qscale = k_packed ? kLog2e / static_cast<float>(D) : kLog2e / sqrtf(static_cast<float>(D));
 #pragma unroll
@@ -544,122 +613,47 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodePa
       for (int s = 0; s < 4; ++s) {
         const int j = 32 * W.grp + 8 * c + 2 * s;
         h[s] = l[s] = 0u;
-        if (W.col < G) split_pair(work[W.col * D + j] * qscale, work[W.col * D + j + 1] * qscale, h[s], l[s]);
+        if (W.col < G) split_pair(qw[W.col * D + j] * qscale, qw[W.col * D + j + 1] * qscale, h[s], l[s]);
       }
       W.bq[c].hi = as_half8(h[0], h[1], h[2], h[3]);
       W.bq[c].lo = as_half8(l[0], l[1], l[2], l[3]);
     }
   }
-  const long rowbase = static_cast<long>(unit) * p.capacity;
-  constexpr int kRowBytes = Wave<KB>::kRowBytes;
-  constexpr int kGroupBytes = kRowBytes / 4;
-  W.kbase = KB ? reinterpret_cast<const char *>(p.k.codes) + rowbase * kRowBytes
-               : reinterpret_cast<const char *>(p.k.fp16) + rowbase * kRowBytes;
-  W.knbase = KB ? reinterpret_cast<const char *>(p.k.norms + rowbase) : W.kbase;
-  W.vbase = reinterpret_cast<const char *>(p.v.codes) + rowbase * 64;
-  W.vnbase = reinterpret_cast<const char *>(p.v.norms + rowbase);
-  W.koff = static_cast<uint32_t>(W.col * kRowBytes + W.grp * kGroupBytes);
-  W.knoff = static_cast<uint32_t>(16 * W.grp);
-  W.voff = static_cast<uint32_t>(W.grp * 4 * 64 + W.col * 4);
-  W.capacity = p.capacity;
-  W.hot_len = p.v.hot > 0 ? p.v.hot : 1;
-  W.ring = (p.v.mode == TQ_SIDE_DELEGATED) ? p.v.fp16 + static_cast<long>(unit) * p.v.hot * D : nullptr;
-  W.m_run = -INFINITY;
-  W.l_run = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) W.accv[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-
-  // V norm scale of this wave: a power of two that keeps p n below 2^9.
-  W.vscale = 1.0f;
-  if (!hot) {
-    const float *vn = p.v.norms + rowbase;
-    float nmax = 0.0f;
-    for (int t = ws + lane; t < we; t += 64) nmax = fmaxf(nmax, vn[t]);
-    for (int m = 32; m >= 1; m >>= 1) nmax = fmaxf(nmax, __shfl_xor(nmax, m));
-    W.vscale = 1.0f / pow2_ceil(nmax);
-  }
 
   // ---- main loop: chunk t0 is processed while chunk t0 + 32 loads into the
   // other of two register buffers (ping-pong, so nothing is copied) --------
   const long score_row = hq0 + W.col;
-  if (!hot) {
-    if (ws < we) {
-      ChunkData<KB> A, B;
-      W.load(ws, A);
-      int t0 = ws;
-      for (;;) {
-        const bool nb = t0 + kChunk < we;
-        if (nb) W.load(t0 + kChunk, B);
-        if (t0 + kChunk <= we) {
-          W.template cold_chunk<false>(t0, we, A, p.scores, score_row, p.length);
-        } else {
-          W.template cold_chunk<true>(t0, we, A, p.scores, score_row, p.length);
-        }
-        t0 += kChunk;
-        if (!nb) break;
-        const bool na = t0 + kChunk < we;
-        if (na) W.load(t0 + kChunk, A);
-        if (t0 + kChunk <= we) {
-          W.template cold_chunk<false>(t0, we, B, p.scores, score_row, p.length);
-        } else {
-          W.template cold_chunk<true>(t0, we, B, p.scores, score_row, p.length);
-        }
-        t0 += kChunk;
-        if (!na) break;
+  if (ws < we) {
+    int t0 = ws;
+    for (;;) {
+      const bool nb = t0 + kChunk < we;
+      if (nb) W.load(t0 + kChunk, B);
+      if (t0 + kChunk <= we) {
+        W.template cold_chunk<false>(t0, we, A, p.scores, score_row, p.length);
+      } else {
+        W.template cold_chunk<true>(t0, we, A, p.scores, score_row, p.length);
       }
-    }
-  } else {
-    for (int t0 = ws; t0 < we; t0 += kChunk) {
-      ChunkData<KB> cur;
-      W.load(t0, cur);
-      W.hot_chunk(t0, we, cur, p.scores, score_row, p.length);
+      t0 += kChunk;
+      if (!nb) break;
+      const bool na = t0 + kChunk < we;
+      if (na) W.load(t0 + kChunk, A);
+      if (t0 + kChunk <= we) {
+        W.template cold_chunk<false>(t0, we, B, p.scores, score_row, p.length);
+      } else {
+        W.template cold_chunk<true>(t0, we, B, p.scores, score_row, p.length);
+      }
+      t0 += kChunk;
+      if (!na) break;
     }
   }
 
-  // ---- merge the waves of this block ------------------------------------
-  const float l_wave = sum16_32(W.l_run);
-  __syncthreads();  // rotation buffer no longer needed
-  float *mw = work + wave * G * (D + 2);
-  if (W.col < G) {
-    float *slot = mw + W.col * (D + 2);
-    if (W.grp == 0) {
-      slot[0] = W.m_run;
-      slot[1] = l_wave;
-    }
-    const float inv = 1.0f / W.vscale;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int coord = hot ? 16 * q + 4 * W.grp + r : 8 * (4 * W.grp + r) + q;
-        slot[2 + coord] = W.accv[q][r] * inv;
-      }
-    }
-  }
+  // ---- merge the waves of this block (tables are dead from here on) -----
+  __syncthreads();
+  W.to_slot(work + wave * G * (D + 2), false);
   __syncthreads();
   float *part = reinterpret_cast<float *>(reinterpret_cast<char *>(p.ws) + p.ws_part_off);
   float *mypart = part + (static_cast<long>(unit) * nsplit + split) * G * (D + 2);
-  for (int i = threadIdx.x; i < G * (D + 2); i += kThreads) {
-    const int h = i / (D + 2), j = i % (D + 2);
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, work[(w * G + h) * (D + 2)]);
-    float v;
-    if (M == -INFINITY) {
-      v = (j == 0) ? -INFINITY : 0.0f;
-    } else if (j == 0) {
-      v = M;
-    } else {
-      v = 0.0f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float mw_ = work[(w * G + h) * (D + 2)];
-        const float sc = (mw_ == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw_ - M);
-        v += sc * work[(w * G + h) * (D + 2) + j];
-      }
-    }
-    store_coherent(mypart + i, v);
-  }
+  for (int i = threadIdx.x; i < G * (D + 2); i += kThreads) store_coherent(mypart + i, merge_waves(work, G, i));
 
   // ---- the last block of the unit merges the splits ----------------------
   // The partials above are L2-coherent stores; once they have completed
@@ -674,29 +668,51 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodePa
   __syncthreads();
   if (*flag == 0) return;
 
+  // delegated V: this block also attends over the fp16 hot window
+  float *hotp = work + kWaves * G * (D + 2);  // [G][D + 2] merged hot partial
+  const int h0 = p.cold_len, h1 = p.length;
+  const bool has_hot = h1 > h0;
+  if (has_hot) {
+    const int hspan = h1 - h0;
+    const int hper = ((hspan + kWaves - 1) / kWaves + kChunk - 1) / kChunk * kChunk;
+    const int hs = h0 + wave * hper, he = min(h1, hs + hper);
+    W.reset();
+    W.vscale = 1.0f;
+    for (int t0 = hs; t0 < he; t0 += kChunk) {
+      W.load(t0, A);
+      W.hot_chunk(t0, he, A, p.scores, score_row, p.length);
+    }
+    W.to_slot(work + wave * G * (D + 2), true);
+    __syncthreads();
+    for (int i = threadIdx.x; i < G * (D + 2); i += kThreads) hotp[i] = merge_waves(work, G, i);
+    __syncthreads();
+  }
+
   // Every load below is independent of the others, so each thread has all of
-  // its partial results in flight at once (one memory round trip instead of
-  // one per split).  Thread (h, j4) owns head h, coordinates 4 j4 .. 4 j4 + 3.
+  // its partial results in flight at once.  Thread (h, j4) owns head h,
+  // coordinates 4 j4 .. 4 j4 + 3.
   const float *up = part + static_cast<long>(unit) * nsplit * G * (D + 2);
-  float *rot = work;          // [G][D] rotated-domain sum
+  float *rot = work;          // [G][D] rotated-domain sum (overwrites the slots)
   float *pln = work + G * D;  // [G][D] plain (hot) sum
   float *Ls = pln + G * D;    // [G] total sums
-  for (int i = threadIdx.x; i < G * (D / 4); i += kThreads) {
-    const int h = i / (D / 4), j = 4 * (i % (D / 4));
-    // one pass, 16 splits per round trip, with a running maximum
-    float M = -INFINITY, L = 0.0f;
-    float4 r = make_float4(0.0f, 0.0f, 0.0f, 0.0f), q = r;
+  float r4[4] = {0.0f, 0.0f, 0.0f, 0.0f}, q4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float Lt = 0.0f;
+  int hh = 0, jj = 0;
+  const bool mine = threadIdx.x < G * (D / 4);
+  if (mine) {
+    hh = threadIdx.x / (D / 4);
+    jj = 4 * (threadIdx.x % (D / 4));
+    float M = -INFINITY;
     for (int sp0 = 0; sp0 < nsplit; sp0 += 16) {
-      float mv[16], lv[16];
-      float4 ov[16];
+      float mv[16], lv[16], ov[16][4];
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         const int sp = min(sp0 + k, nsplit - 1);
-        const float *src = up + (sp * G + h) * (D + 2);
+        const float *src = up + (sp * G + hh) * (D + 2);
         mv[k] = (sp0 + k < nsplit) ? load_coherent(src) : -INFINITY;
         lv[k] = load_coherent(src + 1);
-        ov[k] = make_float4(load_coherent(src + 2 + j), load_coherent(src + 3 + j),
-                            load_coherent(src + 4 + j), load_coherent(src + 5 + j));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ov[k][e] = load_coherent(src + 2 + jj + e);
       }
       float mg = M;
 #pragma unroll
@@ -704,23 +720,40 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodePa
       if (mg == -INFINITY) continue;
       const float a = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - mg);
       M = mg;
-      L *= a;
-      r.x *= a; r.y *= a; r.z *= a; r.w *= a;
-      q.x *= a; q.y *= a; q.z *= a; q.w *= a;
+      Lt *= a;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r4[e] *= a;
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         const float w = (mv[k] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mv[k] - M);
-        L += w * lv[k];
-        if (sp0 + k < p.n_cold_splits) {
-          r.x += w * ov[k].x; r.y += w * ov[k].y; r.z += w * ov[k].z; r.w += w * ov[k].w;
-        } else {
-          q.x += w * ov[k].x; q.y += w * ov[k].y; q.z += w * ov[k].z; q.w += w * ov[k].w;
+        Lt += w * lv[k];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r4[e] += w * ov[k][e];
+      }
+    }
+    if (has_hot) {
+      const float mh = hotp[hh * (D + 2)];
+      if (mh != -INFINITY) {
+        const float mg = fmaxf(M, mh);
+        const float a = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - mg);
+        const float bh = __builtin_amdgcn_exp2f(mh - mg);
+        Lt = Lt * a + bh * hotp[hh * (D + 2) + 1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          r4[e] *= a;
+          q4[e] = bh * hotp[hh * (D + 2) + 2 + jj + e];
         }
       }
     }
-    rot[h * D + j] = r.x; rot[h * D + j + 1] = r.y; rot[h * D + j + 2] = r.z; rot[h * D + j + 3] = r.w;
-    pln[h * D + j] = q.x; pln[h * D + j + 1] = q.y; pln[h * D + j + 2] = q.z; pln[h * D + j + 3] = q.w;
-    if (j == 0) Ls[h] = L;
+  }
+  __syncthreads();  // hot partial and slots no longer needed
+  if (mine) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      rot[hh * D + jj + e] = r4[e];
+      pln[hh * D + jj + e] = q4[e];
+    }
+    if (jj == 0) Ls[hh] = Lt;
   }
   __syncthreads();
   for (int s = 1; s < D; s <<= 1) {
@@ -743,19 +776,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(const DecodePa
   if (threadIdx.x == 0) __hip_atomic_store(p.counters + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int KB>
-size_t lds_bytes(int G) {
-  return G <= Lay<KB>::max_g ? 4 * size_t(Lay<KB>::total) : ~size_t(0);
-}
-
 }  // namespace
 
 size_t decode_mfma_lds_bytes(int k_bits, bool share_lut, int G) {
   (void)share_lut;
   switch (k_bits) {
-    case 0: return lds_bytes<0>(G);
-    case 3: return lds_bytes<3>(G);
-    case 4: return lds_bytes<4>(G);
+    case 0: return G <= Lay<0>::max_g ? 4 * size_t(Lay<0>::total) : ~size_t(0);
+    case 3: return G <= Lay<3>::max_g ? 4 * size_t(Lay<3>::total) : ~size_t(0);
+    case 4: return G <= Lay<4>::max_g ? 4 * size_t(Lay<4>::total) : ~size_t(0);
     default: return ~size_t(0);
   }
 }
@@ -767,9 +795,9 @@ bool decode_mfma_supported(const DecodeParams &p) {
   int kb;
   if (p.k.mode == TQ_SIDE_FP16) {
     kb = 0;
-  } else if (p.k.mode == TQ_SIDE_PACKED && p.k.bits == 3) {
+  } else if (p.k.mode == TQ_SIDE_PACKED && p.k.bits == 3 && p.v.mode == TQ_SIDE_PACKED) {
     kb = 3;
-  } else if (p.k.mode == TQ_SIDE_PACKED && p.k.bits == 4 && p.share_lut) {
+  } else if (p.k.mode == TQ_SIDE_PACKED && p.k.bits == 4 && p.share_lut && p.v.mode == TQ_SIDE_PACKED) {
     kb = 4;  // K and V share one 4-bit codebook table
   } else {
     return false;
@@ -783,8 +811,8 @@ hipError_t launch_decode_mfma(const DecodeParams &p, hipStream_t stream) {
   const int G = p.q_heads / p.kv_heads;
   const int kb = p.k.mode == TQ_SIDE_PACKED ? p.k.bits : 0;
   if (decode_mfma_lds_bytes(kb, p.share_lut != 0, G) > 65536) return hipErrorInvalidValue;
-  const int nsplit = p.n_cold_splits + p.n_hot_splits;
-  if (nsplit > kMaxSplits) return hipErrorInvalidValue;
+  const int nsplit = p.n_cold_splits;
+  if (nsplit < 1 || nsplit > kMaxSplits || p.n_hot_splits != 0) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(p.batch * p.kv_heads * nsplit));
   switch (kb) {
     case 0: hipLaunchKernelGGL(decode_mfma_kernel<0>, grid, dim3(kThreads), 0, stream, p); break;
