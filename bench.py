@@ -125,6 +125,9 @@ def main():
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (profiling only)")
     ap.add_argument("--splits", type=int, default=0,
                     help="context splits per (batch, KV head); 0 = the library's choice")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (a known-size "
+                         "calibration kernel for hardware byte counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -175,6 +178,13 @@ def main():
     print(f"# filled {Lyr} layers in {t_fill:.1f} s", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream()
+    if args.copy_mib:
+        src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)  # reads and writes copy_mib MiB
+        torch.cuda.synchronize()
+        del src, dst
 
     def step(record):
         for cache, kn, vn, q, out, ws in layers:

@@ -53,6 +53,7 @@ namespace {
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int D = 128;
 constexpr int kWaves = 8;
@@ -63,34 +64,31 @@ constexpr int kMaxSplits = 256;   // splits per unit (bounded by the host)
 constexpr float kRescale = 8.0f;  // lazy rescaling threshold (log2 units)
 constexpr float kVscaleMax = 1099511627776.0f;  // 2^40: start and ceiling of the V scale
 
-// Static LDS layout (32-bit words) per K width.  Tables hold fp16 pairs for
-// a code pair index e (first code in the low bits); replica r of entry e sits
-// at word e * reps + r, so lane r of each 32-lane half reads its own bank.
-// The lo tables start one word past a 64-word boundary so the compiler cannot
-// fuse a hi and a lo read into one two-address instruction (which would land
-// hi and lo in adjacent registers and cost register copies).
-//   KB = 3: K hi [64 x 32] | K lo [64 x 32] | V hi [256 x 32] | codebooks | q
-//   KB = 4: K/V hi [256 x 32] (one codebook) | K lo [256 x 16] | ... (2-way
-//           bank conflicts on the lo reads; a 32-replica lo table would not
-//           fit in 64 KB)
-//   KB = 0: V hi [256 x 32] | codebooks | q
-// After the main loop the whole area is reused for the merges.
-template <int KB>
+// Static LDS layout (32-bit words).  The lookup tables hold fp16 pairs for a
+// code pair index e (first code in the low bits, its centroid in the low
+// half).  Entry e occupies 256 bytes at byte e * 256: 32 replicas of the
+// entry at +4 r (lane r of each 32-lane half reads its own bank, so any index
+// pattern reads without bank conflicts) and 32 replicas of a second table at
+// +128 + 4 r.  A byte address is then (e << 8) | 4 r, which one v_perm_b32
+// builds from a byte-aligned pair index.
+//   V hi (all K widths)   entries 0..255, first half
+//   KB = 4                K lo in the second half of entries 0..255 (K hi is
+//                         the V table: one 4-bit codebook)
+//   KB = 3                K hi in the second half of entries 0..63, K lo in
+//                         the second half of entries 64..127
+// After the main loop the table area is reused for the merges.
+constexpr int kTableWords = 256 * 64;
+constexpr int kKhiOff3 = 128;             // byte offsets added to (e << 8) | 4 r
+constexpr int kKloOff3 = 64 * 256 + 128;
+constexpr int kKloOff4 = 128;
+
+template <int GP>
 struct Lay {
-  static constexpr int max_g = KB == 0 ? 8 : 4;  // query heads per KV head supported
-  static constexpr int klo_rep = KB == 4 ? 16 : kRep;
-  static constexpr int khi = 0;
-  static constexpr int klo = KB == 3 ? 64 * kRep + 1 : (KB == 4 ? 256 * kRep + 1 : 0);
-  static constexpr int vhi = KB == 3 ? 2 * 64 * kRep + 2 : 0;
-  static constexpr int end_tables = KB == 3 ? vhi + 256 * kRep
-                                            : (KB == 4 ? klo + 256 * 16 : 256 * kRep);
-  static constexpr int cent = (end_tables + 3) & ~3;
-  static constexpr int qwork = cent + 2 * kMaxLevels;           // [G][D] rotated query
-  static constexpr int red = qwork + max_g * D;                  // [16] reductions, flag
+  static constexpr int cent = kTableWords;
+  static constexpr int qwork = cent + 2 * kMaxLevels;  // [GP][D] rotated query
+  static constexpr int red = qwork + GP * D;           // flag
   static constexpr int total = red + 16;
-  static constexpr int merge_words = kWaves * max_g * (D + 2);  // reuses [0, red)
-  static_assert(merge_words + max_g * (D + 2) <= red, "wave slots + hot partial must fit in the tables");
-  static_assert(4 * total <= 65536, "LDS budget");
+  static_assert((kWaves + 1) * GP * (D + 2) <= kTableWords, "merges must fit in the table area");
 };
 
 __device__ __forceinline__ float4_t mma(const half8_t a, const half8_t b, float4_t c) {
@@ -123,47 +121,15 @@ __device__ __forceinline__ uint32_t lds_at(const uint32_t *lds, uint32_t addr) {
   return *reinterpret_cast<const uint32_t *>(reinterpret_cast<const char *>(lds) + addr + OFF);
 }
 
-// Byte address of table entry (v >> sh) & mask for a table with 32
-// replicas: ((v >> sh) & mask) * 128 + rep * 4, i.e. shift so the index
-// lands at bit 7, mask, and OR the lane's replica offset.
-template <int SH, uint32_t MASK>
-__device__ __forceinline__ uint32_t taddr(uint32_t v, uint32_t rep4) {
-  const uint32_t x = (SH >= 7) ? (v >> (SH - 7)) : (v << (7 - SH));
-  return (x & (MASK << 7)) | rep4;
-}
-
-// 8 x 8 nibble transpose: x[s] holds codes 8w .. 8w+7 of position s; after
-// it, x[p] holds coordinate 8w + p of positions 0 .. 7 (nibble s).
-__device__ __forceinline__ void transpose8(uint32_t (&x)[8]) {
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const uint32_t a = x[s], b = x[s + 4];
-    x[s] = __builtin_amdgcn_perm(b, a, 0x05040100u);
-    x[s + 4] = __builtin_amdgcn_perm(b, a, 0x07060302u);
-  }
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int s = (q & 1) + 4 * (q >> 1);
-    const uint32_t a = x[s], b = x[s + 2];
-    x[s] = __builtin_amdgcn_perm(b, a, 0x06020400u);
-    x[s + 2] = __builtin_amdgcn_perm(b, a, 0x07030501u);
-  }
-#pragma unroll
-  for (int s = 0; s < 8; s += 2) {
-    const uint32_t a = x[s], b = x[s + 1];
-    x[s] = (a & 0x0f0f0f0fu) | ((b << 4) & 0xf0f0f0f0u);
-    x[s + 1] = ((a >> 4) & 0x0f0f0f0fu) | (b & 0xf0f0f0f0u);
-  }
-}
-
-__device__ __forceinline__ float max16_32(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  return fmaxf(x, __shfl_xor(x, 32));
-}
-
-__device__ __forceinline__ float sum16_32(float x) {
-  x += __shfl_xor(x, 16);
-  return x + __shfl_xor(x, 32);
+// Same, as a read the compiler may not merge with a neighbouring one into a
+// two-address instruction: merging a hi and a lo table read of one address
+// lands the two halves in adjacent registers, while the MFMA operands want
+// four hi and four lo words each in consecutive registers (the merge then
+// costs register copies).
+template <int OFF>
+__device__ __forceinline__ uint32_t lds_at_sep(const uint32_t *lds, uint32_t addr) {
+  typedef __attribute__((address_space(3))) const volatile uint32_t lds_u32;
+  return *reinterpret_cast<lds_u32 *>(addr + OFF);
 }
 
 // Smallest power of two >= x (x > 0), as a float; 1 for x <= 0.
@@ -193,21 +159,82 @@ __device__ __forceinline__ float4 bload4f(__amdgpu_buffer_rsrc_t r, uint32_t vof
   return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]));
 }
 
+// Byte address (e << 8) | rep4 of table entry e = byte K of w.
+template <int K>
+__device__ __forceinline__ uint32_t baddr(uint32_t w, uint32_t rep4) {
+  return __builtin_amdgcn_perm(w, rep4, 0x0c0c0000u | ((4u + K) << 8));
+}
+
+// Byte address of table entry (v >> SH) & 63 (a 6-bit pair of 3-bit codes).
+template <int SH>
+__device__ __forceinline__ uint32_t baddr6(uint32_t v, uint32_t rep4) {
+  const uint32_t x = (SH >= 8) ? (v >> (SH - 8)) : (v << (8 - SH));
+  return (x & (63u << 8)) | rep4;
+}
+
+__device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t a, uint32_t b) { return (a & mask) | (b & ~mask); }
+
+// DPP controls (row = 16 lanes, bank = 4 lanes of a row).
+constexpr int kRowShl = 0x100, kRowShr = 0x110, kRowRor = 0x120;
+
+template <int CTRL, int BANKS>
+__device__ __forceinline__ float dpp_f(float old, float src) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), CTRL, 0xf, BANKS, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t src) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(src), CTRL, 0xf, 0xf, true));
+}
+
+// Reductions over the 64 / GP lanes of one query head in the compact layout
+// (lanes whose column agrees modulo GP).
+template <int GP>
+__device__ __forceinline__ float head_max(float x) {
+  if (GP == 4) x = fmaxf(x, dpp_f<kRowRor + 4, 0xf>(0.0f, x));
+  x = fmaxf(x, dpp_f<kRowRor + 8, 0xf>(0.0f, x));
+  const u32x2_t a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const u32x2_t b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+template <int GP>
+__device__ __forceinline__ float head_sum(float x) {
+  if (GP == 4) x += dpp_f<kRowRor + 4, 0xf>(0.0f, x);
+  x += dpp_f<kRowRor + 8, 0xf>(0.0f, x);
+  const u32x2_t a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const u32x2_t b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Global-memory data of one chunk of 32 positions for one lane.
-template <int KB>
+template <int KB, int GP>
 struct ChunkData {
   static constexpr int kw = KB == 0 ? 16 : (KB == 4 ? 4 : 3);  // K dwords per M-tile
+  static constexpr int nv = GP / 2;                            // compact values per lane
   uint32_t k[2][kw];   // K words (packed) or fp16 row piece, M-tiles 0 and 1
-  float4 kn[2];        // K norms of positions t0 + 16 m + 4 grp .. + 3
-  uint32_t v[8];       // V code word `col` of the 8 positions of this K group
-  float4 vn[2];        // V norms, same positions as kn
+  float kn[nv];        // K norms of the lane's compact positions
+  uint32_t v[8];       // V code word `col` of the 8 positions of this lane group
+  float vn[nv];        // V norms of the compact positions
 };
 
-template <int KB>
+// Lane roles.  MFMA layouts (v_mfma_f32_16x16x32_f16): A lane l holds row
+// l % 16, k = 8 (l / 16) + s; B lane l holds k = 8 (l / 16) + s, column
+// l % 16; D lane l holds rows 4 (l / 16) + r, column l % 16.  With col =
+// l % 16 and grp = l / 16, position slot s8 (0..7) of lane group grp is chunk
+// position 16 (s8 / 4) + 4 grp + s8 % 4; the score D of M-tile m, row r is
+// slot 4 m + r.  Only GP of the 16 head columns are real, so the softmax runs
+// on a compact layout: lane (grp, col = GP kc + h) holds head h at slots
+// nv kc .. nv kc + nv - 1 (nv = GP / 2 consecutive positions), moved there
+// from lane (grp, h) with DPP row shifts, and moved back the same way for the
+// value MFMA's B operand.
+template <int KB, int GP>
 struct Wave {
+  static constexpr int NV = GP / 2;
+  static constexpr int kRowBytes = KB == 0 ? 2 * D : (KB == 4 ? 64 : 48);
   // per-lane constants
-  int col, grp;
-  uint32_t rep4, rep4lo;
+  int col, grp, cpos;   // cpos: chunk position of the lane's first compact slot
+  uint32_t rep4;
   uint32_t koff, knoff, voff;   // lane byte offsets inside a chunk
   const uint32_t *lds;
   Frag bq[4];
@@ -220,11 +247,9 @@ struct Wave {
   int capacity, hot_len, G;
   float vscale;        // power of two, n vscale <= 32 for every norm seen, so
                        // p n vscale < 2^13 fits fp16 (lowered as norms grow)
-  // running state
+  // running state (compact layout: head col % GP)
   float m_run, l_run;
-  float4_t accv[8];
-
-  static constexpr int kRowBytes = KB == 0 ? 2 * D : (KB == 4 ? 64 : 48);
+  float4_t accv[8];    // D layout: head col, coordinates of tile q
 
   __device__ __forceinline__ void reset() {
     m_run = -INFINITY;
@@ -233,7 +258,7 @@ struct Wave {
     for (int i = 0; i < 8; ++i) accv[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
-  __device__ __forceinline__ void load(int t0, ChunkData<KB> &c) const {
+  __device__ __forceinline__ void load(int t0, ChunkData<KB, GP> &c) const {
     // rows [t0, t0 + 32) at most; rows past the unit's capacity read 0
     const int rows = min(capacity - t0, kChunk);
     const auto rk = rsrc(kbase + static_cast<long>(t0) * kRowBytes, rows * kRowBytes);
@@ -249,22 +274,36 @@ struct Wave {
         c.k[m][0] = w[0]; c.k[m][1] = w[1]; c.k[m][2] = w[2];
       } else {
 #pragma unroll
-        for (int i = 0; i < ChunkData<KB>::kw; i += 4) {
+        for (int i = 0; i < ChunkData<KB, GP>::kw; i += 4) {
           const u32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(rk, koff + mo + 4 * i, 0, 0);
           c.k[m][i] = w[0]; c.k[m][i + 1] = w[1]; c.k[m][i + 2] = w[2]; c.k[m][i + 3] = w[3];
         }
       }
-      if (KB) c.kn[m] = bload4f(rkn, knoff, 64 * m);
-      c.vn[m] = bload4f(rvn, knoff, 64 * m);
+    }
+    if (NV == 2) {
+      if (KB) {
+        const u32x2_t a = __builtin_amdgcn_raw_buffer_load_b64(rkn, knoff, 0, 0);
+        c.kn[0] = __uint_as_float(a[0]); c.kn[1] = __uint_as_float(a[1]);
+      }
+      const u32x2_t b = __builtin_amdgcn_raw_buffer_load_b64(rvn, knoff, 0, 0);
+      c.vn[0] = __uint_as_float(b[0]); c.vn[1] = __uint_as_float(b[1]);
+    } else {
+      if (KB) {
+        const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(rkn, knoff, 0, 0);
+#pragma unroll
+        for (int j = 0; j < NV; ++j) c.kn[j] = __uint_as_float(a[j]);
+      }
+      const u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(rvn, knoff, 0, 0);
+#pragma unroll
+      for (int j = 0; j < NV; ++j) c.vn[j] = __uint_as_float(b[j]);
     }
 #pragma unroll
     for (int s8 = 0; s8 < 8; ++s8)
       c.v[s8] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff + (16 * (s8 >> 2) + (s8 & 3)) * 64, 0, 0);
   }
 
-  // Scores of the chunk (lane: positions t0 + 16 m + 4 grp + r, head col).
-  __device__ __forceinline__ void score(const ChunkData<KB> &c, float (&s)[8]) const {
-    using L = Lay<KB>;
+  // Scores of the chunk in D layout (lane: slots 4 m + r, head col).
+  __device__ __forceinline__ void score(const ChunkData<KB, GP> &c, float (&s)[8]) const {
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       float4_t acc = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -275,67 +314,94 @@ struct Wave {
           acc = mma(a, bq[q].hi, acc);
           acc = mma(a, bq[q].lo, acc);
         }
-      } else {
-        uint32_t ad[16];   // byte addresses of the 16 code pairs (32-replica tables)
-        uint32_t adl[16];  // same in the lo table
-        if (KB == 3) {
-          const uint32_t w0 = c.k[m][0], w1 = c.k[m][1], w2 = c.k[m][2];
-          ad[0] = taddr<0, 63>(w0, rep4);
-          ad[1] = taddr<6, 63>(w0, rep4);
-          ad[2] = taddr<12, 63>(w0, rep4);
-          ad[3] = taddr<18, 63>(w0, rep4);
-          ad[4] = taddr<24, 63>(w0, rep4);
-          ad[5] = taddr<0, 63>(__builtin_amdgcn_alignbit(w1, w0, 30), rep4);
-          ad[6] = taddr<4, 63>(w1, rep4);
-          ad[7] = taddr<10, 63>(w1, rep4);
-          ad[8] = taddr<16, 63>(w1, rep4);
-          ad[9] = taddr<22, 63>(w1, rep4);
-          ad[10] = taddr<0, 63>(__builtin_amdgcn_alignbit(w2, w1, 28), rep4);
-          ad[11] = taddr<2, 63>(w2, rep4);
-          ad[12] = taddr<8, 63>(w2, rep4);
-          ad[13] = taddr<14, 63>(w2, rep4);
-          ad[14] = taddr<20, 63>(w2, rep4);
-          ad[15] = taddr<26, 63>(w2, rep4);
-#pragma unroll
-          for (int k = 0; k < 16; ++k) adl[k] = ad[k];
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t w = c.k[m][q];
-            ad[4 * q + 0] = taddr<0, 255>(w, rep4);
-            ad[4 * q + 1] = taddr<8, 255>(w, rep4);
-            ad[4 * q + 2] = taddr<16, 255>(w, rep4);
-            ad[4 * q + 3] = taddr<24, 255>(w, rep4);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) adl[4 * q + k] = ((ad[4 * q + k] >> 1) & 0x3fc0u) | rep4lo;
-          }
-        }
+      } else if (KB == 3) {
+        uint32_t ad[16];  // byte addresses of the 16 code pairs of the lane's 32 coordinates
+        const uint32_t w0 = c.k[m][0], w1 = c.k[m][1], w2 = c.k[m][2];
+        ad[0] = baddr6<0>(w0, rep4);
+        ad[1] = baddr6<6>(w0, rep4);
+        ad[2] = baddr6<12>(w0, rep4);
+        ad[3] = baddr6<18>(w0, rep4);
+        ad[4] = baddr6<24>(w0, rep4);
+        ad[5] = baddr6<0>(__builtin_amdgcn_alignbit(w1, w0, 30), rep4);
+        ad[6] = baddr6<4>(w1, rep4);
+        ad[7] = baddr6<10>(w1, rep4);
+        ad[8] = baddr6<16>(w1, rep4);
+        ad[9] = baddr6<22>(w1, rep4);
+        ad[10] = baddr6<0>(__builtin_amdgcn_alignbit(w2, w1, 28), rep4);
+        ad[11] = baddr6<2>(w2, rep4);
+        ad[12] = baddr6<8>(w2, rep4);
+        ad[13] = baddr6<14>(w2, rep4);
+        ad[14] = baddr6<20>(w2, rep4);
+        ad[15] = baddr6<26>(w2, rep4);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const half8_t ah = as_half8(lds_at<4 * L::khi>(lds, ad[4 * q]), lds_at<4 * L::khi>(lds, ad[4 * q + 1]),
-                                      lds_at<4 * L::khi>(lds, ad[4 * q + 2]), lds_at<4 * L::khi>(lds, ad[4 * q + 3]));
-          const half8_t al = as_half8(lds_at<4 * L::klo>(lds, adl[4 * q]), lds_at<4 * L::klo>(lds, adl[4 * q + 1]),
-                                      lds_at<4 * L::klo>(lds, adl[4 * q + 2]), lds_at<4 * L::klo>(lds, adl[4 * q + 3]));
+          const half8_t ah = as_half8(lds_at<kKhiOff3>(lds, ad[4 * q]), lds_at<kKhiOff3>(lds, ad[4 * q + 1]),
+                                      lds_at<kKhiOff3>(lds, ad[4 * q + 2]), lds_at<kKhiOff3>(lds, ad[4 * q + 3]));
+          const half8_t al = as_half8(lds_at_sep<kKloOff3>(lds, ad[4 * q]), lds_at_sep<kKloOff3>(lds, ad[4 * q + 1]),
+                                      lds_at_sep<kKloOff3>(lds, ad[4 * q + 2]), lds_at_sep<kKloOff3>(lds, ad[4 * q + 3]));
+          acc = mma(ah, bq[q].hi, acc);
+          acc = mma(al, bq[q].hi, acc);
+          acc = mma(ah, bq[q].lo, acc);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t w = c.k[m][q];
+          const uint32_t a0 = baddr<0>(w, rep4), a1 = baddr<1>(w, rep4);
+          const uint32_t a2 = baddr<2>(w, rep4), a3 = baddr<3>(w, rep4);
+          const half8_t ah = as_half8(lds_at<0>(lds, a0), lds_at<0>(lds, a1), lds_at<0>(lds, a2), lds_at<0>(lds, a3));
+          const half8_t al = as_half8(lds_at_sep<kKloOff4>(lds, a0), lds_at_sep<kKloOff4>(lds, a1),
+                                      lds_at_sep<kKloOff4>(lds, a2), lds_at_sep<kKloOff4>(lds, a3));
           acc = mma(ah, bq[q].hi, acc);
           acc = mma(al, bq[q].hi, acc);
           acc = mma(ah, bq[q].lo, acc);
         }
       }
-      const float nk[4] = {c.kn[m].x, c.kn[m].y, c.kn[m].z, c.kn[m].w};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s[4 * m + r] = KB ? acc[r] * nk[r] : acc[r];
+      for (int r = 0; r < 4; ++r) s[4 * m + r] = acc[r];
     }
   }
 
-  // Online softmax update (lazy: accumulators are rescaled only when the
-  // running maximum grows by more than 2^8); returns the value-MFMA B
-  // operands p n vscale as hi/lo fp16.
-  template <bool TAIL>
-  __device__ __forceinline__ void softmax(float (&s)[8], const float (&vn)[8], half8_t &bvh, half8_t &bvl) {
-    float cmax = s[0];
+  // D layout -> compact layout (see the struct comment).
+  __device__ __forceinline__ void compact(const float (&s)[8], float (&c)[NV]) const {
+    if (GP == 4) {
+      c[0] = s[0];
+      c[1] = s[1];
+      c[0] = dpp_f<kRowShr + 4, 0x2>(c[0], s[2]);
+      c[1] = dpp_f<kRowShr + 4, 0x2>(c[1], s[3]);
+      c[0] = dpp_f<kRowShr + 8, 0x4>(c[0], s[4]);
+      c[1] = dpp_f<kRowShr + 8, 0x4>(c[1], s[5]);
+      c[0] = dpp_f<kRowShr + 12, 0x8>(c[0], s[6]);
+      c[1] = dpp_f<kRowShr + 12, 0x8>(c[1], s[7]);
+    } else {
 #pragma unroll
-    for (int i = 1; i < 8; ++i) cmax = fmaxf(cmax, s[i]);
-    cmax = max16_32(cmax);
+      for (int j = 0; j < NV; ++j) c[j] = s[j];
+      c[0] = dpp_f<kRowShr + 8, 0xc>(c[0], s[4]);
+      c[1] = dpp_f<kRowShr + 8, 0xc>(c[1], s[5]);
+      c[2] = dpp_f<kRowShr + 8, 0xc>(c[2], s[6]);
+      c[3] = dpp_f<kRowShr + 8, 0xc>(c[3], s[7]);
+    }
+  }
+
+  // Compact hi/lo pair words -> B operand (4 words: slots 2 s2, 2 s2 + 1).
+  __device__ __forceinline__ half8_t expand(const uint32_t (&w)[NV / 2]) const {
+    if (GP == 4) {
+      return as_half8(w[0], dpp_u<kRowShl + 4>(w[0]), dpp_u<kRowShl + 8>(w[0]), dpp_u<kRowShl + 12>(w[0]));
+    } else {
+      return as_half8(w[0], w[1], dpp_u<kRowShl + 8>(w[0]), dpp_u<kRowShl + 8>(w[1]));
+    }
+  }
+
+  // Online softmax on compact scores (base-2 logits; -inf = masked).  The
+  // accumulators are only rescaled when the running maximum grows by more
+  // than 2^8.  Returns the value MFMA's B operand, p n vscale as hi + lo fp16.
+  template <bool TAIL>
+  __device__ __forceinline__ void softmax(const float (&c)[NV], const float (&vn)[NV], half8_t &bvh,
+                                          half8_t &bvl) {
+    float cmax = c[0];
+#pragma unroll
+    for (int j = 1; j < NV; ++j) cmax = fmaxf(cmax, c[j]);
+    cmax = head_max<GP>(cmax);
     const bool grow = cmax > m_run + kRescale;
     if (__ballot(grow)) {
       const float m_new = grow ? cmax : m_run;
@@ -345,30 +411,28 @@ struct Wave {
 #pragma unroll
       for (int i = 0; i < 8; ++i) accv[i] *= alpha;
     }
-    uint32_t bh[4], bl[4];
-    float lsum = 0.0f;
+    uint32_t wh[NV / 2], wl[NV / 2];
 #pragma unroll
-    for (int i = 0; i < 8; i += 2) {
-      float p0 = __builtin_amdgcn_exp2f(s[i] - m_run);
-      float p1 = __builtin_amdgcn_exp2f(s[i + 1] - m_run);
+    for (int j = 0; j < NV; j += 2) {
+      float p0 = __builtin_amdgcn_exp2f(c[j] - m_run);
+      float p1 = __builtin_amdgcn_exp2f(c[j + 1] - m_run);
       if (TAIL) {
-        p0 = (s[i] == -INFINITY) ? 0.0f : p0;
-        p1 = (s[i + 1] == -INFINITY) ? 0.0f : p1;
+        p0 = (c[j] == -INFINITY) ? 0.0f : p0;
+        p1 = (c[j + 1] == -INFINITY) ? 0.0f : p1;
       }
-      lsum += p0 + p1;
-      split_pair(p0 * vn[i], p1 * vn[i + 1], bh[i / 2], bl[i / 2]);
+      l_run += p0 + p1;
+      split_pair(p0 * vn[j], p1 * vn[j + 1], wh[j / 2], wl[j / 2]);
     }
-    l_run += lsum;
-    bvh = as_half8(bh[0], bh[1], bh[2], bh[3]);
-    bvl = as_half8(bl[0], bl[1], bl[2], bl[3]);
+    bvh = expand(wh);
+    bvl = expand(wl);
   }
 
   // Keep n vscale <= 32 for the norms of this chunk: if a larger norm shows
   // up, lower vscale (a power of two) and the accumulators with it.
-  __device__ __forceinline__ void fit_vscale(const float (&v4)[8]) {
-    float lm = v4[0];
+  __device__ __forceinline__ void fit_vscale(const float (&vraw)[NV]) {
+    float lm = vraw[0];
 #pragma unroll
-    for (int i = 1; i < 8; ++i) lm = fmaxf(lm, v4[i]);
+    for (int j = 1; j < NV; ++j) lm = fmaxf(lm, vraw[j]);
     if (__ballot(lm * vscale > 32.0f)) {
       for (int m = 32; m >= 1; m >>= 1) lm = fmaxf(lm, __shfl_xor(lm, m));
       const float nv = fminf(32.0f / pow2_ceil(lm), kVscaleMax);
@@ -379,20 +443,47 @@ struct Wave {
     }
   }
 
-  // Packed values: transpose the 8 code words and accumulate 8 tiles.
-  __device__ __forceinline__ void values(const ChunkData<KB> &c, const half8_t bvh, const half8_t bvl) {
-    using L = Lay<KB>;
-    uint32_t x[8];
+  // Optional raw scores (natural-log units) of the real heads.
+  template <bool TAIL>
+  __device__ __forceinline__ void store_scores(int t0, int we, const float (&c)[NV], float *scores,
+                                               long score_row0, int length) const {
+    const int h = col % GP;
+    if (h < G) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = c.v[i];
-    transpose8(x);
+      for (int j = 0; j < NV; ++j) {
+        const int t = t0 + cpos + j;
+        if (!TAIL || t < we) scores[(score_row0 + h) * length + t] = c[j] * kLn2;
+      }
+    }
+  }
+
+  // Packed values: pair the nibbles of slots 2 s2 and 2 s2 + 1 per byte (one
+  // byte per coordinate pair index), then 8 tiles of lookups and MFMAs.
+  __device__ __forceinline__ void values(const ChunkData<KB, GP> &c, const half8_t bvh, const half8_t bvl) {
+    uint32_t ev[4], od[4];  // bytes j: coordinates 8 col + 2 j (ev) and 8 col + 2 j + 1 (od)
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+      const uint32_t x0 = c.v[2 * s2], x1 = c.v[2 * s2 + 1];
+      ev[s2] = bfi(0x0f0f0f0fu, x0, x1 << 4);
+      od[s2] = bfi(0x0f0f0f0fu, x0 >> 4, x1);
+    }
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const uint32_t y = x[q];
-      const half8_t a = as_half8(lds_at<4 * L::vhi>(lds, taddr<0, 255>(y, rep4)),
-                                 lds_at<4 * L::vhi>(lds, taddr<8, 255>(y, rep4)),
-                                 lds_at<4 * L::vhi>(lds, taddr<16, 255>(y, rep4)),
-                                 lds_at<4 * L::vhi>(lds, taddr<24, 255>(y, rep4)));
+      const uint32_t *src = (q & 1) ? od : ev;
+      uint32_t a4[4];
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) {
+        const uint32_t w = src[s2];
+        uint32_t ad;
+        switch (q >> 1) {
+          case 0: ad = baddr<0>(w, rep4); break;
+          case 1: ad = baddr<1>(w, rep4); break;
+          case 2: ad = baddr<2>(w, rep4); break;
+          default: ad = baddr<3>(w, rep4); break;
+        }
+        a4[s2] = lds_at<0>(lds, ad);
+      }
+      const half8_t a = as_half8(a4[0], a4[1], a4[2], a4[3]);
       accv[q] = mma(a, bvh, accv[q]);
       accv[q] = mma(a, bvl, accv[q]);
     }
@@ -400,47 +491,39 @@ struct Wave {
 
   // One chunk of packed positions [t0, t0 + 32); positions >= we are masked.
   template <bool TAIL>
-  __device__ __forceinline__ void cold_chunk(int t0, int we, const ChunkData<KB> &c, float *scores,
-                                             long score_row, int length) {
-    float s[8], vn[8];
+  __device__ __forceinline__ void cold_chunk(int t0, int we, const ChunkData<KB, GP> &c, float *scores,
+                                             long score_row0, int length) {
+    float s[8], cs[NV], vn[NV];
     score(c, s);
-    const float v4[8] = {c.vn[0].x, c.vn[0].y, c.vn[0].z, c.vn[0].w, c.vn[1].x, c.vn[1].y, c.vn[1].z, c.vn[1].w};
-    fit_vscale(v4);
+    compact(s, cs);
+    fit_vscale(c.vn);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      vn[i] = v4[i] * vscale;
-      if (TAIL && t0 + 16 * (i >> 2) + 4 * grp + (i & 3) >= we) s[i] = -INFINITY;
+    for (int j = 0; j < NV; ++j) {
+      if (KB) cs[j] *= c.kn[j];
+      vn[j] = c.vn[j] * vscale;
+      if (TAIL && t0 + cpos + j >= we) cs[j] = -INFINITY;
     }
-    if (scores && col < G) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int t = t0 + 16 * (i >> 2) + 4 * grp + (i & 3);
-        if (!TAIL || t < we) scores[score_row * length + t] = s[i] * kLn2;
-      }
-    }
+    if (scores) store_scores<TAIL>(t0, we, cs, scores, score_row0, length);
     half8_t bvh, bvl;
-    softmax<TAIL>(s, vn, bvh, bvl);
+    softmax<TAIL>(cs, vn, bvh, bvl);
     values(c, bvh, bvl);
   }
 
   // One chunk of the fp16 hot window (delegated V), positions >= we masked.
-  __device__ __forceinline__ void hot_chunk(int t0, int we, const ChunkData<KB> &c, float *scores,
-                                            long score_row, int length) {
-    float s[8];
-    const float vn[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
+  __device__ __forceinline__ void hot_chunk(int t0, int we, const ChunkData<KB, GP> &c, float *scores,
+                                            long score_row0, int length) {
+    float s[8], cs[NV], vn[NV];
     score(c, s);
+    compact(s, cs);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (t0 + 16 * (i >> 2) + 4 * grp + (i & 3) >= we) s[i] = -INFINITY;
-    if (scores && col < G) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int t = t0 + 16 * (i >> 2) + 4 * grp + (i & 3);
-        if (t < we) scores[score_row * length + t] = s[i] * kLn2;
-      }
+    for (int j = 0; j < NV; ++j) {
+      if (KB) cs[j] *= c.kn[j];
+      vn[j] = 1.0f;
+      if (t0 + cpos + j >= we) cs[j] = -INFINITY;
     }
+    if (scores) store_scores<true>(t0, we, cs, scores, score_row0, length);
     half8_t bvh, bvl;
-    softmax<true>(s, vn, bvh, bvl);
+    softmax<true>(cs, vn, bvh, bvl);
     // fp16 ring rows: tile q covers coordinates 16 q + col
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
@@ -462,10 +545,10 @@ struct Wave {
     }
   }
 
-  // Write this wave's (max, sum, accumulator / vscale) for lanes col < G to
+  // Write this wave's (max, sum, accumulator / vscale) of the real heads to
   // the merge slot [G][D + 2]; `hot_layout` selects the coordinate order.
   __device__ __forceinline__ void to_slot(float *slot_base, bool hot_layout) const {
-    const float l_wave = sum16_32(l_run);
+    const float l_wave = head_sum<GP>(l_run);
     if (col < G) {
       float *slot = slot_base + col * (D + 2);
       if (grp == 0) {
@@ -503,9 +586,11 @@ __device__ __forceinline__ float merge_waves(const float *slots, int G, int i) {
   return v;
 }
 
-template <int KB>
+template <int KB, int GP>
 __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(const DecodeParams p) {
-  using L = Lay<KB>;
+  using L = Lay<GP>;
+  using WaveT = Wave<KB, GP>;
+  constexpr int NV = WaveT::NV;
   // Static LDS: its base address is a compile-time constant, so table reads
   // fold the table offset into the instruction.
   __shared__ uint32_t lds[L::total];
@@ -516,8 +601,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(const DecodePa
   const int G = p.q_heads / p.kv_heads;
   float *cent = reinterpret_cast<float *>(lds + L::cent);
   float *qw = reinterpret_cast<float *>(lds + L::qwork);
-  float *red = reinterpret_cast<float *>(lds + L::red);
-  int *flag = reinterpret_cast<int *>(red + 8);
+  int *flag = reinterpret_cast<int *>(lds + L::red);
   float *work = reinterpret_cast<float *>(lds);  // merge area after the main loop
 
   const int nsplit = p.n_cold_splits;
@@ -534,12 +618,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(const DecodePa
   const int we = min(s1, ws + per);
 
   constexpr bool k_packed = KB != 0;
-  constexpr int kRowBytes = Wave<KB>::kRowBytes;
-  Wave<KB> W;
+  constexpr int kRowBytes = WaveT::kRowBytes;
+  WaveT W;
   W.col = lane & 15;
   W.grp = lane >> 4;
-  W.rep4 = (lane & (kRep - 1)) * 4u;
-  W.rep4lo = (lane & (L::klo_rep - 1)) * 4u;
+  {
+    const int i0 = NV * (W.col / GP);  // first compact slot
+    W.cpos = 16 * (i0 >> 2) + 4 * W.grp + (i0 & 3);
+  }
+  W.rep4 = (lane & 31) * 4u;
   W.lds = lds;
   W.G = G;
   const long rowbase = static_cast<long>(unit) * p.capacity;
@@ -549,7 +636,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(const DecodePa
   W.vbase = reinterpret_cast<const char *>(p.v.codes) + rowbase * 64;
   W.vnbase = reinterpret_cast<const char *>(p.v.norms + rowbase);
   W.koff = static_cast<uint32_t>(W.col * kRowBytes + W.grp * (kRowBytes / 4));
-  W.knoff = static_cast<uint32_t>(16 * W.grp);
+  W.knoff = static_cast<uint32_t>(4 * W.cpos);
   W.voff = static_cast<uint32_t>(W.grp * 4 * 64 + W.col * 4);
   W.capacity = p.capacity;
   W.hot_len = p.v.hot > 0 ? p.v.hot : 1;
@@ -558,7 +645,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(const DecodePa
   W.reset();
 
   // ---- first chunk in flight while the block builds its tables --------
-  ChunkData<KB> A, B;
+  ChunkData<KB, GP> A, B;
   if (ws < we) W.load(ws, A);
 
   for (int i = threadIdx.x; i < kMaxLevels; i += kThreads) {
@@ -570,25 +657,24 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(const DecodePa
     qw[i] = k_packed ? x * sign_of(p.sign, i % D) : x;
   }
   __syncthreads();
-  // value table (for KB = 4 also the K hi table: one codebook)
+  // value table (for KB = 4 also the K hi table), 32 replicas per entry
   for (int i = threadIdx.x; i < 256 * kRep; i += kThreads) {
-    const int e = i / kRep;
-    lds[L::vhi + i] = pack_half2(cent[kMaxLevels + (e & 15)], cent[kMaxLevels + (e >> 4)]);
+    const int e = i / kRep, r = i % kRep;
+    const float c0 = cent[kMaxLevels + (e & 15)], c1 = cent[kMaxLevels + (e >> 4)];
+    lds[e * 64 + r] = pack_half2(c0, c1);
+    if (KB == 4) {
+      uint32_t h, l;
+      split_pair(cent[e & 15], cent[e >> 4], h, l);
+      lds[e * 64 + 32 + r] = l;
+    }
   }
   if (KB == 3) {
     for (int i = threadIdx.x; i < 64 * kRep; i += kThreads) {
-      const int e = i / kRep;
+      const int e = i / kRep, r = i % kRep;
       uint32_t h, l;
       split_pair(cent[e & 7], cent[e >> 3], h, l);
-      lds[L::khi + i] = h;
-      lds[L::klo + i] = l;
-    }
-  } else if (KB == 4) {
-    for (int i = threadIdx.x; i < 256 * L::klo_rep; i += kThreads) {
-      const int e = i / L::klo_rep;
-      uint32_t h, l;
-      split_pair(cent[e & 15], cent[e >> 4], h, l);
-      lds[L::klo + i] = l;
+      lds[e * 64 + 32 + r] = h;
+      lds[(64 + e) * 64 + 32 + r] = l;
     }
   }
   if (k_packed) {
@@ -622,25 +708,24 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(const DecodePa
 
   // ---- main loop: chunk t0 is processed while chunk t0 + 32 loads into the
   // other of two register buffers (ping-pong, so nothing is copied) --------
-  const long score_row = hq0 + W.col;
   if (ws < we) {
     int t0 = ws;
     for (;;) {
       const bool nb = t0 + kChunk < we;
       if (nb) W.load(t0 + kChunk, B);
       if (t0 + kChunk <= we) {
-        W.template cold_chunk<false>(t0, we, A, p.scores, score_row, p.length);
+        W.template cold_chunk<false>(t0, we, A, p.scores, hq0, p.length);
       } else {
-        W.template cold_chunk<true>(t0, we, A, p.scores, score_row, p.length);
+        W.template cold_chunk<true>(t0, we, A, p.scores, hq0, p.length);
       }
       t0 += kChunk;
       if (!nb) break;
       const bool na = t0 + kChunk < we;
       if (na) W.load(t0 + kChunk, A);
       if (t0 + kChunk <= we) {
-        W.template cold_chunk<false>(t0, we, B, p.scores, score_row, p.length);
+        W.template cold_chunk<false>(t0, we, B, p.scores, hq0, p.length);
       } else {
-        W.template cold_chunk<true>(t0, we, B, p.scores, score_row, p.length);
+        W.template cold_chunk<true>(t0, we, B, p.scores, hq0, p.length);
       }
       t0 += kChunk;
       if (!na) break;
@@ -680,14 +765,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(const DecodePa
     W.vscale = 1.0f;
     for (int t0 = hs; t0 < he; t0 += kChunk) {
       W.load(t0, A);
-      W.hot_chunk(t0, he, A, p.scores, score_row, p.length);
+      W.hot_chunk(t0, he, A, p.scores, hq0, p.length);
     }
     W.to_slot(work + wave * G * (D + 2), true);
     __syncthreads();
     for (int i = threadIdx.x; i < G * (D + 2); i += kThreads) hotp[i] = merge_waves(work, G, i);
     __syncthreads();
   }
-
   // Every load below is independent of the others, so each thread has all of
   // its partial results in flight at once.  Thread (h, j4) owns head h,
   // coordinates 4 j4 .. 4 j4 + 3.
@@ -779,18 +863,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(const DecodePa
 }  // namespace
 
 size_t decode_mfma_lds_bytes(int k_bits, bool share_lut, int G) {
+  (void)k_bits;
   (void)share_lut;
-  switch (k_bits) {
-    case 0: return G <= Lay<0>::max_g ? 4 * size_t(Lay<0>::total) : ~size_t(0);
-    case 3: return G <= Lay<3>::max_g ? 4 * size_t(Lay<3>::total) : ~size_t(0);
-    case 4: return G <= Lay<4>::max_g ? 4 * size_t(Lay<4>::total) : ~size_t(0);
-    default: return ~size_t(0);
-  }
+  if (G <= 4) return 4 * size_t(Lay<4>::total);
+  if (G <= 8) return 4 * size_t(Lay<8>::total);
+  return ~size_t(0);
 }
 
 bool decode_mfma_supported(const DecodeParams &p) {
   const int G = p.q_heads / p.kv_heads;
-  if (p.head_dim != D || G > 16) return false;
+  if (p.head_dim != D || G > 8) return false;
   if (!(p.v.mode == TQ_SIDE_PACKED || p.v.mode == TQ_SIDE_DELEGATED) || p.v.bits != 4) return false;
   int kb;
   if (p.k.mode == TQ_SIDE_FP16) {
@@ -802,22 +884,33 @@ bool decode_mfma_supported(const DecodeParams &p) {
   } else {
     return false;
   }
-  return decode_mfma_lds_bytes(kb, p.share_lut != 0, G) <= 65536;
+  (void)kb;
+  return true;
 }
 
 int decode_mfma_max_splits() { return kMaxSplits; }
 
+template <int KB>
+void launch_kb(const DecodeParams &p, dim3 grid, hipStream_t stream) {
+  const int G = p.q_heads / p.kv_heads;
+  if (G <= 4) {
+    hipLaunchKernelGGL((decode_mfma_kernel<KB, 4>), grid, dim3(kThreads), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((decode_mfma_kernel<KB, 8>), grid, dim3(kThreads), 0, stream, p);
+  }
+}
+
 hipError_t launch_decode_mfma(const DecodeParams &p, hipStream_t stream) {
   const int G = p.q_heads / p.kv_heads;
   const int kb = p.k.mode == TQ_SIDE_PACKED ? p.k.bits : 0;
-  if (decode_mfma_lds_bytes(kb, p.share_lut != 0, G) > 65536) return hipErrorInvalidValue;
+  if (G < 1 || G > 8 || p.head_dim != D) return hipErrorInvalidValue;
   const int nsplit = p.n_cold_splits;
   if (nsplit < 1 || nsplit > kMaxSplits || p.n_hot_splits != 0) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(p.batch * p.kv_heads * nsplit));
   switch (kb) {
-    case 0: hipLaunchKernelGGL(decode_mfma_kernel<0>, grid, dim3(kThreads), 0, stream, p); break;
-    case 3: hipLaunchKernelGGL(decode_mfma_kernel<3>, grid, dim3(kThreads), 0, stream, p); break;
-    case 4: hipLaunchKernelGGL(decode_mfma_kernel<4>, grid, dim3(kThreads), 0, stream, p); break;
+    case 0: launch_kb<0>(p, grid, stream); break;
+    case 3: launch_kb<3>(p, grid, stream); break;
+    case 4: launch_kb<4>(p, grid, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
