@@ -648,13 +648,35 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(const DecodePa
   ChunkData<KB, GP> A, B;
   if (ws < we) W.load(ws, A);
 
+  // wave h < G takes query head h, coordinates lane and lane + 64
+  float qa = 0.0f, qb = 0.0f;
+  if (wave < G) {
+    qa = h2f(p.q[(hq0 + wave) * D + lane]);
+    qb = h2f(p.q[(hq0 + wave) * D + lane + 64]);
+  }
   for (int i = threadIdx.x; i < kMaxLevels; i += kThreads) {
     cent[i] = p.k_cent[i];
     cent[kMaxLevels + i] = p.v_cent[i];
   }
-  for (int i = threadIdx.x; i < G * D; i += kThreads) {
-    const float x = h2f(p.q[hq0 * D + i]);
-    qw[i] = k_packed ? x * sign_of(p.sign, i % D) : x;
+  // rotate q in registers: H diag(s) q (unnormalised), butterflies at
+  // stride 64 inside the lane and at strides 32 .. 1 across lanes
+  if (k_packed && wave < G) {
+    qa *= sign_of(p.sign, lane);
+    qb *= sign_of(p.sign, lane + 64);
+    const float a = qa + qb, c = qa - qb;
+    qa = a;
+    qb = c;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      const float pa = __shfl_xor(qa, m), pb = __shfl_xor(qb, m);
+      const bool upper = (lane & m) != 0;
+      qa = upper ? pa - qa : qa + pa;
+      qb = upper ? pb - qb : qb + pb;
+    }
+  }
+  if (wave < G) {
+    qw[wave * D + lane] = qa;
+    qw[wave * D + lane + 64] = qb;
   }
   __syncthreads();
   // value table (for KB = 4 also the K hi table), 32 replicas per entry
@@ -677,19 +699,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(const DecodePa
       lds[(64 + e) * 64 + 32 + r] = l;
     }
   }
-  if (k_packed) {
-    for (int s = 1; s < D; s <<= 1) {
-      for (int i = threadIdx.x; i < G * D / 2; i += kThreads) {
-        const int h = i / (D / 2), r = i % (D / 2);
-        const int j = (r / s) * 2 * s + (r % s);
-        const float a = qw[h * D + j], c = qw[h * D + j + s];
-        qw[h * D + j] = a + c;
-        qw[h * D + j + s] = a - c;
-      }
-      __syncthreads();
-    }
-  }
-  __syncthreads();
+  __syncthreads();  // tables complete before the first lookup
   {
     const float qscale = k_packed ? kLog2e / static_cast<float>(D) : kLog2e / sqrtf(static_cast<float>(D));
 #pragma unroll
@@ -774,89 +784,83 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(const DecodePa
   }
   // Every load below is independent of the others, so each thread has all of
   // its partial results in flight at once.  Thread (h, j4) owns head h,
-  // coordinates 4 j4 .. 4 j4 + 3.
+  // coordinates 4 j4 .. 4 j4 + 3; the 32 threads of a head sit in one wave,
+  // so the inverse rotation needs no block barrier.
+  if (threadIdx.x >= G * (D / 4)) return;
   const float *up = part + static_cast<long>(unit) * nsplit * G * (D + 2);
-  float *rot = work;          // [G][D] rotated-domain sum (overwrites the slots)
-  float *pln = work + G * D;  // [G][D] plain (hot) sum
-  float *Ls = pln + G * D;    // [G] total sums
+  const int hh = threadIdx.x / (D / 4);
+  const int jj = 4 * (threadIdx.x % (D / 4));
   float r4[4] = {0.0f, 0.0f, 0.0f, 0.0f}, q4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   float Lt = 0.0f;
-  int hh = 0, jj = 0;
-  const bool mine = threadIdx.x < G * (D / 4);
-  if (mine) {
-    hh = threadIdx.x / (D / 4);
-    jj = 4 * (threadIdx.x % (D / 4));
-    float M = -INFINITY;
-    for (int sp0 = 0; sp0 < nsplit; sp0 += 16) {
-      float mv[16], lv[16], ov[16][4];
+  float M = -INFINITY;
+  for (int sp0 = 0; sp0 < nsplit; sp0 += 16) {
+    float mv[16], lv[16], ov[16][4];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int sp = min(sp0 + k, nsplit - 1);
-        const float *src = up + (sp * G + hh) * (D + 2);
-        mv[k] = (sp0 + k < nsplit) ? load_coherent(src) : -INFINITY;
-        lv[k] = load_coherent(src + 1);
+    for (int k = 0; k < 16; ++k) {
+      const int sp = min(sp0 + k, nsplit - 1);
+      const float *src = up + (sp * G + hh) * (D + 2);
+      mv[k] = (sp0 + k < nsplit) ? load_coherent(src) : -INFINITY;
+      lv[k] = load_coherent(src + 1);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ov[k][e] = load_coherent(src + 2 + jj + e);
-      }
-      float mg = M;
-#pragma unroll
-      for (int k = 0; k < 16; ++k) mg = fmaxf(mg, mv[k]);
-      if (mg == -INFINITY) continue;
-      const float a = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - mg);
-      M = mg;
-      Lt *= a;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) r4[e] *= a;
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const float w = (mv[k] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mv[k] - M);
-        Lt += w * lv[k];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) r4[e] += w * ov[k][e];
-      }
+      for (int e = 0; e < 4; ++e) ov[k][e] = load_coherent(src + 2 + jj + e);
     }
-    if (has_hot) {
-      const float mh = hotp[hh * (D + 2)];
-      if (mh != -INFINITY) {
-        const float mg = fmaxf(M, mh);
-        const float a = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - mg);
-        const float bh = __builtin_amdgcn_exp2f(mh - mg);
-        Lt = Lt * a + bh * hotp[hh * (D + 2) + 1];
+    float mg = M;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          r4[e] *= a;
-          q4[e] = bh * hotp[hh * (D + 2) + 2 + jj + e];
-        }
+    for (int k = 0; k < 16; ++k) mg = fmaxf(mg, mv[k]);
+    if (mg == -INFINITY) continue;
+    const float a = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - mg);
+    M = mg;
+    Lt *= a;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r4[e] *= a;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float w = (mv[k] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mv[k] - M);
+      Lt += w * lv[k];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r4[e] += w * ov[k][e];
+    }
+  }
+  if (has_hot) {
+    const float mh = hotp[hh * (D + 2)];
+    if (mh != -INFINITY) {
+      const float mg = fmaxf(M, mh);
+      const float a = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - mg);
+      const float bh = __builtin_amdgcn_exp2f(mh - mg);
+      Lt = Lt * a + bh * hotp[hh * (D + 2) + 1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        r4[e] *= a;
+        q4[e] = bh * hotp[hh * (D + 2) + 2 + jj + e];
       }
     }
   }
-  __syncthreads();  // hot partial and slots no longer needed
-  if (mine) {
+  // inverse rotation diag(s) H / sqrt(d): butterflies at strides 1 and 2
+  // inside the thread, strides 4 .. 64 across the head's 32 lanes
+  {
+    const float b0 = r4[0] + r4[1], b1 = r4[0] - r4[1], b2 = r4[2] + r4[3], b3 = r4[2] - r4[3];
+    r4[0] = b0 + b2;
+    r4[1] = b1 + b3;
+    r4[2] = b0 - b2;
+    r4[3] = b1 - b3;
+  }
+#pragma unroll
+  for (int m = 1; m < 32; m <<= 1) {
+    const bool upper = (threadIdx.x & m) != 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      rot[hh * D + jj + e] = r4[e];
-      pln[hh * D + jj + e] = q4[e];
+      const float pe = __shfl_xor(r4[e], m);
+      r4[e] = upper ? pe - r4[e] : r4[e] + pe;
     }
-    if (jj == 0) Ls[hh] = Lt;
-  }
-  __syncthreads();
-  for (int s = 1; s < D; s <<= 1) {
-    for (int i = threadIdx.x; i < G * D / 2; i += kThreads) {
-      const int h = i / (D / 2), r = i % (D / 2);
-      const int j = (r / s) * 2 * s + (r % s);
-      const float a = rot[h * D + j], c = rot[h * D + j + s];
-      rot[h * D + j] = a + c;
-      rot[h * D + j + s] = a - c;
-    }
-    __syncthreads();
   }
   const float rs = 1.0f / sqrtf(static_cast<float>(D));
-  for (int i = threadIdx.x; i < G * D; i += kThreads) {
-    const int h = i / D, j = i % D;
-    const float Lh = Ls[h];
-    const float o = rot[i] * sign_of(p.sign, j) * rs + pln[i];
-    p.out[(hq0 + h) * D + j] = (Lh > 0.0f) ? o / Lh : 0.0f;
-  }
+  const float inv = (Lt > 0.0f) ? 1.0f / Lt : 0.0f;
+  float4 o;
+  o.x = (r4[0] * sign_of(p.sign, jj) * rs + q4[0]) * inv;
+  o.y = (r4[1] * sign_of(p.sign, jj + 1) * rs + q4[1]) * inv;
+  o.z = (r4[2] * sign_of(p.sign, jj + 2) * rs + q4[2]) * inv;
+  o.w = (r4[3] * sign_of(p.sign, jj + 3) * rs + q4[3]) * inv;
+  *reinterpret_cast<float4 *>(p.out + (hq0 + hh) * D + jj) = o;
   if (threadIdx.x == 0) __hip_atomic_store(p.counters + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
