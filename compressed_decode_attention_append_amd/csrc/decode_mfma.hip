@@ -56,8 +56,12 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int D = 128;
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
+// Waves per block: 12 for packed K (about 160 registers a lane, so three
+// waves a SIMD), 8 for fp16 K rows (about 250 registers, two a SIMD).  One
+// block per compute unit either way.
+template <int KB>
+constexpr int waves_of() { return KB == 0 ? 8 : 12; }
+constexpr int kMaxWaves = 12;
 constexpr int kChunk = 32;
 constexpr int kRep = 32;          // pair-table replicas, one per LDS bank
 constexpr int kMaxSplits = 256;   // splits per unit (bounded by the host)
@@ -88,7 +92,7 @@ struct Lay {
   static constexpr int qwork = cent + 2 * kMaxLevels;  // [GP][D] rotated query
   static constexpr int red = qwork + GP * D;           // flag
   static constexpr int total = red + 16;
-  static_assert((kWaves + 1) * GP * (D + 2) <= kTableWords, "merges must fit in the table area");
+  static_assert((kMaxWaves + 1) * GP * (D + 2) <= kTableWords, "merges must fit in the table area");
 };
 
 __device__ __forceinline__ float4_t mma(const half8_t a, const half8_t b, float4_t c) {
@@ -568,18 +572,19 @@ struct Wave {
   }
 };
 
-// Merge kWaves slots [w][G][D + 2] into one (max, sum, accumulator) per head
+// Merge NW slots [w][G][D + 2] into one (max, sum, accumulator) per head
 // element i of [G][D + 2].
+template <int NW>
 __device__ __forceinline__ float merge_waves(const float *slots, int G, int i) {
   const int h = i / (D + 2), j = i % (D + 2);
   float M = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, slots[(w * G + h) * (D + 2)]);
+  for (int w = 0; w < NW; ++w) M = fmaxf(M, slots[(w * G + h) * (D + 2)]);
   if (M == -INFINITY) return (j == 0) ? -INFINITY : 0.0f;
   if (j == 0) return M;
   float v = 0.0f;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const float mw = slots[(w * G + h) * (D + 2)];
     if (mw != -INFINITY) v += __builtin_amdgcn_exp2f(mw - M) * slots[(w * G + h) * (D + 2) + j];
   }
@@ -587,7 +592,9 @@ __device__ __forceinline__ float merge_waves(const float *slots, int G, int i) {
 }
 
 template <int KB, int GP>
-__global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(const DecodeParams p) {
+  constexpr int kWaves = waves_of<KB>();
+  constexpr int kThreads = 64 * kWaves;
   using L = Lay<GP>;
   using WaveT = Wave<KB, GP>;
   constexpr int NV = WaveT::NV;
@@ -716,11 +723,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(const DecodePa
     }
   }
 
-  // ---- main loop: chunk t0 is processed while chunk t0 + 32 loads into the
-  // other of two register buffers (ping-pong, so nothing is copied) --------
-  if (ws < we) {
-    int t0 = ws;
-    for (;;) {
+  // ---- main loop: chunk i is processed while chunk i + 1 loads into the
+  // other of two register buffers (ping-pong, so nothing is copied); chunk i
+  // sits in A for even i, in B for odd i.  Only the wave's last chunk can be
+  // partial: it runs after the loop, so the loop body has no masking -------
+  if (KB == 0) {
+    // fp16 K rows (32 dwords a buffer): the same ping-pong with the masked
+    // variant inside the loop keeps this shape within its registers
+    for (int t0 = ws; t0 < we;) {
       const bool nb = t0 + kChunk < we;
       if (nb) W.load(t0 + kChunk, B);
       if (t0 + kChunk <= we) {
@@ -740,6 +750,25 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(const DecodePa
       t0 += kChunk;
       if (!na) break;
     }
+  } else {
+    const int n = (we - ws + kChunk - 1) / kChunk;  // chunks, the partial one included
+    const int nf = (we - ws) / kChunk;              // full chunks
+    int i = 0;
+    while (i < nf) {
+      if (i + 1 < n) W.load(ws + (i + 1) * kChunk, B);
+      W.template cold_chunk<false>(ws + i * kChunk, we, A, p.scores, hq0, p.length);
+      if (++i >= nf) break;
+      if (i + 1 < n) W.load(ws + (i + 1) * kChunk, A);
+      W.template cold_chunk<false>(ws + i * kChunk, we, B, p.scores, hq0, p.length);
+      ++i;
+    }
+    if (i < n) {
+      if (i & 1) {
+        W.template cold_chunk<true>(ws + i * kChunk, we, B, p.scores, hq0, p.length);
+      } else {
+        W.template cold_chunk<true>(ws + i * kChunk, we, A, p.scores, hq0, p.length);
+      }
+    }
   }
 
   // ---- merge the waves of this block (tables are dead from here on) -----
@@ -748,7 +777,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(const DecodePa
   __syncthreads();
   float *part = reinterpret_cast<float *>(reinterpret_cast<char *>(p.ws) + p.ws_part_off);
   float *mypart = part + (static_cast<long>(unit) * nsplit + split) * G * (D + 2);
-  for (int i = threadIdx.x; i < G * (D + 2); i += kThreads) store_coherent(mypart + i, merge_waves(work, G, i));
+  for (int i = threadIdx.x; i < G * (D + 2); i += kThreads) store_coherent(mypart + i, merge_waves<kWaves>(work, G, i));
 
   // ---- the last block of the unit merges the splits ----------------------
   // The partials above are L2-coherent stores; once they have completed
@@ -779,7 +808,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(const DecodePa
     }
     W.to_slot(work + wave * G * (D + 2), true);
     __syncthreads();
-    for (int i = threadIdx.x; i < G * (D + 2); i += kThreads) hotp[i] = merge_waves(work, G, i);
+    for (int i = threadIdx.x; i < G * (D + 2); i += kThreads) hotp[i] = merge_waves<kWaves>(work, G, i);
     __syncthreads();
   }
   // Every load below is independent of the others, so each thread has all of
@@ -898,9 +927,9 @@ template <int KB>
 void launch_kb(const DecodeParams &p, dim3 grid, hipStream_t stream) {
   const int G = p.q_heads / p.kv_heads;
   if (G <= 4) {
-    hipLaunchKernelGGL((decode_mfma_kernel<KB, 4>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((decode_mfma_kernel<KB, 4>), grid, dim3(64 * waves_of<KB>()), 0, stream, p);
   } else {
-    hipLaunchKernelGGL((decode_mfma_kernel<KB, 8>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((decode_mfma_kernel<KB, 8>), grid, dim3(64 * waves_of<KB>()), 0, stream, p);
   }
 }
 
