@@ -90,7 +90,8 @@ def cpu_baseline(w, budget_s: float = 12.0):
     kb, vb = w["k"][1], w["v"][1]
     R = oracle.rotation_matrix(0, d)
     units, spent, nbytes = 0, 0.0, 0
-    while spent < budget_s and units < 64:
+    total_units = w["batch"] * w["kv_heads"]
+    while spent < budget_s and units < total_units:
         k, v = synth.kv_numpy(1000 + units, 1, 1, T, d, dist=w["dist"], outlier_frac=w["outlier_frac"])
         q = synth.q_numpy(1000 + units, 1, G, d)
         kc, kt = oracle.lloyd_max(d, kb) if w["k"][0] != "fp16" else (None, None)
@@ -112,8 +113,114 @@ def cpu_baseline(w, budget_s: float = 12.0):
         units += 1
         nbytes += (side_bytes_per_token(w["k"][0], kb, d) + side_bytes_per_token(w["v"][0], vb, d)) * T
     return {"value": nbytes / spent / 1e9, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{units} of {w['batch'] * w['kv_heads']} (batch, KV head) units of one layer's "
+            "sample": f"{units} of {total_units} (batch, KV head) units of one layer's "
                       f"decode at context {T} (unpack + dequantize + float64 attention), {spent:.1f} s"}
+
+
+DECODE_SOURCE = os.path.join(ROOT, "compressed_decode_attention_append_amd", "csrc", "decode_mfma.hip")
+
+
+def source_digest(path=DECODE_SOURCE) -> str:
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"decode_mfma_{workload}_hbm_traffic.txt")
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per decode launch from the committed counter summary, or None
+    when there is none or the kernel source changed since it was taken."""
+    path = traffic_file(workload)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("source_sha256") != source_digest():
+        return None
+    try:
+        return int(float(fields["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def counter_summary(fetch_csv: str, write_csv: str, workload: str, copy_mib: int, cmds: list):
+    """Summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per
+    dispatch) of `bench.py --copy-mib N`: the plain copy kernel of known size
+    calibrates each counter, the decode kernel's per-launch HBM bytes follow."""
+    import csv
+    import collections
+
+    def read(path, counter):
+        acc = collections.defaultdict(list)
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    acc[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
+
+    fetch, nf = read(fetch_csv, "FETCH_SIZE")
+    write, nw = read(write_csv, "WRITE_SIZE")
+    copy_name = next(k for k in fetch if "neg_kernel" in k)
+    dec_name = next(k for k in fetch if "decode_mfma_kernel" in k)
+    kib = copy_mib * 1024.0
+    f_fetch = kib / fetch[copy_name]
+    f_write = kib / write[copy_name]
+    w = WORKLOADS[workload]
+    traffic = (fetch[dec_name] * f_fetch + write[dec_name] * f_write) * 1024.0
+    short = dec_name.replace("void tq::(anonymous namespace)::", "").split("(tq::")[0]
+    out = [f"# rocprofv3 hardware byte counters: {short}, workload {workload}",
+           "# commands (from the repository root):"]
+    out += [f"#   {c}" for c in cmds]
+    out += ["#",
+            f"# calibration: a plain copy of {copy_mib} MiB (torch.neg, reads and writes {copy_mib} MiB)",
+            f"#   FETCH_SIZE {fetch[copy_name]:.1f} KiB -> factor {f_fetch:.4f}; "
+            f"WRITE_SIZE {write[copy_name]:.1f} KiB -> factor {f_write:.4f}",
+            f"# {short}: {nf[dec_name]} dispatches; FETCH_SIZE {fetch[dec_name]:.1f} KiB, "
+            f"WRITE_SIZE {write[dec_name]:.1f} KiB per dispatch (raw)",
+            f"kernel: {short}",
+            f"workload: {workload}",
+            f"source_sha256: {source_digest()}",
+            f"fetch_bytes_per_launch: {fetch[dec_name] * f_fetch * 1024.0:.0f}",
+            f"write_bytes_per_launch: {write[dec_name] * f_write * 1024.0:.0f}",
+            f"traffic_bytes_per_launch: {traffic:.0f}",
+            f"algorithmic_bytes_per_launch: {decode_bytes(w)}",
+            f"traffic_over_algorithmic: {traffic / decode_bytes(w):.4f}"]
+    return "\n".join(out) + "\n"
+
+
+def stats_summary(stats_csv: str, workload: str, cmds: list):
+    """Format a rocprofv3 --kernel-trace --stats kernel table (this library's
+    kernels only)."""
+    import csv
+    rows = []
+    with open(stats_csv) as f:
+        for r in csv.DictReader(f):
+            name = r["Name"]
+            if "tq::" not in name:
+                continue
+            short = name.replace("void tq::(anonymous namespace)::", "").split("(tq::")[0]
+            rows.append((short, int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                         float(r["MaxNs"]) / 1e3))
+    w = WORKLOADS[workload]
+    out = [f"# rocprofv3 kernel statistics, workload {workload}: batch {w['batch']}, {w['kv_heads']} KV heads, "
+           f"{w['q_heads']} query heads, head_dim {w['head_dim']}, context {w['tokens']}, "
+           f"K {w['k'][0]}{w['k'][1] or ''}, V {w['v'][0]}{w['v'][1]}",
+           "# commands (from the repository root):"]
+    out += [f"#   {c}" for c in cmds]
+    out += [f"# decode algorithmic bytes per launch: {decode_bytes(w)}",
+            "", f"{'kernel':44s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}"]
+    for short, calls, avg, mn, mx in sorted(rows):
+        out.append(f"{short:44s} {calls:6d} {avg:9.2f} {mn:9.2f} {mx:9.2f}")
+        if "decode_mfma" in short or "decode_split" in short:
+            out.append(f"#   -> {decode_bytes(w) / (avg * 1e-6) / 1e9:.1f} GB/s over the algorithmic bytes")
+    return "\n".join(out) + "\n"
 
 
 def main():
@@ -129,7 +236,21 @@ def main():
                     help="first run one plain device copy of this many MiB (a known-size "
                          "calibration kernel for hardware byte counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--counter-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
+                         "script with --copy-mib and print the traffic summary; runs nothing")
+    ap.add_argument("--command", action="append", default=[],
+                    help="with --counter-summary: a command line to record in the summary")
+    ap.add_argument("--stats-summary", metavar="KERNEL_STATS_CSV",
+                    help="format a rocprofv3 --stats kernel table of this script's run; runs nothing")
     args = ap.parse_args()
+    if args.stats_summary:
+        sys.stdout.write(stats_summary(args.stats_summary, args.workload, args.command))
+        return
+    if args.counter_summary:
+        sys.stdout.write(counter_summary(args.counter_summary[0], args.counter_summary[1], args.workload,
+                                         args.copy_mib or 256, args.command))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}), flush=True)
         sys.exit(2)
@@ -242,7 +363,7 @@ def main():
         "decode_us_per_layer": round(dec_avg_s * 1e6, 2),
         "decode_bytes_per_layer": dbytes,
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(args.workload)},
     }
     if n_new:
         app_avg_s = app_ms / (len(rec) * Lyr) / 1e3

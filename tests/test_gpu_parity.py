@@ -212,8 +212,10 @@ def test_decode_attention(case, variant):
     vr = _oracle_rows(cache, "v", T)
     o_ref, s_ref = oracle.decode_attention(q, kr, vr)
     ok, worst = rows_close(sc.cpu().numpy(), s_ref)
+    print(f"{case[0]} {variant}: scores worst rel {worst:.3e}")
     assert ok, f"scores: worst {worst}"
     ok, worst = rows_close(out.cpu().numpy(), o_ref)
+    print(f"{case[0]} {variant}: out worst rel {worst:.3e}")
     assert ok, f"out: worst {worst}"
 
 
