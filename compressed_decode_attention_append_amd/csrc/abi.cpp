@@ -250,6 +250,7 @@ int tq_quantize_append(const tq_cache *cache, const void *k_new, const void *v_n
   p.capacity = cache->capacity;
   p.n_new = n_new;
   p.offset = offset;
+  p.side_mask = 3;
   fill_signs(cache->seed, d, p.sign);
   copy_levels(cache->k, cache->k.thresholds, (1 << cache->k.bits) - 1, p.k_thr);
   copy_levels(cache->v, cache->v.thresholds, (1 << cache->v.bits) - 1, p.v_thr);

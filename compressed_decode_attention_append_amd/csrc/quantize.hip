@@ -10,6 +10,9 @@
 // by 1/(n sqrt(D)), finds each code by binary search over the thresholds and
 // assembles the LSB-first words with shuffles, so each packed row leaves in
 // one coalesced store.
+#include <stdlib.h>
+#include <string.h>
+
 #include "tq_common.h"
 #include "tq_device.h"
 
@@ -17,6 +20,13 @@ namespace tq {
 namespace {
 
 constexpr int kBlock = 256;
+
+// TQ_QUANTIZE_VARIANT=plain forces the kernel below for every side (A/B
+// measurements and the cross-check tests).
+bool getenv_plain() {
+  const char *e = getenv("TQ_QUANTIZE_VARIANT");
+  return e && strcmp(e, "plain") == 0;
+}
 
 // Encode one row held as four elements per lane.  Writes words and norm when
 // `write` is set for this group (all lanes of the wave must call this, since
@@ -86,10 +96,13 @@ __global__ __launch_bounds__(kBlock) void quantize_append_kernel(const QuantizeP
 
   const int t = threadIdx.x % TPR;
   const long per_side = static_cast<long>(p.batch) * p.heads * p.n_new;
-  const long task = static_cast<long>(blockIdx.x) * (kBlock / TPR) + threadIdx.x / TPR;
+  // tasks: rows of the sides in p.side_mask (K rows first)
+  const long first = (p.side_mask == 2) ? per_side : 0;
+  const long n_tasks = (p.side_mask == 3) ? 2 * per_side : per_side;
+  const long task = first + static_cast<long>(blockIdx.x) * (kBlock / TPR) + threadIdx.x / TPR;
   // Out-of-range groups still run the shuffles of a (dummy) row so that the
   // wave stays converged; they store nothing.
-  const bool live = task < 2 * per_side;
+  const bool live = task < first + n_tasks;
   const int side = live ? static_cast<int>(task / per_side) : 0;
   const long r = live ? task % per_side : 0;
   const long bh = r / p.n_new;
@@ -135,7 +148,7 @@ __global__ __launch_bounds__(kBlock) void quantize_append_kernel(const QuantizeP
 template <int D>
 hipError_t launch_d(const QuantizeParams &p, hipStream_t stream) {
   constexpr int TPR = D / 4;
-  const long tasks = 2L * p.batch * p.heads * p.n_new;
+  const long tasks = (p.side_mask == 3 ? 2L : 1L) * p.batch * p.heads * p.n_new;
   const long blocks = (tasks + (kBlock / TPR) - 1) / (kBlock / TPR);
   hipLaunchKernelGGL(quantize_append_kernel<D>, dim3(static_cast<unsigned>(blocks)),
                      dim3(kBlock), 0, stream, p);
@@ -144,12 +157,36 @@ hipError_t launch_d(const QuantizeParams &p, hipStream_t stream) {
 
 }  // namespace
 
+// Packed sides at head_dim 128 with 1..4 bits and appends of at least 16
+// rows go to the matrix-core encoder; everything else (other head sizes and
+// widths, fp16 copies, the delegated ring, short appends) to the kernel
+// above.  Both write the same bytes.
 hipError_t launch_quantize_append(const QuantizeParams &p, hipStream_t stream) {
+  QuantizeParams m = p;
+  m.k_lut_scale = m.v_lut_scale = 0.0f;
+  int rest = 3;
+  if (p.head_dim == 128 && p.n_new >= 16 && !getenv_plain()) {
+    for (int side = 0; side < 2; ++side) {
+      const SideDev &s = side ? p.v : p.k;
+      if (s.mode != TQ_SIDE_PACKED || s.bits < 1 || s.bits > 4) continue;
+      const float sc = quantize_lut_scale(side ? p.v_thr : p.k_thr, s.bits);
+      if (sc <= 0.0f) continue;
+      (side ? m.v_lut_scale : m.k_lut_scale) = sc;
+      rest &= ~(1 << side);
+    }
+  }
+  if (rest != 3) {
+    const hipError_t e = launch_quantize_mfma(m, stream);
+    if (e != hipSuccess) return e;
+  }
+  if (rest == 0) return hipSuccess;
+  QuantizeParams q = p;
+  q.side_mask = rest;
   switch (p.head_dim) {
-    case 32: return launch_d<32>(p, stream);
-    case 64: return launch_d<64>(p, stream);
-    case 128: return launch_d<128>(p, stream);
-    case 256: return launch_d<256>(p, stream);
+    case 32: return launch_d<32>(q, stream);
+    case 64: return launch_d<64>(q, stream);
+    case 128: return launch_d<128>(q, stream);
+    case 256: return launch_d<256>(q, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -1,0 +1,288 @@
+// Matrix-core quantize-append encoder for packed sides at head_dim 128 and
+// 1..4 bits ("TurboQuant KV Cache Quantization in MLX-VLM": "The
+// TurboQuantKVCache Class", "How TurboQuant KV Cache Quantization Works").
+//
+// The rotation of a row is y = H diag(s) x / (n sqrt(d)).  H diag(s) is a
+// constant +-1 matrix, and fp16 inputs times +-1 are exact MFMA products, so
+// v_mfma_f32_16x16x32_f16 gives H diag(s) x up to the fp32 accumulation; the
+// norm only scales the result.  A wave encodes 16 rows per tile:
+//
+//   A   lane l holds row l % 16, input coordinates 32 q + 8 (l / 16) .. +7 for
+//       K-step q: four 16-byte loads straight from the fp16 rows.
+//   B   M[j][i] = s_j H[i][j] with column n of N-tile t computing output
+//       coordinate i = 8 n + t, so a lane ends up holding 8 consecutive
+//       coordinates of its rows.  With j = 32 q + 8 g + s and i = 8 n + t,
+//       popcount(i & j) = popcount(n & (4 q + g)) + popcount(t & s): each
+//       entry is a per-lane sign times a fixed 8 x 8 Hadamard pattern.  The
+//       128 registers of B are built once per wave.
+//   D   lane (g = l / 16, n = l % 16) holds rows 4 g + r (r = 0..3),
+//       coordinates 8 n .. 8 n + 7, as 8 N-tiles of 4 values.
+//
+// The norm comes from the same fp16 operands (dot2 instructions, fp32 sums).
+// Coding: with a power-of-two scale S, u = y S is exact, and a code table
+// over the unit cells [k - S, k - S + 1) holds, per cell, the number of
+// scaled thresholds below the cell and the one threshold inside it (the
+// host picks S so no cell holds two).  code = base + (u > thr): one table
+// read per coordinate, the same decision as counting thresholds below y.
+// The 8 codes of a lane pack into 8 b bits; b = 4 is one word per lane, other
+// widths assemble words from neighbouring lanes with shuffles.
+#include <math.h>
+
+#include "tq_common.h"
+#include "tq_device.h"
+
+namespace tq {
+namespace {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int D = 128;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTileRows = 16;
+constexpr int kLutCells = 2 * kQuantLutMaxScale + 1;
+
+struct LutEntry {
+  uint32_t base;  // scaled thresholds below the cell
+  float thr;      // the scaled threshold inside the cell, or +inf
+};
+
+__device__ __forceinline__ float4_t mma(const half8_t a, const half8_t b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ half8_t as_half8(u32x4_t v) { return __builtin_bit_cast(half8_t, v); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, long bytes) {
+  const int b = bytes > 0x7fffffffL ? 0x7fffffff : static_cast<int>(bytes > 0 ? bytes : 0);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, b, 0x00020000);
+}
+
+// Sum over the four 16-lane rows of the wave (lanes l, l ^ 16, l ^ 32, l ^ 48).
+__device__ __forceinline__ float sum_rows(float x) {
+  const u32x2_t a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const u32x2_t b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Build the code table of one side: cells k = 0 .. 2 S cover u in
+// [k - S, k - S + 1).
+__device__ void build_lut(LutEntry *lut, const float *thr, int bits, float scale) {
+  const int S = static_cast<int>(scale);
+  const int n_thr = (1 << bits) - 1;
+  for (int k = threadIdx.x; k <= 2 * S; k += kThreads) {
+    const float lo = static_cast<float>(k - S);
+    int cnt = 0;  // thresholds with thr * S < lo (ascending thresholds)
+    for (int step = 128; step >= 1; step >>= 1) {
+      if (cnt + step <= n_thr && thr[cnt + step - 1] * scale < lo) cnt += step;
+    }
+    LutEntry e;
+    e.base = static_cast<uint32_t>(cnt);
+    const float t = cnt < n_thr ? thr[cnt] * scale : INFINITY;
+    e.thr = (t < lo + 1.0f) ? t : INFINITY;
+    lut[k] = e;
+  }
+}
+
+// Assemble word n of a row from the 8 b-bit chunks of the row's 16 lanes
+// (chunk of lane n covers row bits [8 b n, 8 b n + 8 b)).
+template <int BITS>
+__device__ __forceinline__ uint32_t row_word(uint32_t chunk, int lane) {
+  const int n = lane & 15;
+  const int row0 = lane & 48;
+  if (BITS == 4) return chunk;
+  if (BITS == 2) {
+    const uint32_t a = __shfl(chunk, row0 + ((2 * n) & 15));
+    const uint32_t b = __shfl(chunk, row0 + ((2 * n + 1) & 15));
+    return a | (b << 16);
+  }
+  if (BITS == 1) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w |= __shfl(chunk, row0 + ((4 * n + k) & 15)) << (8 * k);
+    return w;
+  }
+  // BITS == 3: word n starts at row bit 32 n = 24 n0 + s0
+  const int n0 = (4 * n) / 3;
+  const int s0 = 32 * n - 24 * n0;
+  const uint32_t a = __shfl(chunk, row0 + (n0 & 15));
+  const uint32_t b = __shfl(chunk, row0 + ((n0 + 1) & 15));
+  return (a >> s0) | (b << (24 - s0));
+}
+
+template <int BITS>
+__device__ __forceinline__ void encode_tile(const float4_t (&acc)[8], const float (&inv_s)[4],
+                                            const LutEntry *lut, int S, int lane, uint32_t (&word)[4]) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    uint32_t chunk = 0;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const float u = acc[t][r] * inv_s[r];
+      int k = static_cast<int>(floorf(u));
+      k = min(max(k, -S), S);
+      const LutEntry e = lut[k + S];
+      const uint32_t c = e.base + (u > e.thr ? 1u : 0u);
+      chunk |= c << (BITS * t);
+    }
+    word[r] = row_word<BITS>(chunk, lane);
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(const QuantizeParams p, int tiles_k,
+                                                                    int tiles_total) {
+  __shared__ LutEntry lut[2][kLutCells];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;
+  const int n = lane & 15;
+
+  if (p.k_lut_scale > 0.0f) build_lut(lut[0], p.k_thr, p.k.bits, p.k_lut_scale);
+  if (p.v_lut_scale > 0.0f) build_lut(lut[1], p.v_thr, p.v.bits, p.v_lut_scale);
+
+  // B = diag(s) H^T in the layout described above, built once per wave.
+  uint32_t bm[8][4][4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t par = static_cast<uint32_t>(__builtin_popcount(n & (4 * q + g)) & 1);
+#pragma unroll
+    for (int pr = 0; pr < 4; ++pr) {
+      const int j0 = 32 * q + 8 * g + 2 * pr;  // even: j0 and j0 + 1 share a sign word
+      const uint32_t sw = p.sign[j0 >> 5] >> (j0 & 31);
+      const uint32_t s0 = (sw & 1u) ^ par, s1 = ((sw >> 1) & 1u) ^ par;
+      const uint32_t base = (0x3c00u | (s0 << 15)) | ((0x3c00u | (s1 << 15)) << 16);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const uint32_t m = (static_cast<uint32_t>(__builtin_popcount(t & (2 * pr)) & 1) << 15) |
+                           (static_cast<uint32_t>(__builtin_popcount(t & (2 * pr + 1)) & 1) << 31);
+        bm[t][q][pr] = base ^ m;
+      }
+    }
+  }
+  __syncthreads();  // tables complete
+
+  const long rows = static_cast<long>(p.batch) * p.heads * p.n_new;
+  const float rsd = 1.0f / sqrtf(static_cast<float>(D));
+  for (int tile = blockIdx.x * kWaves + wave; tile < tiles_total; tile += gridDim.x * kWaves) {
+    const int side = tile < tiles_k ? 0 : 1;
+    const SideDev &sd = side ? p.v : p.k;
+    const float scale = side ? p.v_lut_scale : p.k_lut_scale;
+    const long r0 = static_cast<long>(side ? tile - tiles_k : tile) * kTileRows;
+    const uint16_t *x = (side ? p.v_new : p.k_new) + r0 * D;
+    const long left = rows - r0;
+    const auto rx = rsrc(x, (left < kTileRows ? left : kTileRows) * D * 2);
+
+    // A operands: row n of the tile, coordinates 32 q + 8 g .. + 7
+    half8_t a[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      a[q] = as_half8(__builtin_amdgcn_raw_buffer_load_b128(rx, (n * D + 32 * q + 8 * g) * 2, 0, 0));
+
+    // squared norm of row n: fp16 products are exact, sums in fp32
+    float ss = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const half2_t h = {a[q][e], a[q][e + 1]};
+        ss = __builtin_amdgcn_fdot2(h, h, ss, false);
+      }
+    }
+    ss = sum_rows(ss);
+
+    float4_t acc[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      acc[t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u32x4_t b = {bm[t][q][0], bm[t][q][1], bm[t][q][2], bm[t][q][3]};
+        acc[t] = mma(a[q], as_half8(b), acc[t]);
+      }
+    }
+
+    // rows 4 g + r of this lane: norm and 1 / (n sqrt(d)) times the table scale
+    float nrm[4], inv_s[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float s2 = __shfl(ss, 4 * g + r);
+      nrm[r] = sqrtf(s2);
+      inv_s[r] = nrm[r] > 0.0f ? scale * rsd / nrm[r] : 0.0f;
+    }
+
+    uint32_t word[4];
+    const int S = static_cast<int>(scale);
+    switch (sd.bits) {
+      case 1: encode_tile<1>(acc, inv_s, lut[side], S, lane, word); break;
+      case 2: encode_tile<2>(acc, inv_s, lut[side], S, lane, word); break;
+      case 3: encode_tile<3>(acc, inv_s, lut[side], S, lane, word); break;
+      default: encode_tile<4>(acc, inv_s, lut[side], S, lane, word); break;
+    }
+
+    // output rows: tile row 4 g + r is input row r0 + 4 g + r = (bh, i);
+    // n_new >= 16, so the tile crosses at most one (batch, head) boundary
+    const long bh0 = r0 / p.n_new;
+    const int i0 = static_cast<int>(r0 - bh0 * p.n_new);
+    const int W = sd.words;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tr = 4 * g + r;
+      if (tr >= left) continue;
+      int i = i0 + tr;
+      long bh = bh0;
+      if (i >= p.n_new) {
+        i -= p.n_new;
+        bh += 1;
+      }
+      const long row = bh * p.capacity + p.offset + i;
+      if (n < W) sd.codes[row * W + n] = word[r];
+      if (n == r) sd.norms[row] = nrm[r];
+    }
+  }
+}
+
+}  // namespace
+
+float quantize_lut_scale(const float *thr, int bits) {
+  const int n_thr = (1 << bits) - 1;
+  double gap = 2.0;
+  for (int k = 0; k + 1 < n_thr; ++k) {
+    const double d = static_cast<double>(thr[k + 1]) - static_cast<double>(thr[k]);
+    if (d < gap) gap = d;
+  }
+  for (int s = 1; s <= kQuantLutMaxScale; s *= 2) {
+    // consecutive scaled thresholds more than one cell apart: a unit cell
+    // never holds two
+    if (gap * s > 1.0) return static_cast<float>(s);
+  }
+  return 0.0f;
+}
+
+hipError_t launch_quantize_mfma(const QuantizeParams &p, hipStream_t stream) {
+  if (p.head_dim != D || p.n_new < kTileRows) return hipErrorInvalidValue;
+  const long rows = static_cast<long>(p.batch) * p.heads * p.n_new;
+  const long tiles_side = (rows + kTileRows - 1) / kTileRows;
+  const bool k_on = p.k_lut_scale > 0.0f, v_on = p.v_lut_scale > 0.0f;
+  for (int side = 0; side < 2; ++side) {
+    const SideDev &s = side ? p.v : p.k;
+    const float sc = side ? p.v_lut_scale : p.k_lut_scale;
+    if (sc > 0.0f && (s.mode != TQ_SIDE_PACKED || s.bits < 1 || s.bits > 4 ||
+                      sc > static_cast<float>(kQuantLutMaxScale) || s.words != 4 * s.bits))
+      return hipErrorInvalidValue;
+  }
+  const long tiles_k = k_on ? tiles_side : 0;
+  const long tiles_total = tiles_k + (v_on ? tiles_side : 0);
+  if (tiles_total == 0) return hipSuccess;
+  if (tiles_total > 0x7fffffffL) return hipErrorInvalidValue;
+  const long blocks = std::min<long>((tiles_total + kWaves - 1) / kWaves, 512);
+  hipLaunchKernelGGL(quantize_mfma_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, p,
+                     static_cast<int>(tiles_k), static_cast<int>(tiles_total));
+  return hipGetLastError();
+}
+
+}  // namespace tq

@@ -30,6 +30,9 @@ struct QuantizeParams {
   const uint16_t *k_new;  // [B][H][n_new][d] fp16
   const uint16_t *v_new;
   int batch, heads, head_dim, capacity, n_new, offset;
+  int side_mask;                 // sides this launch encodes: bit 0 K, bit 1 V
+  float k_lut_scale;             // matrix-core kernel: code-table cells per unit of y
+  float v_lut_scale;             //   (a power of two; 0 = side not eligible)
   uint32_t sign[kMaxSignWords];  // bit j set: s_j = -1
   float k_thr[kMaxLevels];       // thresholds (L-1 used)
   float v_thr[kMaxLevels];
@@ -98,6 +101,14 @@ inline size_t decode_mfma_workspace_bytes(int batch, int kv_heads, int q_heads, 
 }
 
 hipError_t launch_quantize_append(const QuantizeParams &p, hipStream_t stream);
+// Matrix-core encoder for packed sides at head_dim 128 and 1..4 bits; the
+// sides it takes are those with a non-zero lut scale in `p` and bit set in
+// p.side_mask.
+hipError_t launch_quantize_mfma(const QuantizeParams &p, hipStream_t stream);
+// Power-of-two code-table scale for the matrix-core encoder (0 when the
+// thresholds are too close for a table of at most kQuantLutMax cells).
+float quantize_lut_scale(const float *thr, int bits);
+constexpr int kQuantLutMaxScale = 512;
 hipError_t launch_dequantize(const DequantParams &p, hipStream_t stream);
 hipError_t launch_decode_ref(const DecodeParams &p, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeParams &p, hipStream_t stream);

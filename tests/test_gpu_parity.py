@@ -76,15 +76,33 @@ def _oracle_rows(cache, side, length):
     return out
 
 
+@pytest.fixture(params=["auto", "plain"])
+def qvariant(request):
+    """Runs a test with the library's own choice of quantize kernel (the
+    matrix-core encoder where it applies) and again with the plain kernel
+    forced (TQ_QUANTIZE_VARIANT=plain)."""
+    old = os.environ.get("TQ_QUANTIZE_VARIANT")
+    os.environ["TQ_QUANTIZE_VARIANT"] = request.param
+    yield request.param
+    if old is None:
+        os.environ.pop("TQ_QUANTIZE_VARIANT", None)
+    else:
+        os.environ["TQ_QUANTIZE_VARIANT"] = old
+
+
 @pytest.mark.parametrize("d,kb,vb,B,H,n,off", [
     (64, 3, 4, 1, 2, 256, 0),      # the 3.5-bit d=64 workload, whole
     (128, 3, 4, 2, 3, 301, 7),     # ragged count at an offset
     (128, 4, 4, 1, 2, 190, 0),
+    (128, 1, 2, 2, 3, 40, 3),      # 1- and 2-bit words from several lanes
+    (128, 3, 4, 1, 1, 16, 0),      # exactly one tile
+    (128, 4, 3, 3, 2, 17, 5),      # every tile crosses a (batch, head) boundary
+    (128, 2, 1, 1, 1, 15, 0),      # too short for the matrix-core encoder
     (32, 1, 2, 2, 2, 77, 5),
     (256, 5, 8, 1, 2, 65, 3),
     (128, 6, 7, 1, 1, 33, 0),
 ])
-def test_quantize_append_packed(d, kb, vb, B, H, n, off):
+def test_quantize_append_packed(d, kb, vb, B, H, n, off, qvariant):
     k, v = synth.kv_numpy(100 + d + n, B, H, n, d, dist="channel", outlier_frac=0.01)
     cache = tq.TQCache(B, H, d, off + n + 9, tq.SideSpec("packed", kb), tq.SideSpec("packed", vb))
     cache.quantize_append(_dev(k), _dev(v), off)
@@ -96,13 +114,14 @@ def test_quantize_append_packed(d, kb, vb, B, H, n, off):
         assert int(untouched.abs().sum()) == 0
 
 
-def test_quantize_zero_and_tiny_rows():
+def test_quantize_zero_and_tiny_rows(qvariant):
     d = 128
-    k = np.zeros((1, 1, 4, d), np.float16)
+    k = np.zeros((1, 1, 20, d), np.float16)  # 20 rows: the matrix-core encoder takes them
     k[0, 0, 1, 5] = np.float16(6e-8)        # smallest subnormal
     k[0, 0, 2, :] = np.float16(65504.0)     # largest finite
     k[0, 0, 3, ::3] = np.float16(-1.0)
-    cache = tq.TQCache(1, 1, d, 4, tq.SideSpec("packed", 3), tq.SideSpec("packed", 4))
+    k[0, 0, 4:] = synth.kv_numpy(3, 1, 1, 16, d)[0][0, 0]
+    cache = tq.TQCache(1, 1, d, 20, tq.SideSpec("packed", 3), tq.SideSpec("packed", 4))
     cache.quantize_append(_dev(k), _dev(k), 0)
     torch.cuda.synchronize()
     _check_packed(cache, "k", k, 0)
@@ -112,7 +131,7 @@ def test_quantize_zero_and_tiny_rows():
     assert float(cache.tensors["k_norms"][0, 0, 0]) == 0.0
 
 
-def test_quantize_append_fp16_side():
+def test_quantize_append_fp16_side(qvariant):
     d, B, H, n = 128, 2, 2, 50
     k, v = synth.kv_numpy(7, B, H, n, d)
     cache = tq.TQCache(B, H, d, 64, tq.SideSpec("fp16"), tq.SideSpec("packed", 4))
@@ -121,6 +140,32 @@ def test_quantize_append_fp16_side():
     assert np.array_equal(cache.tensors["k_fp16"][:, :, 10:60].cpu().numpy(), k)
     assert int(cache.tensors["k_fp16"][:, :, :10].abs().sum()) == 0
     _check_packed(cache, "v", v, 10)
+
+
+@pytest.mark.parametrize("kb,vb", [(3, 4), (4, 4), (1, 2)])
+def test_quantize_kernels_agree(kb, vb):
+    """The matrix-core encoder and the plain kernel write the same words and
+    norms, up to the threshold band, on the 32K-context distribution."""
+    d, B, H, n = 128, 2, 4, 1000
+    k, v = synth.kv_numpy(77 + kb, B, H, n, d, dist="channel", outlier_frac=0.01)
+    out = {}
+    for var in ("auto", "plain"):
+        os.environ["TQ_QUANTIZE_VARIANT"] = var
+        cache = tq.TQCache(B, H, d, n, tq.SideSpec("packed", kb), tq.SideSpec("packed", vb))
+        cache.quantize_append(_dev(k), _dev(v), 0)
+        torch.cuda.synchronize()
+        out[var] = {key: cache.tensors[key].cpu().numpy() for key in ("k_codes", "k_norms", "v_codes", "v_norms")}
+    os.environ.pop("TQ_QUANTIZE_VARIANT", None)
+    R = oracle.rotation_matrix(0, d)
+    for side, bits, x in (("k", kb, k), ("v", vb, v)):
+        _, t = oracle.lloyd_max(d, bits)
+        _, _, y = oracle.quantize(x, R, t)
+        a = words_to_codes(out["auto"][side + "_codes"], bits, d)
+        b = words_to_codes(out["plain"][side + "_codes"], bits, d)
+        ok, ndiff, _ = codes_agree(a, b, y, t)
+        assert ok, f"{side}: {ndiff} codes differ outside the band"
+        na, nb = out["auto"][side + "_norms"], out["plain"][side + "_norms"]
+        assert np.all(np.abs(na - nb) <= 1e-6 * np.abs(nb) + 1e-30)
 
 
 @pytest.mark.parametrize("chunks,hot", [
