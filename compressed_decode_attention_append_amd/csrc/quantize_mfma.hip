@@ -115,18 +115,26 @@ __device__ __forceinline__ uint32_t row_word(uint32_t chunk, int lane) {
   return (a >> s0) | (b << (24 - s0));
 }
 
+// floor(x) as an integer in one instruction (v_cvt_flr_i32_f32).
+__device__ __forceinline__ int floor_to_int(float x) {
+  int r;
+  asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+
+// lut points at the cell of u = 0 (cell index S of the side's table).
 template <int BITS>
 __device__ __forceinline__ void encode_tile(const float4_t (&acc)[8], const float (&inv_s)[4],
-                                            const LutEntry *lut, int S, int lane, uint32_t (&word)[4]) {
+                                            const LutEntry *lut0, float S, int lane, uint32_t (&word)[4]) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     uint32_t chunk = 0;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const float u = acc[t][r] * inv_s[r];
-      int k = static_cast<int>(floorf(u));
-      k = min(max(k, -S), S);
-      const LutEntry e = lut[k + S];
+      // |u| <= S up to rounding; the clamp keeps the cell in the table
+      const int k = floor_to_int(__builtin_amdgcn_fmed3f(u, -S, S));
+      const LutEntry e = lut0[k];
       const uint32_t c = e.base + (u > e.thr ? 1u : 0u);
       chunk |= c << (BITS * t);
     }
@@ -168,20 +176,30 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(const Quanti
 
   const long rows = static_cast<long>(p.batch) * p.heads * p.n_new;
   const float rsd = 1.0f / sqrtf(static_cast<float>(D));
-  for (int tile = blockIdx.x * kWaves + wave; tile < tiles_total; tile += gridDim.x * kWaves) {
+  const int stride = gridDim.x * kWaves;
+  // A operands of a tile: row n of the tile, coordinates 32 q + 8 g .. + 7.
+  // The next tile's operands load while the current one is encoded.
+  auto load_tile = [&](int tile, half8_t (&dst)[4]) {
+    const int side = tile < tiles_k ? 0 : 1;
+    const long r0 = static_cast<long>(side ? tile - tiles_k : tile) * kTileRows;
+    const long left = rows - r0;
+    const auto rx = rsrc((side ? p.v_new : p.k_new) + r0 * D, (left < kTileRows ? left : kTileRows) * D * 2);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      dst[q] = as_half8(__builtin_amdgcn_raw_buffer_load_b128(rx, (n * D + 32 * q + 8 * g) * 2, 0, 0));
+  };
+  half8_t a[4], an[4];
+  int tile = blockIdx.x * kWaves + wave;
+  if (tile < tiles_total) load_tile(tile, an);
+  for (; tile < tiles_total; tile += stride) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) a[q] = an[q];
+    if (tile + stride < tiles_total) load_tile(tile + stride, an);
     const int side = tile < tiles_k ? 0 : 1;
     const SideDev &sd = side ? p.v : p.k;
     const float scale = side ? p.v_lut_scale : p.k_lut_scale;
     const long r0 = static_cast<long>(side ? tile - tiles_k : tile) * kTileRows;
-    const uint16_t *x = (side ? p.v_new : p.k_new) + r0 * D;
     const long left = rows - r0;
-    const auto rx = rsrc(x, (left < kTileRows ? left : kTileRows) * D * 2);
-
-    // A operands: row n of the tile, coordinates 32 q + 8 g .. + 7
-    half8_t a[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      a[q] = as_half8(__builtin_amdgcn_raw_buffer_load_b128(rx, (n * D + 32 * q + 8 * g) * 2, 0, 0));
 
     // squared norm of row n: fp16 products are exact, sums in fp32
     float ss = 0.0f;
@@ -206,42 +224,41 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(const Quanti
       }
     }
 
-    // rows 4 g + r of this lane: norm and 1 / (n sqrt(d)) times the table scale
+    // rows 4 g + r of this lane: norm and 1 / (n sqrt(d)) times the table
+    // scale (a power of two, so the scaling is exact)
     float nrm[4], inv_s[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float s2 = __shfl(ss, 4 * g + r);
       nrm[r] = sqrtf(s2);
-      inv_s[r] = nrm[r] > 0.0f ? scale * rsd / nrm[r] : 0.0f;
+      inv_s[r] = nrm[r] > 0.0f ? scale * (rsd * __builtin_amdgcn_rcpf(nrm[r])) : 0.0f;
     }
 
     uint32_t word[4];
-    const int S = static_cast<int>(scale);
+    const LutEntry *lut0 = lut[side] + static_cast<int>(scale);
     switch (sd.bits) {
-      case 1: encode_tile<1>(acc, inv_s, lut[side], S, lane, word); break;
-      case 2: encode_tile<2>(acc, inv_s, lut[side], S, lane, word); break;
-      case 3: encode_tile<3>(acc, inv_s, lut[side], S, lane, word); break;
-      default: encode_tile<4>(acc, inv_s, lut[side], S, lane, word); break;
+      case 1: encode_tile<1>(acc, inv_s, lut0, scale, lane, word); break;
+      case 2: encode_tile<2>(acc, inv_s, lut0, scale, lane, word); break;
+      case 3: encode_tile<3>(acc, inv_s, lut0, scale, lane, word); break;
+      default: encode_tile<4>(acc, inv_s, lut0, scale, lane, word); break;
     }
 
-    // output rows: tile row 4 g + r is input row r0 + 4 g + r = (bh, i);
-    // n_new >= 16, so the tile crosses at most one (batch, head) boundary
+    // output rows: tile row tr = 4 g + r is input row r0 + tr = (bh, i).
+    // n_new >= 16, so the tile crosses at most one (batch, head) boundary;
+    // crossing it skips the capacity - n_new rows the append leaves alone.
     const long bh0 = r0 / p.n_new;
     const int i0 = static_cast<int>(r0 - bh0 * p.n_new);
     const int W = sd.words;
+    uint32_t *codes0 = sd.codes + (bh0 * p.capacity + p.offset + i0) * W;
+    float *norms0 = sd.norms + bh0 * p.capacity + p.offset + i0;
+    const int skip = p.capacity - p.n_new;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int tr = 4 * g + r;
       if (tr >= left) continue;
-      int i = i0 + tr;
-      long bh = bh0;
-      if (i >= p.n_new) {
-        i -= p.n_new;
-        bh += 1;
-      }
-      const long row = bh * p.capacity + p.offset + i;
-      if (n < W) sd.codes[row * W + n] = word[r];
-      if (n == r) sd.norms[row] = nrm[r];
+      const int rel = tr + (i0 + tr >= p.n_new ? skip : 0);
+      if (n < W) codes0[rel * W + n] = word[r];
+      if (n == r) norms0[rel] = nrm[r];
     }
   }
 }
