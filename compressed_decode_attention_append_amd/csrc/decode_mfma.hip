@@ -189,6 +189,14 @@ template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u(uint32_t src) {
   return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(src), CTRL, 0xf, 0xf, true));
 }
+// DPP move into the lanes of the banks in BANKS; other lanes keep `old`.
+// kRowShl + 0 is the identity (row_shl:0 encodes quad_perm [0,1,2,3]).
+template <int CTRL, int BANKS>
+__device__ __forceinline__ uint32_t dpp_bank(uint32_t old, uint32_t src) {
+  constexpr int ctrl = CTRL == 0x100 ? 0xe4 : CTRL;
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(static_cast<int>(old), static_cast<int>(src), ctrl, 0xf, BANKS, false));
+}
 
 // Reductions over the 64 / GP lanes of one query head in the compact layout
 // (lanes whose column agrees modulo GP).
@@ -387,21 +395,64 @@ struct Wave {
     }
   }
 
-  // Compact hi/lo pair words -> B operand (4 words: slots 2 s2, 2 s2 + 1).
-  __device__ __forceinline__ half8_t expand(const uint32_t (&w)[NV / 2]) const {
+  // Compact hi/lo weight pairs -> A operand of the value MFMA.  Row r of A
+  // (lane column r) is P_hi of head r for r < GP, P_lo of head r - GP for
+  // GP <= r < 2 GP, zero beyond; word s2 holds slots 2 s2, 2 s2 + 1, which
+  // compact lane (grp, GP kc + h) holds for kc = 2 s2 / NV.
+  __device__ __forceinline__ half8_t weights_operand(const uint32_t (&wh)[NV / 2], const uint32_t (&wl)[NV / 2]) const {
+    uint32_t x[4];
     if (GP == 4) {
-      return as_half8(w[0], dpp_u<kRowShl + 4>(w[0]), dpp_u<kRowShl + 8>(w[0]), dpp_u<kRowShl + 12>(w[0]));
+      // hi rows (banks 0): source lane + 4 s2; lo rows (bank 1): source lane + 4 s2 - 4
+      x[0] = dpp_bank<kRowShl + 0, 0x1>(0u, wh[0]);
+      x[0] = dpp_bank<kRowShr + 4, 0x2>(x[0], wl[0]);
+      x[1] = dpp_bank<kRowShl + 4, 0x1>(0u, wh[0]);
+      x[1] = dpp_bank<kRowShl + 0, 0x2>(x[1], wl[0]);
+      x[2] = dpp_bank<kRowShl + 8, 0x1>(0u, wh[0]);
+      x[2] = dpp_bank<kRowShl + 4, 0x2>(x[2], wl[0]);
+      x[3] = dpp_bank<kRowShl + 12, 0x1>(0u, wh[0]);
+      x[3] = dpp_bank<kRowShl + 8, 0x2>(x[3], wl[0]);
     } else {
-      return as_half8(w[0], w[1], dpp_u<kRowShl + 8>(w[0]), dpp_u<kRowShl + 8>(w[1]));
+      // hi rows (banks 0, 1): source lane + 8 kc; lo rows (banks 2, 3): source lane + 8 kc - 8
+      x[0] = dpp_bank<kRowShl + 0, 0x3>(0u, wh[0]);
+      x[0] = dpp_bank<kRowShr + 8, 0xc>(x[0], wl[0]);
+      x[1] = dpp_bank<kRowShl + 0, 0x3>(0u, wh[1]);
+      x[1] = dpp_bank<kRowShr + 8, 0xc>(x[1], wl[1]);
+      x[2] = dpp_bank<kRowShl + 8, 0x3>(0u, wh[0]);
+      x[2] = dpp_bank<kRowShl + 0, 0xc>(x[2], wl[0]);
+      x[3] = dpp_bank<kRowShl + 8, 0x3>(0u, wh[1]);
+      x[3] = dpp_bank<kRowShl + 0, 0xc>(x[3], wl[1]);
+    }
+    return as_half8(x[0], x[1], x[2], x[3]);
+  }
+
+  // Scale the value accumulators of each head by its own factor (compact
+  // lane h holds head h's factor): rows r of lane group g belong to head r
+  // (GP = 4) or 4 (g & 1) + r (GP = 8).
+  __device__ __forceinline__ void scale_heads(float f) {
+    float fr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), r));
+      if (GP == 4) {
+        fr[r] = lo;
+      } else {
+        const float hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), 4 + r));
+        fr[r] = (grp & 1) ? hi : lo;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) accv[q][r] *= fr[r];
     }
   }
 
   // Online softmax on compact scores (base-2 logits; -inf = masked).  The
   // accumulators are only rescaled when the running maximum grows by more
-  // than 2^8.  Returns the value MFMA's B operand, p n vscale as hi + lo fp16.
+  // than 2^8.  Returns the value MFMA's A operand: p n vscale as hi and lo
+  // fp16 rows.
   template <bool TAIL>
-  __device__ __forceinline__ void softmax(const float (&c)[NV], const float (&vn)[NV], half8_t &bvh,
-                                          half8_t &bvl) {
+  __device__ __forceinline__ half8_t softmax(const float (&c)[NV], const float (&vn)[NV]) {
     float cmax = c[0];
 #pragma unroll
     for (int j = 1; j < NV; ++j) cmax = fmaxf(cmax, c[j]);
@@ -412,8 +463,7 @@ struct Wave {
       const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
       m_run = m_new;
       l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) accv[i] *= alpha;
+      scale_heads(alpha);
     }
     uint32_t wh[NV / 2], wl[NV / 2];
 #pragma unroll
@@ -427,8 +477,7 @@ struct Wave {
       l_run += p0 + p1;
       split_pair(p0 * vn[j], p1 * vn[j + 1], wh[j / 2], wl[j / 2]);
     }
-    bvh = expand(wh);
-    bvl = expand(wl);
+    return weights_operand(wh, wl);
   }
 
   // Keep n vscale <= 32 for the norms of this chunk: if a larger norm shows
@@ -462,8 +511,10 @@ struct Wave {
   }
 
   // Packed values: pair the nibbles of slots 2 s2 and 2 s2 + 1 per byte (one
-  // byte per coordinate pair index), then 8 tiles of lookups and MFMAs.
-  __device__ __forceinline__ void values(const ChunkData<KB, GP> &c, const half8_t bvh, const half8_t bvl) {
+  // byte per coordinate pair index), then per tile q one table lookup per
+  // slot pair and one MFMA: D[(head, hi/lo)][coordinate 8 col + q] +=
+  // P[(head, hi/lo)][slot] * c[code of slot, coordinate].
+  __device__ __forceinline__ void values(const ChunkData<KB, GP> &c, const half8_t ap) {
     uint32_t ev[4], od[4];  // bytes j: coordinates 8 col + 2 j (ev) and 8 col + 2 j + 1 (od)
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2) {
@@ -487,9 +538,7 @@ struct Wave {
         }
         a4[s2] = lds_at<0>(lds, ad);
       }
-      const half8_t a = as_half8(a4[0], a4[1], a4[2], a4[3]);
-      accv[q] = mma(a, bvh, accv[q]);
-      accv[q] = mma(a, bvl, accv[q]);
+      accv[q] = mma(ap, as_half8(a4[0], a4[1], a4[2], a4[3]), accv[q]);
     }
   }
 
@@ -508,9 +557,7 @@ struct Wave {
       if (TAIL && t0 + cpos + j >= we) cs[j] = -INFINITY;
     }
     if (scores) store_scores<TAIL>(t0, we, cs, scores, score_row0, length);
-    half8_t bvh, bvl;
-    softmax<TAIL>(cs, vn, bvh, bvl);
-    values(c, bvh, bvl);
+    values(c, softmax<TAIL>(cs, vn));
   }
 
   // One chunk of the fp16 hot window (delegated V), positions >= we masked.
@@ -526,8 +573,7 @@ struct Wave {
       if (t0 + cpos + j >= we) cs[j] = -INFINITY;
     }
     if (scores) store_scores<true>(t0, we, cs, scores, score_row0, length);
-    half8_t bvh, bvl;
-    softmax<true>(cs, vn, bvh, bvl);
+    const half8_t ap = softmax<true>(cs, vn);
     // fp16 ring rows: tile q covers coordinates 16 q + col
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
@@ -543,29 +589,41 @@ struct Wave {
         }
         u[s2] = h2[0] | (h2[1] << 16);
       }
-      const half8_t a = as_half8(u[0], u[1], u[2], u[3]);
-      accv[q] = mma(a, bvh, accv[q]);
-      accv[q] = mma(a, bvl, accv[q]);
+      accv[q] = mma(ap, as_half8(u[0], u[1], u[2], u[3]), accv[q]);
     }
   }
 
   // Write this wave's (max, sum, accumulator / vscale) of the real heads to
   // the merge slot [G][D + 2]; `hot_layout` selects the coordinate order.
+  // The hi and lo rows of the value accumulators are summed first: lane
+  // group g = 0 (and 1 for GP = 8) then holds head 4 g + r in row r.
   __device__ __forceinline__ void to_slot(float *slot_base, bool hot_layout) const {
     const float l_wave = head_sum<GP>(l_run);
-    if (col < G) {
+    if (col < G && grp == 0) {
       float *slot = slot_base + col * (D + 2);
-      if (grp == 0) {
-        slot[0] = m_run;
-        slot[1] = l_wave;
+      slot[0] = m_run;
+      slot[1] = l_wave;
+    }
+    const float inv = 1.0f / vscale;
+    float4_t sum[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t x = __float_as_uint(accv[q][r]);
+        const u32x2_t sw = (GP == 4) ? __builtin_amdgcn_permlane16_swap(x, x, false, false)
+                                     : __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        sum[q][r] = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * inv;
       }
-      const float inv = 1.0f / vscale;
+    }
+    if (grp < GP / 4) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
+      for (int r = 0; r < 4; ++r) {
+        const int h = 4 * grp + r;
+        if (h < G) {
+          float *slot = slot_base + h * (D + 2);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int coord = hot_layout ? 16 * q + 4 * grp + r : 8 * (4 * grp + r) + q;
-          slot[2 + coord] = accv[q][r] * inv;
+          for (int q = 0; q < 8; ++q) slot[2 + (hot_layout ? 16 * q + col : 8 * col + q)] = sum[q][r];
         }
       }
     }
