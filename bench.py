@@ -230,6 +230,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c4_tq35_32k", choices=sorted(WORKLOADS))
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (profiling only)")
+    ap.add_argument("--tokens", type=int, default=0, help="override the context length (profiling only)")
     ap.add_argument("--splits", type=int, default=0,
                     help="context splits per (batch, KV head); 0 = the library's choice")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -263,6 +264,9 @@ def main():
     w = dict(WORKLOADS[args.workload])
     if args.layers:
         w["layers"] = args.layers
+    if args.tokens:
+        w["tokens"] = args.tokens
+        w["prefill"] = min(w.get("prefill", 0), args.tokens)
     dev = "cuda:0"
     torch.cuda.set_device(0)
     B, Hkv, Hq, d, T, Lyr = w["batch"], w["kv_heads"], w["q_heads"], w["head_dim"], w["tokens"], w["layers"]

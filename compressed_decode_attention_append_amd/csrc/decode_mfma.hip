@@ -719,15 +719,30 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
     qa = h2f(p.q[(hq0 + wave) * D + lane]);
     qb = h2f(p.q[(hq0 + wave) * D + lane + 64]);
   }
-  for (int i = threadIdx.x; i < kMaxLevels; i += kThreads) {
-    cent[i] = p.k_cent[i];
-    cent[kMaxLevels + i] = p.v_cent[i];
+  // The 16 (V) and up to 16 (K) centroids the tables need, read with
+  // uniform indices (scalar loads of the kernel arguments) and spread over
+  // the lanes of wave 0, rather than one vector load of the argument block
+  // per thread.
+  if (wave == 0) {
+    float kc = 0.0f, vc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      kc = (lane == i) ? p.k_cent[i] : kc;
+      vc = (lane == i) ? p.v_cent[i] : vc;
+    }
+    if (lane < 16) {
+      cent[lane] = kc;
+      cent[kMaxLevels + lane] = vc;
+    }
   }
   // rotate q in registers: H diag(s) q (unnormalised), butterflies at
   // stride 64 inside the lane and at strides 32 .. 1 across lanes
   if (k_packed && wave < G) {
-    qa *= sign_of(p.sign, lane);
-    qb *= sign_of(p.sign, lane + 64);
+    // signs of coordinates lane and lane + 64 (uniform words, per-lane select)
+    const uint32_t sa = lane < 32 ? p.sign[0] : p.sign[1];
+    const uint32_t sb = lane < 32 ? p.sign[2] : p.sign[3];
+    qa = ((sa >> (lane & 31)) & 1u) ? -qa : qa;
+    qb = ((sb >> (lane & 31)) & 1u) ? -qb : qb;
     const float a = qa + qb, c = qa - qb;
     qa = a;
     qb = c;
@@ -943,10 +958,18 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   const float rs = 1.0f / sqrtf(static_cast<float>(D));
   const float inv = (Lt > 0.0f) ? 1.0f / Lt : 0.0f;
   float4 o;
-  o.x = (r4[0] * sign_of(p.sign, jj) * rs + q4[0]) * inv;
-  o.y = (r4[1] * sign_of(p.sign, jj + 1) * rs + q4[1]) * inv;
-  o.z = (r4[2] * sign_of(p.sign, jj + 2) * rs + q4[2]) * inv;
-  o.w = (r4[3] * sign_of(p.sign, jj + 3) * rs + q4[3]) * inv;
+  // sign word of coordinates jj .. jj + 3 (uniform words, per-lane select)
+  const int wsel = jj >> 5;
+  const uint32_t swd = (wsel & 2) ? ((wsel & 1) ? p.sign[3] : p.sign[2]) : ((wsel & 1) ? p.sign[1] : p.sign[0]);
+  const uint32_t sbits = swd >> (jj & 31);
+  o.x = ((sbits & 1u) ? -r4[0] : r4[0]) * rs;
+  o.y = ((sbits & 2u) ? -r4[1] : r4[1]) * rs;
+  o.z = ((sbits & 4u) ? -r4[2] : r4[2]) * rs;
+  o.w = ((sbits & 8u) ? -r4[3] : r4[3]) * rs;
+  o.x = (o.x + q4[0]) * inv;
+  o.y = (o.y + q4[1]) * inv;
+  o.z = (o.z + q4[2]) * inv;
+  o.w = (o.w + q4[3]) * inv;
   *reinterpret_cast<float4 *>(p.out + (hq0 + hh) * D + jj) = o;
   if (threadIdx.x == 0) __hip_atomic_store(p.counters + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
