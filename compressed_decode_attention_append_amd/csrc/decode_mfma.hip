@@ -89,8 +89,9 @@ constexpr int kKloOff4 = 128;
 template <int GP>
 struct Lay {
   static constexpr int cent = kTableWords;
-  static constexpr int qwork = cent + 2 * kMaxLevels;  // [GP][D] rotated query
-  static constexpr int red = qwork + GP * D;           // flag
+  static constexpr int qstride = D + 4;                // padded row: fewer bank conflicts
+  static constexpr int qwork = cent + 2 * kMaxLevels;  // [GP][D + 4] rotated query
+  static constexpr int red = qwork + GP * qstride;     // flag
   static constexpr int total = red + 16;
   static_assert((kMaxWaves + 1) * GP * (D + 2) <= kTableWords, "merges must fit in the table area");
 };
@@ -735,6 +736,28 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
       cent[kMaxLevels + lane] = vc;
     }
   }
+  __syncthreads();  // centroids visible
+  // value table (for KB = 4 also the K hi table), 32 replicas per entry;
+  // built while the query and the first chunk are in flight
+  for (int i = threadIdx.x; i < 256 * kRep; i += kThreads) {
+    const int e = i / kRep, r = i % kRep;
+    const float c0 = cent[kMaxLevels + (e & 15)], c1 = cent[kMaxLevels + (e >> 4)];
+    lds[e * 64 + r] = pack_half2(c0, c1);
+    if (KB == 4) {
+      uint32_t h, l;
+      split_pair(cent[e & 15], cent[e >> 4], h, l);
+      lds[e * 64 + 32 + r] = l;
+    }
+  }
+  if (KB == 3) {
+    for (int i = threadIdx.x; i < 64 * kRep; i += kThreads) {
+      const int e = i / kRep, r = i % kRep;
+      uint32_t h, l;
+      split_pair(cent[e & 7], cent[e >> 3], h, l);
+      lds[e * 64 + 32 + r] = h;
+      lds[(64 + e) * 64 + 32 + r] = l;
+    }
+  }
   // rotate q in registers: H diag(s) q (unnormalised), butterflies at
   // stride 64 inside the lane and at strides 32 .. 1 across lanes
   if (k_packed && wave < G) {
@@ -755,41 +778,21 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
     }
   }
   if (wave < G) {
-    qw[wave * D + lane] = qa;
-    qw[wave * D + lane + 64] = qb;
+    qw[wave * L::qstride + lane] = qa;
+    qw[wave * L::qstride + lane + 64] = qb;
   }
-  __syncthreads();
-  // value table (for KB = 4 also the K hi table), 32 replicas per entry
-  for (int i = threadIdx.x; i < 256 * kRep; i += kThreads) {
-    const int e = i / kRep, r = i % kRep;
-    const float c0 = cent[kMaxLevels + (e & 15)], c1 = cent[kMaxLevels + (e >> 4)];
-    lds[e * 64 + r] = pack_half2(c0, c1);
-    if (KB == 4) {
-      uint32_t h, l;
-      split_pair(cent[e & 15], cent[e >> 4], h, l);
-      lds[e * 64 + 32 + r] = l;
-    }
-  }
-  if (KB == 3) {
-    for (int i = threadIdx.x; i < 64 * kRep; i += kThreads) {
-      const int e = i / kRep, r = i % kRep;
-      uint32_t h, l;
-      split_pair(cent[e & 7], cent[e >> 3], h, l);
-      lds[e * 64 + 32 + r] = h;
-      lds[(64 + e) * 64 + 32 + r] = l;
-    }
-  }
-  __syncthreads();  // tables complete before the first lookup
+  __syncthreads();  // tables and rotated query complete
   {
     const float qscale = k_packed ? kLog2e / static_cast<float>(D) : kLog2e / sqrtf(static_cast<float>(D));
+    const float2 *qrow = reinterpret_cast<const float2 *>(qw + (W.col < G ? W.col : 0) * L::qstride + 32 * W.grp);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       uint32_t h[4], l[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const int j = 32 * W.grp + 8 * c + 2 * s;
+        const float2 v2 = qrow[4 * c + s];  // coordinates 32 grp + 8 c + 2 s, + 1
         h[s] = l[s] = 0u;
-        if (W.col < G) split_pair(qw[W.col * D + j] * qscale, qw[W.col * D + j + 1] * qscale, h[s], l[s]);
+        if (W.col < G) split_pair(v2.x * qscale, v2.y * qscale, h[s], l[s]);
       }
       W.bq[c].hi = as_half8(h[0], h[1], h[2], h[3]);
       W.bq[c].lo = as_half8(l[0], l[1], l[2], l[3]);
