@@ -679,9 +679,11 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   const int s0 = split * p.cold_split_len;
   const int s1 = min(p.cold_len, s0 + p.cold_split_len);
   const int span = max(0, s1 - s0);
-  const int per = ((span + kWaves - 1) / kWaves + kChunk - 1) / kChunk * kChunk;
-  const int ws = s0 + wave * per;
-  const int we = min(s1, ws + per);
+  // chunks of 32 positions of the split, dealt round-robin to the waves
+  // (wave w takes chunks w, w + kWaves, ...): balanced to one chunk, and
+  // the same assignment, hence the same sums, on every call
+  const int n_chunks = (span + kChunk - 1) / kChunk;
+  const int n_full = span / kChunk;
 
   constexpr bool k_packed = KB != 0;
   constexpr int kRowBytes = WaveT::kRowBytes;
@@ -712,7 +714,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
 
   // ---- first chunk in flight while the block builds its tables --------
   ChunkData<KB, GP> A, B;
-  if (ws < we) W.load(ws, A);
+  if (wave < n_chunks) W.load(s0 + wave * kChunk, A);
 
   // wave h < G takes query head h, coordinates lane and lane + 64
   float qa = 0.0f, qb = 0.0f;
@@ -799,50 +801,55 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
     }
   }
 
-  // ---- main loop: chunk i is processed while chunk i + 1 loads into the
-  // other of two register buffers (ping-pong, so nothing is copied); chunk i
-  // sits in A for even i, in B for odd i.  Only the wave's last chunk can be
-  // partial: it runs after the loop, so the loop body has no masking -------
+  // ---- main loop: the wave processes its chunk while its next one loads
+  // into the other of two register buffers (ping-pong, so nothing is
+  // copied).  Only the split's last chunk can be partial.
   if (KB == 0) {
-    // fp16 K rows (32 dwords a buffer): the same ping-pong with the masked
-    // variant inside the loop keeps this shape within its registers
-    for (int t0 = ws; t0 < we;) {
-      const bool nb = t0 + kChunk < we;
-      if (nb) W.load(t0 + kChunk, B);
-      if (t0 + kChunk <= we) {
-        W.template cold_chunk<false>(t0, we, A, p.scores, hq0, p.length);
+    // fp16 K rows (32 dwords a buffer): the masked variant stays inside the
+    // loop, which keeps this shape within its registers
+    int c = wave;
+    while (c < n_chunks) {
+      int cn = c + kWaves;
+      if (cn < n_chunks) W.load(s0 + cn * kChunk, B);
+      if (c < n_full) {
+        W.template cold_chunk<false>(s0 + c * kChunk, s1, A, p.scores, hq0, p.length);
       } else {
-        W.template cold_chunk<true>(t0, we, A, p.scores, hq0, p.length);
+        W.template cold_chunk<true>(s0 + c * kChunk, s1, A, p.scores, hq0, p.length);
       }
-      t0 += kChunk;
-      if (!nb) break;
-      const bool na = t0 + kChunk < we;
-      if (na) W.load(t0 + kChunk, A);
-      if (t0 + kChunk <= we) {
-        W.template cold_chunk<false>(t0, we, B, p.scores, hq0, p.length);
+      c = cn;
+      if (c >= n_chunks) break;
+      cn = c + kWaves;
+      if (cn < n_chunks) W.load(s0 + cn * kChunk, A);
+      if (c < n_full) {
+        W.template cold_chunk<false>(s0 + c * kChunk, s1, B, p.scores, hq0, p.length);
       } else {
-        W.template cold_chunk<true>(t0, we, B, p.scores, hq0, p.length);
+        W.template cold_chunk<true>(s0 + c * kChunk, s1, B, p.scores, hq0, p.length);
       }
-      t0 += kChunk;
-      if (!na) break;
+      c = cn;
     }
   } else {
-    const int n = (we - ws + kChunk - 1) / kChunk;  // chunks, the partial one included
-    const int nf = (we - ws) / kChunk;              // full chunks
-    int i = 0;
-    while (i < nf) {
-      if (i + 1 < n) W.load(ws + (i + 1) * kChunk, B);
-      W.template cold_chunk<false>(ws + i * kChunk, we, A, p.scores, hq0, p.length);
-      if (++i >= nf) break;
-      if (i + 1 < n) W.load(ws + (i + 1) * kChunk, A);
-      W.template cold_chunk<false>(ws + i * kChunk, we, B, p.scores, hq0, p.length);
-      ++i;
+    // the loop body has no masking; a claimed partial chunk runs after it
+    int c = wave;
+    bool in_b = false;  // the buffer holding chunk c
+    while (c < n_full) {
+      int cn = c + kWaves;
+      if (cn < n_chunks) W.load(s0 + cn * kChunk, B);
+      W.template cold_chunk<false>(s0 + c * kChunk, s1, A, p.scores, hq0, p.length);
+      c = cn;
+      if (c >= n_full) {
+        in_b = true;
+        break;
+      }
+      cn = c + kWaves;
+      if (cn < n_chunks) W.load(s0 + cn * kChunk, A);
+      W.template cold_chunk<false>(s0 + c * kChunk, s1, B, p.scores, hq0, p.length);
+      c = cn;
     }
-    if (i < n) {
-      if (i & 1) {
-        W.template cold_chunk<true>(ws + i * kChunk, we, B, p.scores, hq0, p.length);
+    if (c < n_chunks) {
+      if (in_b) {
+        W.template cold_chunk<true>(s0 + c * kChunk, s1, B, p.scores, hq0, p.length);
       } else {
-        W.template cold_chunk<true>(ws + i * kChunk, we, A, p.scores, hq0, p.length);
+        W.template cold_chunk<true>(s0 + c * kChunk, s1, A, p.scores, hq0, p.length);
       }
     }
   }
