@@ -712,16 +712,17 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   W.vscale = kVscaleMax;
   W.reset();
 
-  // ---- first chunk in flight while the block builds its tables --------
+  // ---- the query, then the first chunk, in flight while the block builds
+  // its tables.  Wave h < G takes query head h, coordinates lane and
+  // lane + 64.  The query is issued first: waiting for it (loads complete
+  // in issue order) then does not wait for the chunk.
+  // (Both loads are unconditional, so the wait for the query can count
+  // the chunk's loads as still outstanding: waves past G read head G - 1,
+  // waves past the split read an empty range, which returns zeros.)
+  uint32_t qa_raw = p.q[(hq0 + min(wave, G - 1)) * D + lane];  // fp16 bits
+  uint32_t qb_raw = p.q[(hq0 + min(wave, G - 1)) * D + lane + 64];
   ChunkData<KB, GP> A, B;
-  if (wave < n_chunks) W.load(s0 + wave * kChunk, A);
-
-  // wave h < G takes query head h, coordinates lane and lane + 64
-  float qa = 0.0f, qb = 0.0f;
-  if (wave < G) {
-    qa = h2f(p.q[(hq0 + wave) * D + lane]);
-    qb = h2f(p.q[(hq0 + wave) * D + lane + 64]);
-  }
+  W.load(s0 + wave * kChunk, A);
   // The 16 (V) and up to 16 (K) centroids the tables need, read with
   // uniform indices (scalar loads of the kernel arguments) and spread over
   // the lanes of wave 0, rather than one vector load of the argument block
@@ -760,6 +761,10 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
       lds[(64 + e) * 64 + 32 + r] = l;
     }
   }
+  // first use of the query after the tables, so the wait for it comes here
+  asm volatile("" : "+v"(qa_raw), "+v"(qb_raw)::"memory");
+  float qa = h2f(static_cast<uint16_t>(qa_raw));
+  float qb = h2f(static_cast<uint16_t>(qb_raw));
   // rotate q in registers: H diag(s) q (unnormalised), butterflies at
   // stride 64 inside the lane and at strides 32 .. 1 across lanes
   if (k_packed && wave < G) {
