@@ -220,6 +220,32 @@ __device__ __forceinline__ float head_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// One Walsh-Hadamard butterfly at lane stride M (lane l pairs with l ^ M):
+// the lower lane gets x + partner, the upper partner - x.  Strides below 16
+// move data with DPP, 16 and 32 with the lane-swap instructions.
+template <int M>
+__device__ __forceinline__ float xor_butterfly(float x, int lane) {
+  const bool upper = (lane & M) != 0;
+  if (M == 16 || M == 32) {
+    const u32x2_t ab = (M == 16) ? __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false)
+                                 : __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float a = __uint_as_float(ab[0]), b = __uint_as_float(ab[1]);  // lower, upper lane's value
+    return upper ? a - b : a + b;
+  }
+  float pt;
+  if (M == 1) {
+    pt = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xb1, 0xf, 0xf, false));  // quad_perm [1,0,3,2]
+  } else if (M == 2) {
+    pt = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4e, 0xf, 0xf, false));  // quad_perm [2,3,0,1]
+  } else {
+    // banks with bit M clear read lane + M, the others lane - M
+    constexpr int lo_banks = M == 4 ? 0x5 : 0x3;
+    pt = dpp_f<kRowShl + M, lo_banks>(0.0f, x);
+    pt = dpp_f<kRowShr + M, 0xf ^ lo_banks>(pt, x);
+  }
+  return upper ? pt - x : x + pt;
+}
+
 // Global-memory data of one chunk of 32 positions for one lane.
 template <int KB, int GP>
 struct ChunkData {
@@ -776,33 +802,47 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
     const float a = qa + qb, c = qa - qb;
     qa = a;
     qb = c;
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      const float pa = __shfl_xor(qa, m), pb = __shfl_xor(qb, m);
-      const bool upper = (lane & m) != 0;
-      qa = upper ? pa - qa : qa + pa;
-      qb = upper ? pb - qb : qb + pb;
-    }
+    qa = xor_butterfly<32>(qa, lane);
+    qb = xor_butterfly<32>(qb, lane);
+    qa = xor_butterfly<16>(qa, lane);
+    qb = xor_butterfly<16>(qb, lane);
+    qa = xor_butterfly<8>(qa, lane);
+    qb = xor_butterfly<8>(qb, lane);
+    qa = xor_butterfly<4>(qa, lane);
+    qb = xor_butterfly<4>(qb, lane);
+    qa = xor_butterfly<2>(qa, lane);
+    qb = xor_butterfly<2>(qb, lane);
+    qa = xor_butterfly<1>(qa, lane);
+    qb = xor_butterfly<1>(qb, lane);
   }
+  // scaled query as fp16 hi/lo pair words: word j of head h holds
+  // coordinates 2 j, 2 j + 1 (hi at [0, 64), lo at [64, 128) of the row).
+  // Even lanes pair their qa with the odd neighbour's, odd lanes their qb
+  // with the even neighbour's.
+  uint32_t *qhl = reinterpret_cast<uint32_t *>(qw);
   if (wave < G) {
-    qw[wave * L::qstride + lane] = qa;
-    qw[wave * L::qstride + lane + 64] = qb;
+    const float qscale = k_packed ? kLog2e / static_cast<float>(D) : kLog2e / sqrtf(static_cast<float>(D));
+    const float pa = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(qa), 0xb1, 0xf, 0xf, false));
+    const float pb = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(qb), 0xb1, 0xf, 0xf, false));
+    const bool odd = lane & 1;
+    const float x0 = odd ? pb : qa, x1 = odd ? qb : pa;
+    uint32_t h, l;
+    split_pair(x0 * qscale, x1 * qscale, h, l);
+    const int j = (odd ? 32 : 0) + (lane >> 1);
+    qhl[wave * L::qstride + j] = h;
+    qhl[wave * L::qstride + 64 + j] = l;
   }
   __syncthreads();  // tables and rotated query complete
   {
-    const float qscale = k_packed ? kLog2e / static_cast<float>(D) : kLog2e / sqrtf(static_cast<float>(D));
-    const float2 *qrow = reinterpret_cast<const float2 *>(qw + (W.col < G ? W.col : 0) * L::qstride + 32 * W.grp);
+    const uint32_t *row = qhl + (W.col < G ? W.col : 0) * L::qstride + 16 * W.grp;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      uint32_t h[4], l[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const float2 v2 = qrow[4 * c + s];  // coordinates 32 grp + 8 c + 2 s, + 1
-        h[s] = l[s] = 0u;
-        if (W.col < G) split_pair(v2.x * qscale, v2.y * qscale, h[s], l[s]);
-      }
-      W.bq[c].hi = as_half8(h[0], h[1], h[2], h[3]);
-      W.bq[c].lo = as_half8(l[0], l[1], l[2], l[3]);
+      // words 16 grp + 4 c .. + 3: coordinates 32 grp + 8 c .. + 7
+      u32x4_t h = *reinterpret_cast<const u32x4_t *>(row + 4 * c);
+      u32x4_t l = *reinterpret_cast<const u32x4_t *>(row + 64 + 4 * c);
+      if (W.col >= G) h = l = u32x4_t{0u, 0u, 0u, 0u};
+      W.bq[c].hi = __builtin_bit_cast(half8_t, h);
+      W.bq[c].lo = __builtin_bit_cast(half8_t, l);
     }
   }
 
@@ -962,13 +1002,12 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
     r4[3] = b1 - b3;
   }
 #pragma unroll
-  for (int m = 1; m < 32; m <<= 1) {
-    const bool upper = (threadIdx.x & m) != 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float pe = __shfl_xor(r4[e], m);
-      r4[e] = upper ? pe - r4[e] : r4[e] + pe;
-    }
+  for (int e = 0; e < 4; ++e) {
+    r4[e] = xor_butterfly<1>(r4[e], lane);
+    r4[e] = xor_butterfly<2>(r4[e], lane);
+    r4[e] = xor_butterfly<4>(r4[e], lane);
+    r4[e] = xor_butterfly<8>(r4[e], lane);
+    r4[e] = xor_butterfly<16>(r4[e], lane);
   }
   const float rs = 1.0f / sqrtf(static_cast<float>(D));
   const float inv = (Lt > 0.0f) ? 1.0f / Lt : 0.0f;
