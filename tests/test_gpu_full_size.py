@@ -1,0 +1,113 @@
+"""Parity at the full workload sizes, in the launch configuration the bench
+times (library-chosen splits, one layer of each workload).
+
+The whole cache is quantized and attended on the GPU.  The oracle checks
+sampled parts it can compute in seconds:
+
+* the codes and norms of a slice of rows of sampled (batch, KV head) units,
+  against the oracle's quantization of the same fp16 rows;
+* every query head of sampled units: the decode output against float64
+  attention over the rows the oracle rebuilds from what the GPU wrote
+  (dequantized packed rows, fp16 rows as stored, the delegated ring).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from parity import codes_agree, rows_close, words_to_codes
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import compressed_decode_attention_append_amd as tq  # noqa: E402
+
+# name: batch, KV heads, query heads, head_dim, context, K side, V side, hot,
+# distribution, outlier fraction, positions appended in the timed step
+FULL = {
+    "c2_sym4_4k": (1, 8, 32, 128, 4096, ("packed", 4), ("packed", 4), 0, "channel", 0.01, 0),
+    "c3_asym_16k": (8, 8, 32, 128, 16384, ("fp16", 0), ("packed", 4), 0, "channel", 0.01, 1),
+    "c4_tq35_32k": (4, 8, 32, 128, 32768, ("packed", 3), ("packed", 4), 0, "channel", 0.01, 8192),
+    "c5_delegated_64k": (16, 4, 32, 128, 65536, ("fp16", 0), ("delegated", 4), 256, "channel", 0.0, 0),
+}
+
+
+def _unit_rows(cache, side, b, h, length):
+    """float64 rows [0, length) of one (batch, KV head) unit of one side, as
+    the decode must see them, rebuilt from what the GPU wrote."""
+    spec = cache.k_spec if side == "k" else cache.v_spec
+    d = cache.head_dim
+    if spec.mode == "fp16":
+        return cache.tensors[side + "_fp16"][b, h, :length].cpu().numpy().astype(np.float64)
+    R = oracle.rotation_matrix(cache.seed, d)
+    c, _ = oracle.lloyd_max(d, spec.bits)
+    n_cold = length if spec.mode == "packed" else max(0, length - spec.hot)
+    out = np.zeros((length, d))
+    if n_cold:
+        words = cache.tensors[side + "_codes"][b, h, :n_cold].cpu().numpy()
+        norms = cache.tensors[side + "_norms"][b, h, :n_cold].cpu().numpy().astype(np.float64)
+        out[:n_cold] = oracle.dequantize(words_to_codes(words, spec.bits, d), norms, R, c)
+    if spec.mode == "delegated":
+        ring = cache.tensors[side + "_ring"][b, h].cpu().numpy()
+        for p in range(n_cold, length):
+            out[p] = ring[p % spec.hot].astype(np.float64)
+    return out
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_full_size_sampled(name):
+    B, Hkv, Hq, d, T, ks, vs, hot, dist, outl, n_new = FULL[name]
+    G = Hq // Hkv
+    kspec = tq.SideSpec(ks[0], ks[1])
+    vspec = tq.SideSpec(vs[0], vs[1], hot or 256)
+    cache = tq.TQCache(B, Hkv, d, T, kspec, vspec, seed=0, device="cuda:0")
+    base = T - n_new
+    chunk = 4096
+    samples = {}  # (b, h) -> (start, fp16 K rows, fp16 V rows) kept for the code checks
+    pick = [(0, 0), (B - 1, Hkv - 1)]
+    for s in range(0, base, chunk):
+        n = min(chunk, base - s)
+        k, v = synth.kv_torch(1009 + s, B, Hkv, n, d, dist=dist, outlier_frac=outl, device="cuda:0")
+        cache.quantize_append(k, v, s)
+        if s == 0:
+            for (b, h) in pick:
+                samples[(b, h)] = (0, k[b, h, :512].cpu().numpy(), v[b, h, :512].cpu().numpy())
+        del k, v
+    if n_new:
+        k, v = synth.kv_torch(4243, B, Hkv, n_new, d, dist=dist, outlier_frac=outl, device="cuda:0")
+        cache.quantize_append(k, v, base)  # the timed append: one prefill chunk or one token
+        if n_new >= 512:
+            for (b, h) in pick:
+                samples[(b, h, "new")] = (base, k[b, h, :512].cpu().numpy(), v[b, h, :512].cpu().numpy())
+        del k, v
+    q = synth.q_torch(77, B, Hq, d, device="cuda:0")
+    out = cache.decode_attention(q, T)
+    torch.cuda.synchronize()
+
+    # codes and norms of sampled rows
+    for key, (start, krows, vrows) in samples.items():
+        b, h = key[0], key[1]
+        for side, spec, rows in (("k", kspec, krows), ("v", vspec, vrows)):
+            if spec.mode != "packed":
+                continue
+            R = oracle.rotation_matrix(0, d)
+            _, t = oracle.lloyd_max(d, spec.bits)
+            codes_o, n_o, y_o = oracle.quantize(rows[None, None], R, t)
+            words = cache.tensors[side + "_codes"][b, h, start:start + rows.shape[0]].cpu().numpy()
+            got = words_to_codes(words[None, None], spec.bits, d)
+            ok, ndiff, nnear = codes_agree(got, codes_o, y_o, t)
+            assert ok, f"{name} {side} ({b},{h}) rows {start}+: {ndiff} codes off ({nnear} near a threshold)"
+            norms = cache.tensors[side + "_norms"][b, h, start:start + rows.shape[0]].cpu().numpy()
+            assert np.all(np.abs(norms - n_o[0, 0]) <= 1e-6 * n_o[0, 0] + 1e-30)
+
+    # decode outputs of every query head of the sampled units
+    qn = q.cpu().numpy()
+    got = out.cpu().numpy()
+    for (b, h) in pick:
+        kr = _unit_rows(cache, "k", b, h, T)[None, None]
+        vr = _unit_rows(cache, "v", b, h, T)[None, None]
+        heads = slice(h * G, (h + 1) * G)
+        o_ref, _ = oracle.decode_attention(qn[b:b + 1, heads], kr, vr)
+        ok, worst = rows_close(got[b, heads], o_ref[0])
+        print(f"{name} unit ({b},{h}): out worst rel {worst:.3e}")
+        assert ok, f"{name} unit ({b},{h}): worst {worst}"
