@@ -874,11 +874,16 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
     }
   } else {
     // the loop body has no masking; a claimed partial chunk runs after it
+    // The next chunk's loads are issued unconditionally (past the split
+    // they re-read the last chunk, which the caches hold) and pinned before
+    // the current chunk's work, so the compiler cannot sink them.
     int c = wave;
     bool in_b = false;  // the buffer holding chunk c
+    const int last = max(n_chunks - 1, 0);
     while (c < n_full) {
       int cn = c + kWaves;
-      if (cn < n_chunks) W.load(s0 + cn * kChunk, B);
+      W.load(s0 + min(cn, last) * kChunk, B);
+      asm volatile("" ::: "memory");
       W.template cold_chunk<false>(s0 + c * kChunk, s1, A, p.scores, hq0, p.length);
       c = cn;
       if (c >= n_full) {
@@ -886,7 +891,8 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
         break;
       }
       cn = c + kWaves;
-      if (cn < n_chunks) W.load(s0 + cn * kChunk, A);
+      W.load(s0 + min(cn, last) * kChunk, A);
+      asm volatile("" ::: "memory");
       W.template cold_chunk<false>(s0 + c * kChunk, s1, B, p.scores, hq0, p.length);
       c = cn;
     }
