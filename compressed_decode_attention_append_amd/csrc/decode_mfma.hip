@@ -853,9 +853,11 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
     // fp16 K rows (32 dwords a buffer): the masked variant stays inside the
     // loop, which keeps this shape within its registers
     int c = wave;
+    const int last = max(n_chunks - 1, 0);
     while (c < n_chunks) {
       int cn = c + kWaves;
-      if (cn < n_chunks) W.load(s0 + cn * kChunk, B);
+      W.load(s0 + min(cn, last) * kChunk, B);
+      asm volatile("" ::: "memory");
       if (c < n_full) {
         W.template cold_chunk<false>(s0 + c * kChunk, s1, A, p.scores, hq0, p.length);
       } else {
@@ -864,7 +866,8 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
       c = cn;
       if (c >= n_chunks) break;
       cn = c + kWaves;
-      if (cn < n_chunks) W.load(s0 + cn * kChunk, A);
+      W.load(s0 + min(cn, last) * kChunk, A);
+      asm volatile("" ::: "memory");
       if (c < n_full) {
         W.template cold_chunk<false>(s0 + c * kChunk, s1, B, p.scores, hq0, p.length);
       } else {
