@@ -82,6 +82,11 @@ constexpr float kVscaleMax = 1099511627776.0f;  // 2^40: start and ceiling of th
 //                         the second half of entries 64..127
 // After the main loop the table area is reused for the merges.
 constexpr int kTableWords = 256 * 64;
+// A partial result (merge slot, workspace partial) of one query head: max,
+// sum, two pad words, then the D accumulator values, so the values start
+// 16-byte aligned.
+constexpr int kPS = D + 4;
+constexpr int kPV = 4;
 constexpr int kKhiOff3 = 128;             // byte offsets added to (e << 8) | 4 r
 constexpr int kKloOff3 = 64 * 256 + 128;
 constexpr int kKloOff4 = 128;
@@ -93,7 +98,7 @@ struct Lay {
   static constexpr int qwork = cent + 2 * kMaxLevels;  // [GP][D + 4] rotated query
   static constexpr int red = qwork + GP * qstride;     // flag
   static constexpr int total = red + 16;
-  static_assert((kMaxWaves + 1) * GP * (D + 2) <= kTableWords, "merges must fit in the table area");
+  static_assert((kMaxWaves + 1) * GP * kPS <= kTableWords, "merges must fit in the table area");
 };
 
 __device__ __forceinline__ float4_t mma(const half8_t a, const half8_t b, float4_t c) {
@@ -144,6 +149,10 @@ __device__ __forceinline__ float pow2_ceil(float x) {
   const float m = frexpf(x, &e);  // x = m 2^e, m in [0.5, 1)
   return ldexpf(1.0f, m == 0.5f ? e - 1 : e);
 }
+
+// Cache policy of a buffer load that reads past the non-coherent caches
+// (sc1), the same bits an agent-scope atomic load carries.
+constexpr int kCoherentLoad = 16;
 
 __device__ __forceinline__ void store_coherent(float *p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -621,13 +630,13 @@ struct Wave {
   }
 
   // Write this wave's (max, sum, accumulator / vscale) of the real heads to
-  // the merge slot [G][D + 2]; `hot_layout` selects the coordinate order.
+  // the merge slot [G][kPS]; `hot_layout` selects the coordinate order.
   // The hi and lo rows of the value accumulators are summed first: lane
   // group g = 0 (and 1 for GP = 8) then holds head 4 g + r in row r.
   __device__ __forceinline__ void to_slot(float *slot_base, bool hot_layout) const {
     const float l_wave = head_sum<GP>(l_run);
     if (col < G && grp == 0) {
-      float *slot = slot_base + col * (D + 2);
+      float *slot = slot_base + col * kPS;
       slot[0] = m_run;
       slot[1] = l_wave;
     }
@@ -648,30 +657,30 @@ struct Wave {
       for (int r = 0; r < 4; ++r) {
         const int h = 4 * grp + r;
         if (h < G) {
-          float *slot = slot_base + h * (D + 2);
+          float *slot = slot_base + h * kPS;
 #pragma unroll
-          for (int q = 0; q < 8; ++q) slot[2 + (hot_layout ? 16 * q + col : 8 * col + q)] = sum[q][r];
+          for (int q = 0; q < 8; ++q) slot[kPV + (hot_layout ? 16 * q + col : 8 * col + q)] = sum[q][r];
         }
       }
     }
   }
 };
 
-// Merge NW slots [w][G][D + 2] into one (max, sum, accumulator) per head
-// element i of [G][D + 2].
+// Merge NW slots [w][G][kPS] into one (max, sum, accumulator) per head:
+// element i of [G][kPS] (pad words come out 0).
 template <int NW>
 __device__ __forceinline__ float merge_waves(const float *slots, int G, int i) {
-  const int h = i / (D + 2), j = i % (D + 2);
+  const int h = i / kPS, j = i % kPS;
   float M = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) M = fmaxf(M, slots[(w * G + h) * (D + 2)]);
-  if (M == -INFINITY) return (j == 0) ? -INFINITY : 0.0f;
+  for (int w = 0; w < NW; ++w) M = fmaxf(M, slots[(w * G + h) * kPS]);
   if (j == 0) return M;
+  if (M == -INFINITY || j == 2 || j == 3) return 0.0f;
   float v = 0.0f;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
-    const float mw = slots[(w * G + h) * (D + 2)];
-    if (mw != -INFINITY) v += __builtin_amdgcn_exp2f(mw - M) * slots[(w * G + h) * (D + 2) + j];
+    const float mw = slots[(w * G + h) * kPS];
+    if (mw != -INFINITY) v += __builtin_amdgcn_exp2f(mw - M) * slots[(w * G + h) * kPS + j];
   }
   return v;
 }
@@ -910,11 +919,11 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
 
   // ---- merge the waves of this block (tables are dead from here on) -----
   __syncthreads();
-  W.to_slot(work + wave * G * (D + 2), false);
+  W.to_slot(work + wave * G * kPS, false);
   __syncthreads();
   float *part = reinterpret_cast<float *>(reinterpret_cast<char *>(p.ws) + p.ws_part_off);
-  float *mypart = part + (static_cast<long>(unit) * nsplit + split) * G * (D + 2);
-  for (int i = threadIdx.x; i < G * (D + 2); i += kThreads) store_coherent(mypart + i, merge_waves<kWaves>(work, G, i));
+  float *mypart = part + (static_cast<long>(unit) * nsplit + split) * G * kPS;
+  for (int i = threadIdx.x; i < G * kPS; i += kThreads) store_coherent(mypart + i, merge_waves<kWaves>(work, G, i));
 
   // ---- the last block of the unit merges the splits ----------------------
   // The partials above are L2-coherent stores; once they have completed
@@ -930,7 +939,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   if (*flag == 0) return;
 
   // delegated V: this block also attends over the fp16 hot window
-  float *hotp = work + kWaves * G * (D + 2);  // [G][D + 2] merged hot partial
+  float *hotp = work + kWaves * G * kPS;  // [G][kPS] merged hot partial
   const int h0 = p.cold_len, h1 = p.length;
   const bool has_hot = h1 > h0;
   if (has_hot) {
@@ -943,9 +952,9 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
       W.load(t0, A);
       W.hot_chunk(t0, he, A, p.scores, hq0, p.length);
     }
-    W.to_slot(work + wave * G * (D + 2), true);
+    W.to_slot(work + wave * G * kPS, true);
     __syncthreads();
-    for (int i = threadIdx.x; i < G * (D + 2); i += kThreads) hotp[i] = merge_waves<kWaves>(work, G, i);
+    for (int i = threadIdx.x; i < G * kPS; i += kThreads) hotp[i] = merge_waves<kWaves>(work, G, i);
     __syncthreads();
   }
   // Every load below is independent of the others, so each thread has all of
@@ -953,26 +962,31 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   // coordinates 4 j4 .. 4 j4 + 3; the 32 threads of a head sit in one wave,
   // so the inverse rotation needs no block barrier.
   if (threadIdx.x >= G * (D / 4)) return;
-  const float *up = part + static_cast<long>(unit) * nsplit * G * (D + 2);
+  const float *up = part + static_cast<long>(unit) * nsplit * G * kPS;
   const int hh = threadIdx.x / (D / 4);
   const int jj = 4 * (threadIdx.x % (D / 4));
   float r4[4] = {0.0f, 0.0f, 0.0f, 0.0f}, q4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   float Lt = 0.0f;
   float M = -INFINITY;
-  for (int sp0 = 0; sp0 < nsplit; sp0 += 16) {
-    float mv[16], lv[16], ov[16][4];
+  // partials of the unit, read past the non-coherent caches (sc1)
+  const auto rp = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(up), 0, nsplit * G * kPS * 4, 0x00020000);
+  constexpr int kB = 8;  // splits per batch of independent loads
+  for (int sp0 = 0; sp0 < nsplit; sp0 += kB) {
+    float mv[kB], lv[kB], ov[kB][4];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
+    for (int k = 0; k < kB; ++k) {
       const int sp = min(sp0 + k, nsplit - 1);
-      const float *src = up + (sp * G + hh) * (D + 2);
-      mv[k] = (sp0 + k < nsplit) ? load_coherent(src) : -INFINITY;
-      lv[k] = load_coherent(src + 1);
+      const int base = ((sp * G + hh) * kPS) * 4;
+      const u32x2_t ml = __builtin_amdgcn_raw_buffer_load_b64(rp, base, 0, kCoherentLoad);
+      const u32x4_t o4 = __builtin_amdgcn_raw_buffer_load_b128(rp, base + (kPV + jj) * 4, 0, kCoherentLoad);
+      mv[k] = (sp0 + k < nsplit) ? __uint_as_float(ml[0]) : -INFINITY;
+      lv[k] = __uint_as_float(ml[1]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ov[k][e] = load_coherent(src + 2 + jj + e);
+      for (int e = 0; e < 4; ++e) ov[k][e] = __uint_as_float(o4[e]);
     }
     float mg = M;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) mg = fmaxf(mg, mv[k]);
+    for (int k = 0; k < kB; ++k) mg = fmaxf(mg, mv[k]);
     if (mg == -INFINITY) continue;
     const float a = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - mg);
     M = mg;
@@ -980,7 +994,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
 #pragma unroll
     for (int e = 0; e < 4; ++e) r4[e] *= a;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
+    for (int k = 0; k < kB; ++k) {
       const float w = (mv[k] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mv[k] - M);
       Lt += w * lv[k];
 #pragma unroll
@@ -988,16 +1002,16 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
     }
   }
   if (has_hot) {
-    const float mh = hotp[hh * (D + 2)];
+    const float mh = hotp[hh * kPS];
     if (mh != -INFINITY) {
       const float mg = fmaxf(M, mh);
       const float a = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - mg);
       const float bh = __builtin_amdgcn_exp2f(mh - mg);
-      Lt = Lt * a + bh * hotp[hh * (D + 2) + 1];
+      Lt = Lt * a + bh * hotp[hh * kPS + 1];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         r4[e] *= a;
-        q4[e] = bh * hotp[hh * (D + 2) + 2 + jj + e];
+        q4[e] = bh * hotp[hh * kPS + kPV + jj + e];
       }
     }
   }

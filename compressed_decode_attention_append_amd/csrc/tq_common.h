@@ -97,7 +97,7 @@ __host__ __device__ inline DecodeWorkspace decode_workspace_layout(int batch, in
 inline size_t decode_mfma_workspace_bytes(int batch, int kv_heads, int q_heads, int splits,
                                           int head_dim) {
   const size_t G = size_t(q_heads / kv_heads);
-  return kCounterBytes + align256(size_t(batch) * kv_heads * splits * G * (head_dim + 2) * sizeof(float));
+  return kCounterBytes + align256(size_t(batch) * kv_heads * splits * G * (head_dim + 4) * sizeof(float));
 }
 
 hipError_t launch_quantize_append(const QuantizeParams &p, hipStream_t stream);
