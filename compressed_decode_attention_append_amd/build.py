@@ -37,6 +37,12 @@ def sources():
                   if f.endswith((".hip", ".cpp")))
 
 
+# Per-source flags.  The decode kernel never sees NaN scores (infinities,
+# which mark masked positions, keep their meaning), so its max reductions
+# need not quiet NaNs first.
+EXTRA_FLAGS = {"decode_mfma.hip": ["-fno-honor-nans"]}
+
+
 def compile_one(src: str, debug: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     cmd = [hipcc()] + (["-x", "hip"] if src.endswith(".hip") else []) + ["-c", src, "-o", obj, "-fPIC", "-std=c++17",
@@ -45,6 +51,7 @@ def compile_one(src: str, debug: bool) -> str:
     if src.endswith(".hip"):
         cmd += [f"--offload-arch={ARCH}",
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+    cmd += EXTRA_FLAGS.get(os.path.basename(src), [])
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
