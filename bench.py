@@ -205,7 +205,7 @@ def stats_summary(stats_csv: str, workload: str, cmds: list):
             name = r["Name"]
             if "tq::" not in name:
                 continue
-            short = name.replace("void tq::(anonymous namespace)::", "").split("(tq::")[0]
+            short = name.replace("void ", "").replace("tq::(anonymous namespace)::", "").split("(tq::")[0]
             rows.append((short, int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
                          float(r["MaxNs"]) / 1e3))
     w = WORKLOADS[workload]
