@@ -153,8 +153,11 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(const Quanti
   if (p.k_lut_scale > 0.0f) build_lut(lut[0], p.k_thr, p.k.bits, p.k_lut_scale);
   if (p.v_lut_scale > 0.0f) build_lut(lut[1], p.v_thr, p.v.bits, p.v_lut_scale);
 
-  // B = diag(s) H^T in the layout described above, built once per wave.
-  uint32_t bm[8][4][4];
+  // B = diag(s) H^T in the layout described above, built once per wave for
+  // the N-tiles t < 4.  Tile t + 4 differs from tile t only by the sign of
+  // its k slots 4..7 (popcount((t ^ 4) & s) flips with bit 2 of s), which
+  // the product takes from A instead: A with those slots negated.
+  uint32_t bm[4][4][4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const uint32_t par = static_cast<uint32_t>(__builtin_popcount(n & (4 * q + g)) & 1);
@@ -165,7 +168,7 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(const Quanti
       const uint32_t s0 = (sw & 1u) ^ par, s1 = ((sw >> 1) & 1u) ^ par;
       const uint32_t base = (0x3c00u | (s0 << 15)) | ((0x3c00u | (s1 << 15)) << 16);
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
+      for (int t = 0; t < 4; ++t) {
         const uint32_t m = (static_cast<uint32_t>(__builtin_popcount(t & (2 * pr)) & 1) << 15) |
                            (static_cast<uint32_t>(__builtin_popcount(t & (2 * pr + 1)) & 1) << 31);
         bm[t][q][pr] = base ^ m;
@@ -215,12 +218,18 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(const Quanti
 
     float4_t acc[8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      acc[t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int t = 0; t < 8; ++t) acc[t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 4; ++q) {
+      u32x4_t af = __builtin_bit_cast(u32x4_t, a[q]);
+      af[2] ^= 0x80008000u;
+      af[3] ^= 0x80008000u;
+      const half8_t a_flip = as_half8(af);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
         const u32x4_t b = {bm[t][q][0], bm[t][q][1], bm[t][q][2], bm[t][q][3]};
         acc[t] = mma(a[q], as_half8(b), acc[t]);
+        acc[t + 4] = mma(a_flip, as_half8(b), acc[t + 4]);
       }
     }
 
