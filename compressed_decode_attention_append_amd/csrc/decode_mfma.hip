@@ -93,9 +93,8 @@ constexpr int kKloOff4 = 128;
 
 template <int GP>
 struct Lay {
-  static constexpr int cent = kTableWords;
-  static constexpr int qstride = D + 4;                // padded row: fewer bank conflicts
-  static constexpr int qwork = cent + 2 * kMaxLevels;  // [GP][D + 4] rotated query
+  static constexpr int qstride = D + 4;   // padded row: fewer bank conflicts
+  static constexpr int qwork = kTableWords;  // [GP][D + 4] rotated query
   static constexpr int red = qwork + GP * qstride;     // flag
   static constexpr int total = red + 16;
   static_assert((kMaxWaves + 1) * GP * kPS <= kTableWords, "merges must fit in the table area");
@@ -153,14 +152,6 @@ __device__ __forceinline__ float pow2_ceil(float x) {
 // Cache policy of a buffer load that reads past the non-coherent caches
 // (sc1), the same bits an agent-scope atomic load carries.
 constexpr int kCoherentLoad = 16;
-
-__device__ __forceinline__ void store_coherent(float *p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ float load_coherent(const float *p) {
-  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // Buffer resource over [base, base + bytes): loads past the end read 0.
 constexpr int kBufFlags = 0x00020000;
@@ -629,60 +620,88 @@ struct Wave {
     }
   }
 
-  // Write this wave's (max, sum, accumulator / vscale) of the real heads to
-  // the merge slot [G][kPS]; `hot_layout` selects the coordinate order.
-  // The hi and lo rows of the value accumulators are summed first: lane
-  // group g = 0 (and 1 for GP = 8) then holds head 4 g + r in row r.
+  // Write this wave's partial result of the real heads into its merge slot
+  // [G][kPS]: (max, sum, 1 / vscale, 0), then the accumulator in coordinate
+  // order (`hot_layout` selects the value tiles' coordinate map).  The hi
+  // and lo rows of the value accumulators are summed first with the partner
+  // lane group; after that, for GP = 4 lane groups 0 and 1 both hold heads
+  // 0-3 in rows 0-3, for GP = 8 groups 0 and 2 hold heads 0-3 and groups 1
+  // and 3 heads 4-7, and each lane writes two of its four heads.
   __device__ __forceinline__ void to_slot(float *slot_base, bool hot_layout) const {
+    // the lane index is recomputed here: reusing the prologue's lane
+    // offsets would keep them live (in registers) across the main loop
+    uint32_t lid;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lid));
+    const int col = lid & 15, grp = lid >> 4;
     const float l_wave = head_sum<GP>(l_run);
-    if (col < G && grp == 0) {
-      float *slot = slot_base + col * kPS;
-      slot[0] = m_run;
-      slot[1] = l_wave;
-    }
-    const float inv = 1.0f / vscale;
-    float4_t sum[8];
+    if (col < G && grp == 0)
+      *reinterpret_cast<float4 *>(slot_base + col * kPS) = make_float4(m_run, l_wave, 1.0f / vscale, 0.0f);
+    const int half = (GP == 4) ? (grp & 1) : (grp >> 1);  // rows 2 half, 2 half + 1
+    const int h0 = ((GP == 4) ? 0 : 4 * (grp & 1)) + 2 * half;
+    float v[2][8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
+      float sum[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const uint32_t x = __float_as_uint(accv[q][r]);
         const u32x2_t sw = (GP == 4) ? __builtin_amdgcn_permlane16_swap(x, x, false, false)
                                      : __builtin_amdgcn_permlane32_swap(x, x, false, false);
-        sum[q][r] = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * inv;
+        sum[r] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
       }
+      v[0][q] = half ? sum[2] : sum[0];
+      v[1][q] = half ? sum[3] : sum[1];
     }
-    if (grp < GP / 4) {
+    if (GP == 4 && grp >= 2) return;  // padding rows
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int h = 4 * grp + r;
-        if (h < G) {
-          float *slot = slot_base + h * kPS;
+    for (int e = 0; e < 2; ++e) {
+      const int h = h0 + e;
+      if (h < G) {
+        float *dst = slot_base + h * kPS + kPV;
+        if (hot_layout) {
 #pragma unroll
-          for (int q = 0; q < 8; ++q) slot[kPV + (hot_layout ? 16 * q + col : 8 * col + q)] = sum[q][r];
+          for (int q = 0; q < 8; ++q) dst[16 * q + col] = v[e][q];
+        } else {
+          *reinterpret_cast<float4 *>(dst + 8 * col) = make_float4(v[e][0], v[e][1], v[e][2], v[e][3]);
+          *reinterpret_cast<float4 *>(dst + 8 * col + 4) = make_float4(v[e][4], v[e][5], v[e][6], v[e][7]);
         }
       }
     }
   }
 };
 
-// Merge NW slots [w][G][kPS] into one (max, sum, accumulator) per head:
-// element i of [G][kPS] (pad words come out 0).
+// Merge the NW wave slots [w][G][kPS] of head h, values 4 j4 .. 4 j4 + 3:
+// hdr = (max M, sum, 0, 0), val = sum_w 2^(m_w - M) acc_w / vscale_w.  A
+// wave that saw no position of the head has m_w = -inf and weighs 0.
 template <int NW>
-__device__ __forceinline__ float merge_waves(const float *slots, int G, int i) {
-  const int h = i / kPS, j = i % kPS;
+__device__ __forceinline__ void merge_slots(const float *slots, int G, int h, int j4, float4 &hdr, float4 &val) {
+  float4 st[NW];
   float M = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) M = fmaxf(M, slots[(w * G + h) * kPS]);
-  if (j == 0) return M;
-  if (M == -INFINITY || j == 2 || j == 3) return 0.0f;
-  float v = 0.0f;
+  for (int w = 0; w < NW; ++w) {
+    st[w] = *reinterpret_cast<const float4 *>(slots + (w * G + h) * kPS);
+    M = fmaxf(M, st[w].x);
+  }
+  float L = 0.0f;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
-    const float mw = slots[(w * G + h) * kPS];
-    if (mw != -INFINITY) v += __builtin_amdgcn_exp2f(mw - M) * slots[(w * G + h) * kPS + j];
+    const float4 a = *reinterpret_cast<const float4 *>(slots + (w * G + h) * kPS + kPV + 4 * j4);
+    const float e = (st[w].x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(st[w].x - M);
+    L += e * st[w].y;
+    const float f = e * st[w].z;
+    acc.x += f * a.x;
+    acc.y += f * a.y;
+    acc.z += f * a.z;
+    acc.w += f * a.w;
   }
-  return v;
+  hdr = make_float4(M, L, 0.0f, 0.0f);
+  val = acc;
+}
+
+__device__ __forceinline__ void store4_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off, float4 v) {
+  const u32x4_t u = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)};
+  __builtin_amdgcn_raw_buffer_store_b128(u, r, off, 0, kCoherentLoad);
 }
 
 template <int KB, int GP>
@@ -694,13 +713,12 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   constexpr int NV = WaveT::NV;
   // Static LDS: its base address is a compile-time constant, so table reads
   // fold the table offset into the instruction.
-  __shared__ uint32_t lds[L::total];
+  __shared__ __align__(16) uint32_t lds[L::total];
   const int lane = threadIdx.x & 63;
   // wave index as a scalar: everything derived from it (the wave's range of
   // positions, the buffer descriptors) then stays in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = p.q_heads / p.kv_heads;
-  float *cent = reinterpret_cast<float *>(lds + L::cent);
   float *qw = reinterpret_cast<float *>(lds + L::qwork);
   int *flag = reinterpret_cast<int *>(lds + L::red);
   float *work = reinterpret_cast<float *>(lds);  // merge area after the main loop
@@ -758,42 +776,38 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   uint32_t qb_raw = p.q[(hq0 + min(wave, G - 1)) * D + lane + 64];
   ChunkData<KB, GP> A, B;
   W.load(s0 + wave * kChunk, A);
-  // The 16 (V) and up to 16 (K) centroids the tables need, read with
-  // uniform indices (scalar loads of the kernel arguments) and spread over
-  // the lanes of wave 0, rather than one vector load of the argument block
-  // per thread.
-  if (wave == 0) {
-    float kc = 0.0f, vc = 0.0f;
+  // The 16 (V) and up to 16 (K) centroids the tables need: every wave reads
+  // them with uniform indices (scalar loads of the kernel arguments) into
+  // its lanes 0-15, rather than one vector load of the argument block per
+  // thread, and takes an entry's pair from those lanes with a shuffle.
+  float kc = 0.0f, vc = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      kc = (lane == i) ? p.k_cent[i] : kc;
-      vc = (lane == i) ? p.v_cent[i] : vc;
-    }
-    if (lane < 16) {
-      cent[lane] = kc;
-      cent[kMaxLevels + lane] = vc;
-    }
+  for (int i = 0; i < 16; ++i) {
+    if (KB) kc = (lane == i) ? p.k_cent[i] : kc;
+    vc = (lane == i) ? p.v_cent[i] : vc;
   }
-  __syncthreads();  // centroids visible
-  // value table (for KB = 4 also the K hi table), 32 replicas per entry;
-  // built while the query and the first chunk are in flight
-  for (int i = threadIdx.x; i < 256 * kRep; i += kThreads) {
-    const int e = i / kRep, r = i % kRep;
-    const float c0 = cent[kMaxLevels + (e & 15)], c1 = cent[kMaxLevels + (e >> 4)];
-    lds[e * 64 + r] = pack_half2(c0, c1);
+  // Tables, written four replicas (16 bytes) at a time: the value table
+  // (for KB = 4 also the K lo table) and, for KB = 3, the K hi and lo
+  // tables.  Built while the query and the first chunk are in flight.
+  // Every loop below runs whole waves (the counts are multiples of 64), as
+  // the shuffles need.
+  for (int i = threadIdx.x; i < 256 * (kRep / 4); i += kThreads) {
+    const int e = i >> 3, r4 = 4 * (i & 7);
+    const uint32_t w = pack_half2(__shfl(vc, e & 15), __shfl(vc, e >> 4));
+    *reinterpret_cast<u32x4_t *>(lds + e * 64 + r4) = u32x4_t{w, w, w, w};
     if (KB == 4) {
       uint32_t h, l;
-      split_pair(cent[e & 15], cent[e >> 4], h, l);
-      lds[e * 64 + 32 + r] = l;
+      split_pair(__shfl(kc, e & 15), __shfl(kc, e >> 4), h, l);
+      *reinterpret_cast<u32x4_t *>(lds + e * 64 + 32 + r4) = u32x4_t{l, l, l, l};
     }
   }
   if (KB == 3) {
-    for (int i = threadIdx.x; i < 64 * kRep; i += kThreads) {
-      const int e = i / kRep, r = i % kRep;
+    for (int i = threadIdx.x; i < 64 * (kRep / 4); i += kThreads) {
+      const int e = i >> 3, r4 = 4 * (i & 7);
       uint32_t h, l;
-      split_pair(cent[e & 7], cent[e >> 3], h, l);
-      lds[e * 64 + 32 + r] = h;
-      lds[(64 + e) * 64 + 32 + r] = l;
+      split_pair(__shfl(kc, e & 7), __shfl(kc, e >> 3), h, l);
+      *reinterpret_cast<u32x4_t *>(lds + e * 64 + 32 + r4) = u32x4_t{h, h, h, h};
+      *reinterpret_cast<u32x4_t *>(lds + (64 + e) * 64 + 32 + r4) = u32x4_t{l, l, l, l};
     }
   }
   // first use of the query after the tables, so the wait for it comes here
@@ -923,7 +937,15 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   __syncthreads();
   float *part = reinterpret_cast<float *>(reinterpret_cast<char *>(p.ws) + p.ws_part_off);
   float *mypart = part + (static_cast<long>(unit) * nsplit + split) * G * kPS;
-  for (int i = threadIdx.x; i < G * kPS; i += kThreads) store_coherent(mypart + i, merge_waves<kWaves>(work, G, i));
+  if (threadIdx.x < G * (D / 4)) {
+    // thread (h, j4): head h, values 4 j4 .. 4 j4 + 3, L2-coherent stores
+    const int h = threadIdx.x / (D / 4), j4 = threadIdx.x % (D / 4);
+    float4 hdr, val;
+    merge_slots<kWaves>(work, G, h, j4, hdr, val);
+    const auto rs = rsrc(mypart, G * kPS * 4);
+    if (j4 == 0) store4_coherent(rs, h * kPS * 4, hdr);
+    store4_coherent(rs, (h * kPS + kPV + 4 * j4) * 4, val);
+  }
 
   // ---- the last block of the unit merges the splits ----------------------
   // The partials above are L2-coherent stores; once they have completed
@@ -954,7 +976,13 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
     }
     W.to_slot(work + wave * G * kPS, true);
     __syncthreads();
-    for (int i = threadIdx.x; i < G * kPS; i += kThreads) hotp[i] = merge_waves<kWaves>(work, G, i);
+    if (threadIdx.x < G * (D / 4)) {
+      const int h = threadIdx.x / (D / 4), j4 = threadIdx.x % (D / 4);
+      float4 hdr, val;
+      merge_slots<kWaves>(work, G, h, j4, hdr, val);
+      if (j4 == 0) *reinterpret_cast<float4 *>(hotp + h * kPS) = hdr;
+      *reinterpret_cast<float4 *>(hotp + h * kPS + kPV + 4 * j4) = val;
+    }
     __syncthreads();
   }
   // Every load below is independent of the others, so each thread has all of
