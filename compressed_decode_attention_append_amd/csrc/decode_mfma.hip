@@ -620,13 +620,15 @@ struct Wave {
     }
   }
 
-  // Write this wave's partial result of the real heads into its merge slot
-  // [G][kPS]: (max, sum, 1 / vscale, 0), then the accumulator in coordinate
-  // order (`hot_layout` selects the value tiles' coordinate map).  The hi
-  // and lo rows of the value accumulators are summed first with the partner
-  // lane group; after that, for GP = 4 lane groups 0 and 1 both hold heads
-  // 0-3 in rows 0-3, for GP = 8 groups 0 and 2 hold heads 0-3 and groups 1
-  // and 3 heads 4-7, and each lane writes two of its four heads.
+  // Write this wave's partial result of the real heads (h < G) into its
+  // merge slot [GP][kPS]: (max, sum, 1 / vscale, 0), then the accumulator in
+  // coordinate order (`hot_layout` selects the value tiles' coordinate map).
+  // The hi and lo rows of the value accumulators sit in partner lane groups
+  // (GP = 4: groups 0 / 1 hold rows 0-3 / 4-7, i.e. hi / lo of heads 0-3;
+  // GP = 8: groups 0, 1 / 2, 3 hold hi / lo of heads 0-3, 4-7).  One lane
+  // swap of rows r and r + 2 brings each lane the hi and lo of one head:
+  // after swapping and adding, lane group g holds heads h0 + e (e = 0 from
+  // rows 0 and 2, e = 1 from rows 1 and 3), which the lane then writes.
   __device__ __forceinline__ void to_slot(float *slot_base, bool hot_layout) const {
     // the lane index is recomputed here: reusing the prologue's lane
     // offsets would keep them live (in registers) across the main loop
@@ -634,23 +636,23 @@ struct Wave {
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lid));
     const int col = lid & 15, grp = lid >> 4;
     const float l_wave = head_sum<GP>(l_run);
-    if (col < G && grp == 0)
-      *reinterpret_cast<float4 *>(slot_base + col * kPS) = make_float4(m_run, l_wave, 1.0f / vscale, 0.0f);
-    const int half = (GP == 4) ? (grp & 1) : (grp >> 1);  // rows 2 half, 2 half + 1
-    const int h0 = ((GP == 4) ? 0 : 4 * (grp & 1)) + 2 * half;
+    if (col < G && grp == 0) {
+      // 1 / vscale, exactly (vscale is a power of two)
+      int ex;
+      (void)frexpf(vscale, &ex);
+      *reinterpret_cast<float4 *>(slot_base + col * kPS) = make_float4(m_run, l_wave, ldexpf(1.0f, 1 - ex), 0.0f);
+    }
+    const int h0 = (GP == 4) ? 2 * (grp & 1) : 4 * (grp & 1) + 2 * (grp >> 1);
     float v[2][8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      float sum[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint32_t x = __float_as_uint(accv[q][r]);
-        const u32x2_t sw = (GP == 4) ? __builtin_amdgcn_permlane16_swap(x, x, false, false)
-                                     : __builtin_amdgcn_permlane32_swap(x, x, false, false);
-        sum[r] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      for (int e = 0; e < 2; ++e) {
+        const uint32_t x = __float_as_uint(accv[q][e]), y = __float_as_uint(accv[q][e + 2]);
+        const u32x2_t sw = (GP == 4) ? __builtin_amdgcn_permlane16_swap(x, y, false, false)
+                                     : __builtin_amdgcn_permlane32_swap(x, y, false, false);
+        v[e][q] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
       }
-      v[0][q] = half ? sum[2] : sum[0];
-      v[1][q] = half ? sum[3] : sum[1];
     }
     if (GP == 4 && grp >= 2) return;  // padding rows
 #pragma unroll
@@ -670,23 +672,23 @@ struct Wave {
   }
 };
 
-// Merge the NW wave slots [w][G][kPS] of head h, values 4 j4 .. 4 j4 + 3:
+// Merge the NW wave slots [w][GP][kPS] of head h, values 4 j4 .. 4 j4 + 3:
 // hdr = (max M, sum, 0, 0), val = sum_w 2^(m_w - M) acc_w / vscale_w.  A
 // wave that saw no position of the head has m_w = -inf and weighs 0.
-template <int NW>
-__device__ __forceinline__ void merge_slots(const float *slots, int G, int h, int j4, float4 &hdr, float4 &val) {
+template <int NW, int GP>
+__device__ __forceinline__ void merge_slots(const float *slots, int h, int j4, float4 &hdr, float4 &val) {
   float4 st[NW];
   float M = -INFINITY;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
-    st[w] = *reinterpret_cast<const float4 *>(slots + (w * G + h) * kPS);
+    st[w] = *reinterpret_cast<const float4 *>(slots + (w * GP + h) * kPS);
     M = fmaxf(M, st[w].x);
   }
   float L = 0.0f;
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
-    const float4 a = *reinterpret_cast<const float4 *>(slots + (w * G + h) * kPS + kPV + 4 * j4);
+    const float4 a = *reinterpret_cast<const float4 *>(slots + (w * GP + h) * kPS + kPV + 4 * j4);
     const float e = (st[w].x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(st[w].x - M);
     L += e * st[w].y;
     const float f = e * st[w].z;
@@ -933,7 +935,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
 
   // ---- merge the waves of this block (tables are dead from here on) -----
   __syncthreads();
-  W.to_slot(work + wave * G * kPS, false);
+  W.to_slot(work + wave * GP * kPS, false);
   __syncthreads();
   float *part = reinterpret_cast<float *>(reinterpret_cast<char *>(p.ws) + p.ws_part_off);
   float *mypart = part + (static_cast<long>(unit) * nsplit + split) * G * kPS;
@@ -941,7 +943,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
     // thread (h, j4): head h, values 4 j4 .. 4 j4 + 3, L2-coherent stores
     const int h = threadIdx.x / (D / 4), j4 = threadIdx.x % (D / 4);
     float4 hdr, val;
-    merge_slots<kWaves>(work, G, h, j4, hdr, val);
+    merge_slots<kWaves, GP>(work, h, j4, hdr, val);
     const auto rs = rsrc(mypart, G * kPS * 4);
     if (j4 == 0) store4_coherent(rs, h * kPS * 4, hdr);
     store4_coherent(rs, (h * kPS + kPV + 4 * j4) * 4, val);
@@ -961,7 +963,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   if (*flag == 0) return;
 
   // delegated V: this block also attends over the fp16 hot window
-  float *hotp = work + kWaves * G * kPS;  // [G][kPS] merged hot partial
+  float *hotp = work + kWaves * GP * kPS;  // [G][kPS] merged hot partial
   const int h0 = p.cold_len, h1 = p.length;
   const bool has_hot = h1 > h0;
   if (has_hot) {
@@ -974,12 +976,12 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
       W.load(t0, A);
       W.hot_chunk(t0, he, A, p.scores, hq0, p.length);
     }
-    W.to_slot(work + wave * G * kPS, true);
+    W.to_slot(work + wave * GP * kPS, true);
     __syncthreads();
     if (threadIdx.x < G * (D / 4)) {
       const int h = threadIdx.x / (D / 4), j4 = threadIdx.x % (D / 4);
       float4 hdr, val;
-      merge_slots<kWaves>(work, G, h, j4, hdr, val);
+      merge_slots<kWaves, GP>(work, h, j4, hdr, val);
       if (j4 == 0) *reinterpret_cast<float4 *>(hotp + h * kPS) = hdr;
       *reinterpret_cast<float4 *>(hotp + h * kPS + kPV + 4 * j4) = val;
     }
