@@ -33,9 +33,9 @@ _MODES = {"fp16": SIDE_FP16, "packed": SIDE_PACKED, "delegated": SIDE_DELEGATED}
 
 
 class TQError(RuntimeError):
-    def __init__(self, status: int, what: str):
+    def __init__(self, status: int, what: str, detail: str = None):
         self.status = status
-        super().__init__(f"{what}: {status_string(status)} ({status})")
+        super().__init__(f"{what}: {detail if detail is not None else status_string(status)} ({status})")
 
 
 class tq_side(ctypes.Structure):
@@ -71,7 +71,7 @@ def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
-            raise TQError(TQ_ERR_HIP, f"libtq.so is not built at {LIB_PATH}")
+            raise TQError(TQ_ERR_HIP, f"libtq.so is not built at {LIB_PATH}", "libtq not built")
         L = ctypes.CDLL(LIB_PATH)
         P = ctypes.c_void_p
         I = ctypes.c_int

@@ -27,6 +27,16 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, n), n
 
 
+def test_missing_library_raises_tq_error(monkeypatch):
+    # the product path fails loudly (a TQError naming the missing library)
+    # when libtq.so is absent, and never falls back to anything else
+    monkeypatch.setattr(tq, "_lib", None)
+    monkeypatch.setattr(tq, "LIB_PATH", os.path.join(ROOT, "no_such_dir", "libtq.so"))
+    with pytest.raises(tq.TQError, match="not built"):
+        tq.lib()
+    assert tq.status_string(-1) == "libtq not built"
+
+
 def test_status_strings():
     for s in range(0, -8, -1):
         assert tq.status_string(s) not in ("", "unknown status")
