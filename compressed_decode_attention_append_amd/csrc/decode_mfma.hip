@@ -75,26 +75,30 @@ constexpr float kVscaleMax = 1099511627776.0f;  // 2^40: start and ceiling of th
 // pattern reads without bank conflicts) and 32 replicas of a second table at
 // +128 + 4 r.  A byte address is then (e << 8) | 4 r, which one v_perm_b32
 // builds from a byte-aligned pair index.
-//   V hi (all K widths)   entries 0..255, first half
-//   KB = 4                K lo in the second half of entries 0..255 (K hi is
-//                         the V table: one 4-bit codebook)
-//   KB = 3                K hi in the second half of entries 0..63, K lo in
-//                         the second half of entries 64..127
+//   KB = 0, 4   V hi in the first half of entries 0..255; for KB = 4 K lo in
+//               the second half (K hi is the V table: one 4-bit codebook)
+//   KB = 3      K hi / K lo in the first / second half of entries 0..255,
+//               indexed by a byte whose low 6 bits hold a pair of 3-bit codes
+//               (the top 2 bits are ignored, so every pair is read straight
+//               from a byte of the code stream shifted by 0, 6, 12, ...);
+//               V hi in the first half of entries 256..511
 // After the main loop the table area is reused for the merges.
-constexpr int kTableWords = 256 * 64;
+constexpr int kTableWords = 256 * 64;  // one 256-entry region (64 KB)
+template <int KB>
+constexpr int table_words() { return KB == 3 ? 2 * kTableWords : kTableWords; }
+template <int KB>
+constexpr uint32_t v_table_byte() { return KB == 3 ? 4u * kTableWords : 0u; }
 // A partial result (merge slot, workspace partial) of one query head: max,
 // sum, two pad words, then the D accumulator values, so the values start
 // 16-byte aligned.
 constexpr int kPS = D + 4;
 constexpr int kPV = 4;
-constexpr int kKhiOff3 = 128;             // byte offsets added to (e << 8) | 4 r
-constexpr int kKloOff3 = 64 * 256 + 128;
-constexpr int kKloOff4 = 128;
+constexpr int kKloOff = 128;  // byte offset of the K lo table from the K hi / V one
 
-template <int GP>
+template <int KB, int GP>
 struct Lay {
-  static constexpr int qstride = D + 4;   // padded row: fewer bank conflicts
-  static constexpr int qwork = kTableWords;  // [GP][D + 4] rotated query
+  static constexpr int qstride = D + 4;              // padded row: fewer bank conflicts
+  static constexpr int qwork = table_words<KB>();    // [GP][D + 4] rotated query
   static constexpr int red = qwork + GP * qstride;     // flag
   static constexpr int total = red + 16;
   static_assert((kMaxWaves + 1) * GP * kPS <= kTableWords, "merges must fit in the table area");
@@ -170,11 +174,11 @@ __device__ __forceinline__ uint32_t baddr(uint32_t w, uint32_t rep4) {
   return __builtin_amdgcn_perm(w, rep4, 0x0c0c0000u | ((4u + K) << 8));
 }
 
-// Byte address of table entry (v >> SH) & 63 (a 6-bit pair of 3-bit codes).
-template <int SH>
-__device__ __forceinline__ uint32_t baddr6(uint32_t v, uint32_t rep4) {
-  const uint32_t x = (SH >= 8) ? (v >> (SH - 8)) : (v << (8 - SH));
-  return (x & (63u << 8)) | rep4;
+// The same for a table in the second 64 KB: rep4v = 4 r + 65536, and byte 2
+// of the address is taken from it.
+template <int K>
+__device__ __forceinline__ uint32_t baddr_hi(uint32_t w, uint32_t rep4v) {
+  return __builtin_amdgcn_perm(w, rep4v, 0x0c020000u | ((4u + K) << 8));
 }
 
 __device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t a, uint32_t b) { return (a & mask) | (b & ~mask); }
@@ -273,7 +277,8 @@ struct Wave {
   static constexpr int kRowBytes = KB == 0 ? 2 * D : (KB == 4 ? 64 : 48);
   // per-lane constants
   int col, grp, cpos;   // cpos: chunk position of the lane's first compact slot
-  uint32_t rep4;
+  uint32_t rep4;        // 4 r: the lane's replica
+  uint32_t rep4v;       // 4 r + the V table's byte offset
   uint32_t koff, knoff, voff;   // lane byte offsets inside a chunk
   const uint32_t *lds;
   Frag bq[4];
@@ -354,30 +359,38 @@ struct Wave {
           acc = mma(a, bq[q].lo, acc);
         }
       } else if (KB == 3) {
-        uint32_t ad[16];  // byte addresses of the 16 code pairs of the lane's 32 coordinates
+        // byte addresses of the 16 code pairs of the lane's 32 coordinates:
+        // pair j sits at bit 6 j of the 96-bit stream w2:w1:w0, which is
+        // byte 0 or 3 of one of the windows below (stream shifted right by
+        // 0, 6, 12, 18, 48, 54, 60, 66 bits)
+        uint32_t ad[16];
         const uint32_t w0 = c.k[m][0], w1 = c.k[m][1], w2 = c.k[m][2];
-        ad[0] = baddr6<0>(w0, rep4);
-        ad[1] = baddr6<6>(w0, rep4);
-        ad[2] = baddr6<12>(w0, rep4);
-        ad[3] = baddr6<18>(w0, rep4);
-        ad[4] = baddr6<24>(w0, rep4);
-        ad[5] = baddr6<0>(__builtin_amdgcn_alignbit(w1, w0, 30), rep4);
-        ad[6] = baddr6<4>(w1, rep4);
-        ad[7] = baddr6<10>(w1, rep4);
-        ad[8] = baddr6<16>(w1, rep4);
-        ad[9] = baddr6<22>(w1, rep4);
-        ad[10] = baddr6<0>(__builtin_amdgcn_alignbit(w2, w1, 28), rep4);
-        ad[11] = baddr6<2>(w2, rep4);
-        ad[12] = baddr6<8>(w2, rep4);
-        ad[13] = baddr6<14>(w2, rep4);
-        ad[14] = baddr6<20>(w2, rep4);
-        ad[15] = baddr6<26>(w2, rep4);
+        const uint32_t x6 = __builtin_amdgcn_alignbit(w1, w0, 6), x12 = __builtin_amdgcn_alignbit(w1, w0, 12);
+        const uint32_t x18 = __builtin_amdgcn_alignbit(w1, w0, 18), x48 = __builtin_amdgcn_alignbit(w2, w1, 16);
+        const uint32_t x54 = __builtin_amdgcn_alignbit(w2, w1, 22), x60 = __builtin_amdgcn_alignbit(w2, w1, 28);
+        const uint32_t x66 = w2 >> 2;
+        ad[0] = baddr<0>(w0, rep4);
+        ad[1] = baddr<0>(x6, rep4);
+        ad[2] = baddr<0>(x12, rep4);
+        ad[3] = baddr<0>(x18, rep4);
+        ad[4] = baddr<3>(w0, rep4);
+        ad[5] = baddr<3>(x6, rep4);
+        ad[6] = baddr<3>(x12, rep4);
+        ad[7] = baddr<3>(x18, rep4);
+        ad[8] = baddr<0>(x48, rep4);
+        ad[9] = baddr<0>(x54, rep4);
+        ad[10] = baddr<0>(x60, rep4);
+        ad[11] = baddr<0>(x66, rep4);
+        ad[12] = baddr<3>(x48, rep4);
+        ad[13] = baddr<3>(x54, rep4);
+        ad[14] = baddr<3>(x60, rep4);
+        ad[15] = baddr<3>(x66, rep4);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const half8_t ah = as_half8(lds_at<kKhiOff3>(lds, ad[4 * q]), lds_at<kKhiOff3>(lds, ad[4 * q + 1]),
-                                      lds_at<kKhiOff3>(lds, ad[4 * q + 2]), lds_at<kKhiOff3>(lds, ad[4 * q + 3]));
-          const half8_t al = as_half8(lds_at_sep<kKloOff3>(lds, ad[4 * q]), lds_at_sep<kKloOff3>(lds, ad[4 * q + 1]),
-                                      lds_at_sep<kKloOff3>(lds, ad[4 * q + 2]), lds_at_sep<kKloOff3>(lds, ad[4 * q + 3]));
+          const half8_t ah = as_half8(lds_at<0>(lds, ad[4 * q]), lds_at<0>(lds, ad[4 * q + 1]),
+                                      lds_at<0>(lds, ad[4 * q + 2]), lds_at<0>(lds, ad[4 * q + 3]));
+          const half8_t al = as_half8(lds_at_sep<kKloOff>(lds, ad[4 * q]), lds_at_sep<kKloOff>(lds, ad[4 * q + 1]),
+                                      lds_at_sep<kKloOff>(lds, ad[4 * q + 2]), lds_at_sep<kKloOff>(lds, ad[4 * q + 3]));
           acc = mma(ah, bq[q].hi, acc);
           acc = mma(al, bq[q].hi, acc);
           acc = mma(ah, bq[q].lo, acc);
@@ -389,8 +402,8 @@ struct Wave {
           const uint32_t a0 = baddr<0>(w, rep4), a1 = baddr<1>(w, rep4);
           const uint32_t a2 = baddr<2>(w, rep4), a3 = baddr<3>(w, rep4);
           const half8_t ah = as_half8(lds_at<0>(lds, a0), lds_at<0>(lds, a1), lds_at<0>(lds, a2), lds_at<0>(lds, a3));
-          const half8_t al = as_half8(lds_at_sep<kKloOff4>(lds, a0), lds_at_sep<kKloOff4>(lds, a1),
-                                      lds_at_sep<kKloOff4>(lds, a2), lds_at_sep<kKloOff4>(lds, a3));
+          const half8_t al = as_half8(lds_at_sep<kKloOff>(lds, a0), lds_at_sep<kKloOff>(lds, a1),
+                                      lds_at_sep<kKloOff>(lds, a2), lds_at_sep<kKloOff>(lds, a3));
           acc = mma(ah, bq[q].hi, acc);
           acc = mma(al, bq[q].hi, acc);
           acc = mma(ah, bq[q].lo, acc);
@@ -557,11 +570,20 @@ struct Wave {
       for (int s2 = 0; s2 < 4; ++s2) {
         const uint32_t w = src[s2];
         uint32_t ad;
-        switch (q >> 1) {
-          case 0: ad = baddr<0>(w, rep4); break;
-          case 1: ad = baddr<1>(w, rep4); break;
-          case 2: ad = baddr<2>(w, rep4); break;
-          default: ad = baddr<3>(w, rep4); break;
+        if (KB == 3) {
+          switch (q >> 1) {
+            case 0: ad = baddr_hi<0>(w, rep4v); break;
+            case 1: ad = baddr_hi<1>(w, rep4v); break;
+            case 2: ad = baddr_hi<2>(w, rep4v); break;
+            default: ad = baddr_hi<3>(w, rep4v); break;
+          }
+        } else {
+          switch (q >> 1) {
+            case 0: ad = baddr<0>(w, rep4); break;
+            case 1: ad = baddr<1>(w, rep4); break;
+            case 2: ad = baddr<2>(w, rep4); break;
+            default: ad = baddr<3>(w, rep4); break;
+          }
         }
         a4[s2] = lds_at<0>(lds, ad);
       }
@@ -710,7 +732,7 @@ template <int KB, int GP>
 __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(const DecodeParams p) {
   constexpr int kWaves = waves_of<KB>();
   constexpr int kThreads = 64 * kWaves;
-  using L = Lay<GP>;
+  using L = Lay<KB, GP>;
   using WaveT = Wave<KB, GP>;
   constexpr int NV = WaveT::NV;
   // Static LDS: its base address is a compile-time constant, so table reads
@@ -750,6 +772,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
     W.cpos = 16 * (i0 >> 2) + 4 * W.grp + (i0 & 3);
   }
   W.rep4 = (lane & 31) * 4u;
+  W.rep4v = W.rep4 + v_table_byte<KB>();
   W.lds = lds;
   W.G = G;
   const long rowbase = static_cast<long>(unit) * p.capacity;
@@ -789,27 +812,24 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
     vc = (lane == i) ? p.v_cent[i] : vc;
   }
   // Tables, written four replicas (16 bytes) at a time: the value table
-  // (for KB = 4 also the K lo table) and, for KB = 3, the K hi and lo
-  // tables.  Built while the query and the first chunk are in flight.
+  // (for KB = 4 also the K lo table; for KB = 3 also the K hi and lo
+  // tables).  Built while the query and the first chunk are in flight.
   // Every loop below runs whole waves (the counts are multiples of 64), as
   // the shuffles need.
+  constexpr int kVWord = v_table_byte<KB>() / 4;
   for (int i = threadIdx.x; i < 256 * (kRep / 4); i += kThreads) {
     const int e = i >> 3, r4 = 4 * (i & 7);
     const uint32_t w = pack_half2(__shfl(vc, e & 15), __shfl(vc, e >> 4));
-    *reinterpret_cast<u32x4_t *>(lds + e * 64 + r4) = u32x4_t{w, w, w, w};
-    if (KB == 4) {
+    *reinterpret_cast<u32x4_t *>(lds + kVWord + e * 64 + r4) = u32x4_t{w, w, w, w};
+    if (KB) {
       uint32_t h, l;
-      split_pair(__shfl(kc, e & 15), __shfl(kc, e >> 4), h, l);
+      if (KB == 4) {
+        split_pair(__shfl(kc, e & 15), __shfl(kc, e >> 4), h, l);
+      } else {
+        split_pair(__shfl(kc, e & 7), __shfl(kc, (e >> 3) & 7), h, l);
+        *reinterpret_cast<u32x4_t *>(lds + e * 64 + r4) = u32x4_t{h, h, h, h};
+      }
       *reinterpret_cast<u32x4_t *>(lds + e * 64 + 32 + r4) = u32x4_t{l, l, l, l};
-    }
-  }
-  if (KB == 3) {
-    for (int i = threadIdx.x; i < 64 * (kRep / 4); i += kThreads) {
-      const int e = i >> 3, r4 = 4 * (i & 7);
-      uint32_t h, l;
-      split_pair(__shfl(kc, e & 7), __shfl(kc, e >> 3), h, l);
-      *reinterpret_cast<u32x4_t *>(lds + e * 64 + 32 + r4) = u32x4_t{h, h, h, h};
-      *reinterpret_cast<u32x4_t *>(lds + (64 + e) * 64 + 32 + r4) = u32x4_t{l, l, l, l};
     }
   }
   // first use of the query after the tables, so the wait for it comes here
@@ -1082,14 +1102,6 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
 }
 
 }  // namespace
-
-size_t decode_mfma_lds_bytes(int k_bits, bool share_lut, int G) {
-  (void)k_bits;
-  (void)share_lut;
-  if (G <= 4) return 4 * size_t(Lay<4>::total);
-  if (G <= 8) return 4 * size_t(Lay<8>::total);
-  return ~size_t(0);
-}
 
 bool decode_mfma_supported(const DecodeParams &p) {
   const int G = p.q_heads / p.kv_heads;

@@ -113,7 +113,6 @@ hipError_t launch_dequantize(const DequantParams &p, hipStream_t stream);
 hipError_t launch_decode_ref(const DecodeParams &p, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeParams &p, hipStream_t stream);
 bool decode_mfma_supported(const DecodeParams &p);
-size_t decode_mfma_lds_bytes(int k_bits, bool share_lut, int G);
 int decode_mfma_max_splits();
 
 }  // namespace tq
