@@ -12,13 +12,14 @@
 // flight, then each wave walks its share of the split in chunks of 32
 // positions, loading chunk i + 1 while it computes chunk i:
 //
-//   score   v_mfma_f32_16x16x32_f16 with M = 16 positions, N = 16 (the G
-//           query heads, rest padding), K = 32 coordinates.  A holds the
-//           centroids of the position's codes, decoded two codes at a time
-//           from pair tables in LDS (32 replicas of every 32-bit entry, one
-//           per bank, so any index pattern reads without bank conflicts); B
-//           holds R q, rotated once per block with 1/sqrt(d) and log2(e)
-//           folded in.  Times the position's norm this is the base-2 logit.
+//   score   v_mfma_f32_16x16x32_f16 with M = 16 positions, N = 16 (hi and
+//           lo halves of the G query heads, rest padding), K = 32
+//           coordinates.  A holds the centroids of the position's codes,
+//           decoded two codes at a time from pair tables in LDS (32 replicas
+//           of every 32-bit entry, one per bank, so any index pattern reads
+//           without bank conflicts); B holds R q, rotated once per block with
+//           1/sqrt(d) and log2(e) folded in.  Times the position's norm this
+//           is the base-2 logit.
 //   softmax online per query head; the accumulators are only rescaled when
 //           the running maximum grows by more than 2^8.
 //   value   the same MFMA with M = 16 coordinates, N = 16 heads, K = 32
@@ -31,8 +32,9 @@
 //           softmax is much smaller than the rows it averages, so plain fp16
 //           leaves output errors near 1e-3.  Each fp16 operand that is not
 //           exact is therefore a hi + lo pair (lo = the fp16 rounding of the
-//           remainder): the score takes A_hi B_hi + A_lo B_hi + A_hi B_lo,
-//           the value sum takes A_hi (P_hi + P_lo); fp16 K rows are exact.
+//           remainder): the score takes (A_hi + A_lo)(B_hi + B_lo) in two
+//           MFMAs, B_hi and B_lo side by side in N; the value sum takes
+//           A_hi (P_hi + P_lo); fp16 K rows are exact (one MFMA).
 //
 // The 8 waves merge in LDS (over the dead tables) and write one partial
 // (max, sum, accumulator) per query head with L2-coherent stores; the last
@@ -100,6 +102,7 @@ struct Lay {
   static constexpr int qstride = D + 4;              // padded row: fewer bank conflicts
   static constexpr int qwork = table_words<KB>();    // [GP][D + 4] rotated query
   static constexpr int red = qwork + GP * qstride;     // flag
+  static constexpr int prog = red + 4;                 // [kMaxWaves] chunks done per wave
   static constexpr int total = red + 16;
   static_assert((kMaxWaves + 1) * GP * kPS <= kTableWords, "merges must fit in the table area");
 };
@@ -123,10 +126,6 @@ __device__ __forceinline__ void split_pair(float x0, float x1, uint32_t &hi, uin
   hi = pack_half2(h0, h1);
   lo = pack_half2(x0 - h0, x1 - h1);
 }
-
-struct Frag {
-  half8_t hi, lo;
-};
 
 // LDS word at byte address `addr` plus a compile-time byte offset.
 template <int OFF>
@@ -281,7 +280,7 @@ struct Wave {
   uint32_t rep4v;       // 4 r + the V table's byte offset
   uint32_t koff, knoff, voff;   // lane byte offsets inside a chunk
   const uint32_t *lds;
-  Frag bq[4];
+  half8_t bq[4];         // R q: column h < GP hi, column GP + h lo of head h
   // per-unit bases
   const char *kbase;   // K codes or fp16 rows of this unit
   const char *knbase;  // K norms
@@ -355,8 +354,7 @@ struct Wave {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const half8_t a = as_half8(c.k[m][4 * q], c.k[m][4 * q + 1], c.k[m][4 * q + 2], c.k[m][4 * q + 3]);
-          acc = mma(a, bq[q].hi, acc);
-          acc = mma(a, bq[q].lo, acc);
+          acc = mma(a, bq[q], acc);
         }
       } else if (KB == 3) {
         // byte addresses of the 16 code pairs of the lane's 32 coordinates:
@@ -391,9 +389,8 @@ struct Wave {
                                       lds_at<0>(lds, ad[4 * q + 2]), lds_at<0>(lds, ad[4 * q + 3]));
           const half8_t al = as_half8(lds_at_sep<kKloOff>(lds, ad[4 * q]), lds_at_sep<kKloOff>(lds, ad[4 * q + 1]),
                                       lds_at_sep<kKloOff>(lds, ad[4 * q + 2]), lds_at_sep<kKloOff>(lds, ad[4 * q + 3]));
-          acc = mma(ah, bq[q].hi, acc);
-          acc = mma(al, bq[q].hi, acc);
-          acc = mma(ah, bq[q].lo, acc);
+          acc = mma(ah, bq[q], acc);
+          acc = mma(al, bq[q], acc);
         }
       } else {
 #pragma unroll
@@ -404,13 +401,13 @@ struct Wave {
           const half8_t ah = as_half8(lds_at<0>(lds, a0), lds_at<0>(lds, a1), lds_at<0>(lds, a2), lds_at<0>(lds, a3));
           const half8_t al = as_half8(lds_at_sep<kKloOff>(lds, a0), lds_at_sep<kKloOff>(lds, a1),
                                       lds_at_sep<kKloOff>(lds, a2), lds_at_sep<kKloOff>(lds, a3));
-          acc = mma(ah, bq[q].hi, acc);
-          acc = mma(al, bq[q].hi, acc);
-          acc = mma(ah, bq[q].lo, acc);
+          acc = mma(ah, bq[q], acc);
+          acc = mma(al, bq[q], acc);
         }
       }
+      // column h + GP holds the lo half of head h's query: fold it in
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s[4 * m + r] = acc[r];
+      for (int r = 0; r < 4; ++r) s[4 * m + r] = acc[r] + dpp_f<kRowShl + GP, 0xf>(0.0f, acc[r]);
     }
   }
 
@@ -728,6 +725,45 @@ __device__ __forceinline__ void store4_coherent(__amdgpu_buffer_rsrc_t r, uint32
   __builtin_amdgcn_raw_buffer_store_b128(u, r, off, 0, kCoherentLoad);
 }
 
+// Issue priority 0..3 from a wave-uniform value (clamped).
+__device__ __forceinline__ void set_priority(int k) {
+  if (k >= 3) {
+    __builtin_amdgcn_s_setprio(3);
+  } else if (k == 2) {
+    __builtin_amdgcn_s_setprio(2);
+  } else if (k == 1) {
+    __builtin_amdgcn_s_setprio(1);
+  } else {
+    __builtin_amdgcn_s_setprio(0);
+  }
+}
+
+// Wave balancing.  The instruction arbiter of a SIMD favours the oldest of
+// its waves, so with equal shares of chunks the oldest wave finishes far
+// ahead and the youngest runs alone at the end, without other waves to hide
+// its latencies.  Each wave therefore publishes how many chunks it has done
+// and runs at a priority equal to how far it lags the leading wave of the
+// block.  Only the issue order changes: which wave takes which chunk, and so
+// every sum, stays the same.
+template <int NW>
+struct Balance {
+  volatile int *prog;  // [NW] in LDS
+  int done = 0;
+  // this wave finished a chunk: publish its count, then set its priority
+  // from the counts of all waves
+  __device__ __forceinline__ void step(int wave, int lane) {
+    ++done;
+    if (lane == 0) prog[wave] = done;
+    int m = 0;
+#pragma unroll
+    for (int w = 0; w < NW; w += 4) {
+      const u32x4_t c = *reinterpret_cast<const volatile u32x4_t *>(prog + w);
+      m = max(m, static_cast<int>(max(max(c[0], c[1]), max(c[2], c[3]))));
+    }
+    set_priority(__builtin_amdgcn_readfirstlane(m) - done);
+  }
+};
+
 template <int KB, int GP>
 __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(const DecodeParams p) {
   constexpr int kWaves = waves_of<KB>();
@@ -745,6 +781,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   const int G = p.q_heads / p.kv_heads;
   float *qw = reinterpret_cast<float *>(lds + L::qwork);
   int *flag = reinterpret_cast<int *>(lds + L::red);
+  int *prog = reinterpret_cast<int *>(lds + L::prog);
   float *work = reinterpret_cast<float *>(lds);  // merge area after the main loop
 
   const int nsplit = p.n_cold_splits;
@@ -877,23 +914,29 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
     qhl[wave * L::qstride + j] = h;
     qhl[wave * L::qstride + 64 + j] = l;
   }
-  __syncthreads();  // tables and rotated query complete
+  if (lane == 0) prog[wave] = 0;
+  __syncthreads();  // tables, rotated query and progress counters complete
   {
-    const uint32_t *row = qhl + (W.col < G ? W.col : 0) * L::qstride + 16 * W.grp;
+    // B operand of the score: column h < G the hi half of head h's query,
+    // column GP + h its lo half, zero elsewhere; the MFMA then yields both
+    // products, which the score adds (column h + GP into column h)
+    const int hsel = W.col < GP ? W.col : W.col - GP;
+    const bool live = W.col < 2 * GP && hsel < G;
+    const uint32_t *row = qhl + (live ? hsel : 0) * L::qstride + (W.col < GP ? 0 : 64) + 16 * W.grp;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       // words 16 grp + 4 c .. + 3: coordinates 32 grp + 8 c .. + 7
       u32x4_t h = *reinterpret_cast<const u32x4_t *>(row + 4 * c);
-      u32x4_t l = *reinterpret_cast<const u32x4_t *>(row + 64 + 4 * c);
-      if (W.col >= G) h = l = u32x4_t{0u, 0u, 0u, 0u};
-      W.bq[c].hi = __builtin_bit_cast(half8_t, h);
-      W.bq[c].lo = __builtin_bit_cast(half8_t, l);
+      if (!live) h = u32x4_t{0u, 0u, 0u, 0u};
+      W.bq[c] = __builtin_bit_cast(half8_t, h);
     }
   }
 
   // ---- main loop: the wave processes its chunk while its next one loads
   // into the other of two register buffers (ping-pong, so nothing is
   // copied).  Only the split's last chunk can be partial.
+  Balance<kWaves> bal;
+  bal.prog = prog;
   if (KB == 0) {
     // fp16 K rows (32 dwords a buffer): the masked variant stays inside the
     // loop, which keeps this shape within its registers
@@ -908,6 +951,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
       } else {
         W.template cold_chunk<true>(s0 + c * kChunk, s1, A, p.scores, hq0, p.length);
       }
+      bal.step(wave, lane);
       c = cn;
       if (c >= n_chunks) break;
       cn = c + kWaves;
@@ -918,6 +962,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
       } else {
         W.template cold_chunk<true>(s0 + c * kChunk, s1, B, p.scores, hq0, p.length);
       }
+      bal.step(wave, lane);
       c = cn;
     }
   } else {
@@ -933,6 +978,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
       W.load(s0 + min(cn, last) * kChunk, B);
       asm volatile("" ::: "memory");
       W.template cold_chunk<false>(s0 + c * kChunk, s1, A, p.scores, hq0, p.length);
+      bal.step(wave, lane);
       c = cn;
       if (c >= n_full) {
         in_b = true;
@@ -942,6 +988,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
       W.load(s0 + min(cn, last) * kChunk, A);
       asm volatile("" ::: "memory");
       W.template cold_chunk<false>(s0 + c * kChunk, s1, B, p.scores, hq0, p.length);
+      bal.step(wave, lane);
       c = cn;
     }
     if (c < n_chunks) {
@@ -954,6 +1001,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   }
 
   // ---- merge the waves of this block (tables are dead from here on) -----
+  __builtin_amdgcn_s_setprio(0);
   __syncthreads();
   W.to_slot(work + wave * GP * kPS, false);
   __syncthreads();
