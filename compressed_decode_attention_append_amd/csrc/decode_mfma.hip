@@ -745,22 +745,26 @@ __device__ __forceinline__ void set_priority(int k) {
 // and runs at a priority equal to how far it lags the leading wave of the
 // block.  Only the issue order changes: which wave takes which chunk, and so
 // every sum, stays the same.
-template <int NW>
+// The counters live at LDS byte address PROG (the kernel's only LDS array
+// starts at address 0); volatile LDS-space accesses, so every step reads
+// the other waves' current counts with ds_read.
+template <int NW, uint32_t PROG>
 struct Balance {
-  volatile int *prog;  // [NW] in LDS
+  typedef __attribute__((address_space(3))) volatile int lds_int;
+  typedef __attribute__((address_space(3))) const volatile u32x4_t lds_u32x4;
   int done = 0;
   // this wave finished a chunk: publish its count, then set its priority
   // from the counts of all waves
   __device__ __forceinline__ void step(int wave, int lane) {
     ++done;
-    if (lane == 0) prog[wave] = done;
-    int m = 0;
+    if (lane == 0) *reinterpret_cast<lds_int *>(PROG + 4u * wave) = done;
+    uint32_t m = 0;
 #pragma unroll
     for (int w = 0; w < NW; w += 4) {
-      const u32x4_t c = *reinterpret_cast<const volatile u32x4_t *>(prog + w);
-      m = max(m, static_cast<int>(max(max(c[0], c[1]), max(c[2], c[3]))));
+      const u32x4_t c = *reinterpret_cast<lds_u32x4 *>(PROG + 4u * w);
+      m = max(m, max(max(c[0], c[1]), max(c[2], c[3])));
     }
-    set_priority(__builtin_amdgcn_readfirstlane(m) - done);
+    set_priority(static_cast<int>(__builtin_amdgcn_readfirstlane(m)) - done);
   }
 };
 
@@ -935,8 +939,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   // ---- main loop: the wave processes its chunk while its next one loads
   // into the other of two register buffers (ping-pong, so nothing is
   // copied).  Only the split's last chunk can be partial.
-  Balance<kWaves> bal;
-  bal.prog = prog;
+  Balance<kWaves, 4u * L::prog> bal;
   if (KB == 0) {
     // fp16 K rows (32 dwords a buffer): the masked variant stays inside the
     // loop, which keeps this shape within its registers
