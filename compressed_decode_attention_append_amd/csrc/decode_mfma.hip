@@ -103,7 +103,14 @@ struct Lay {
   static constexpr int qwork = table_words<KB>();    // [GP][D + 4] rotated query
   static constexpr int red = qwork + GP * qstride;     // flag
   static constexpr int prog = red + 4;                 // [kMaxWaves] chunks done per wave
-  static constexpr int total = red + 16;
+  static constexpr int tail = red + 16;
+  // Merge slots of the main loop's waves: an area of their own when it fits
+  // (a wave then writes its slot as soon as its own loop ends), else over
+  // the tables once every wave is done with them.
+  static constexpr int kLdsWords = 160 * 1024 / 4;
+  static constexpr bool own_slots = tail + kMaxWaves * GP * kPS <= kLdsWords;
+  static constexpr int slots = own_slots ? tail : 0;
+  static constexpr int total = own_slots ? tail + kMaxWaves * GP * kPS : tail;
   static_assert((kMaxWaves + 1) * GP * kPS <= kTableWords, "merges must fit in the table area");
 };
 
@@ -787,6 +794,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   int *flag = reinterpret_cast<int *>(lds + L::red);
   int *prog = reinterpret_cast<int *>(lds + L::prog);
   float *work = reinterpret_cast<float *>(lds);  // merge area after the main loop
+  float *slots = reinterpret_cast<float *>(lds + L::slots);
 
   const int nsplit = p.n_cold_splits;
   const int unit = blockIdx.x / nsplit;
@@ -879,6 +887,16 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   float qb = h2f(static_cast<uint16_t>(qb_raw));
   // rotate q in registers: H diag(s) q (unnormalised), butterflies at
   // stride 64 inside the lane and at strides 32 .. 1 across lanes
+  // sign word of coordinates 4 j4 .. 4 j4 + 3 for the output stage (thread
+  // j4 = threadIdx % 32 of each head), taken now, while the kernel
+  // arguments are at hand, and kept in a register
+  uint32_t out_sign;
+  {
+    const int wsel = (threadIdx.x & 31) >> 3;
+    out_sign = wsel == 0 ? p.sign[0] : p.sign[1];
+    out_sign = wsel == 2 ? p.sign[2] : out_sign;
+    out_sign = wsel == 3 ? p.sign[3] : out_sign;
+  }
   if (k_packed && wave < G) {
     // signs of coordinates lane and lane + 64 (uniform words, per-lane select)
     const uint32_t sa = lane < 32 ? p.sign[0] : p.sign[1];
@@ -1005,8 +1023,8 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
 
   // ---- merge the waves of this block (tables are dead from here on) -----
   __builtin_amdgcn_s_setprio(0);
-  __syncthreads();
-  W.to_slot(work + wave * GP * kPS, false);
+  if (!L::own_slots) __syncthreads();  // the slots overlay the tables
+  W.to_slot(slots + wave * GP * kPS, false);
   __syncthreads();
   float *part = reinterpret_cast<float *>(reinterpret_cast<char *>(p.ws) + p.ws_part_off);
   float *mypart = part + (static_cast<long>(unit) * nsplit + split) * G * kPS;
@@ -1014,7 +1032,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
     // thread (h, j4): head h, values 4 j4 .. 4 j4 + 3, L2-coherent stores
     const int h = threadIdx.x / (D / 4), j4 = threadIdx.x % (D / 4);
     float4 hdr, val;
-    merge_slots<kWaves, GP>(work, h, j4, hdr, val);
+    merge_slots<kWaves, GP>(slots, h, j4, hdr, val);
     const auto rs = rsrc(mypart, G * kPS * 4);
     if (j4 == 0) store4_coherent(rs, h * kPS * 4, hdr);
     store4_coherent(rs, (h * kPS + kPV + 4 * j4) * 4, val);
@@ -1066,6 +1084,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   const float *up = part + static_cast<long>(unit) * nsplit * G * kPS;
   const int hh = threadIdx.x / (D / 4);
   const int jj = 4 * (threadIdx.x % (D / 4));
+  float *orow = p.out + (hq0 + hh) * D + jj;
   float r4[4] = {0.0f, 0.0f, 0.0f, 0.0f}, q4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   float Lt = 0.0f;
   float M = -INFINITY;
@@ -1134,12 +1153,9 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
     r4[e] = xor_butterfly<16>(r4[e], lane);
   }
   const float rs = 1.0f / sqrtf(static_cast<float>(D));
-  const float inv = (Lt > 0.0f) ? 1.0f / Lt : 0.0f;
+  const float inv = (Lt > 0.0f) ? __builtin_amdgcn_rcpf(Lt) : 0.0f;  // within 1 ulp
   float4 o;
-  // sign word of coordinates jj .. jj + 3 (uniform words, per-lane select)
-  const int wsel = jj >> 5;
-  const uint32_t swd = (wsel & 2) ? ((wsel & 1) ? p.sign[3] : p.sign[2]) : ((wsel & 1) ? p.sign[1] : p.sign[0]);
-  const uint32_t sbits = swd >> (jj & 31);
+  const uint32_t sbits = out_sign >> (jj & 31);
   o.x = ((sbits & 1u) ? -r4[0] : r4[0]) * rs;
   o.y = ((sbits & 2u) ? -r4[1] : r4[1]) * rs;
   o.z = ((sbits & 4u) ? -r4[2] : r4[2]) * rs;
@@ -1148,7 +1164,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   o.y = (o.y + q4[1]) * inv;
   o.z = (o.z + q4[2]) * inv;
   o.w = (o.w + q4[3]) * inv;
-  *reinterpret_cast<float4 *>(p.out + (hq0 + hh) * D + jj) = o;
+  *reinterpret_cast<float4 *>(orow) = o;
   if (threadIdx.x == 0) __hip_atomic_store(p.counters + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
