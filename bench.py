@@ -121,9 +121,16 @@ DECODE_SOURCE = os.path.join(ROOT, "compressed_decode_attention_append_amd", "cs
 
 
 def source_digest(path=DECODE_SOURCE) -> str:
+    """sha256 of the kernel's code: the source with its comments removed and
+    its whitespace collapsed, so that editing a comment does not void the
+    counters recorded for the kernel."""
     import hashlib
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    import re
+    text = open(path, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = " ".join(text.split())
+    return hashlib.sha256(text.encode()).hexdigest()
 
 
 def traffic_file(workload: str) -> str:

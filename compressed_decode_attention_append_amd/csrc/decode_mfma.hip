@@ -5,9 +5,9 @@
 // "TurboQuant KV cache", "Available modes": fp16 K with TurboQuant V and the
 // delegated hot/cold V split).
 //
-// head_dim 128, 4-bit V codes, K packed (3 or 4 bits) or fp16, up to 8 (fp16
-// K) or 4 (packed K) query heads per KV head.  Grid = (B * Hkv units) x
-// splits, about one 8-wave block per compute unit.  A block issues its first
+// head_dim 128, 4-bit V codes, K packed (3 or 4 bits) or fp16, up to 8 query
+// heads per KV head.  Grid = (B * Hkv units) x splits, about one block per
+// compute unit (12 waves for packed K, 8 for fp16 K).  A block issues its first
 // loads, builds its lookup tables and rotated query while they are in
 // flight, then each wave walks its share of the split in chunks of 32
 // positions, loading chunk i + 1 while it computes chunk i:
@@ -36,7 +36,7 @@
 //           MFMAs, B_hi and B_lo side by side in N; the value sum takes
 //           A_hi (P_hi + P_lo); fp16 K rows are exact (one MFMA).
 //
-// The 8 waves merge in LDS (over the dead tables) and write one partial
+// The waves merge in LDS (one slot each) and the block writes one partial
 // (max, sum, accumulator) per query head with L2-coherent stores; the last
 // block of a unit to arrive (atomic counter) attends over the fp16 hot window
 // of a delegated V (original domain), merges the splits with L2-coherent
