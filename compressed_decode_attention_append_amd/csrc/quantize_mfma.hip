@@ -13,8 +13,9 @@
 //       coordinate i = 8 n + t, so a lane ends up holding 8 consecutive
 //       coordinates of its rows.  With j = 32 q + 8 g + s and i = 8 n + t,
 //       popcount(i & j) = popcount(n & (4 q + g)) + popcount(t & s): each
-//       entry is a per-lane sign times a fixed 8 x 8 Hadamard pattern.  The
-//       128 registers of B are built once per wave.
+//       entry is a per-lane sign times a fixed 8 x 8 Hadamard pattern.  B is
+//       built once per block into LDS (16 KB) and read per tile, which keeps
+//       the wave at about 120 registers: four waves per SIMD.
 //   D   lane (g = l / 16, n = l % 16) holds rows 4 g + r (r = 0..3),
 //       coordinates 8 n .. 8 n + 7, as 8 N-tiles of 4 values.
 //
@@ -142,9 +143,10 @@ __device__ __forceinline__ void encode_tile(const float4_t (&acc)[8], const floa
   }
 }
 
-__global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(const QuantizeParams p, int tiles_k,
+__global__ __launch_bounds__(kThreads, 4) void quantize_mfma_kernel(const QuantizeParams p, int tiles_k,
                                                                     int tiles_total) {
   __shared__ LutEntry lut[2][kLutCells];
+  __shared__ u32x4_t bsh[16][64];  // B operands [4 t + q][lane] for the N-tiles t < 4
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
@@ -153,11 +155,11 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(const Quanti
   if (p.k_lut_scale > 0.0f) build_lut(lut[0], p.k_thr, p.k.bits, p.k_lut_scale);
   if (p.v_lut_scale > 0.0f) build_lut(lut[1], p.v_thr, p.v.bits, p.v_lut_scale);
 
-  // B = diag(s) H^T in the layout described above, built once per wave for
-  // the N-tiles t < 4.  Tile t + 4 differs from tile t only by the sign of
-  // its k slots 4..7 (popcount((t ^ 4) & s) flips with bit 2 of s), which
-  // the product takes from A instead: A with those slots negated.
-  uint32_t bm[4][4][4];
+  // B = diag(s) H^T in the layout described above, for the N-tiles t < 4,
+  // written to LDS by wave 0.  Tile t + 4 differs from tile t only by the
+  // sign of its k slots 4..7 (popcount((t ^ 4) & s) flips with bit 2 of s),
+  // which the product takes from A instead: A with those slots negated.
+  if (wave == 0) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const uint32_t par = static_cast<uint32_t>(__builtin_popcount(n & (4 * q + g)) & 1);
@@ -171,9 +173,10 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(const Quanti
       for (int t = 0; t < 4; ++t) {
         const uint32_t m = (static_cast<uint32_t>(__builtin_popcount(t & (2 * pr)) & 1) << 15) |
                            (static_cast<uint32_t>(__builtin_popcount(t & (2 * pr + 1)) & 1) << 31);
-        bm[t][q][pr] = base ^ m;
+        reinterpret_cast<uint32_t *>(&bsh[4 * t + q][lane])[pr] = base ^ m;
       }
     }
+  }
   }
   __syncthreads();  // tables complete
 
@@ -219,6 +222,7 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(const Quanti
     float4_t acc[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) acc[t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    asm volatile("" ::: "memory");  // B is read from LDS per tile, not kept in registers
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       u32x4_t af = __builtin_bit_cast(u32x4_t, a[q]);
@@ -227,7 +231,7 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(const Quanti
       const half8_t a_flip = as_half8(af);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const u32x4_t b = {bm[t][q][0], bm[t][q][1], bm[t][q][2], bm[t][q][3]};
+        const u32x4_t b = bsh[4 * t + q][lane];
         acc[t] = mma(a[q], as_half8(b), acc[t]);
         acc[t + 4] = mma(a_flip, as_half8(b), acc[t + 4]);
       }
@@ -255,7 +259,10 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_mfma_kernel(const Quanti
     // output rows: tile row tr = 4 g + r is input row r0 + tr = (bh, i).
     // n_new >= 16, so the tile crosses at most one (batch, head) boundary;
     // crossing it skips the capacity - n_new rows the append leaves alone.
-    const long bh0 = r0 / p.n_new;
+    // (32-bit division when the rows allow: a 64-bit one costs about a
+    // hundred scalar instructions per tile)
+    const long bh0 = rows <= 0x7fffffffL ? static_cast<long>(static_cast<uint32_t>(r0) / static_cast<uint32_t>(p.n_new))
+                                         : r0 / p.n_new;
     const int i0 = static_cast<int>(r0 - bh0 * p.n_new);
     const int W = sd.words;
     uint32_t *codes0 = sd.codes + (bh0 * p.capacity + p.offset + i0) * W;
@@ -305,7 +312,7 @@ hipError_t launch_quantize_mfma(const QuantizeParams &p, hipStream_t stream) {
   const long tiles_total = tiles_k + (v_on ? tiles_side : 0);
   if (tiles_total == 0) return hipSuccess;
   if (tiles_total > 0x7fffffffL) return hipErrorInvalidValue;
-  const long blocks = std::min<long>((tiles_total + kWaves - 1) / kWaves, 512);
+  const long blocks = std::min<long>((tiles_total + kWaves - 1) / kWaves, 1024);  // up to four per CU
   hipLaunchKernelGGL(quantize_mfma_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, p,
                      static_cast<int>(tiles_k), static_cast<int>(tiles_total));
   return hipGetLastError();
