@@ -94,6 +94,8 @@ def lib():
         L.tq_dequantize.restype = I
         L.tq_status_string.argtypes = [I]
         L.tq_status_string.restype = ctypes.c_char_p
+        L.tq_read_probe.argtypes = [P, ctypes.c_size_t, P, P]
+        L.tq_read_probe.restype = I
         _lib = L
     return _lib
 
@@ -168,6 +170,16 @@ def _stream_handle(stream) -> int:
     import torch
     s = stream if stream is not None else torch.cuda.current_stream()
     return int(s.cuda_stream)
+
+
+def read_probe(buf, sink, stream=None) -> None:
+    """Stream-read the device tensor `buf` (a multiple of 16 bytes, 16-byte
+    aligned) with the library's probe kernel and write the xor of its 32-bit
+    words to the 1-element int32/uint32 device tensor `sink`.  A measurement
+    aid for the attainable HBM read bandwidth, not part of the method."""
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib().tq_read_probe(_ptr(buf) if nbytes else None, nbytes, _ptr(sink), _stream_handle(stream)),
+           "tq_read_probe")
 
 
 @dataclass

@@ -321,4 +321,11 @@ int tq_dequantize(const tq_cache *cache, int side, int start, int count, float *
   return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
 
+int tq_read_probe(const void *buf, size_t bytes, unsigned *sink, void *hip_stream) {
+  if (!sink || (bytes > 0 && !buf)) return TQ_ERR_ARG;
+  if ((bytes & 15u) || (reinterpret_cast<uintptr_t>(buf) & 15u)) return TQ_ERR_ARG;
+  const hipError_t e = tq::launch_read_probe(buf, bytes, sink, static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
 }  // extern "C"

@@ -110,6 +110,7 @@ hipError_t launch_quantize_mfma(const QuantizeParams &p, hipStream_t stream);
 float quantize_lut_scale(const float *thr, int bits);
 constexpr int kQuantLutMaxScale = 512;
 hipError_t launch_dequantize(const DequantParams &p, hipStream_t stream);
+hipError_t launch_read_probe(const void *buf, size_t bytes, unsigned *sink, hipStream_t stream);
 hipError_t launch_decode_ref(const DecodeParams &p, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeParams &p, hipStream_t stream);
 bool decode_mfma_supported(const DecodeParams &p);

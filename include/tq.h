@@ -177,6 +177,16 @@ int tq_dequantize(const tq_cache *cache, int side, int start, int count,
 /* Static description of a status code. */
 const char *tq_status_string(int status);
 
+/* Measurement aid, not part of the method: stream-read `bytes` of DEVICE
+ * memory at `buf` (16-byte loads, a few in flight per thread, one block per
+ * compute unit) and write the xor of all its 32-bit words to DEVICE *sink.
+ * Timing it gives the HBM read bandwidth a plain streaming kernel attains
+ * on this GPU, against which the decode's bandwidth can be read (the
+ * published peak stays the roofline).  `bytes` must be a multiple of 16 and
+ * `buf` 16-byte aligned, else TQ_ERR_ARG; 0 bytes writes 0 to *sink. */
+int tq_read_probe(const void *buf, size_t bytes, unsigned *sink,
+                  void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

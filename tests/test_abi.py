@@ -196,3 +196,13 @@ def test_dequantize_errors():
     assert L.tq_dequantize(ctypes.byref(_desc(f, cap=10)), 1, 5, 6, f.p(), None) == tq.TQ_ERR_CAPACITY
     assert L.tq_dequantize(ctypes.byref(_desc(f)), 1, 0, 1, None, None) == tq.TQ_ERR_ARG
     assert L.tq_dequantize(ctypes.byref(_desc(f)), 1, 0, 0, None, None) == tq.TQ_OK
+
+
+def test_read_probe_argument_errors():
+    # every rejection happens before a launch, so no GPU is needed
+    L = tq.lib()
+    fake = ctypes.c_void_p(4096)  # never dereferenced: rejected first
+    assert L.tq_read_probe(fake, 16, None, None) == tq.TQ_ERR_ARG             # no sink
+    assert L.tq_read_probe(None, 16, fake, None) == tq.TQ_ERR_ARG             # no buffer
+    assert L.tq_read_probe(fake, 20, fake, None) == tq.TQ_ERR_ARG             # not a multiple of 16
+    assert L.tq_read_probe(ctypes.c_void_p(4100), 32, fake, None) == tq.TQ_ERR_ARG  # misaligned

@@ -352,3 +352,16 @@ def test_end_to_end_against_oracle_quantization():
     o_ref, _ = oracle.decode_attention(q, ks.rows(0, T), vs.rows(0, T))
     ok, worst = rows_close(out, o_ref)
     assert ok, worst
+
+
+@pytest.mark.parametrize("nbytes", [0, 16, 48, 4096 * 16 + 48, 3 * 1024 * 1024 + 16 * 37])
+def test_read_probe_xor(nbytes):
+    # the probe's sink is the xor of every 32-bit word it streamed
+    g = torch.Generator(device="cpu").manual_seed(nbytes)
+    words = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int64, generator=g).to(torch.int32)
+    buf = words.to("cuda:0")
+    sink = torch.full((1,), 12345, dtype=torch.int32, device="cuda:0")
+    tq.read_probe(buf, sink)
+    torch.cuda.synchronize()
+    want = np.bitwise_xor.reduce(words.numpy().view(np.uint32)) if nbytes else np.uint32(0)
+    assert int(sink.cpu().numpy().view(np.uint32)[0]) == int(want)
