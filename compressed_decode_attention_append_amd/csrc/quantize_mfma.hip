@@ -45,7 +45,9 @@ constexpr int D = 128;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTileRows = 16;
-constexpr int kLutCells = 2 * kQuantLutMaxScale + 1;
+// cells k = 0 .. 2 S + 2 cover u in [k - S - 1, k - S): one guard cell on
+// each side of [-S, S]
+constexpr int kLutCells = 2 * kQuantLutMaxScale + 3;
 
 struct LutEntry {
   uint32_t base;  // scaled thresholds below the cell
@@ -71,13 +73,16 @@ __device__ __forceinline__ float sum_rows(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Build the code table of one side: cells k = 0 .. 2 S cover u in
-// [k - S, k - S + 1).
+// Build the code table of one side: cells k = 0 .. 2 S + 2 cover u in
+// [k - S - 1, k - S).  The guard cells below -S and at or above S hold code 0
+// and the top code, so a coordinate a rounding step outside [-1, 1] needs no
+// clamp: |y| <= 1 for every row (the rotation is orthonormal), and a non-finite
+// u (only from a non-finite row, whose scale is 0) converts to cell 0 of u.
 __device__ void build_lut(LutEntry *lut, const float *thr, int bits, float scale) {
   const int S = static_cast<int>(scale);
   const int n_thr = (1 << bits) - 1;
-  for (int k = threadIdx.x; k <= 2 * S; k += kThreads) {
-    const float lo = static_cast<float>(k - S);
+  for (int k = threadIdx.x; k <= 2 * S + 2; k += kThreads) {
+    const float lo = static_cast<float>(k - S - 1);
     int cnt = 0;  // thresholds with thr * S < lo (ascending thresholds)
     for (int step = 128; step >= 1; step >>= 1) {
       if (cnt + step <= n_thr && thr[cnt + step - 1] * scale < lo) cnt += step;
@@ -123,19 +128,17 @@ __device__ __forceinline__ int floor_to_int(float x) {
   return r;
 }
 
-// lut points at the cell of u = 0 (cell index S of the side's table).
+// lut0 points at the cell of u = 0 (cell index S + 1 of the side's table).
 template <int BITS>
 __device__ __forceinline__ void encode_tile(const float4_t (&acc)[8], const float (&inv_s)[4],
-                                            const LutEntry *lut0, float S, int lane, uint32_t (&word)[4]) {
+                                            const LutEntry *lut0, int lane, uint32_t (&word)[4]) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     uint32_t chunk = 0;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const float u = acc[t][r] * inv_s[r];
-      // |u| <= S up to rounding; the clamp keeps the cell in the table
-      const int k = floor_to_int(__builtin_amdgcn_fmed3f(u, -S, S));
-      const LutEntry e = lut0[k];
+      const LutEntry e = lut0[floor_to_int(u)];
       const uint32_t c = e.base + (u > e.thr ? 1u : 0u);
       chunk |= c << (BITS * t);
     }
@@ -243,17 +246,17 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_mfma_kernel(const Quanti
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float s2 = __shfl(ss, 4 * g + r);
-      nrm[r] = sqrtf(s2);
+      nrm[r] = __builtin_amdgcn_sqrtf(s2);  // v_sqrt_f32: within 1 ulp
       inv_s[r] = nrm[r] > 0.0f ? scale * (rsd * __builtin_amdgcn_rcpf(nrm[r])) : 0.0f;
     }
 
     uint32_t word[4];
-    const LutEntry *lut0 = lut[side] + static_cast<int>(scale);
+    const LutEntry *lut0 = lut[side] + static_cast<int>(scale) + 1;
     switch (sd.bits) {
-      case 1: encode_tile<1>(acc, inv_s, lut0, scale, lane, word); break;
-      case 2: encode_tile<2>(acc, inv_s, lut0, scale, lane, word); break;
-      case 3: encode_tile<3>(acc, inv_s, lut0, scale, lane, word); break;
-      default: encode_tile<4>(acc, inv_s, lut0, scale, lane, word); break;
+      case 1: encode_tile<1>(acc, inv_s, lut0, lane, word); break;
+      case 2: encode_tile<2>(acc, inv_s, lut0, lane, word); break;
+      case 3: encode_tile<3>(acc, inv_s, lut0, lane, word); break;
+      default: encode_tile<4>(acc, inv_s, lut0, lane, word); break;
     }
 
     // output rows: tile row tr = 4 g + r is input row r0 + tr = (bh, i).
