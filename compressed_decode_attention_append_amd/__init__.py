@@ -60,6 +60,9 @@ class tq_cache(ctypes.Structure):
         ("seed", ctypes.c_uint64),
         ("k", tq_side),
         ("v", tq_side),
+        ("block_table", ctypes.c_void_p),
+        ("block_size", ctypes.c_int),
+        ("max_blocks", ctypes.c_int),
     ]
 
 
@@ -198,7 +201,12 @@ class TQCache:
     """
 
     def __init__(self, batch, kv_heads, head_dim, capacity, k: SideSpec, v: SideSpec,
-                 seed: int = 0, device="cuda"):
+                 seed: int = 0, device="cuda", block_table=None, block_size: int = 0,
+                 num_blocks: int = 0):
+        """Contiguous sides by default.  Paged: ``block_table`` is an int32
+        [B][capacity / block_size] tensor of block indices (kept on the
+        device), and the sides are pools of ``num_blocks`` blocks
+        ([num_blocks][Hkv][block_size][...]); see tq_cache in tq.h."""
         import torch
         self.batch, self.kv_heads, self.head_dim = int(batch), int(kv_heads), int(head_dim)
         self.capacity, self.seed = int(capacity), int(seed)
@@ -210,11 +218,26 @@ class TQCache:
         self.desc.head_dim, self.desc.capacity = self.head_dim, self.capacity
         self.desc.seed = self.seed
         self.tensors = {}
+        self.paged = block_table is not None
+        if self.paged:
+            bs = int(block_size)
+            if bs <= 0 or self.capacity % bs:
+                raise ValueError("paged cache: capacity must be a multiple of block_size")
+            table = block_table.to(device=device, dtype=torch.int32).contiguous()
+            if tuple(table.shape) != (self.batch, self.capacity // bs):
+                raise ValueError(f"block_table must be [{self.batch}][{self.capacity // bs}]")
+            self.block_table, self.block_size, self.num_blocks = table, bs, int(num_blocks)
+            self.desc.block_table = _ptr(table)
+            self.desc.block_size, self.desc.max_blocks = bs, self.capacity // bs
         for name, spec, side in (("k", k, self.desc.k), ("v", v, self.desc.v)):
             side.mode = _MODES[spec.mode]
             side.bits = int(spec.bits) if spec.mode != "fp16" else 0
             side.hot = int(spec.hot) if spec.mode == "delegated" else 0
             B, H, cap, d = self.batch, self.kv_heads, self.capacity, self.head_dim
+            if self.paged:
+                # pools: [num_blocks][Hkv][block_size][...] in the same tensor
+                # shapes (B -> num_blocks, cap -> block_size)
+                B, cap = self.num_blocks, self.block_size
             if spec.mode in ("packed", "delegated"):
                 cb = Codebook.get(d, spec.bits)
                 self._keep.append(cb)
@@ -231,7 +254,7 @@ class TQCache:
                 side.fp16 = _ptr(rows)
                 self.tensors[name + "_fp16"] = rows
             if spec.mode == "delegated":
-                ring = torch.zeros((B, H, spec.hot, d), dtype=torch.float16, device=device)
+                ring = torch.zeros((self.batch, H, spec.hot, d), dtype=torch.float16, device=device)
                 side.fp16 = _ptr(ring)
                 self.tensors[name + "_ring"] = ring
         self._ws = None
@@ -289,6 +312,17 @@ class TQCache:
                                    int(count), _ptr(out), _stream_handle(stream)),
                "tq_dequantize")
         return out[:, :, :count]
+
+    def logical(self, name: str):
+        """A side tensor in the logical [B][Hkv][capacity][...] layout: the
+        tensor itself for a contiguous cache (and for the delegated ring); for
+        a paged cache the pool gathered through the block table."""
+        t = self.tensors[name]
+        if not self.paged or name.endswith("_ring"):
+            return t
+        g = t[self.block_table.long()]          # [B][max_blocks][Hkv][bs][...]
+        g = g.transpose(1, 2)                    # [B][Hkv][max_blocks][bs][...]
+        return g.reshape(self.batch, self.kv_heads, self.capacity, *t.shape[3:])
 
     def _check_rows(self, x):
         import torch

@@ -56,9 +56,24 @@ int check_cache(const tq_cache *c) {
   if (!head_dim_ok(c->head_dim)) return TQ_ERR_HEAD_DIM;
   if (c->batch < 1 || c->kv_heads < 1 || c->capacity < 0) return TQ_ERR_ARG;
   if (static_cast<long long>(c->batch) * c->kv_heads > 65535) return TQ_ERR_ARG;
+  if (c->block_table) {
+    // paged: whole 32-position chunks per block, and the table covers the
+    // capacity exactly
+    if (c->block_size < 32 || c->block_size % 32 || c->max_blocks < 1) return TQ_ERR_ARG;
+    if (static_cast<long long>(c->block_size) * c->max_blocks != c->capacity) return TQ_ERR_ARG;
+  }
   int r = check_side(c->k, false);
   if (r != TQ_OK) return r;
   return check_side(c->v, true);
+}
+
+tq::Paging paging_of(const tq_cache *c) {
+  tq::Paging pg;
+  pg.table = c->block_table;
+  pg.bs = c->block_table ? c->block_size : 0;
+  pg.max_blocks = c->block_table ? c->max_blocks : 0;
+  pg.kv_heads = c->kv_heads;
+  return pg;
 }
 
 tq::SideDev side_dev(const tq_side &s, int d) {
@@ -159,6 +174,7 @@ void fill_decode_params(const tq_cache *cache, const void *q, int q_heads, int l
   p->head_dim = d;
   p->capacity = cache->capacity;
   p->length = length;
+  p->pg = paging_of(cache);
   fill_signs(cache->seed, d, p->sign);
   copy_levels(cache->k, cache->k.centroids, 1 << cache->k.bits, p->k_cent);
   copy_levels(cache->v, cache->v.centroids, 1 << cache->v.bits, p->v_cent);
@@ -250,6 +266,7 @@ int tq_quantize_append(const tq_cache *cache, const void *k_new, const void *v_n
   p.capacity = cache->capacity;
   p.n_new = n_new;
   p.offset = offset;
+  p.pg = paging_of(cache);
   p.side_mask = 3;
   fill_signs(cache->seed, d, p.sign);
   copy_levels(cache->k, cache->k.thresholds, (1 << cache->k.bits) - 1, p.k_thr);
@@ -315,6 +332,7 @@ int tq_dequantize(const tq_cache *cache, int side, int start, int count, float *
   p.capacity = cache->capacity;
   p.start = start;
   p.count = count;
+  p.pg = paging_of(cache);
   fill_signs(cache->seed, d, p.sign);
   copy_levels(s, s.centroids, 1 << s.bits, p.cent);
   const hipError_t e = tq::launch_dequantize(p, static_cast<hipStream_t>(hip_stream));

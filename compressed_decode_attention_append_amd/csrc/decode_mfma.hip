@@ -277,7 +277,7 @@ struct ChunkData {
 // nv kc .. nv kc + nv - 1 (nv = GP / 2 consecutive positions), moved there
 // from lane (grp, h) with DPP row shifts, and moved back the same way for the
 // value MFMA's B operand.
-template <int KB, int GP>
+template <int KB, int GP, bool PG>
 struct Wave {
   static constexpr int NV = GP / 2;
   static constexpr int kRowBytes = KB == 0 ? 2 * D : (KB == 4 ? 64 : 48);
@@ -295,6 +295,8 @@ struct Wave {
   const char *vnbase;  // V norms
   const uint16_t *ring;
   int capacity, hot_len, G;
+  Paging pg;           // PG: where the unit's rows live
+  int unit;
   float vscale;        // power of two, n vscale <= 32 for every norm seen, so
                        // p n vscale < 2^13 fits fp16 (lowered as norms grow)
   // running state (compact layout: head col % GP)
@@ -309,12 +311,17 @@ struct Wave {
   }
 
   __device__ __forceinline__ void load(int t0, ChunkData<KB, GP> &c) const {
-    // rows [t0, t0 + 32) at most; rows past the unit's capacity read 0
+    // rows [t0, t0 + 32) at most; rows past the unit's capacity read 0.
+    // Paged: t0 is a multiple of 32 and a block a multiple of 32 positions,
+    // so the chunk's rows are consecutive rows of one block.
+    // (A wave past the end of its split may ask for t0 >= capacity: it reads
+    // nothing, and the block table is not consulted.)
     const int rows = min(capacity - t0, kChunk);
-    const auto rk = rsrc(kbase + static_cast<long>(t0) * kRowBytes, rows * kRowBytes);
-    const auto rkn = rsrc(knbase + static_cast<long>(t0) * 4, rows * 4);
-    const auto rv = rsrc(vbase + static_cast<long>(t0) * 64, rows * 64);
-    const auto rvn = rsrc(vnbase + static_cast<long>(t0) * 4, rows * 4);
+    const long row0 = PG ? (t0 < capacity ? cache_row(pg, unit, t0, capacity) : 0L) : static_cast<long>(t0);
+    const auto rk = rsrc(kbase + row0 * kRowBytes, rows * kRowBytes);
+    const auto rkn = rsrc(knbase + row0 * 4, rows * 4);
+    const auto rv = rsrc(vbase + row0 * 64, rows * 64);
+    const auto rvn = rsrc(vnbase + row0 * 4, rows * 4);
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const int mo = m * 16 * kRowBytes;
@@ -775,12 +782,12 @@ struct Balance {
   }
 };
 
-template <int KB, int GP>
+template <int KB, int GP, bool PG>
 __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(const DecodeParams p) {
   constexpr int kWaves = waves_of<KB>();
   constexpr int kThreads = 64 * kWaves;
   using L = Lay<KB, GP>;
-  using WaveT = Wave<KB, GP>;
+  using WaveT = Wave<KB, GP, PG>;
   constexpr int NV = WaveT::NV;
   // Static LDS: its base address is a compile-time constant, so table reads
   // fold the table offset into the instruction.
@@ -824,7 +831,11 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   W.rep4v = W.rep4 + v_table_byte<KB>();
   W.lds = lds;
   W.G = G;
-  const long rowbase = static_cast<long>(unit) * p.capacity;
+  // contiguous: the unit's rows start at unit * capacity; paged: load()
+  // finds each chunk's block
+  const long rowbase = PG ? 0L : static_cast<long>(unit) * p.capacity;
+  W.pg = p.pg;
+  W.unit = unit;
   W.kbase = KB ? reinterpret_cast<const char *>(p.k.codes) + rowbase * kRowBytes
                : reinterpret_cast<const char *>(p.k.fp16) + rowbase * kRowBytes;
   W.knbase = KB ? reinterpret_cast<const char *>(p.k.norms + rowbase) : W.kbase;
@@ -1174,6 +1185,9 @@ bool decode_mfma_supported(const DecodeParams &p) {
   const int G = p.q_heads / p.kv_heads;
   if (p.head_dim != D || G > 8) return false;
   if (!(p.v.mode == TQ_SIDE_PACKED || p.v.mode == TQ_SIDE_DELEGATED) || p.v.bits != 4) return false;
+  // paged with a delegated V: the hot window's chunks need not start on a
+  // block's 32-position grid; the plain kernel reads row by row
+  if (p.pg.table && p.v.mode == TQ_SIDE_DELEGATED) return false;
   int kb;
   if (p.k.mode == TQ_SIDE_FP16) {
     kb = 0;
@@ -1190,13 +1204,22 @@ bool decode_mfma_supported(const DecodeParams &p) {
 
 int decode_mfma_max_splits() { return kMaxSplits; }
 
+template <int KB, int GP>
+void launch_gp(const DecodeParams &p, dim3 grid, hipStream_t stream) {
+  if (p.pg.table) {
+    hipLaunchKernelGGL((decode_mfma_kernel<KB, GP, true>), grid, dim3(64 * waves_of<KB>()), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((decode_mfma_kernel<KB, GP, false>), grid, dim3(64 * waves_of<KB>()), 0, stream, p);
+  }
+}
+
 template <int KB>
 void launch_kb(const DecodeParams &p, dim3 grid, hipStream_t stream) {
   const int G = p.q_heads / p.kv_heads;
   if (G <= 4) {
-    hipLaunchKernelGGL((decode_mfma_kernel<KB, 4>), grid, dim3(64 * waves_of<KB>()), 0, stream, p);
+    launch_gp<KB, 4>(p, grid, stream);
   } else {
-    hipLaunchKernelGGL((decode_mfma_kernel<KB, 8>), grid, dim3(64 * waves_of<KB>()), 0, stream, p);
+    launch_gp<KB, 8>(p, grid, stream);
   }
 }
 

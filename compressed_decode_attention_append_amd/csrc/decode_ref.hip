@@ -44,7 +44,7 @@ __device__ __forceinline__ float block_reduce(float x, float *red, bool is_max) 
 // Is V row `t` served from fp16 storage?  Returns the fp16 row or null.
 __device__ __forceinline__ const uint16_t *v_plain_row(const DecodeParams &p, long bk, int t) {
   const int D = p.head_dim;
-  if (p.v.mode == TQ_SIDE_FP16) return p.v.fp16 + (bk * p.capacity + t) * D;
+  if (p.v.mode == TQ_SIDE_FP16) return p.v.fp16 + cache_row(p.pg, bk, t, p.capacity) * D;
   if (p.v.mode == TQ_SIDE_DELEGATED && t >= p.length - p.v.hot)
     return p.v.fp16 + (bk * p.v.hot + (t % p.v.hot)) * D;
   return nullptr;
@@ -101,11 +101,11 @@ __global__ __launch_bounds__(kBlock) void decode_split_kernel(const DecodeParams
     const int t = t0 + tok;
     float acc = 0.0f;
     if (k_packed) {
-      const uint32_t *row = p.k.codes + (bk * p.capacity + t) * p.k.words;
+      const uint32_t *row = p.k.codes + cache_row(p.pg, bk, t, p.capacity) * p.k.words;
       for (int j = 0; j < D; ++j) acc += qr[h * D + j] * ck[extract_code(row, p.k.bits, j)];
-      acc *= p.k.norms[bk * p.capacity + t];
+      acc *= p.k.norms[cache_row(p.pg, bk, t, p.capacity)];
     } else {
-      const uint16_t *row = p.k.fp16 + (bk * p.capacity + t) * D;
+      const uint16_t *row = p.k.fp16 + cache_row(p.pg, bk, t, p.capacity) * D;
       for (int j = 0; j < D; ++j) acc += qr[h * D + j] * h2f(row[j]);
     }
     sc[h * SL + tok] = acc;
@@ -145,8 +145,8 @@ __global__ __launch_bounds__(kBlock) void decode_split_kernel(const DecodeParams
       if (vrow) {
         plain += w * h2f(vrow[j]);
       } else {
-        const uint32_t *row = p.v.codes + (bk * p.capacity + t) * p.v.words;
-        rot += w * p.v.norms[bk * p.capacity + t] * cv[extract_code(row, p.v.bits, j)];
+        const uint32_t *row = p.v.codes + cache_row(p.pg, bk, t, p.capacity) * p.v.words;
+        rot += w * p.v.norms[cache_row(p.pg, bk, t, p.capacity)] * cv[extract_code(row, p.v.bits, j)];
       }
     }
     const long u = (hq0 + h) * p.n_splits + split;

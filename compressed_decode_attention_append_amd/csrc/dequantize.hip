@@ -26,12 +26,12 @@ __global__ __launch_bounds__(kBlock) void dequantize_kernel(const DequantParams 
   const long r = live ? task : 0;
   const long bh = r / p.count;
   const int pos = p.start + static_cast<int>(r % p.count);
-  const uint32_t *row = p.s.codes + (bh * p.capacity + pos) * p.s.words;
+  const uint32_t *row = p.s.codes + cache_row(p.pg, bh, pos, p.capacity) * p.s.words;
   float v[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) v[e] = cent[extract_code(row, p.s.bits, 4 * t + e)];
   fwht_group4<TPR>(v, t);
-  const float n = p.s.norms[bh * p.capacity + pos];
+  const float n = p.s.norms[cache_row(p.pg, bh, pos, p.capacity)];
   const float scale = n / sqrtf(static_cast<float>(D));
   if (live) {
     float4 o;

@@ -116,9 +116,9 @@ __global__ __launch_bounds__(kBlock) void quantize_append_kernel(const QuantizeP
     float x[4];
     load4<D>(src, t, x);
     encode_row<D>(x, t, p.sign, th, s.bits, s.words, live,
-                  s.codes + (bh * p.capacity + pos) * s.words, s.norms + bh * p.capacity + pos);
+                  s.codes + cache_row(p.pg, bh, pos, p.capacity) * s.words, s.norms + cache_row(p.pg, bh, pos, p.capacity));
   } else if (s.mode == TQ_SIDE_FP16) {
-    if (live) copy4(src, s.fp16 + (bh * p.capacity + pos) * D, t);
+    if (live) copy4(src, s.fp16 + cache_row(p.pg, bh, pos, p.capacity) * D, t);
   } else {  // TQ_SIDE_DELEGATED (V only)
     const int hot = s.hot;
     const int end = p.offset + p.n_new;
@@ -127,7 +127,7 @@ __global__ __launch_bounds__(kBlock) void quantize_append_kernel(const QuantizeP
       float x[4];
       load4<D>(src, t, x);
       encode_row<D>(x, t, p.sign, th, s.bits, s.words, live,
-                    s.codes + (bh * p.capacity + pos) * s.words, s.norms + bh * p.capacity + pos);
+                    s.codes + cache_row(p.pg, bh, pos, p.capacity) * s.words, s.norms + cache_row(p.pg, bh, pos, p.capacity));
     } else {
       // Last new position of its ring slot: evict the slot's old occupant
       // (the position o < offset with o = pos mod hot) into the cold rows,
@@ -138,8 +138,8 @@ __global__ __launch_bounds__(kBlock) void quantize_append_kernel(const QuantizeP
       float x[4];
       load4<D>(ring, t, x);
       encode_row<D>(x, t, p.sign, th, s.bits, s.words, live && o >= 0,
-                    s.codes + (bh * p.capacity + (o >= 0 ? o : 0)) * s.words,
-                    s.norms + bh * p.capacity + (o >= 0 ? o : 0));
+                    s.codes + cache_row(p.pg, bh, o >= 0 ? o : 0, p.capacity) * s.words,
+                    s.norms + cache_row(p.pg, bh, o >= 0 ? o : 0, p.capacity));
       if (live) copy4(src, ring, t);
     }
   }

@@ -271,6 +271,19 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_mfma_kernel(const Quanti
     uint32_t *codes0 = sd.codes + (bh0 * p.capacity + p.offset + i0) * W;
     float *norms0 = sd.norms + bh0 * p.capacity + p.offset + i0;
     const int skip = p.capacity - p.n_new;
+    if (p.pg.table) {
+      // paged: each row's block from the table
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tr = 4 * g + r;
+        if (tr >= left) continue;
+        const bool wrap = i0 + tr >= p.n_new;
+        const long row = cache_row(p.pg, bh0 + (wrap ? 1 : 0), p.offset + i0 + tr - (wrap ? p.n_new : 0), p.capacity);
+        if (n < W) sd.codes[row * W + n] = word[r];
+        if (n == r) sd.norms[row] = nrm[r];
+      }
+      continue;
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int tr = 4 * g + r;

@@ -25,11 +25,26 @@ struct SideDev {
   uint16_t *fp16;  // fp16 rows (FP16) or hot ring (DELEGATED)
 };
 
+// Where a cache row lives.  Contiguous (table null): row (b Hkv + kv) cap
+// + t.  Paged: row (table[b][t / bs] Hkv + kv) bs + t % bs of the block
+// pools.  `bh` is b Hkv + kv.
+struct Paging {
+  const int32_t *table;  // [B][max_blocks] or null
+  int bs, max_blocks, kv_heads;
+};
+
+__host__ __device__ inline long cache_row(const Paging &pg, long bh, int t, int capacity) {
+  if (!pg.table) return bh * capacity + t;
+  const long b = bh / pg.kv_heads, kv = bh - b * pg.kv_heads;
+  return (static_cast<long>(pg.table[b * pg.max_blocks + t / pg.bs]) * pg.kv_heads + kv) * pg.bs + t % pg.bs;
+}
+
 struct QuantizeParams {
   SideDev k, v;
   const uint16_t *k_new;  // [B][H][n_new][d] fp16
   const uint16_t *v_new;
   int batch, heads, head_dim, capacity, n_new, offset;
+  Paging pg;
   int side_mask;                 // sides this launch encodes: bit 0 K, bit 1 V
   float k_lut_scale;             // matrix-core kernel: code-table cells per unit of y
   float v_lut_scale;             //   (a power of two; 0 = side not eligible)
@@ -42,6 +57,7 @@ struct DequantParams {
   SideDev s;
   float *out;  // [B][H][count][d]
   int batch, heads, head_dim, capacity, start, count;
+  Paging pg;
   uint32_t sign[kMaxSignWords];
   float cent[kMaxLevels];
 };
@@ -55,6 +71,7 @@ struct DecodeParams {
   unsigned *counters; // per-unit arrival counters (start of the workspace)
   size_t ws_part_off; // byte offset of the partial results
   int batch, kv_heads, q_heads, head_dim, capacity, length;
+  Paging pg;
   // plain split-context variant
   int n_splits, split_len;
   // matrix-core variant: packed (cold) positions [0, cold_len) in

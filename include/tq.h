@@ -114,7 +114,25 @@ typedef struct tq_side {
 } tq_side;
 
 /* One layer's cache.  K may be FP16 or PACKED; V may be FP16, PACKED or
- * DELEGATED.  `seed` selects the rotation shared by both sides. */
+ * DELEGATED.  `seed` selects the rotation shared by both sides.
+ *
+ * Paged storage (mlxcel "TurboQuant KV cache", "Paged cache and server
+ * batching": TurboQuant modes in a block-table decode layout).  With
+ * block_table NULL (zero-initialised descriptor) every side is contiguous as
+ * described in tq_side.  With a block table, the codes, norms and fp16 rows
+ * of both sides live in pools of fixed-size blocks instead:
+ *   codes [num_blocks][Hkv][block_size][row_words], norms
+ *   [num_blocks][Hkv][block_size], fp16 rows [num_blocks][Hkv][block_size][d],
+ * and position t of sequence b sits in block block_table[b][t / block_size]
+ * at row t % block_size.  The DELEGATED hot ring stays [B][Hkv][hot][d].
+ *   block_table: DEVICE int32 [B][max_blocks]; entries are block indices of
+ *                the pools (each in [0, num_blocks); not checked -- the
+ *                library does not read device memory on the host).  Blocks
+ *                may be shared between sequences for positions they share.
+ *   block_size:  positions per block, a multiple of 32.
+ *   max_blocks:  table row length; capacity must equal max_blocks * block_size.
+ * Errors: TQ_ERR_ARG if block_size or max_blocks is invalid or capacity does
+ * not match. */
 typedef struct tq_cache {
   int batch;
   int kv_heads;
@@ -123,6 +141,9 @@ typedef struct tq_cache {
   uint64_t seed;
   tq_side k;
   tq_side v;
+  const int32_t *block_table; /* NULL: contiguous sides */
+  int block_size;
+  int max_blocks;
 } tq_cache;
 
 /* Quantize-append ("update_and_fetch" of the TurboQuantKVCache; one launch

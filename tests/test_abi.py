@@ -206,3 +206,25 @@ def test_read_probe_argument_errors():
     assert L.tq_read_probe(None, 16, fake, None) == tq.TQ_ERR_ARG             # no buffer
     assert L.tq_read_probe(fake, 20, fake, None) == tq.TQ_ERR_ARG             # not a multiple of 16
     assert L.tq_read_probe(ctypes.c_void_p(4100), 32, fake, None) == tq.TQ_ERR_ARG  # misaligned
+
+
+def test_paged_descriptor_errors():
+    # paged storage: block_size a multiple of 32, max_blocks >= 1 and
+    # capacity == max_blocks * block_size; checked before any launch
+    f = _Fake()
+    table = np.zeros(64, np.int32)
+
+    def paged(bs, mb, cap):
+        c = _desc(f, cap=cap)
+        c.block_table, c.block_size, c.max_blocks = table.ctypes.data, bs, mb
+        return c
+
+    for bs, mb, cap in ((48, 4, 192), (16, 8, 128), (0, 4, 0), (64, 0, 0), (64, 4, 192), (64, 4, 320)):
+        c = paged(bs, mb, cap)
+        assert _qa(c, f, n=0) == tq.TQ_ERR_ARG, (bs, mb, cap)
+        assert tq.lib().tq_decode_workspace_bytes(ctypes.byref(c), 8, 0, 0) == 0
+        assert tq.lib().tq_dequantize(ctypes.byref(c), 1, 0, 0, None, None) == tq.TQ_ERR_ARG
+    ok = paged(64, 4, 256)
+    assert _qa(ok, f, n=0) == tq.TQ_OK
+    assert tq.lib().tq_decode_workspace_bytes(ctypes.byref(ok), 8, 256, 0) > 0
+    assert _qa(ok, f, n=4, off=253) == tq.TQ_ERR_CAPACITY
