@@ -262,6 +262,9 @@ def main():
     ap.add_argument("--workload", default="c4_tq35_32k", choices=sorted(WORKLOADS))
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (profiling only)")
     ap.add_argument("--tokens", type=int, default=0, help="override the context length (profiling only)")
+    ap.add_argument("--block-size", type=int, default=0,
+                    help="paged storage with blocks of this many positions (a multiple of 32), "
+                         "each layer's blocks in a random order; 0 = contiguous")
     ap.add_argument("--splits", type=int, default=0,
                     help="context splits per (batch, KV head); 0 = the library's choice")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -310,8 +313,17 @@ def main():
     vspec = tq.SideSpec(w["v"][0], w["v"][1], w.get("hot", 256))
     layers = []
     t_fill = time.time()
+    bsz = args.block_size
+    if bsz and (bsz % 32 or T % bsz):
+        print(json.dumps({"error": "--block-size must be a multiple of 32 dividing the context"}), flush=True)
+        sys.exit(2)
     for li in range(Lyr):
-        cache = tq.TQCache(B, Hkv, d, T, kspec, vspec, seed=0, device=dev)
+        paging = {}
+        if bsz:
+            nb = B * (T // bsz)
+            perm = torch.randperm(nb, generator=torch.Generator().manual_seed(li)).to(torch.int32)
+            paging = dict(block_table=perm.reshape(B, T // bsz), block_size=bsz, num_blocks=nb)
+        cache = tq.TQCache(B, Hkv, d, T, kspec, vspec, seed=0, device=dev, **paging)
         # fill positions [0, base) with the layer's own synthetic rows
         chunk = 4096
         for s in range(0, base, chunk):
@@ -395,12 +407,14 @@ def main():
         "config": {"workload": args.workload, "batch": B, "kv_heads": Hkv, "q_heads": Hq,
                    "head_dim": d, "context": T, "layers": Lyr,
                    "k": f"{w['k'][0]}{w['k'][1] or ''}", "v": f"{w['v'][0]}{w['v'][1]}",
-                   "append_per_layer": n_new},
+                   "append_per_layer": n_new, "block_size": bsz},
         "hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4),
         "decode_us_per_layer": round(dec_avg_s * 1e6, 2),
         "decode_bytes_per_layer": dbytes,
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(args.workload)},
+                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                     # counters were taken on contiguous caches
+                     "traffic": None if bsz else recorded_traffic(args.workload)},
         # context for the roofline: what a plain streaming-read kernel attains
         "attainable_read": {"gbs": round(attain, 1), "bytes": 4 << 30,
                             "kernel": "tq_read_probe: 16-byte loads, 256 blocks of 768 threads",

@@ -310,14 +310,37 @@ struct Wave {
     for (int i = 0; i < 8; ++i) accv[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
-  __device__ __forceinline__ void load(int t0, ChunkData<KB, GP> &c) const {
-    // rows [t0, t0 + 32) at most; rows past the unit's capacity read 0.
-    // Paged: t0 is a multiple of 32 and a block a multiple of 32 positions,
-    // so the chunk's rows are consecutive rows of one block.
-    // (A wave past the end of its split may ask for t0 >= capacity: it reads
-    // nothing, and the block table is not consulted.)
+  // First storage row of the chunk at t0.  Paged: t0 is a multiple of 32
+  // and a block a multiple of 32 positions, so the chunk's rows are
+  // consecutive rows of one block.  (A wave past the end of its split may
+  // ask for t0 >= capacity: it reads nothing, and the table is not read.)
+  __device__ __forceinline__ long row_of(int t0) const {
+    if (!PG) return t0;
+    return t0 < capacity ? cache_row(pg, unit, t0, capacity) : 0L;
+  }
+
+  // Paged: the table entry of the chunk at t0 as a vector load (its wait is
+  // ordered with the chunk loads, unlike a scalar load's, which every LDS
+  // wait would have to include); past the table it reads 0.
+  __device__ __forceinline__ uint32_t blk_fetch(int t0) const {
+    if (!PG) return 0u;
+    const int b = unit / pg.kv_heads;
+    const auto rt = rsrc(pg.table + static_cast<long>(b) * pg.max_blocks, 4 * pg.max_blocks);
+    return __builtin_amdgcn_raw_buffer_load_b32(rt, 4 * (t0 / pg.bs), 0, 0);
+  }
+  __device__ __forceinline__ long row_from(uint32_t blk, int t0) const {
+    if (!PG) return t0;
+    const int kv = unit % pg.kv_heads;
+    const long bl = static_cast<long>(__builtin_amdgcn_readfirstlane(blk));
+    return (bl * pg.kv_heads + kv) * pg.bs + t0 % pg.bs;
+  }
+
+  __device__ __forceinline__ void load(int t0, ChunkData<KB, GP> &c) const { load_row(row_of(t0), t0, c); }
+
+  // rows [t0, t0 + 32) at most, from storage row row0 on; rows past the
+  // unit's capacity read 0
+  __device__ __forceinline__ void load_row(long row0, int t0, ChunkData<KB, GP> &c) const {
     const int rows = min(capacity - t0, kChunk);
-    const long row0 = PG ? (t0 < capacity ? cache_row(pg, unit, t0, capacity) : 0L) : static_cast<long>(t0);
     const auto rk = rsrc(kbase + row0 * kRowBytes, rows * kRowBytes);
     const auto rkn = rsrc(knbase + row0 * 4, rows * 4);
     const auto rv = rsrc(vbase + row0 * 64, rows * 64);
@@ -974,9 +997,13 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
     // loop, which keeps this shape within its registers
     int c = wave;
     const int last = max(n_chunks - 1, 0);
+    uint32_t nblk = W.blk_fetch(s0 + min(c + kWaves, last) * kChunk);
     while (c < n_chunks) {
       int cn = c + kWaves;
-      W.load(s0 + min(cn, last) * kChunk, B);
+      uint32_t nblk2 = W.blk_fetch(s0 + min(cn + kWaves, last) * kChunk);
+      if (PG) asm volatile("" ::: "memory");
+      W.load_row(W.row_from(nblk, s0 + min(cn, last) * kChunk), s0 + min(cn, last) * kChunk, B);
+      nblk = nblk2;
       asm volatile("" ::: "memory");
       if (c < n_full) {
         W.template cold_chunk<false>(s0 + c * kChunk, s1, A, p.scores, hq0, p.length);
@@ -987,7 +1014,10 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
       c = cn;
       if (c >= n_chunks) break;
       cn = c + kWaves;
-      W.load(s0 + min(cn, last) * kChunk, A);
+      nblk2 = W.blk_fetch(s0 + min(cn + kWaves, last) * kChunk);
+      if (PG) asm volatile("" ::: "memory");
+      W.load_row(W.row_from(nblk, s0 + min(cn, last) * kChunk), s0 + min(cn, last) * kChunk, A);
+      nblk = nblk2;
       asm volatile("" ::: "memory");
       if (c < n_full) {
         W.template cold_chunk<false>(s0 + c * kChunk, s1, B, p.scores, hq0, p.length);
@@ -1005,9 +1035,16 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
     int c = wave;
     bool in_b = false;  // the buffer holding chunk c
     const int last = max(n_chunks - 1, 0);
+    // Paged: the table entry of the chunk loaded next is fetched one load
+    // ahead, before the loads it runs ahead of, so waiting for it never
+    // waits for a chunk still needed later.
+    uint32_t nblk = W.blk_fetch(s0 + min(c + kWaves, last) * kChunk);
     while (c < n_full) {
       int cn = c + kWaves;
-      W.load(s0 + min(cn, last) * kChunk, B);
+      uint32_t nblk2 = W.blk_fetch(s0 + min(cn + kWaves, last) * kChunk);
+      if (PG) asm volatile("" ::: "memory");
+      W.load_row(W.row_from(nblk, s0 + min(cn, last) * kChunk), s0 + min(cn, last) * kChunk, B);
+      nblk = nblk2;
       asm volatile("" ::: "memory");
       W.template cold_chunk<false>(s0 + c * kChunk, s1, A, p.scores, hq0, p.length);
       bal.step(wave, lane);
@@ -1017,7 +1054,10 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
         break;
       }
       cn = c + kWaves;
-      W.load(s0 + min(cn, last) * kChunk, A);
+      nblk2 = W.blk_fetch(s0 + min(cn + kWaves, last) * kChunk);
+      if (PG) asm volatile("" ::: "memory");
+      W.load_row(W.row_from(nblk, s0 + min(cn, last) * kChunk), s0 + min(cn, last) * kChunk, A);
+      nblk = nblk2;
       asm volatile("" ::: "memory");
       W.template cold_chunk<false>(s0 + c * kChunk, s1, B, p.scores, hq0, p.length);
       bal.step(wave, lane);

@@ -197,13 +197,46 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_mfma_kernel(const Quanti
     for (int q = 0; q < 4; ++q)
       dst[q] = as_half8(__builtin_amdgcn_raw_buffer_load_b128(rx, (n * D + 32 * q + 8 * g) * 2, 0, 0));
   };
+  // Paged storage: the storage rows of this lane's output rows (4 g + r) of
+  // a tile, looked up in the block table together with the tile's loads, so
+  // the lookups are in flight while the tile before it is encoded.
+  auto paged_rows = [&](int tl, long (&rw)[4]) {
+    const int sd_ = tl < tiles_k ? 0 : 1;
+    const long q0 = static_cast<long>(sd_ ? tl - tiles_k : tl) * kTileRows;
+    const long lf = rows - q0;
+    const long b0 = rows <= 0x7fffffffL ? static_cast<long>(static_cast<uint32_t>(q0) / static_cast<uint32_t>(p.n_new))
+                                        : q0 / p.n_new;
+    const int j0 = static_cast<int>(q0 - b0 * p.n_new);
+    // (sequence, head) of the tile's first row and of the next one (a tile
+    // crosses at most one boundary), divided once per tile
+    const int sq0 = static_cast<int>(b0) / p.heads, hd0 = static_cast<int>(b0) - sq0 * p.heads;
+    const int sq1 = hd0 + 1 == p.heads ? sq0 + 1 : sq0, hd1 = hd0 + 1 == p.heads ? 0 : hd0 + 1;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tr = min(4 * g + r, static_cast<int>(lf) - 1);
+      const bool wrap = j0 + tr >= p.n_new;
+      rw[r] = paged_row(p.pg, wrap ? sq1 : sq0, wrap ? hd1 : hd0, p.offset + j0 + tr - (wrap ? p.n_new : 0));
+    }
+  };
+  const bool paged = p.pg.table != nullptr;
   half8_t a[4], an[4];
+  long prow[4] = {0, 0, 0, 0}, prow_n[4] = {0, 0, 0, 0};
   int tile = blockIdx.x * kWaves + wave;
-  if (tile < tiles_total) load_tile(tile, an);
+  if (tile < tiles_total) {
+    load_tile(tile, an);
+    if (paged) paged_rows(tile, prow_n);
+  }
   for (; tile < tiles_total; tile += stride) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) a[q] = an[q];
-    if (tile + stride < tiles_total) load_tile(tile + stride, an);
+    if (paged) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) prow[r] = prow_n[r];
+    }
+    if (tile + stride < tiles_total) {
+      load_tile(tile + stride, an);
+      if (paged) paged_rows(tile + stride, prow_n);
+    }
     const int side = tile < tiles_k ? 0 : 1;
     const SideDev &sd = side ? p.v : p.k;
     const float scale = side ? p.v_lut_scale : p.k_lut_scale;
@@ -271,16 +304,12 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_mfma_kernel(const Quanti
     uint32_t *codes0 = sd.codes + (bh0 * p.capacity + p.offset + i0) * W;
     float *norms0 = sd.norms + bh0 * p.capacity + p.offset + i0;
     const int skip = p.capacity - p.n_new;
-    if (p.pg.table) {
-      // paged: each row's block from the table
+    if (paged) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int tr = 4 * g + r;
-        if (tr >= left) continue;
-        const bool wrap = i0 + tr >= p.n_new;
-        const long row = cache_row(p.pg, bh0 + (wrap ? 1 : 0), p.offset + i0 + tr - (wrap ? p.n_new : 0), p.capacity);
-        if (n < W) sd.codes[row * W + n] = word[r];
-        if (n == r) sd.norms[row] = nrm[r];
+        if (4 * g + r >= left) continue;
+        if (n < W) sd.codes[prow[r] * W + n] = word[r];
+        if (n == r) sd.norms[prow[r]] = nrm[r];
       }
       continue;
     }

@@ -33,10 +33,21 @@ struct Paging {
   int bs, max_blocks, kv_heads;
 };
 
+// Paged row of position t of (sequence b, KV head kv).  Unsigned 32-bit
+// arithmetic for the divisions: positions and bh = b Hkv + kv (at most 65535)
+// fit, and a 64-bit division costs tens of instructions.
+__host__ __device__ inline long paged_row(const Paging &pg, int b, int kv, int t) {
+  const unsigned ut = static_cast<unsigned>(t), ubs = static_cast<unsigned>(pg.bs);
+  const unsigned blk = ut / ubs;
+  return (static_cast<long>(pg.table[b * pg.max_blocks + static_cast<int>(blk)]) * pg.kv_heads + kv) * pg.bs +
+         static_cast<int>(ut - blk * ubs);
+}
+
 __host__ __device__ inline long cache_row(const Paging &pg, long bh, int t, int capacity) {
   if (!pg.table) return bh * capacity + t;
-  const long b = bh / pg.kv_heads, kv = bh - b * pg.kv_heads;
-  return (static_cast<long>(pg.table[b * pg.max_blocks + t / pg.bs]) * pg.kv_heads + kv) * pg.bs + t % pg.bs;
+  const unsigned u = static_cast<unsigned>(bh), kvh = static_cast<unsigned>(pg.kv_heads);
+  const unsigned b = u / kvh;
+  return paged_row(pg, static_cast<int>(b), static_cast<int>(u - b * kvh), t);
 }
 
 struct QuantizeParams {
