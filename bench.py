@@ -265,6 +265,9 @@ def main():
     ap.add_argument("--block-size", type=int, default=0,
                     help="paged storage with blocks of this many positions (a multiple of 32), "
                          "each layer's blocks in a random order; 0 = contiguous")
+    ap.add_argument("--sparse-v", type=float, default=0.0,
+                    help="decode with tq_decode_attention_sparse at this weight threshold "
+                         "(an approximation; 0 = the exact decode)")
     ap.add_argument("--splits", type=int, default=0,
                     help="context splits per (batch, KV head); 0 = the library's choice")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -369,7 +372,8 @@ def main():
         if ev:
             ev[1].record(stream)
         for cache, kn, vn, q, out, ws in layers:
-            cache.decode_attention(q, T, n_splits=args.splits, out=out, workspace=ws, stream=stream)
+            cache.decode_attention(q, T, n_splits=args.splits, out=out, workspace=ws, stream=stream,
+                                   sparse_v=args.sparse_v)
         if ev:
             ev[2].record(stream)
             record.append(ev)
@@ -407,7 +411,7 @@ def main():
         "config": {"workload": args.workload, "batch": B, "kv_heads": Hkv, "q_heads": Hq,
                    "head_dim": d, "context": T, "layers": Lyr,
                    "k": f"{w['k'][0]}{w['k'][1] or ''}", "v": f"{w['v'][0]}{w['v'][1]}",
-                   "append_per_layer": n_new, "block_size": bsz},
+                   "append_per_layer": n_new, "block_size": bsz, "sparse_v": args.sparse_v},
         "hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4),
         "decode_us_per_layer": round(dec_avg_s * 1e6, 2),
         "decode_bytes_per_layer": dbytes,

@@ -93,6 +93,9 @@ def lib():
         L.tq_decode_attention.argtypes = [ctypes.POINTER(tq_cache), P, I, I, I, P, P, P,
                                           ctypes.c_size_t, P]
         L.tq_decode_attention.restype = I
+        L.tq_decode_attention_sparse.argtypes = [ctypes.POINTER(tq_cache), P, I, I, I, ctypes.c_float, P, P,
+                                                 P, ctypes.c_size_t, P]
+        L.tq_decode_attention_sparse.restype = I
         L.tq_dequantize.argtypes = [ctypes.POINTER(tq_cache), I, I, I, P, P]
         L.tq_dequantize.restype = I
         L.tq_status_string.argtypes = [I]
@@ -285,9 +288,10 @@ class TQCache:
         return self._ws
 
     def decode_attention(self, q, length: int, n_splits: int = 0, out=None, scores=False,
-                         workspace=None, stream=None):
+                         workspace=None, stream=None, sparse_v: float = 0.0):
         """q: fp16 [B][Hq][d].  Returns out fp32 [B][Hq][d] (and scores
-        fp32 [B][Hq][length] when ``scores`` is true)."""
+        fp32 [B][Hq][length] when ``scores`` is true).  ``sparse_v`` > 0 runs
+        tq_decode_attention_sparse with that threshold."""
         import torch
         if q.dtype != torch.float16 or not q.is_contiguous() or q.dim() != 3:
             raise ValueError("q must be contiguous fp16 [B, Hq, d]")
@@ -298,10 +302,17 @@ class TQCache:
             out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
         sc = torch.empty((B, Hq, max(int(length), 1)), dtype=torch.float32, device=q.device) if scores else None
         ws = workspace if workspace is not None else self.workspace(Hq, length, n_splits)
-        _check(lib().tq_decode_attention(ctypes.byref(self.desc), _ptr(q), int(Hq), int(length),
-                                         int(n_splits), _ptr(out), _ptr(sc), _ptr(ws),
-                                         ws.numel() * ws.element_size(), _stream_handle(stream)),
-               "tq_decode_attention")
+        if sparse_v:
+            _check(lib().tq_decode_attention_sparse(ctypes.byref(self.desc), _ptr(q), int(Hq), int(length),
+                                                    int(n_splits), float(sparse_v), _ptr(out), _ptr(sc),
+                                                    _ptr(ws), ws.numel() * ws.element_size(),
+                                                    _stream_handle(stream)),
+                   "tq_decode_attention_sparse")
+        else:
+            _check(lib().tq_decode_attention(ctypes.byref(self.desc), _ptr(q), int(Hq), int(length),
+                                             int(n_splits), _ptr(out), _ptr(sc), _ptr(ws),
+                                             ws.numel() * ws.element_size(), _stream_handle(stream)),
+                   "tq_decode_attention")
         return (out, sc[:, :, :length]) if scores else out
 
     def dequantize(self, side: str, start: int, count: int, stream=None):

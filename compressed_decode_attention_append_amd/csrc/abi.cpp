@@ -287,6 +287,14 @@ size_t tq_decode_workspace_bytes(const tq_cache *cache, int q_heads, int length,
 int tq_decode_attention(const tq_cache *cache, const void *q, int q_heads, int length, int n_splits,
                         float *out, float *scores, void *workspace, size_t workspace_bytes,
                         void *hip_stream) {
+  return tq_decode_attention_sparse(cache, q, q_heads, length, n_splits, 0.0f, out, scores, workspace,
+                                    workspace_bytes, hip_stream);
+}
+
+int tq_decode_attention_sparse(const tq_cache *cache, const void *q, int q_heads, int length, int n_splits,
+                               float sparse_v, float *out, float *scores, void *workspace,
+                               size_t workspace_bytes, void *hip_stream) {
+  if (!(sparse_v >= 0.0f && sparse_v < 1.0f)) return TQ_ERR_ARG;
   int r = check_cache(cache);
   if (r != TQ_OK) return r;
   if (!q || !out) return TQ_ERR_ARG;
@@ -304,6 +312,7 @@ int tq_decode_attention(const tq_cache *cache, const void *q, int q_heads, int l
   p.scores = scores;
   p.ws = static_cast<float *>(workspace);
   p.counters = static_cast<unsigned *>(workspace);
+  p.sparse_lg = sparse_v > 0.0f ? log2f(sparse_v) : -INFINITY;
   p.ws_part_off = tq::kCounterBytes;
   const hipError_t e = (v == kMfma) ? tq::launch_decode_mfma(p, static_cast<hipStream_t>(hip_stream))
                                     : tq::launch_decode_ref(p, static_cast<hipStream_t>(hip_stream));

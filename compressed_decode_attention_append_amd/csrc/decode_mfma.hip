@@ -297,6 +297,8 @@ struct Wave {
   int capacity, hot_len, G;
   Paging pg;           // PG: where the unit's rows live
   int unit;
+  float sparse_lg;     // sparse-V threshold (log2), -inf = exact
+  float chunk_max;     // the last softmax's chunk maximum of the lane's head
   float vscale;        // power of two, n vscale <= 32 for every norm seen, so
                        // p n vscale < 2^13 fits fp16 (lowered as norms grow)
   // running state (compact layout: head col % GP)
@@ -531,6 +533,7 @@ struct Wave {
 #pragma unroll
     for (int j = 1; j < NV; ++j) cmax = fmaxf(cmax, c[j]);
     cmax = head_max<GP>(cmax);
+    chunk_max = cmax;
     const bool grow = cmax > m_run + kRescale;
     if (__ballot(grow)) {
       const float m_new = grow ? cmax : m_run;
@@ -640,7 +643,12 @@ struct Wave {
       if (TAIL && t0 + cpos + j >= we) cs[j] = -INFINITY;
     }
     if (scores) store_scores<TAIL>(t0, we, cs, scores, score_row0, length);
-    values(c, softmax<TAIL>(cs, vn));
+    const half8_t ap = softmax<TAIL>(cs, vn);
+    // sparse-V: every weight of the chunk, for every head, below the
+    // threshold times the running maximum (which never exceeds the final
+    // one): the chunk's values are skipped; its weights stay in the sum
+    if (sparse_lg != -INFINITY && !__ballot(chunk_max - m_run >= sparse_lg)) return;
+    values(c, ap);
   }
 
   // One chunk of the fp16 hot window (delegated V), positions >= we masked.
@@ -871,6 +879,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   W.hot_len = p.v.hot > 0 ? p.v.hot : 1;
   W.ring = (p.v.mode == TQ_SIDE_DELEGATED) ? p.v.fp16 + static_cast<long>(unit) * p.v.hot * D : nullptr;
   W.vscale = kVscaleMax;
+  W.sparse_lg = p.sparse_lg;
   W.reset();
 
   // ---- the query, then the first chunk, in flight while the block builds

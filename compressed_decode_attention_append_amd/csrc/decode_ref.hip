@@ -141,6 +141,8 @@ __global__ __launch_bounds__(kBlock) void decode_split_kernel(const DecodeParams
     for (int tok = 0; tok < n; ++tok) {
       const int t = t0 + tok;
       const float w = sc[h * SL + tok];
+      // sparse-V: weight relative to the split's maximum below the threshold
+      if (p.sparse_lg != -INFINITY && !(log2f(w) >= p.sparse_lg)) continue;
       const uint16_t *vrow = v_plain_row(p, bk, t);
       if (vrow) {
         plain += w * h2f(vrow[j]);

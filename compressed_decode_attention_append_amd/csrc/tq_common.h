@@ -83,6 +83,9 @@ struct DecodeParams {
   size_t ws_part_off; // byte offset of the partial results
   int batch, kv_heads, q_heads, head_dim, capacity, length;
   Paging pg;
+  // sparse-V: log2 of the weight threshold below which a group's values may
+  // be skipped; -inf = exact
+  float sparse_lg;
   // plain split-context variant
   int n_splits, split_len;
   // matrix-core variant: packed (cold) positions [0, cold_len) in

@@ -188,6 +188,23 @@ int tq_decode_attention(const tq_cache *cache, const void *q, int q_heads,
                         void *workspace, size_t workspace_bytes,
                         void *hip_stream);
 
+/* Sparse-V decode (mlxcel "TurboQuant KV cache", "CLI and server flags":
+ * the sparse-V threshold, 0 disabling it): tq_decode_attention, except that
+ * the value contribution of positions whose softmax weight is below
+ * `sparse_v` times the largest weight may be dropped.  The softmax
+ * denominator keeps every position; only values are skipped, and only where
+ * a whole group of positions (a 32-position chunk of the matrix-core kernel,
+ * one position in the plain kernel) is below the threshold, judged against
+ * a running maximum that never exceeds the final one.  So each dropped
+ * position i has p_i < sparse_v (p relative to the largest weight), and
+ * every output element moves by at most sum over such i of p_i |v_i| / sum p.
+ *   sparse_v: in [0, 1); 0 is exactly tq_decode_attention.
+ * Errors: as tq_decode_attention; TQ_ERR_ARG if sparse_v is outside [0, 1). */
+int tq_decode_attention_sparse(const tq_cache *cache, const void *q, int q_heads,
+                               int length, int n_splits, float sparse_v, float *out,
+                               float *scores, void *workspace, size_t workspace_bytes,
+                               void *hip_stream);
+
 /* Dequantize packed rows [start, start + count) of one side (0 = K, 1 = V;
  * for a DELEGATED V this reads the packed cold rows) into DEVICE fp32
  * out[B][Hkv][count][d] (the FAQ's "dequantize" back to float32).  A check

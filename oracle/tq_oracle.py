@@ -60,7 +60,7 @@ __all__ = [
     "cell_second_moment", "lloyd_max", "distortion", "split_bits",
     "row_words", "bytes_per_token_head", "quantize", "pack_codes",
     "unpack_codes", "codes_from_rotated", "dequantize", "attention", "PackedSide", "DelegatedSide",
-    "decode_attention",
+    "decode_attention", "sparse_v_bound", "sparse_v_attention",
 ]
 
 
@@ -360,6 +360,54 @@ def attention(q, k, v):
             scores[b, h] = s
             out[b, h] = p @ v[b, kv] if T else 0.0
     return out, scores
+
+
+def sparse_v_bound(q, k, v, tau):
+    """Sparse-V (mlxcel "TurboQuant KV cache", "CLI and server flags": a
+    weight threshold below which value work is skipped, 0 disabling it).
+    With p_i = exp(s_i - max s) the weights relative to the largest, a
+    decode that drops the value contribution of some positions with
+    p_i < tau, keeping every p_i in the denominator, moves output element j
+    by at most  sum_{i: p_i < tau} p_i |v_ij| / sum_i p_i.  Returns that
+    bound [B, Hq, d] (zero for tau = 0)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, d = q.shape
+    G = Hq // k.shape[1]
+    bound = np.zeros((B, Hq, d))
+    if k.shape[2] == 0:
+        return bound
+    for b in range(B):
+        for h in range(Hq):
+            kv = h // G
+            s = k[b, kv] @ q[b, h] / math.sqrt(d)
+            p = np.exp(s - np.max(s))
+            low = p < tau
+            bound[b, h] = (p[low] @ np.abs(v[b, kv][low])) / np.sum(p)
+    return bound
+
+
+def sparse_v_attention(q, k, v, tau):
+    """Attention that drops the value contribution of every position with
+    p_i < tau (relative weight, as in sparse_v_bound) and keeps all of them
+    in the softmax denominator: the largest drop the bound allows."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, d = q.shape
+    G = Hq // k.shape[1]
+    out = np.zeros((B, Hq, d))
+    if k.shape[2] == 0:
+        return out
+    for b in range(B):
+        for h in range(Hq):
+            kv = h // G
+            s = k[b, kv] @ q[b, h] / math.sqrt(d)
+            p = np.exp(s - np.max(s))
+            keep = ~(p < tau)
+            out[b, h] = (p[keep] @ v[b, kv][keep]) / np.sum(p)
+    return out
 
 
 # ---------------------------------------------------------------------------

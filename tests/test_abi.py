@@ -228,3 +228,13 @@ def test_paged_descriptor_errors():
     assert _qa(ok, f, n=0) == tq.TQ_OK
     assert tq.lib().tq_decode_workspace_bytes(ctypes.byref(ok), 8, 256, 0) > 0
     assert _qa(ok, f, n=4, off=253) == tq.TQ_ERR_CAPACITY
+
+
+def test_sparse_v_threshold_errors():
+    # the threshold must lie in [0, 1); checked before any launch
+    f = _Fake()
+    c = _desc(f)
+    for tau in (-0.1, 1.0, 2.0, float("nan")):
+        r = tq.lib().tq_decode_attention_sparse(ctypes.byref(c), f.p(4096), 8, 100, 0, tau, f.p(8192), None,
+                                                f.p(0), 1 << 30, None)
+        assert r == tq.TQ_ERR_ARG, tau

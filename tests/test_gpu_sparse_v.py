@@ -1,0 +1,115 @@
+"""Sparse-V decode (tq_decode_attention_sparse) against the exact decode and
+the oracle's bound on what dropping small-weight values may change.
+
+Inputs are peaked on purpose: the first 64 positions of each KV head point
+along the queries' direction, so every later chunk's weights are far below
+the threshold and its values are skipped; the oracle bound is computed on
+the GPU-written cache rows."""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from parity import rows_close, words_to_codes
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import compressed_decode_attention_append_amd as tq  # noqa: E402
+
+S = tq.SideSpec
+CASES = [
+    ("tq35", S("packed", 3), S("packed", 4)),
+    ("asym", S("fp16", 0), S("packed", 4)),
+    ("delegated", S("fp16", 0), S("delegated", 4, 128)),
+]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    tq.lib()
+
+
+@pytest.fixture(params=["auto", "ref"])
+def dvariant(request):
+    old = os.environ.get("TQ_DECODE_VARIANT")
+    os.environ["TQ_DECODE_VARIANT"] = request.param
+    yield request.param
+    if old is None:
+        os.environ.pop("TQ_DECODE_VARIANT", None)
+    else:
+        os.environ["TQ_DECODE_VARIANT"] = old
+
+
+def _peaked(B, H, Hq, d, T, seed):
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal((B, H, d))
+    u /= np.linalg.norm(u, axis=-1, keepdims=True)
+    k = rng.standard_normal((B, H, T, d))
+    k[:, :, :64] = 8.0 * u[:, :, None, :] + 0.5 * rng.standard_normal((B, H, 64, d))
+    v = rng.standard_normal((B, H, T, d))
+    G = Hq // H
+    q = 32.0 * np.repeat(u, G, axis=1) + 0.1 * rng.standard_normal((B, Hq, d))
+    return k.astype(np.float16), v.astype(np.float16), q.astype(np.float16)
+
+
+def _rows(cache, side, length):
+    spec = cache.k_spec if side == "k" else cache.v_spec
+    if spec.mode == "fp16":
+        return cache.tensors[side + "_fp16"][:, :, :length].cpu().numpy().astype(np.float64)
+    d = cache.head_dim
+    R = oracle.rotation_matrix(cache.seed, d)
+    c, _ = oracle.lloyd_max(d, spec.bits)
+    words = cache.tensors[side + "_codes"][:, :, :length].cpu().numpy()
+    norms = cache.tensors[side + "_norms"][:, :, :length].cpu().numpy().astype(np.float64)
+    rows = oracle.dequantize(words_to_codes(words, spec.bits, d), norms, R, c)
+    if spec.mode == "delegated":
+        ring = cache.tensors[side + "_ring"].cpu().numpy()
+        for p in range(max(0, length - spec.hot), length):
+            rows[:, :, p] = ring[:, :, p % spec.hot].astype(np.float64)
+    return rows
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("tau", [1e-3, 0.2])
+def test_sparse_v_within_bound(case, tau, dvariant):
+    name, ks, vs = case
+    B, H, Hq, d, T = 1, 2, 8, 128, 1000
+    k, v, q = _peaked(B, H, Hq, d, T, 7)
+    cache = tq.TQCache(B, H, d, 1024, ks, vs)
+    cache.quantize_append(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), 0)
+    qd = torch.from_numpy(q).cuda()
+    exact = cache.decode_attention(qd, T)
+    sparse = cache.decode_attention(qd, T, sparse_v=tau)
+    torch.cuda.synchronize()
+    exact, sparse = exact.cpu().numpy().astype(np.float64), sparse.cpu().numpy().astype(np.float64)
+    kr, vr = _rows(cache, "k", T), _rows(cache, "v", T)
+    bound = oracle.sparse_v_bound(q, kr, vr, tau)
+    scale = np.max(np.abs(exact), axis=-1, keepdims=True)
+    # what the skipped values may change, plus the kernels' own rounding
+    assert np.all(np.abs(sparse - exact) <= bound * (1 + 1e-3) + 1e-5 * scale)
+    # values were skipped (the later chunks' weights are ~e^-20 of the peak)
+    assert not np.array_equal(sparse, exact)
+    # and the sparse output is within tolerance of the exact attention
+    ref, _ = oracle.decode_attention(q, kr, vr)
+    ok, worst = rows_close(sparse, ref, rel=2e-3 + float(np.max(bound / scale)))
+    assert ok, f"worst {worst}"
+
+
+def test_zero_threshold_is_the_exact_call():
+    B, H, Hq, d, T = 2, 2, 8, 128, 700
+    k, v, q = _peaked(B, H, Hq, d, T, 9)
+    cache = tq.TQCache(B, H, d, 1024, S("packed", 3), S("packed", 4))
+    cache.quantize_append(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), 0)
+    qd = torch.from_numpy(q).cuda()
+    exact = cache.decode_attention(qd, T)
+    ws = cache.workspace(Hq, T)
+    out = torch.empty_like(exact)
+    r = tq.lib().tq_decode_attention_sparse(ctypes.byref(cache.desc), qd.data_ptr(), Hq, T, 0, 0.0,
+                                            out.data_ptr(), None, ws.data_ptr(), ws.numel(), None)
+    torch.cuda.synchronize()
+    assert r == tq.TQ_OK
+    assert torch.equal(out, exact)

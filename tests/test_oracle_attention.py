@@ -108,3 +108,56 @@ def test_packed_side_writes_only_its_rows():
     assert np.all(side.codes[:, :, 40:] == 0) and np.all(side.norms[:, :, 40:] == 0)
     codes, n, _ = oracle.quantize(k, side.R, side.thresholds)
     assert np.array_equal(side.codes[:, :, :40], codes)
+
+
+# ---- sparse-V bound (mlxcel "TurboQuant KV cache", sparse-V threshold) ----
+
+def test_sparse_v_bound_hand_case():
+    # two positions, scores 0 and -10 ln 2 (relative weights 1 and 2^-10):
+    # with tau = 1e-2 the second is dropped; by hand the bound is
+    # 2^-10 |v_1| / (1 + 2^-10) and the sparse output p_0 v_0 / (1 + 2^-10)
+    d = 4
+    q = np.zeros((1, 1, d))
+    q[0, 0, 0] = 1.0
+    k = np.zeros((1, 1, 2, d))
+    k[0, 0, 1, 0] = -10.0 * np.log(2.0) * np.sqrt(d)
+    v = np.array([[[[1.0, -2.0, 3.0, 0.5], [-4.0, 8.0, 0.25, -1.0]]]])
+    w = 2.0 ** -10
+    b = oracle.sparse_v_bound(q, k, v, 1e-2)
+    assert np.allclose(b[0, 0], w * np.abs(v[0, 0, 1]) / (1 + w), rtol=1e-14, atol=0)
+    o = oracle.sparse_v_attention(q, k, v, 1e-2)
+    assert np.allclose(o[0, 0], v[0, 0, 0] / (1 + w), rtol=1e-14, atol=0)
+    # a threshold below both weights drops nothing
+    assert np.all(oracle.sparse_v_bound(q, k, v, w / 2) == 0)
+
+
+def test_sparse_v_zero_threshold_is_exact():
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((2, 4, 16))
+    k = rng.standard_normal((2, 2, 50, 16))
+    v = rng.standard_normal((2, 2, 50, 16))
+    assert np.all(oracle.sparse_v_bound(q, k, v, 0.0) == 0)
+    o, _ = oracle.attention(q, k, v)
+    assert np.allclose(oracle.sparse_v_attention(q, k, v, 0.0), o, rtol=1e-13, atol=1e-15)
+
+
+@pytest.mark.parametrize("tau", [1e-3, 0.05, 0.5, 0.99])
+def test_sparse_v_drop_stays_within_bound(tau):
+    # the largest allowed drop, and a random subset of it, both move every
+    # output element by no more than the bound
+    rng = np.random.default_rng(int(tau * 1e4))
+    q = 3.0 * rng.standard_normal((1, 4, 32))
+    k = rng.standard_normal((1, 2, 200, 32))
+    v = rng.standard_normal((1, 2, 200, 32))
+    o, _ = oracle.attention(q, k, v)
+    b = oracle.sparse_v_bound(q, k, v, tau)
+    full = oracle.sparse_v_attention(q, k, v, tau)
+    assert np.all(np.abs(full - o) <= b * (1 + 1e-12) + 1e-15)
+    # a random subset of the droppable positions (rebuilt from the definition)
+    G = 2
+    for h in range(4):
+        s = k[0, h // G] @ q[0, h] / np.sqrt(32)
+        p = np.exp(s - s.max())
+        drop = (p < tau) & (rng.random(200) < 0.5)
+        part = (p[~drop] @ v[0, h // G][~drop]) / p.sum()
+        assert np.all(np.abs(part - o[0, h]) <= b[0, h] * (1 + 1e-12) + 1e-15)
