@@ -128,7 +128,9 @@ typedef struct tq_side {
  *   block_table: DEVICE int32 [B][max_blocks]; entries are block indices of
  *                the pools (each in [0, num_blocks); not checked -- the
  *                library does not read device memory on the host).  Blocks
- *                may be shared between sequences for positions they share.
+ *                may be shared between sequences for positions they share;
+ *                an append must not write different rows into a shared block
+ *                (copy it first).
  *   block_size:  positions per block, a multiple of 32.
  *   max_blocks:  table row length; capacity must equal max_blocks * block_size.
  * Errors: TQ_ERR_ARG if block_size or max_blocks is invalid or capacity does
