@@ -61,6 +61,7 @@ __all__ = [
     "row_words", "bytes_per_token_head", "quantize", "pack_codes",
     "unpack_codes", "codes_from_rotated", "dequantize", "attention", "PackedSide", "DelegatedSide",
     "decode_attention", "sparse_v_bound", "sparse_v_attention",
+    "int8_quantize", "int8_dequantize", "int8_bytes_per_token_head",
 ]
 
 
@@ -408,6 +409,40 @@ def sparse_v_attention(q, k, v, tau):
             keep = ~(p < tau)
             out[b, h] = (p[keep] @ v[b, kv][keep]) / np.sum(p)
     return out
+
+
+# ---------------------------------------------------------------------------
+# INT8 per-token absmax cache (mlxcel "TurboQuant KV cache", "Available
+# modes": int8 is per-token INT8 absmax quantization, ~2x)
+# ---------------------------------------------------------------------------
+
+def int8_quantize(x):
+    """Per row (one token of one head): a = max_j |x_j|, scale = a / 127 and
+    code_j = x_j / scale rounded to the nearest integer (ties to even),
+    clamped to [-127, 127]; a zero row has scale 0 and codes 0.  The scale
+    and the division are float32 (the codes are integers decided by float
+    arithmetic, so the reference takes the decision in the precision the
+    kernels use: fp16 inputs are exact in float32, and float32 division and
+    round-to-nearest-even are IEEE operations).  Returns (codes int8
+    [..., d], scales float32 [...])."""
+    x32 = np.asarray(x).astype(np.float32)
+    a = np.max(np.abs(x32), axis=-1)
+    scale = (a / np.float32(127.0)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    v = (x32 / safe[..., None]).astype(np.float32)
+    codes = np.clip(np.rint(v), -127, 127)
+    codes = np.where(scale[..., None] > 0, codes, 0).astype(np.int8)
+    return codes, scale
+
+
+def int8_dequantize(codes, scales):
+    """codes x scale, in float64."""
+    return np.asarray(codes).astype(np.float64) * np.asarray(scales).astype(np.float64)[..., None]
+
+
+def int8_bytes_per_token_head(d: int) -> int:
+    """One byte per coordinate plus a float32 scale."""
+    return d + 4
 
 
 # ---------------------------------------------------------------------------
