@@ -36,6 +36,11 @@ WORKLOADS = {
     "c3_asym_16k": dict(batch=8, kv_heads=8, q_heads=32, head_dim=128, tokens=16384, layers=36,
                         k=("fp16", 0), v=("packed", 4), prefill=0, append=1, dist="channel",
                         outlier_frac=0.01),
+    # the pages' int8 mode (per-token absmax) at the asymmetric workload's
+    # shape, a comparison point; it runs the plain split kernel
+    "c3_int8_16k": dict(batch=8, kv_heads=8, q_heads=32, head_dim=128, tokens=16384, layers=36,
+                        k=("int8", 0), v=("int8", 0), prefill=0, append=1, dist="channel",
+                        outlier_frac=0.01),
     "c5_delegated_64k": dict(batch=16, kv_heads=4, q_heads=32, head_dim=128, tokens=65536, layers=48,
                              k=("fp16", 0), v=("delegated", 4), prefill=0, dist="channel",
                              outlier_frac=0.0, hot=256),
@@ -45,6 +50,8 @@ WORKLOADS = {
 def side_bytes_per_token(mode: str, bits: int, d: int) -> int:
     if mode == "fp16":
         return 2 * d
+    if mode == "int8":
+        return d + 4
     return 4 * ((bits * d + 31) // 32) + 4
 
 
@@ -91,24 +98,31 @@ def cpu_baseline(w, budget_s: float = 12.0):
     R = oracle.rotation_matrix(0, d)
     units, spent, nbytes = 0, 0.0, 0
     total_units = w["batch"] * w["kv_heads"]
+    def prepare(mode, bits, x):
+        """Storage of one side, built outside the timed part."""
+        if mode == "fp16":
+            return ("fp16", x)
+        if mode == "int8":
+            return ("int8",) + oracle.int8_quantize(x)
+        c, t = oracle.lloyd_max(d, bits)
+        codes, n, _ = oracle.quantize(x, R, t)
+        return ("packed", oracle.pack_codes(codes, bits), n.astype(np.float32), c, bits)
+
+    def rows(st):
+        """Rows the decode reads, rebuilt from the storage (timed)."""
+        if st[0] == "fp16":
+            return st[1].astype(np.float64)
+        if st[0] == "int8":
+            return oracle.int8_dequantize(st[1], st[2])
+        _, words, n, c, bits = st
+        return oracle.dequantize(oracle.unpack_codes(words, bits, d), n, R, c)
+
     while spent < budget_s and units < total_units:
         k, v = synth.kv_numpy(1000 + units, 1, 1, T, d, dist=w["dist"], outlier_frac=w["outlier_frac"])
         q = synth.q_numpy(1000 + units, 1, G, d)
-        kc, kt = oracle.lloyd_max(d, kb) if w["k"][0] != "fp16" else (None, None)
-        vc, vt = oracle.lloyd_max(d, vb)
-        # pre-quantize outside the timed part: the decode reads packed rows
-        if w["k"][0] != "fp16":
-            kcodes, kn, _ = oracle.quantize(k, R, kt)
-            kwords = oracle.pack_codes(kcodes, kb)
-        vcodes, vn, _ = oracle.quantize(v, R, vt)
-        vwords = oracle.pack_codes(vcodes, vb)
+        ks, vs = prepare(w["k"][0], kb, k), prepare(w["v"][0], vb, v)
         t0 = time.perf_counter()
-        if w["k"][0] != "fp16":
-            krows = oracle.dequantize(oracle.unpack_codes(kwords, kb, d), kn.astype(np.float32), R, kc)
-        else:
-            krows = k.astype(np.float64)
-        vrows = oracle.dequantize(oracle.unpack_codes(vwords, vb, d), vn.astype(np.float32), R, vc)
-        oracle.decode_attention(q, krows, vrows)
+        oracle.decode_attention(q, rows(ks), rows(vs))
         spent += time.perf_counter() - t0
         units += 1
         nbytes += (side_bytes_per_token(w["k"][0], kb, d) + side_bytes_per_token(w["v"][0], vb, d)) * T
@@ -218,7 +232,7 @@ def stats_summary(stats_csv: str, workload: str, cmds: list):
     w = WORKLOADS[workload]
     out = [f"# rocprofv3 kernel statistics, workload {workload}: batch {w['batch']}, {w['kv_heads']} KV heads, "
            f"{w['q_heads']} query heads, head_dim {w['head_dim']}, context {w['tokens']}, "
-           f"K {w['k'][0]}{w['k'][1] or ''}, V {w['v'][0]}{w['v'][1]}",
+           f"K {w['k'][0]}{w['k'][1] or ''}, V {w['v'][0]}{w['v'][1] or ''}",
            "# commands (from the repository root):"]
     out += [f"#   {c}" for c in cmds]
     out += [f"# decode algorithmic bytes per launch: {decode_bytes(w)}",
@@ -410,7 +424,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": B, "kv_heads": Hkv, "q_heads": Hq,
                    "head_dim": d, "context": T, "layers": Lyr,
-                   "k": f"{w['k'][0]}{w['k'][1] or ''}", "v": f"{w['v'][0]}{w['v'][1]}",
+                   "k": f"{w['k'][0]}{w['k'][1] or ''}", "v": f"{w['v'][0]}{w['v'][1] or ''}",
                    "append_per_layer": n_new, "block_size": bsz, "sparse_v": args.sparse_v},
         "hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4),
         "decode_us_per_layer": round(dec_avg_s * 1e6, 2),

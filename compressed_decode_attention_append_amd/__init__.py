@@ -29,7 +29,8 @@ TQ_ERR_HIP = -7
 SIDE_FP16 = 0
 SIDE_PACKED = 1
 SIDE_DELEGATED = 2
-_MODES = {"fp16": SIDE_FP16, "packed": SIDE_PACKED, "delegated": SIDE_DELEGATED}
+SIDE_INT8 = 3
+_MODES = {"fp16": SIDE_FP16, "packed": SIDE_PACKED, "delegated": SIDE_DELEGATED, "int8": SIDE_INT8}
 
 
 class TQError(RuntimeError):
@@ -234,7 +235,7 @@ class TQCache:
             self.desc.block_size, self.desc.max_blocks = bs, self.capacity // bs
         for name, spec, side in (("k", k, self.desc.k), ("v", v, self.desc.v)):
             side.mode = _MODES[spec.mode]
-            side.bits = int(spec.bits) if spec.mode != "fp16" else 0
+            side.bits = int(spec.bits) if spec.mode in ("packed", "delegated") else 0
             side.hot = int(spec.hot) if spec.mode == "delegated" else 0
             B, H, cap, d = self.batch, self.kv_heads, self.capacity, self.head_dim
             if self.paged:
@@ -248,6 +249,13 @@ class TQCache:
                 side.thresholds = cb.thresholds.ctypes.data
                 W = row_words(d, spec.bits)
                 codes = torch.zeros((B, H, cap, W), dtype=torch.int32, device=device)
+                norms = torch.zeros((B, H, cap), dtype=torch.float32, device=device)
+                side.codes, side.norms = _ptr(codes), _ptr(norms)
+                self.tensors[name + "_codes"] = codes
+                self.tensors[name + "_norms"] = norms
+            if spec.mode == "int8":
+                # codes: d int8 a row as d / 4 words; norms: the per-row scale
+                codes = torch.zeros((B, H, cap, d // 4), dtype=torch.int32, device=device)
                 norms = torch.zeros((B, H, cap), dtype=torch.float32, device=device)
                 side.codes, side.norms = _ptr(codes), _ptr(norms)
                 self.tensors[name + "_codes"] = codes

@@ -39,6 +39,8 @@ int check_side(const tq_side &s, bool is_v) {
   switch (s.mode) {
     case TQ_SIDE_FP16:
       return s.fp16 ? TQ_OK : TQ_ERR_ARG;
+    case TQ_SIDE_INT8:
+      return (s.codes && s.norms) ? TQ_OK : TQ_ERR_ARG;
     case TQ_SIDE_PACKED:
     case TQ_SIDE_DELEGATED:
       if (s.mode == TQ_SIDE_DELEGATED && !is_v) return TQ_ERR_MODE;
@@ -79,8 +81,8 @@ tq::Paging paging_of(const tq_cache *c) {
 tq::SideDev side_dev(const tq_side &s, int d) {
   tq::SideDev o;
   o.mode = s.mode;
-  o.bits = (s.mode == TQ_SIDE_FP16) ? 0 : s.bits;
-  o.words = (s.mode == TQ_SIDE_FP16) ? 0 : words_of(d, s.bits);
+  o.bits = (s.mode == TQ_SIDE_FP16) ? 0 : (s.mode == TQ_SIDE_INT8 ? 8 : s.bits);
+  o.words = (s.mode == TQ_SIDE_FP16) ? 0 : words_of(d, o.bits);
   o.hot = s.hot;
   o.codes = s.codes;
   o.norms = s.norms;
@@ -88,9 +90,15 @@ tq::SideDev side_dev(const tq_side &s, int d) {
   return o;
 }
 
+// Codebook levels of a side: 2^bits for the TurboQuant modes, none for fp16
+// and INT8 sides (whose bit field is not read).
+int n_levels(const tq_side &s) {
+  return (s.mode == TQ_SIDE_PACKED || s.mode == TQ_SIDE_DELEGATED) ? (1 << s.bits) : 0;
+}
+
 void copy_levels(const tq_side &s, const float *src, int n, float *dst) {
   for (int i = 0; i < tq::kMaxLevels; ++i) dst[i] = 0.0f;
-  if (s.mode != TQ_SIDE_FP16 && src) memcpy(dst, src, sizeof(float) * n);
+  if ((s.mode == TQ_SIDE_PACKED || s.mode == TQ_SIDE_DELEGATED) && src) memcpy(dst, src, sizeof(float) * n);
 }
 
 // Context split of the plain decode: the block keeps G * (d + split) floats
@@ -176,8 +184,8 @@ void fill_decode_params(const tq_cache *cache, const void *q, int q_heads, int l
   p->length = length;
   p->pg = paging_of(cache);
   fill_signs(cache->seed, d, p->sign);
-  copy_levels(cache->k, cache->k.centroids, 1 << cache->k.bits, p->k_cent);
-  copy_levels(cache->v, cache->v.centroids, 1 << cache->v.bits, p->v_cent);
+  copy_levels(cache->k, cache->k.centroids, n_levels(cache->k), p->k_cent);
+  copy_levels(cache->v, cache->v.centroids, n_levels(cache->v), p->v_cent);
   p->share_lut = (cache->k.mode == TQ_SIDE_PACKED && cache->k.bits == 4 && cache->v.bits == 4 &&
                   memcmp(p->k_cent, p->v_cent, sizeof(float) * 16) == 0)
                      ? 1
@@ -269,8 +277,8 @@ int tq_quantize_append(const tq_cache *cache, const void *k_new, const void *v_n
   p.pg = paging_of(cache);
   p.side_mask = 3;
   fill_signs(cache->seed, d, p.sign);
-  copy_levels(cache->k, cache->k.thresholds, (1 << cache->k.bits) - 1, p.k_thr);
-  copy_levels(cache->v, cache->v.thresholds, (1 << cache->v.bits) - 1, p.v_thr);
+  copy_levels(cache->k, cache->k.thresholds, n_levels(cache->k) - 1, p.k_thr);
+  copy_levels(cache->v, cache->v.thresholds, n_levels(cache->v) - 1, p.v_thr);
   const hipError_t e = tq::launch_quantize_append(p, static_cast<hipStream_t>(hip_stream));
   return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
@@ -343,7 +351,7 @@ int tq_dequantize(const tq_cache *cache, int side, int start, int count, float *
   p.count = count;
   p.pg = paging_of(cache);
   fill_signs(cache->seed, d, p.sign);
-  copy_levels(s, s.centroids, 1 << s.bits, p.cent);
+  copy_levels(s, s.centroids, n_levels(s), p.cent);
   const hipError_t e = tq::launch_dequantize(p, static_cast<hipStream_t>(hip_stream));
   return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }

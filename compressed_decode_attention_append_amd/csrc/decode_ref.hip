@@ -104,6 +104,11 @@ __global__ __launch_bounds__(kBlock) void decode_split_kernel(const DecodeParams
       const uint32_t *row = p.k.codes + cache_row(p.pg, bk, t, p.capacity) * p.k.words;
       for (int j = 0; j < D; ++j) acc += qr[h * D + j] * ck[extract_code(row, p.k.bits, j)];
       acc *= p.k.norms[cache_row(p.pg, bk, t, p.capacity)];
+    } else if (p.k.mode == TQ_SIDE_INT8) {
+      // INT8 rows: q . code times the row's scale (original domain)
+      const uint32_t *row = p.k.codes + cache_row(p.pg, bk, t, p.capacity) * p.k.words;
+      for (int j = 0; j < D; ++j) acc += qr[h * D + j] * int8_at(row[j >> 2], j);
+      acc *= p.k.norms[cache_row(p.pg, bk, t, p.capacity)];
     } else {
       const uint16_t *row = p.k.fp16 + cache_row(p.pg, bk, t, p.capacity) * D;
       for (int j = 0; j < D; ++j) acc += qr[h * D + j] * h2f(row[j]);
@@ -146,6 +151,9 @@ __global__ __launch_bounds__(kBlock) void decode_split_kernel(const DecodeParams
       const uint16_t *vrow = v_plain_row(p, bk, t);
       if (vrow) {
         plain += w * h2f(vrow[j]);
+      } else if (p.v.mode == TQ_SIDE_INT8) {
+        const uint32_t *row = p.v.codes + cache_row(p.pg, bk, t, p.capacity) * p.v.words;
+        plain += w * p.v.norms[cache_row(p.pg, bk, t, p.capacity)] * int8_at(row[j >> 2], j);
       } else {
         const uint32_t *row = p.v.codes + cache_row(p.pg, bk, t, p.capacity) * p.v.words;
         rot += w * p.v.norms[cache_row(p.pg, bk, t, p.capacity)] * cv[extract_code(row, p.v.bits, j)];

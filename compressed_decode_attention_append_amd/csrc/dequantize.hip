@@ -27,6 +27,16 @@ __global__ __launch_bounds__(kBlock) void dequantize_kernel(const DequantParams 
   const long bh = r / p.count;
   const int pos = p.start + static_cast<int>(r % p.count);
   const uint32_t *row = p.s.codes + cache_row(p.pg, bh, pos, p.capacity) * p.s.words;
+  if (p.s.mode == TQ_SIDE_INT8) {
+    // INT8 rows: code times the row's scale, no rotation
+    const uint32_t w = row[t];
+    const float sc = p.s.norms[cache_row(p.pg, bh, pos, p.capacity)];
+    if (live) {
+      const float4 o = make_float4(int8_at(w, 0) * sc, int8_at(w, 1) * sc, int8_at(w, 2) * sc, int8_at(w, 3) * sc);
+      *reinterpret_cast<float4 *>(p.out + r * D + 4 * t) = o;
+    }
+    return;
+  }
   float v[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) v[e] = cent[extract_code(row, p.s.bits, 4 * t + e)];

@@ -71,6 +71,30 @@ __device__ __forceinline__ void encode_row(const float (&x)[4], int t,
   }
 }
 
+// INT8 per-token absmax (mlxcel "TurboQuant KV cache", "Available modes"):
+// scale = max|x| / 127, code = x / scale rounded to the nearest integer
+// (ties to even), clamped to [-127, 127]; float32 throughout.  Lane t writes
+// word t of the row (its four codes, coordinate 4 t + e in byte e).
+template <int D>
+__device__ __forceinline__ void encode_int8(const float (&x)[4], int t, bool write, uint32_t *row_out,
+                                            float *scale_out) {
+  constexpr int TPR = D / 4;
+  float a = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+  a = group_max<TPR>(a);
+  const float scale = a / 127.0f;
+  uint32_t w = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float v = scale > 0.0f ? x[e] / scale : 0.0f;
+    const int c = min(127, max(-127, static_cast<int>(rintf(v))));
+    w |= (static_cast<uint32_t>(c) & 0xffu) << (8 * e);
+  }
+  if (write) {
+    row_out[t] = w;
+    if (t == 0) *scale_out = scale;
+  }
+}
+
 template <int D>
 __device__ __forceinline__ void load4(const uint16_t *src, int t, float (&x)[4]) {
   const uint2 raw = *reinterpret_cast<const uint2 *>(src + 4 * t);
@@ -112,7 +136,12 @@ __global__ __launch_bounds__(kBlock) void quantize_append_kernel(const QuantizeP
   const uint16_t *src = (side ? p.v_new : p.k_new) + (bh * p.n_new + i) * D;
   const float *th = thr[side];
 
-  if (s.mode == TQ_SIDE_PACKED) {
+  if (s.mode == TQ_SIDE_INT8) {
+    float x[4];
+    load4<D>(src, t, x);
+    encode_int8<D>(x, t, live, s.codes + cache_row(p.pg, bh, pos, p.capacity) * s.words,
+                   s.norms + cache_row(p.pg, bh, pos, p.capacity));
+  } else if (s.mode == TQ_SIDE_PACKED) {
     float x[4];
     load4<D>(src, t, x);
     encode_row<D>(x, t, p.sign, th, s.bits, s.words, live,

@@ -51,6 +51,19 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Maximum over the TPR lanes of a group (all lanes receive it).
+template <int TPR>
+__device__ __forceinline__ float group_max(float x) {
+#pragma unroll
+  for (int m = 1; m < TPR; m <<= 1) x = fmaxf(x, __shfl_xor(x, m));
+  return x;
+}
+
+// Signed byte j % 4 of word w, as a float (INT8 rows: coordinate j in byte j).
+__device__ __forceinline__ float int8_at(uint32_t w, int j) {
+  return static_cast<float>(static_cast<int8_t>((w >> (8 * (j & 3))) & 0xffu));
+}
+
 // Number of thresholds strictly below y: branch-free binary search over the
 // ascending array thr[0 .. 2^bits - 2].
 __device__ __forceinline__ int count_below(const float *thr, int bits, float y) {

@@ -18,8 +18,9 @@ What it follows:
   ("TurboQuant KV Cache Quantization in MLX-VLM", "Programmatic API
   Integration", passes ``quantized_kv_start`` to the generation loop.)
 * mlxcel "TurboQuant KV cache": "Available modes" (the user-facing mode names:
-  fp16, turbo4 / turbo4-sym, fp16+turbo4 / turbo4-asym, turbo4-delegated,
-  fp16+turbo3 / turbo3-asym / turbo3; symmetric 3-bit is not offered), "CLI
+  fp16, int8, turbo4 / turbo4-sym, fp16+turbo4 / turbo4-asym,
+  turbo4-delegated, fp16+turbo3 / turbo3-asym / turbo3; symmetric 3-bit is
+  not offered), "CLI
   and server flags" (the supported K/V split-flag combinations) and
   "Boundary-V layer protection" (``--turbo-boundary-v N``: the first N and
   last N layers keep their V cache in fp16 while a Turbo mode is active).
@@ -30,7 +31,8 @@ Readings where the pages leave a step open:
   a 256-position hot window, the window of the delegated configuration here.
 * With boundary-V a layer keeps its mode's K side; if that is fp16 too, the
   layer stays wholly full precision.
-* ``int8`` is not TurboQuant and is rejected here.
+* ``int8`` is the per-token absmax cache on both sides (no rotation or
+  codebook); boundary-V gives its boundary layers an fp16 V.
 """
 from __future__ import annotations
 
@@ -45,6 +47,7 @@ DEFAULT_HOT = 256
 # user-facing mode name -> (K side, V side); None = the layer stays fp16
 _NAMED = {
     "fp16": None,
+    "int8": (SideSpec("int8", 0), SideSpec("int8", 0)),
     "turbo4": (SideSpec("packed", 4), SideSpec("packed", 4)),
     "turbo4-sym": (SideSpec("packed", 4), SideSpec("packed", 4)),
     "fp16+turbo4": (SideSpec("fp16", 0), SideSpec("packed", 4)),
@@ -97,8 +100,6 @@ def mode_sides(mode: Union[str, float, int], hot: int = DEFAULT_HOT) -> Sides:
         kb, vb = split_bits(mode)
         return SideSpec("packed", kb), SideSpec("packed", vb)
     name = str(mode).strip().lower()
-    if name == "int8":
-        raise ValueError("int8 is a per-token absmax cache, not a TurboQuant mode")
     if name not in _NAMED:
         raise ValueError(f"unknown cache mode {mode!r}; known: {', '.join(sorted(_NAMED))}")
     sides = _NAMED[name]

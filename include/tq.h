@@ -62,8 +62,13 @@ enum {
 enum {
   TQ_SIDE_FP16 = 0,      /* plain fp16 rows                                 */
   TQ_SIDE_PACKED = 1,    /* TurboQuant codes + fp32 norms                   */
-  TQ_SIDE_DELEGATED = 2  /* V only: newest `hot` tokens fp16 in a ring
+  TQ_SIDE_DELEGATED = 2, /* V only: newest `hot` tokens fp16 in a ring
                             (slot = position mod hot), older tokens packed  */
+  TQ_SIDE_INT8 = 3       /* per-token INT8 absmax (mlxcel "TurboQuant KV cache",
+                            "Available modes"): codes int8 [B][Hkv][capacity][d]
+                            in `codes` (d / 4 words a row, coordinate j in byte
+                            j), the per-row scale max|x| / 127 in `norms`; no
+                            rotation, codebook or bit width (bits ignored)     */
 };
 
 #define TQ_MIN_BITS 1

@@ -238,3 +238,18 @@ def test_sparse_v_threshold_errors():
         r = tq.lib().tq_decode_attention_sparse(ctypes.byref(c), f.p(4096), 8, 100, 0, tau, f.p(8192), None,
                                                 f.p(0), 1 << 30, None)
         assert r == tq.TQ_ERR_ARG, tau
+
+
+def test_int8_side_arguments():
+    # an INT8 side needs its codes and scales; its bit field is not read
+    f = _Fake()
+    c = _desc(f, kmode=3, vmode=3, kb=0, vb=77)
+    assert _qa(c, f, n=0) == tq.TQ_OK
+    assert tq.lib().tq_decode_workspace_bytes(ctypes.byref(c), 8, 100, 0) > 0
+    c.k.codes = None
+    assert _qa(c, f, n=0) == tq.TQ_ERR_ARG
+    c = _desc(f, kmode=0, vmode=3)
+    c.v.norms = None
+    assert _qa(c, f, n=0) == tq.TQ_ERR_ARG
+    # delegated stays V-only; INT8 K with a delegated V is fine
+    assert _qa(_desc(f, kmode=3, vmode=2), f, n=0) == tq.TQ_OK

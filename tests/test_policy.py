@@ -36,6 +36,7 @@ def test_split_bits_out_of_range(bits):
 # mlxcel "Available modes"
 @pytest.mark.parametrize("name,want", [
     ("fp16", None),
+    ("int8", _sides("int8", 0, "int8", 0)),
     ("turbo4", _sides("packed", 4, "packed", 4)),
     ("turbo4-sym", _sides("packed", 4, "packed", 4)),
     ("fp16+turbo4", _sides("fp16", 0, "packed", 4)),
@@ -56,7 +57,7 @@ def test_delegated_hot_window():
     assert P.mode_sides("turbo4-delegated")[1].hot == 256
 
 
-@pytest.mark.parametrize("name", ["int8", "turbo5", "turbo3-sym", ""])
+@pytest.mark.parametrize("name", ["turbo5", "turbo3-sym", "int4", ""])
 def test_rejected_modes(name):
     with pytest.raises(ValueError):
         P.mode_sides(name)
