@@ -31,6 +31,9 @@ WORKLOADS = {
     "c4_tq35_32k": dict(batch=4, kv_heads=8, q_heads=32, head_dim=128, tokens=32768, layers=36,
                         k=("packed", 3), v=("packed", 4), prefill=8192, dist="channel",
                         outlier_frac=0.01),
+    # the small parity case: quantize all 256 positions, then one decode step
+    "c1_tq35_d64_256": dict(batch=1, kv_heads=2, q_heads=4, head_dim=64, tokens=256, layers=1,
+                            k=("packed", 3), v=("packed", 4), prefill=256, dist="iid", outlier_frac=0.0),
     "c2_sym4_4k": dict(batch=1, kv_heads=8, q_heads=32, head_dim=128, tokens=4096, layers=36,
                        k=("packed", 4), v=("packed", 4), prefill=0, dist="channel", outlier_frac=0.01),
     "c3_asym_16k": dict(batch=8, kv_heads=8, q_heads=32, head_dim=128, tokens=16384, layers=36,

@@ -101,25 +101,22 @@ void copy_levels(const tq_side &s, const float *src, int n, float *dst) {
   if ((s.mode == TQ_SIDE_PACKED || s.mode == TQ_SIDE_DELEGATED) && src) memcpy(dst, src, sizeof(float) * n);
 }
 
-// Context split of the plain decode: the block keeps G * (d + split) floats
-// in LDS, so the split length shrinks as the query group grows.
-int ref_max_split(int G, int d) {
-  const int budget = 16384 - 2 * tq::kMaxLevels - 4;
-  return budget / G - d;
-}
-
+// Context split of the plain decode.  A block walks its range in tiles of 32
+// positions for up to eight query heads; the automatic split aims at about
+// 2048 blocks (eight per compute unit) in whole tiles.  Any split length
+// fits the block's LDS.
 bool choose_split(const tq_cache *c, int q_heads, int length, int n_splits, int *ns, int *sl) {
+  constexpr long kTargetBlocks = 2048;
+  constexpr int kTile = 32;
   const int G = q_heads / c->kv_heads;
-  const int cap = ref_max_split(G, c->head_dim);
-  if (cap < 1) return false;
   int split;
   if (n_splits > 0) {
     split = length > 0 ? (length + n_splits - 1) / n_splits : 1;
-    if (split > cap) return false;
     *ns = n_splits;
   } else {
-    split = std::min(cap, 1024);
-    split = split >= 64 ? split / 64 * 64 : split;
+    const long per_split = static_cast<long>(c->batch) * c->kv_heads * ((G + 7) / 8);
+    const long want = (static_cast<long>(length) * per_split + kTargetBlocks - 1) / kTargetBlocks;
+    split = static_cast<int>(std::max<long>(kTile, (want + kTile - 1) / kTile * kTile));
     *ns = length > 0 ? (length + split - 1) / split : 1;
   }
   *sl = std::max(split, 1);

@@ -1,19 +1,30 @@
 // Decode attention straight from the packed cache: the plain split-context
 // variant ("TurboQuant KV Cache Quantization in MLX-VLM", "How TurboQuant KV
 // Cache Quantization Works": scores from the compressed representation; FAQ
-// on dequantization: the stored rotation and codebooks).
+// on dequantization: the stored rotation and codebooks).  It serves every
+// cache layout the matrix-core kernel does not: head_dim other than 128,
+// INT8 sides, paged delegated caches.
 //
-// Grid (n_splits, B * Hkv); one block handles the G query heads of one KV
-// head over one contiguous range of positions:
+// Grid (n_splits, B * Hkv, head groups); one block handles up to eight query
+// heads of one KV head over one contiguous range of positions:
 //   1. q is rotated once: R q = H diag(s) q / sqrt(d) by butterflies in LDS;
 //      the softmax scale 1/sqrt(d) and log2(e) are folded in.
-//   2. score of position i: n_i <R q, c[code_i]> (packed K) or q . k_i
-//      (fp16 K), one thread per (position, head).
-//   3. running max and sum per head (base-2 exponent).
-//   4. value accumulation, one thread per (head, coordinate): packed rows
-//      accumulate p_i n_i c[code_i,j] in the rotated domain; fp16 rows (fp16
-//      V, or the delegated hot window) accumulate p_i v_ij as they are.
-//   5. partial (max, sum, rotated sum, plain sum) to the workspace.
+//   2. the range is walked in tiles of 32 positions.  Each tile's K and V
+//      rows (packed codes, INT8 codes or fp16, as stored) are copied to LDS
+//      with row-contiguous loads, 16 bytes a lane where rows allow it; the
+//      next tile's loads are in flight while the current one is computed.
+//   3. scores from the LDS rows: n_i <R q, c[code_i]> (packed K), s_i q .
+//      code_i (INT8 K) or q . k_i (fp16 K).  A lane takes one position and
+//      an eighth of the coordinates for every head of the block; the eight
+//      partial sums are added in the softmax step.
+//   4. online softmax per head (base-2 exponent): the running maximum and
+//      sum, and the factor that rescales the accumulators.
+//   5. value accumulation: a lane owns one coordinate j for every head and
+//      takes every (256 / d)-th position of the tile.  Packed rows add
+//      p_i n_i c[code_i,j] in the rotated domain; fp16 rows (fp16 V, the
+//      delegated hot window) add p_i v_ij and INT8 rows p_i s_i code_ij in
+//      the original domain.  The lane groups' sums are added at the end.
+//   6. partial (max, sum, rotated sum, plain sum) to the workspace.
 // A second kernel merges the splits by their maxima, applies the inverse
 // rotation diag(s) H / sqrt(d) once per output head, adds the plain part and
 // divides by the sum.
@@ -26,62 +37,255 @@ namespace tq {
 namespace {
 
 constexpr int kBlock = 256;
+constexpr int kTile = 32;           // positions staged per step
+constexpr int kMaxGroupHeads = 8;   // query heads per block
+constexpr int kScoreParts = kBlock / kTile;  // lanes per position in the score step
 
-__device__ __forceinline__ float block_reduce(float x, float *red, bool is_max) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int m = 32; m >= 1; m >>= 1) {
-    const float o = __shfl_xor(x, m);
-    x = is_max ? fmaxf(x, o) : x + o;
-  }
-  __syncthreads();
-  if (lane == 0) red[wave] = x;
-  __syncthreads();
-  float r = red[0];
-  for (int w = 1; w < kBlock / 64; ++w) r = is_max ? fmaxf(r, red[w]) : r + red[w];
-  return r;
-}
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-// Is V row `t` served from fp16 storage?  Returns the fp16 row or null.
-__device__ __forceinline__ const uint16_t *v_plain_row(const DecodeParams &p, long bk, int t) {
-  const int D = p.head_dim;
-  if (p.v.mode == TQ_SIDE_FP16) return p.v.fp16 + cache_row(p.pg, bk, t, p.capacity) * D;
-  if (p.v.mode == TQ_SIDE_DELEGATED && t >= p.length - p.v.hot)
-    return p.v.fp16 + (bk * p.v.hot + (t % p.v.hot)) * D;
-  return nullptr;
-}
+// LDS plan of one block (offsets in 32-bit words).  Row strides are odd so
+// that the same word of consecutive rows falls in different banks.  HB is
+// the head count the block's arrays are sized for (1, 2, 4 or 8, at least
+// its gb heads); unused heads carry zero weights.
+struct RefLayout {
+  int gb, ngroups, hb;      // query heads per block, blocks per KV head, array heads
+  int kw, vw_cold, vw_hot;  // words of a staged K row, packed / INT8 V row, fp16 V row
+  int sk, sv;               // LDS row strides
+  int qr, sp, pw, kt, vt, kn, vn, ck, cv, al, total;
+};
 
-template <int D>
-__global__ __launch_bounds__(kBlock) void decode_split_kernel(const DecodeParams p) {
-  extern __shared__ float smem[];
+__host__ __device__ inline RefLayout ref_layout(const DecodeParams &p, int D) {
+  RefLayout L;
   const int G = p.q_heads / p.kv_heads;
-  const int SL = p.split_len;
-  float *qr = smem;                  // [G][D]
-  float *sc = qr + G * D;            // [G][SL]
-  float *ck = sc + G * SL;           // [256]
-  float *cv = ck + kMaxLevels;       // [256]
-  float *red = cv + kMaxLevels;      // [4]
+  L.ngroups = (G + kMaxGroupHeads - 1) / kMaxGroupHeads;
+  L.gb = (G + L.ngroups - 1) / L.ngroups;
+  L.hb = L.gb <= 1 ? 1 : (L.gb <= 2 ? 2 : (L.gb <= 4 ? 4 : 8));
+  L.kw = p.k.mode == TQ_SIDE_FP16 ? D / 2 : p.k.words;
+  L.vw_cold = p.v.mode == TQ_SIDE_FP16 ? D / 2 : p.v.words;
+  L.vw_hot = (p.v.mode == TQ_SIDE_FP16 || p.v.mode == TQ_SIDE_DELEGATED) ? D / 2 : L.vw_cold;
+  L.sk = L.kw | 1;
+  L.sv = (L.vw_cold > L.vw_hot ? L.vw_cold : L.vw_hot) | 1;
+  int o = 0;
+  L.qr = o; o += L.hb * D;                 // rotated, scaled queries [head][d]
+  L.sp = o; o += kBlock * L.hb;            // partial scores [part][head][pos] (8 x 32 x hb);
+                                           // at the end the value sums [lane group][head][d]
+                                           // (256 / d x hb x d)
+  L.pw = o; o += kTile * L.hb;             // weight times the V row's norm or scale [pos][head]
+  L.kt = o; o += kTile * L.sk;             // K tile
+  L.vt = o; o += kTile * L.sv;             // V tile
+  L.kn = o; o += kTile;                    // K norms / scales (1 for fp16 rows)
+  L.vn = o; o += kTile;                    // V norms / scales (1 for fp16 rows)
+  L.ck = o; o += kMaxLevels;               // centroids
+  L.cv = o; o += kMaxLevels;
+  L.al = o; o += kMaxGroupHeads;           // per-head rescale factor of the tile
+  L.total = o;
+  return L;
+}
 
+// First position served from fp16 storage: all of an fp16 V, the hot window
+// of a delegated V, none otherwise.
+__device__ __forceinline__ int v_hot_start(const DecodeParams &p) {
+  if (p.v.mode == TQ_SIDE_FP16) return 0;
+  if (p.v.mode == TQ_SIDE_DELEGATED) return p.length - p.v.hot;
+  return 0x7fffffff;
+}
+
+// Start of piece `piece` (GW words) of the stored row of position t, or null
+// where that row kind is shorter (the cold rows of a delegated V).
+template <int D, int GW>
+__device__ __forceinline__ const uint32_t *piece_src(const DecodeParams &p, const RefLayout &L, long bk, int t,
+                                                     bool is_k, int piece, int hot_start) {
+  const uint32_t *src;
+  if (is_k) {
+    src = p.k.mode == TQ_SIDE_FP16
+              ? reinterpret_cast<const uint32_t *>(p.k.fp16 + cache_row(p.pg, bk, t, p.capacity) * D)
+              : p.k.codes + cache_row(p.pg, bk, t, p.capacity) * p.k.words;
+  } else if (t >= hot_start) {
+    if (piece * GW >= L.vw_hot) return nullptr;
+    src = p.v.mode == TQ_SIDE_FP16
+              ? reinterpret_cast<const uint32_t *>(p.v.fp16 + cache_row(p.pg, bk, t, p.capacity) * D)
+              : reinterpret_cast<const uint32_t *>(p.v.fp16 + (bk * p.v.hot + t % p.v.hot) * D);
+  } else {
+    if (piece * GW >= L.vw_cold) return nullptr;
+    src = p.v.codes + cache_row(p.pg, bk, t, p.capacity) * p.v.words;
+  }
+  return src + piece * GW;
+}
+
+// Copy of one tile's K and V rows from HBM to LDS.  The tile is cut into
+// GW-word pieces, K rows first; lane l owns pieces l + 256 u.  For the first
+// four (u < 4, every piece of a tile at head_dim <= 128 with 16-byte loads)
+// the row, the piece and the LDS offset are the same for every tile, so they
+// are worked out once, and the loads of the next tile are issued before the
+// current one is scored and stored after it, so HBM latency overlaps
+// compute.  Pieces beyond those (fp16 rows at head_dim 256, 4-byte loads)
+// are copied when the tile is stored.
+template <int D, int GW>
+struct Stager {
+  static constexpr int kSlots = 4;
+  u32x4_t buf[kSlots];
+  int row[kSlots];      // tile row of the piece, -1 = no piece
+  int piece[kSlots];    // piece index within the row
+  int dst[kSlots];      // LDS word offset
+  bool is_k[kSlots];
+  bool live[kSlots];    // the piece was loaded for the current tile
+  float norm;           // lanes 0..31: K norm, 64..95: V norm of the tile row
+  int norm_dst;         // LDS word offset of that norm, -1 = none
+  int kg, vg;           // pieces per K row, per V row (the longer kind)
+  int tb, nt;           // the loaded tile
+
+  __device__ void init(const RefLayout &L) {
+    const int tid = threadIdx.x;
+    kg = L.kw / GW;
+    const int vgc = L.vw_cold / GW, vgh = L.vw_hot / GW;
+    vg = vgc > vgh ? vgc : vgh;
+#pragma unroll
+    for (int u = 0; u < kSlots; ++u) {
+      const int i = tid + u * kBlock;
+      row[u] = -1;
+      if (i < kTile * (kg + vg)) {
+        is_k[u] = i < kTile * kg;
+        const int ii = is_k[u] ? i : i - kTile * kg;
+        const int per = is_k[u] ? kg : vg;
+        row[u] = ii / per;
+        piece[u] = ii - row[u] * per;
+        dst[u] = (is_k[u] ? L.kt + row[u] * L.sk : L.vt + row[u] * L.sv) + piece[u] * GW;
+      }
+    }
+    norm_dst = tid < kTile ? L.kn + tid : ((tid >= 64 && tid < 64 + kTile) ? L.vn + tid - 64 : -1);
+  }
+
+  // Issue the loads of positions [t, t + n).
+  __device__ void load(const DecodeParams &p, const RefLayout &L, long bk, int t, int n, int hot_start) {
+    const int tid = threadIdx.x;
+    tb = t;
+    nt = n;
+#pragma unroll
+    for (int u = 0; u < kSlots; ++u) {
+      live[u] = false;
+      if (row[u] >= 0 && row[u] < n) {
+        const uint32_t *src = piece_src<D, GW>(p, L, bk, t + row[u], is_k[u], piece[u], hot_start);
+        if (src) {
+          if (GW == 4) {
+            buf[u] = *reinterpret_cast<const u32x4_t *>(src);
+          } else {
+            buf[u].x = *src;
+          }
+          live[u] = true;
+        }
+      }
+    }
+    norm = 1.0f;
+    if (tid < n) {
+      if (p.k.mode != TQ_SIDE_FP16) norm = p.k.norms[cache_row(p.pg, bk, t + tid, p.capacity)];
+    } else if (tid >= 64 && tid < 64 + n && t + tid - 64 < hot_start) {
+      norm = p.v.norms[cache_row(p.pg, bk, t + tid - 64, p.capacity)];
+    }
+  }
+
+  // Write the loaded tile to LDS (waits for its loads), and copy the pieces
+  // beyond the lanes' slots.
+  __device__ void store(const DecodeParams &p, const RefLayout &L, long bk, int hot_start, uint32_t *lds) {
+#pragma unroll
+    for (int u = 0; u < kSlots; ++u) {
+      if (live[u]) {
+        lds[dst[u]] = buf[u].x;
+        if (GW == 4) {
+          lds[dst[u] + 1] = buf[u].y;
+          lds[dst[u] + 2] = buf[u].z;
+          lds[dst[u] + 3] = buf[u].w;
+        }
+      }
+    }
+    if (norm_dst >= 0) reinterpret_cast<float *>(lds)[norm_dst] = norm;
+    for (int i = threadIdx.x + kSlots * kBlock; i < kTile * (kg + vg); i += kBlock) {
+      const bool k = i < kTile * kg;
+      const int ii = k ? i : i - kTile * kg;
+      const int per = k ? kg : vg;
+      const int r = ii / per, pc = ii - r * per;
+      if (r >= nt) continue;
+      const uint32_t *src = piece_src<D, GW>(p, L, bk, tb + r, k, pc, hot_start);
+      if (!src) continue;
+      const int o = (k ? L.kt + r * L.sk : L.vt + r * L.sv) + pc * GW;
+#pragma unroll
+      for (int e = 0; e < GW; ++e) lds[o + e] = src[e];
+    }
+  }
+};
+
+// fp16 element j of a row held as 32-bit words.
+__device__ __forceinline__ float half_at(const uint32_t *row, int j) {
+  return h2f(static_cast<uint16_t>(row[j >> 1] >> (16 * (j & 1))));
+}
+
+// Value sums of one run of positions (every TS-th from `first` below
+// `end`) for one coordinate j and all HB heads: acc[h] += w[pos][h] * value.
+// KIND 0: packed rows (centroid of the code), 1: INT8 rows (the code), 2:
+// fp16 rows.
+template <int D, int HB, int KIND>
+__device__ __forceinline__ void accumulate(float (&acc)[HB], const uint32_t *vt, int sv, const float *pw,
+                                           const float *cv, int bits, int j, int first, int end) {
+  constexpr int TS = kBlock / D;
+#pragma unroll 4
+  for (int tok = first; tok < end; tok += TS) {
+    const uint32_t *row = vt + tok * sv;
+    float x;
+    if (KIND == 0) {
+      x = cv[extract_code(row, bits, j)];
+    } else if (KIND == 1) {
+      x = int8_at(row[j >> 2], j);
+    } else {
+      x = half_at(row, j);
+    }
+    const float *w = pw + tok * HB;
+#pragma unroll
+    for (int h = 0; h < HB; ++h) acc[h] += w[h] * x;
+  }
+}
+
+// GW: words per staging load (4 = 16-byte loads; the host picks 4 when every
+// row kind is a multiple of 16 bytes and the storage is 16-byte aligned).
+// HB: heads the per-lane arrays hold (>= the block's heads).
+template <int D, int GW, int HB>
+__global__ __launch_bounds__(kBlock) void decode_split_kernel(const DecodeParams p) {
+  extern __shared__ __align__(16) uint32_t lds[];
+  const RefLayout L = ref_layout(p, D);
+  float *qr = reinterpret_cast<float *>(lds + L.qr);
+  float *sp = reinterpret_cast<float *>(lds + L.sp);
+  float *pw = reinterpret_cast<float *>(lds + L.pw);
+  const uint32_t *kt = lds + L.kt;
+  const uint32_t *vt = lds + L.vt;
+  const float *kn = reinterpret_cast<const float *>(lds + L.kn);
+  const float *vn = reinterpret_cast<const float *>(lds + L.vn);
+  float *ck = reinterpret_cast<float *>(lds + L.ck);
+  float *cv = reinterpret_cast<float *>(lds + L.cv);
+  float *al = reinterpret_cast<float *>(lds + L.al);
+
+  const int tid = threadIdx.x;
+  const int G = p.q_heads / p.kv_heads;
   const int split = blockIdx.x;
   const long bk = blockIdx.y;
+  const int g0 = blockIdx.z * L.gb;
+  const int gn = min(L.gb, G - g0);  // query heads of this block, 1 <= gn <= HB
   const int b = static_cast<int>(bk / p.kv_heads), kv = static_cast<int>(bk % p.kv_heads);
-  const int t0 = split * SL;
-  const int t1 = min(p.length, t0 + SL);
-  const int n = max(0, t1 - t0);
-  const long hq0 = static_cast<long>(b) * p.q_heads + static_cast<long>(kv) * G;
+  const int t0 = split * p.split_len;
+  const int t1 = min(p.length, t0 + p.split_len);
+  const long hq0 = static_cast<long>(b) * p.q_heads + static_cast<long>(kv) * G + g0;
+  const int hot_start = v_hot_start(p);
 
-  for (int i = threadIdx.x; i < kMaxLevels; i += kBlock) {
+  for (int i = tid; i < kMaxLevels; i += kBlock) {
     ck[i] = p.k_cent[i];
     cv[i] = p.v_cent[i];
   }
   const bool k_packed = p.k.mode == TQ_SIDE_PACKED;
-  for (int i = threadIdx.x; i < G * D; i += kBlock) {
-    const float x = h2f(p.q[hq0 * D + i]);
+  for (int i = tid; i < HB * D; i += kBlock) {
+    const float x = i < gn * D ? h2f(p.q[hq0 * D + i]) : 0.0f;
     qr[i] = k_packed ? x * sign_of(p.sign, i % D) : x;
   }
   __syncthreads();
   if (k_packed) {
     for (int s = 1; s < D; s <<= 1) {
-      for (int i = threadIdx.x; i < G * D / 2; i += kBlock) {
+      for (int i = tid; i < gn * D / 2; i += kBlock) {
         const int h = i / (D / 2), r = i % (D / 2);
         const int j = (r / s) * 2 * s + (r % s);
         const float a = qr[h * D + j], c = qr[h * D + j + s];
@@ -93,75 +297,145 @@ __global__ __launch_bounds__(kBlock) void decode_split_kernel(const DecodeParams
   }
   // score(i) = n_i <H s q / sqrt(D), c> / sqrt(D), here in base-2 units.
   const float qscale = k_packed ? kLog2e / static_cast<float>(D) : kLog2e / sqrtf(static_cast<float>(D));
-  for (int i = threadIdx.x; i < G * D; i += kBlock) qr[i] *= qscale;
-  __syncthreads();
+  for (int i = tid; i < gn * D; i += kBlock) qr[i] *= qscale;
 
-  for (int i = threadIdx.x; i < n * G; i += kBlock) {
-    const int tok = i / G, h = i % G;
-    const int t = t0 + tok;
-    float acc = 0.0f;
-    if (k_packed) {
-      const uint32_t *row = p.k.codes + cache_row(p.pg, bk, t, p.capacity) * p.k.words;
-      for (int j = 0; j < D; ++j) acc += qr[h * D + j] * ck[extract_code(row, p.k.bits, j)];
-      acc *= p.k.norms[cache_row(p.pg, bk, t, p.capacity)];
-    } else if (p.k.mode == TQ_SIDE_INT8) {
-      // INT8 rows: q . code times the row's scale (original domain)
-      const uint32_t *row = p.k.codes + cache_row(p.pg, bk, t, p.capacity) * p.k.words;
-      for (int j = 0; j < D; ++j) acc += qr[h * D + j] * int8_at(row[j >> 2], j);
-      acc *= p.k.norms[cache_row(p.pg, bk, t, p.capacity)];
-    } else {
-      const uint16_t *row = p.k.fp16 + cache_row(p.pg, bk, t, p.capacity) * D;
-      for (int j = 0; j < D; ++j) acc += qr[h * D + j] * h2f(row[j]);
-    }
-    sc[h * SL + tok] = acc;
-    if (p.scores) p.scores[(hq0 + h) * p.length + t] = acc * kLn2;
-  }
+  // score lanes: position stok, coordinates [part * D/8, (part + 1) * D/8)
+  const int stok = tid % kTile, part = tid / kTile;
+  constexpr int kCpl = D / kScoreParts;
+  // softmax lanes: half-wave sh handles head sh, lane stok position stok
+  const int sh = part;
+  float m_run = -INFINITY, l_run = 0.0f;
+  // value lanes: coordinate vj, every TS-th position from vsub
+  constexpr int TS = kBlock / D;
+  const int vj = tid % D, vsub = tid / D;
+  float acc_rot[HB], acc_plain[HB];
+#pragma unroll
+  for (int h = 0; h < HB; ++h) acc_rot[h] = acc_plain[h] = 0.0f;
+
+  Stager<D, GW> st;
+  st.init(L);
   __syncthreads();
+  if (t0 < t1) st.load(p, L, bk, t0, min(kTile, t1 - t0), hot_start);
+  for (int tb = t0; tb < t1; tb += kTile) {
+    const int nt = min(kTile, t1 - tb);
+    st.store(p, L, bk, hot_start, lds);
+    __syncthreads();
+    if (tb + kTile < t1) st.load(p, L, bk, tb + kTile, min(kTile, t1 - tb - kTile), hot_start);
+
+    // scores: partial dot products of one position over a slice of the
+    // coordinates, for every head
+    {
+      float acc[HB];
+#pragma unroll
+      for (int h = 0; h < HB; ++h) acc[h] = 0.0f;
+      if (stok < nt) {
+        const uint32_t *row = kt + stok * L.sk;
+        const int j0 = part * kCpl;
+        if (k_packed) {
+#pragma unroll 4
+          for (int j = j0; j < j0 + kCpl; ++j) {
+            const float c = ck[extract_code(row, p.k.bits, j)];
+#pragma unroll
+            for (int h = 0; h < HB; ++h) acc[h] += qr[h * D + j] * c;
+          }
+        } else if (p.k.mode == TQ_SIDE_INT8) {
+#pragma unroll
+          for (int j = j0; j < j0 + kCpl; j += 4) {
+            const uint32_t w = row[j >> 2];
+            const float x0 = int8_at(w, 0), x1 = int8_at(w, 1), x2 = int8_at(w, 2), x3 = int8_at(w, 3);
+#pragma unroll
+            for (int h = 0; h < HB; ++h) {
+              const float4 q4 = *reinterpret_cast<const float4 *>(qr + h * D + j);
+              acc[h] += q4.x * x0 + q4.y * x1 + q4.z * x2 + q4.w * x3;
+            }
+          }
+        } else {
+#pragma unroll
+          for (int j = j0; j < j0 + kCpl; j += 2) {
+            const float x0 = half_at(row, j), x1 = half_at(row, j + 1);
+#pragma unroll
+            for (int h = 0; h < HB; ++h) {
+              const float2 q2 = *reinterpret_cast<const float2 *>(qr + h * D + j);
+              acc[h] += q2.x * x0 + q2.y * x1;
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < HB; ++h) sp[(part * HB + h) * kTile + stok] = acc[h];
+    }
+    __syncthreads();
+
+    // online softmax, one half-wave per head
+    if (sh < HB) {
+      if (sh < gn) {
+        float s = -INFINITY;
+        if (stok < nt) {
+          float a = 0.0f;
+#pragma unroll
+          for (int q = 0; q < kScoreParts; ++q) a += sp[(q * HB + sh) * kTile + stok];
+          s = a * kn[stok];
+          if (p.scores) p.scores[(hq0 + sh) * p.length + tb + stok] = s * kLn2;
+        }
+        const float m_new = fmaxf(m_run, group_max<32>(s));
+        const float alpha = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - m_new);
+        float w = (stok < nt && m_new != -INFINITY) ? exp2f(s - m_new) : 0.0f;
+        l_run = l_run * alpha + group_sum<32>(w);
+        m_run = m_new;
+        // sparse-V: drop the value of a position whose weight, relative to
+        // the running maximum, is below the threshold (it stays in the sum)
+        if (p.sparse_lg != -INFINITY && !(s - m_new >= p.sparse_lg)) w = 0.0f;
+        pw[stok * HB + sh] = stok < nt ? w * vn[stok] : 0.0f;
+        if (stok == 0) al[sh] = alpha;
+      } else {
+        pw[stok * HB + sh] = 0.0f;
+        if (stok == 0) al[sh] = 0.0f;
+      }
+    }
+    __syncthreads();
+
+    // values: coordinate vj of every head over this lane's positions; the
+    // cold (packed or INT8) positions first, then the fp16 ones
+#pragma unroll
+    for (int h = 0; h < HB; ++h) {
+      acc_rot[h] *= al[h];
+      acc_plain[h] *= al[h];
+    }
+    const int nc = min(nt, max(0, hot_start - tb));
+    if (nc > 0) {
+      if (p.v.mode == TQ_SIDE_INT8) {
+        accumulate<D, HB, 1>(acc_plain, vt, L.sv, pw, cv, p.v.bits, vj, vsub, nc);
+      } else {
+        accumulate<D, HB, 0>(acc_rot, vt, L.sv, pw, cv, p.v.bits, vj, vsub, nc);
+      }
+    }
+    if (nc < nt) accumulate<D, HB, 2>(acc_plain, vt, L.sv, pw, cv, p.v.bits, vj, nc + vsub, nt);
+    __syncthreads();
+  }
 
   const DecodeWorkspace lay = decode_workspace_layout(p.batch, p.q_heads, p.n_splits, D);
   float *ml = reinterpret_cast<float *>(reinterpret_cast<char *>(p.ws) + lay.ml_off);
-  for (int h = 0; h < G; ++h) {
-    float m = -INFINITY;
-    for (int tok = threadIdx.x; tok < n; tok += kBlock) m = fmaxf(m, sc[h * SL + tok]);
-    m = block_reduce(m, red, true);
-    float l = 0.0f;
-    for (int tok = threadIdx.x; tok < n; tok += kBlock) {
-      const float e = (n > 0) ? exp2f(sc[h * SL + tok] - m) : 0.0f;
-      sc[h * SL + tok] = e;
-      l += e;
-    }
-    l = block_reduce(l, red, false);
-    if (threadIdx.x == 0) {
-      ml[((hq0 + h) * p.n_splits + split) * 2 + 0] = m;
-      ml[((hq0 + h) * p.n_splits + split) * 2 + 1] = l;
-    }
-  }
-  __syncthreads();
-
   float *orot = reinterpret_cast<float *>(reinterpret_cast<char *>(p.ws) + lay.orot_off);
   float *ohot = reinterpret_cast<float *>(reinterpret_cast<char *>(p.ws) + lay.ohot_off);
-  for (int o = threadIdx.x; o < G * D; o += kBlock) {
-    const int h = o / D, j = o % D;
-    float rot = 0.0f, plain = 0.0f;
-    for (int tok = 0; tok < n; ++tok) {
-      const int t = t0 + tok;
-      const float w = sc[h * SL + tok];
-      // sparse-V: weight relative to the split's maximum below the threshold
-      if (p.sparse_lg != -INFINITY && !(log2f(w) >= p.sparse_lg)) continue;
-      const uint16_t *vrow = v_plain_row(p, bk, t);
-      if (vrow) {
-        plain += w * h2f(vrow[j]);
-      } else if (p.v.mode == TQ_SIDE_INT8) {
-        const uint32_t *row = p.v.codes + cache_row(p.pg, bk, t, p.capacity) * p.v.words;
-        plain += w * p.v.norms[cache_row(p.pg, bk, t, p.capacity)] * int8_at(row[j >> 2], j);
-      } else {
-        const uint32_t *row = p.v.codes + cache_row(p.pg, bk, t, p.capacity) * p.v.words;
-        rot += w * p.v.norms[cache_row(p.pg, bk, t, p.capacity)] * cv[extract_code(row, p.v.bits, j)];
-      }
+  if (sh < gn && stok == 0) {
+    ml[((hq0 + sh) * p.n_splits + split) * 2 + 0] = m_run;
+    ml[((hq0 + sh) * p.n_splits + split) * 2 + 1] = l_run;
+  }
+  // sum the TS lane groups' value sums (through LDS), then write them
+  float *red = sp;  // [TS][HB][D]
+  for (int pass = 0; pass < 2; ++pass) {
+    float *dst = pass == 0 ? orot : ohot;
+#pragma unroll
+    for (int h = 0; h < HB; ++h) red[(vsub * HB + h) * D + vj] = pass == 0 ? acc_rot[h] : acc_plain[h];
+    __syncthreads();
+    for (int o = tid; o < gn * D; o += kBlock) {
+      const int h = o / D, j = o % D;
+      float sum = 0.0f;
+#pragma unroll
+      for (int g = 0; g < TS; ++g) sum += red[(g * HB + h) * D + j];
+      dst[((hq0 + h) * p.n_splits + split) * D + j] = sum;
     }
-    const long u = (hq0 + h) * p.n_splits + split;
-    orot[u * D + j] = rot;
-    ohot[u * D + j] = plain;
+    __syncthreads();
   }
 }
 
@@ -206,13 +480,29 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const DecodeParams p)
   p.out[bh * D + j] = (L > 0.0f) ? (o + plain) / L : 0.0f;
 }
 
+template <int D, int GW>
+void launch_hb(int hb, dim3 grid, size_t smem, hipStream_t stream, const DecodeParams &p) {
+  switch (hb) {
+    case 1: hipLaunchKernelGGL((decode_split_kernel<D, GW, 1>), grid, dim3(kBlock), smem, stream, p); break;
+    case 2: hipLaunchKernelGGL((decode_split_kernel<D, GW, 2>), grid, dim3(kBlock), smem, stream, p); break;
+    case 4: hipLaunchKernelGGL((decode_split_kernel<D, GW, 4>), grid, dim3(kBlock), smem, stream, p); break;
+    default: hipLaunchKernelGGL((decode_split_kernel<D, GW, 8>), grid, dim3(kBlock), smem, stream, p); break;
+  }
+}
+
 template <int D>
 hipError_t launch_d(const DecodeParams &p, hipStream_t stream) {
-  const int G = p.q_heads / p.kv_heads;
-  const size_t smem = sizeof(float) * (static_cast<size_t>(G) * D + static_cast<size_t>(G) * p.split_len +
-                                       2 * kMaxLevels + 4);
-  hipLaunchKernelGGL(decode_split_kernel<D>, dim3(p.n_splits, p.batch * p.kv_heads), dim3(kBlock), smem,
-                     stream, p);
+  const RefLayout L = ref_layout(p, D);
+  const size_t smem = sizeof(uint32_t) * static_cast<size_t>(L.total);
+  auto a16 = [](const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; };
+  const bool vec = L.kw % 4 == 0 && L.vw_cold % 4 == 0 && L.vw_hot % 4 == 0 && a16(p.k.codes) && a16(p.k.fp16) &&
+                   a16(p.v.codes) && a16(p.v.fp16);
+  const dim3 grid(p.n_splits, p.batch * p.kv_heads, L.ngroups);
+  if (vec) {
+    launch_hb<D, 4>(L.hb, grid, smem, stream, p);
+  } else {
+    launch_hb<D, 1>(L.hb, grid, smem, stream, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(p.batch * p.q_heads), dim3(D), 0, stream, p);

@@ -219,6 +219,13 @@ DECODE_CASES = [
     ("fp16_fp16", 1, 2, 4, 64, 333, ("fp16", 0), ("fp16", 0), "iid"),
     ("d32_mqa", 1, 1, 8, 32, 97, ("packed", 2), ("packed", 5), "iid"),
     ("d256", 1, 2, 4, 256, 130, ("packed", 4), ("packed", 3), "iid"),
+    # query-group sizes of the plain kernel's head blocks: one head, three
+    # (arrays sized for four), twelve (two blocks of six); fp16 rows at
+    # d = 256 (more row pieces than the lanes' prefetch slots)
+    ("mha_d128", 2, 4, 4, 128, 300, ("packed", 3), ("packed", 4), "channel"),
+    ("g3_d64", 1, 2, 6, 64, 250, ("fp16", 0), ("packed", 2), "iid"),
+    ("g12_d128", 1, 1, 12, 128, 200, ("packed", 4), ("packed", 4), "iid"),
+    ("fp16_d256", 1, 1, 2, 256, 150, ("fp16", 0), ("fp16", 0), "iid"),
 ]
 
 
