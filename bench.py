@@ -134,7 +134,13 @@ def cpu_baseline(w, budget_s: float = 12.0):
                       f"decode at context {T} (unpack + dequantize + float64 attention), {spent:.1f} s"}
 
 
-DECODE_SOURCE = os.path.join(ROOT, "compressed_decode_attention_append_amd", "csrc", "decode_mfma.hip")
+# the decode kernels whose counters can be recorded, by name prefix, with the
+# source each one is built from
+DECODE_SOURCES = {
+    "decode_mfma": os.path.join(ROOT, "compressed_decode_attention_append_amd", "csrc", "decode_mfma.hip"),
+    "decode_split": os.path.join(ROOT, "compressed_decode_attention_append_amd", "csrc", "decode_ref.hip"),
+}
+DECODE_SOURCE = DECODE_SOURCES["decode_mfma"]
 
 
 def source_digest(path=DECODE_SOURCE) -> str:
@@ -150,28 +156,34 @@ def source_digest(path=DECODE_SOURCE) -> str:
     return hashlib.sha256(text.encode()).hexdigest()
 
 
-def traffic_file(workload: str) -> str:
-    return os.path.join(ROOT, "profiles", f"decode_mfma_{workload}_hbm_traffic.txt")
+def traffic_file(workload: str, kernel: str = "decode_mfma") -> str:
+    return os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_traffic.txt")
 
 
 def recorded_traffic(workload: str):
-    """HBM bytes per decode launch from the committed counter summary, or None
-    when there is none or the kernel source changed since it was taken."""
-    path = traffic_file(workload)
-    if not os.path.exists(path):
+    """HBM bytes per launch of the workload's decode kernel from the committed
+    counter summary, or None when there is none or the kernel's source
+    changed since it was taken (or a decode variant is forced through the
+    environment, so the recorded kernel may not be the one that runs)."""
+    if os.environ.get("TQ_DECODE_VARIANT"):
         return None
-    fields = {}
-    with open(path) as f:
-        for line in f:
-            if ":" in line and not line.startswith("#"):
-                k, v = line.split(":", 1)
-                fields[k.strip()] = v.strip()
-    if fields.get("source_sha256") != source_digest():
-        return None
-    try:
-        return int(float(fields["traffic_bytes_per_launch"]))
-    except (KeyError, ValueError):
-        return None
+    for kernel, src in DECODE_SOURCES.items():
+        path = traffic_file(workload, kernel)
+        if not os.path.exists(path):
+            continue
+        fields = {}
+        with open(path) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    fields[k.strip()] = v.strip()
+        if fields.get("source_sha256") != source_digest(src):
+            return None
+        try:
+            return int(float(fields["traffic_bytes_per_launch"]))
+        except (KeyError, ValueError):
+            return None
+    return None
 
 
 def counter_summary(fetch_csv: str, write_csv: str, workload: str, copy_mib: int, cmds: list):
@@ -192,7 +204,8 @@ def counter_summary(fetch_csv: str, write_csv: str, workload: str, copy_mib: int
     fetch, nf = read(fetch_csv, "FETCH_SIZE")
     write, nw = read(write_csv, "WRITE_SIZE")
     copy_name = next(k for k in fetch if "neg_kernel" in k)
-    dec_name = next(k for k in fetch if "decode_mfma_kernel" in k)
+    dec_name = next(k for k in fetch if "decode_mfma_kernel" in k or "decode_split_kernel" in k)
+    src = DECODE_SOURCES["decode_mfma" if "decode_mfma_kernel" in dec_name else "decode_split"]
     kib = copy_mib * 1024.0
     f_fetch = kib / fetch[copy_name]
     f_write = kib / write[copy_name]
@@ -210,7 +223,8 @@ def counter_summary(fetch_csv: str, write_csv: str, workload: str, copy_mib: int
             f"WRITE_SIZE {write[dec_name]:.1f} KiB per dispatch (raw)",
             f"kernel: {short}",
             f"workload: {workload}",
-            f"source_sha256: {source_digest()}",
+            f"source: {os.path.relpath(src, ROOT)}",
+            f"source_sha256: {source_digest(src)}",
             f"fetch_bytes_per_launch: {fetch[dec_name] * f_fetch * 1024.0:.0f}",
             f"write_bytes_per_launch: {write[dec_name] * f_write * 1024.0:.0f}",
             f"traffic_bytes_per_launch: {traffic:.0f}",

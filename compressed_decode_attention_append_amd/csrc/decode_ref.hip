@@ -448,10 +448,13 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const DecodeParams p)
   const float *ml = reinterpret_cast<const float *>(reinterpret_cast<const char *>(p.ws) + lay.ml_off);
   const float *orot = reinterpret_cast<const float *>(reinterpret_cast<const char *>(p.ws) + lay.orot_off);
   const float *ohot = reinterpret_cast<const float *>(reinterpret_cast<const char *>(p.ws) + lay.ohot_off);
+  // unrolled by eight so that eight splits' loads are in flight at once
   float M = -INFINITY;
+#pragma unroll 8
   for (int s = 0; s < p.n_splits; ++s) M = fmaxf(M, ml[(bh * p.n_splits + s) * 2]);
   float L = 0.0f, rot = 0.0f, plain = 0.0f;
   if (M != -INFINITY) {
+#pragma unroll 8
     for (int s = 0; s < p.n_splits; ++s) {
       const long u = bh * p.n_splits + s;
       const float w = exp2f(ml[u * 2] - M);
