@@ -652,7 +652,10 @@ struct Wave {
   }
 
   // One chunk of the fp16 hot window (delegated V), positions >= we masked.
-  __device__ __forceinline__ void hot_chunk(int t0, int we, const ChunkData<KB, GP> &c, float *scores,
+  // Chunk [t0, t0 + 32) of the fp16 hot window [wb, we): t0 is on the
+  // 32-position grid (a paged chunk then lies in one block), and positions
+  // outside the window are masked.
+  __device__ __forceinline__ void hot_chunk(int t0, int wb, int we, const ChunkData<KB, GP> &c, float *scores,
                                             long score_row0, int length) {
     float s[8], cs[NV], vn[NV];
     score(c, s);
@@ -661,9 +664,16 @@ struct Wave {
     for (int j = 0; j < NV; ++j) {
       if (KB) cs[j] *= c.kn[j];
       vn[j] = 1.0f;
-      if (t0 + cpos + j >= we) cs[j] = -INFINITY;
+      const int t = t0 + cpos + j;
+      if (t < wb || t >= we) cs[j] = -INFINITY;
     }
-    if (scores) store_scores<true>(t0, we, cs, scores, score_row0, length);
+    if (scores && col % GP < G) {
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int t = t0 + cpos + j;
+        if (t >= wb && t < we) scores[(score_row0 + col % GP) * length + t] = cs[j] * kLn2;
+      }
+    }
     const half8_t ap = softmax<true>(cs, vn);
     // fp16 ring rows: tile q covers coordinates 16 q + col
 #pragma unroll
@@ -1116,14 +1126,17 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   const int h0 = p.cold_len, h1 = p.length;
   const bool has_hot = h1 > h0;
   if (has_hot) {
-    const int hspan = h1 - h0;
+    // the window's chunks on the 32-position grid from floor(h0 / 32) 32,
+    // dealt to the waves in equal runs; positions below h0 are masked
+    const int c0 = h0 / kChunk * kChunk;
+    const int hspan = h1 - c0;
     const int hper = ((hspan + kWaves - 1) / kWaves + kChunk - 1) / kChunk * kChunk;
-    const int hs = h0 + wave * hper, he = min(h1, hs + hper);
+    const int hs = c0 + wave * hper, he = min(h1, hs + hper);
     W.reset();
     W.vscale = 1.0f;
     for (int t0 = hs; t0 < he; t0 += kChunk) {
       W.load(t0, A);
-      W.hot_chunk(t0, he, A, p.scores, hq0, p.length);
+      W.hot_chunk(t0, h0, he, A, p.scores, hq0, p.length);
     }
     W.to_slot(work + wave * GP * kPS, true);
     __syncthreads();
@@ -1234,9 +1247,6 @@ bool decode_mfma_supported(const DecodeParams &p) {
   const int G = p.q_heads / p.kv_heads;
   if (p.head_dim != D || G > 8) return false;
   if (!(p.v.mode == TQ_SIDE_PACKED || p.v.mode == TQ_SIDE_DELEGATED) || p.v.bits != 4) return false;
-  // paged with a delegated V: the hot window's chunks need not start on a
-  // block's 32-position grid; the plain kernel reads row by row
-  if (p.pg.table && p.v.mode == TQ_SIDE_DELEGATED) return false;
   int kb;
   if (p.k.mode == TQ_SIDE_FP16) {
     kb = 0;

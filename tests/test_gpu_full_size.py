@@ -113,7 +113,7 @@ def test_full_size_sampled(name):
         assert ok, f"{name} unit ({b},{h}): worst {worst}"
 
 
-@pytest.mark.parametrize("name", ["c4_tq35_32k", "c3_asym_16k"])
+@pytest.mark.parametrize("name", ["c4_tq35_32k", "c3_asym_16k", "c5_delegated_64k"])
 def test_full_size_paged_matches_contiguous(name):
     # the same appends into a contiguous cache and a paged one (blocks of 256
     # positions in a random order): decode outputs bit-identical, and the
