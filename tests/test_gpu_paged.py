@@ -145,3 +145,18 @@ def test_shared_prefix_blocks():
     ref, _ = oracle.decode_attention(q.cpu().numpy(), rows["k"], rows["v"])
     ok, worst = rows_close(op.cpu().numpy(), ref)
     assert ok, f"out: worst {worst}"
+
+
+@pytest.mark.parametrize("ns", [3, 7])
+def test_paged_split_counts_match_contiguous(ns):
+    # explicit split counts give split lengths off the 32-position grid, so
+    # the plain kernel's tiles (d = 64 runs it) cross block boundaries
+    case = CASES[4]
+    contig, paged = _pair(case, 2024 + ns)
+    for length in LENGTHS:
+        q = torch.from_numpy(synth.q_numpy(78, case[1], case[3], case[4])).cuda()
+        oc, sc = contig.decode_attention(q, length, n_splits=ns, scores=True)
+        op, sp = paged.decode_attention(q, length, n_splits=ns, scores=True)
+        torch.cuda.synchronize()
+        assert torch.equal(sc, sp), f"scores differ at length {length}"
+        assert torch.equal(oc, op), f"outputs differ at length {length}"

@@ -24,6 +24,7 @@ CASES = [
     ("tq35", S("packed", 3), S("packed", 4)),
     ("asym", S("fp16", 0), S("packed", 4)),
     ("delegated", S("fp16", 0), S("delegated", 4, 128)),
+    ("int8", S("int8", 0), S("int8", 0)),
 ]
 
 
@@ -60,6 +61,9 @@ def _rows(cache, side, length):
     spec = cache.k_spec if side == "k" else cache.v_spec
     if spec.mode == "fp16":
         return cache.tensors[side + "_fp16"][:, :, :length].cpu().numpy().astype(np.float64)
+    if spec.mode == "int8":
+        codes = cache.tensors[side + "_codes"][:, :, :length].cpu().numpy().view(np.int8)  # byte j = coordinate j
+        return oracle.int8_dequantize(codes, cache.tensors[side + "_norms"][:, :, :length].cpu().numpy())
     d = cache.head_dim
     R = oracle.rotation_matrix(cache.seed, d)
     c, _ = oracle.lloyd_max(d, spec.bits)
