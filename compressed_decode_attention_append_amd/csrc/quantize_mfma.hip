@@ -211,11 +211,29 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_mfma_kernel(const Quanti
     // crosses at most one boundary), divided once per tile
     const int sq0 = static_cast<int>(b0) / p.heads, hd0 = static_cast<int>(b0) - sq0 * p.heads;
     const int sq1 = hd0 + 1 == p.heads ? sq0 + 1 : sq0, hd1 = hd0 + 1 == p.heads ? 0 : hd0 + 1;
+    // the lane's four rows are consecutive positions of one unit unless they
+    // cross the unit boundary, a block boundary or the end of the rows: the
+    // first row is looked up, the others follow it; only lanes with such a
+    // crossing look each row up
+    const int trf = min(4 * g, static_cast<int>(lf) - 1);
+    const bool wrapf = j0 + trf >= p.n_new;
+    const unsigned tf = static_cast<unsigned>(p.offset + j0 + trf - (wrapf ? p.n_new : 0));
+    const unsigned ubs = static_cast<unsigned>(p.pg.bs), blkf = tf / ubs;
+    const int within = static_cast<int>(tf - blkf * ubs);
+    const int sqf = wrapf ? sq1 : sq0, hdf = wrapf ? hd1 : hd0;
+    rw[0] = (static_cast<long>(p.pg.table[sqf * p.pg.max_blocks + static_cast<int>(blkf)]) * p.pg.kv_heads + hdf) *
+                p.pg.bs + within;
+    const bool run = 4 * g + 3 <= lf - 1 && (j0 + 4 * g + 3 >= p.n_new) == wrapf && within + 3 < p.pg.bs;
+    if (run) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int tr = min(4 * g + r, static_cast<int>(lf) - 1);
-      const bool wrap = j0 + tr >= p.n_new;
-      rw[r] = paged_row(p.pg, wrap ? sq1 : sq0, wrap ? hd1 : hd0, p.offset + j0 + tr - (wrap ? p.n_new : 0));
+      for (int r = 1; r < 4; ++r) rw[r] = rw[0] + r;
+    } else {
+#pragma unroll
+      for (int r = 1; r < 4; ++r) {
+        const int tr = min(4 * g + r, static_cast<int>(lf) - 1);
+        const bool wrap = j0 + tr >= p.n_new;
+        rw[r] = paged_row(p.pg, wrap ? sq1 : sq0, wrap ? hd1 : hd0, p.offset + j0 + tr - (wrap ? p.n_new : 0));
+      }
     }
   };
   const bool paged = p.pg.table != nullptr;
