@@ -9,13 +9,14 @@
 // heads of one KV head over one contiguous range of positions:
 //   1. q is rotated once: R q = H diag(s) q / sqrt(d) by butterflies in LDS;
 //      the softmax scale 1/sqrt(d) and log2(e) are folded in.
-//   2. the range is walked in tiles of 32 positions.  Each tile's K and V
+//   2. the range is walked in tiles of 64 positions (32 where a tile's
+//      rows do not fit the lanes' prefetch slots).  Each tile's K and V
 //      rows (packed codes, INT8 codes or fp16, as stored) are copied to LDS
 //      with row-contiguous loads, 16 bytes a lane where rows allow it; the
 //      next tile's loads are in flight while the current one is computed.
 //   3. scores from the LDS rows: n_i <R q, c[code_i]> (packed K), s_i q .
 //      code_i (INT8 K) or q . k_i (fp16 K).  A lane takes one position and
-//      an eighth of the coordinates for every head of the block; the eight
+//      a slice of the coordinates for every head of the block; the slices'
 //      partial sums are added in the softmax step.
 //   4. online softmax per head (base-2 exponent): the running maximum and
 //      sum, and the factor that rescales the accumulators.
@@ -37,9 +38,7 @@ namespace tq {
 namespace {
 
 constexpr int kBlock = 256;
-constexpr int kTile = 32;           // positions staged per step
 constexpr int kMaxGroupHeads = 8;   // query heads per block
-constexpr int kScoreParts = kBlock / kTile;  // lanes per position in the score step
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -54,7 +53,8 @@ struct RefLayout {
   int qr, sp, pw, kt, vt, kn, vn, ck, cv, al, total;
 };
 
-__host__ __device__ inline RefLayout ref_layout(const DecodeParams &p, int D) {
+// tt: positions per tile (32 or 64).
+__host__ __device__ inline RefLayout ref_layout(const DecodeParams &p, int D, int tt) {
   RefLayout L;
   const int G = p.q_heads / p.kv_heads;
   L.ngroups = (G + kMaxGroupHeads - 1) / kMaxGroupHeads;
@@ -67,14 +67,14 @@ __host__ __device__ inline RefLayout ref_layout(const DecodeParams &p, int D) {
   L.sv = (L.vw_cold > L.vw_hot ? L.vw_cold : L.vw_hot) | 1;
   int o = 0;
   L.qr = o; o += L.hb * D;                 // rotated, scaled queries [head][d]
-  L.sp = o; o += kBlock * L.hb;            // partial scores [part][head][pos] (8 x 32 x hb);
+  L.sp = o; o += kBlock * L.hb;            // partial scores [part][head][pos] (256 / tt x tt x hb);
                                            // at the end the value sums [lane group][head][d]
                                            // (256 / d x hb x d)
-  L.pw = o; o += kTile * L.hb;             // weight times the V row's norm or scale [pos][head]
-  L.kt = o; o += kTile * L.sk;             // K tile
-  L.vt = o; o += kTile * L.sv;             // V tile
-  L.kn = o; o += kTile;                    // K norms / scales (1 for fp16 rows)
-  L.vn = o; o += kTile;                    // V norms / scales (1 for fp16 rows)
+  L.pw = o; o += tt * L.hb;                // weight times the V row's norm or scale [pos][head]
+  L.kt = o; o += tt * L.sk;                // K tile
+  L.vt = o; o += tt * L.sv;                // V tile
+  L.kn = o; o += tt;                       // K norms / scales (1 for fp16 rows)
+  L.vn = o; o += tt;                       // V norms / scales (1 for fp16 rows)
   L.ck = o; o += kMaxLevels;               // centroids
   L.cv = o; o += kMaxLevels;
   L.al = o; o += kMaxGroupHeads;           // per-head rescale factor of the tile
@@ -120,7 +120,7 @@ __device__ __forceinline__ const uint32_t *piece_src(const DecodeParams &p, cons
 // current one is scored and stored after it, so HBM latency overlaps
 // compute.  Pieces beyond those (fp16 rows at head_dim 256, 4-byte loads)
 // are copied when the tile is stored.
-template <int D, int GW>
+template <int D, int GW, int TT>
 struct Stager {
   static constexpr int kSlots = 4;
   u32x4_t buf[kSlots];
@@ -143,16 +143,16 @@ struct Stager {
     for (int u = 0; u < kSlots; ++u) {
       const int i = tid + u * kBlock;
       row[u] = -1;
-      if (i < kTile * (kg + vg)) {
-        is_k[u] = i < kTile * kg;
-        const int ii = is_k[u] ? i : i - kTile * kg;
+      if (i < TT * (kg + vg)) {
+        is_k[u] = i < TT * kg;
+        const int ii = is_k[u] ? i : i - TT * kg;
         const int per = is_k[u] ? kg : vg;
         row[u] = ii / per;
         piece[u] = ii - row[u] * per;
         dst[u] = (is_k[u] ? L.kt + row[u] * L.sk : L.vt + row[u] * L.sv) + piece[u] * GW;
       }
     }
-    norm_dst = tid < kTile ? L.kn + tid : ((tid >= 64 && tid < 64 + kTile) ? L.vn + tid - 64 : -1);
+    norm_dst = tid < TT ? L.kn + tid : ((tid >= 64 && tid < 64 + TT) ? L.vn + tid - 64 : -1);
   }
 
   // Issue the loads of positions [t, t + n).
@@ -198,9 +198,9 @@ struct Stager {
       }
     }
     if (norm_dst >= 0) reinterpret_cast<float *>(lds)[norm_dst] = norm;
-    for (int i = threadIdx.x + kSlots * kBlock; i < kTile * (kg + vg); i += kBlock) {
-      const bool k = i < kTile * kg;
-      const int ii = k ? i : i - kTile * kg;
+    for (int i = threadIdx.x + kSlots * kBlock; i < TT * (kg + vg); i += kBlock) {
+      const bool k = i < TT * kg;
+      const int ii = k ? i : i - TT * kg;
       const int per = k ? kg : vg;
       const int r = ii / per, pc = ii - r * per;
       if (r >= nt) continue;
@@ -245,11 +245,12 @@ __device__ __forceinline__ void accumulate(float (&acc)[HB], const uint32_t *vt,
 
 // GW: words per staging load (4 = 16-byte loads; the host picks 4 when every
 // row kind is a multiple of 16 bytes and the storage is 16-byte aligned).
-// HB: heads the per-lane arrays hold (>= the block's heads).
-template <int D, int GW, int HB>
+// HB: heads the per-lane arrays hold (>= the block's heads).  TT: positions
+// per tile, 64 where a tile's pieces fit the lanes' prefetch slots, else 32.
+template <int D, int GW, int HB, int TT>
 __global__ __launch_bounds__(kBlock) void decode_split_kernel(const DecodeParams p) {
   extern __shared__ __align__(16) uint32_t lds[];
-  const RefLayout L = ref_layout(p, D);
+  const RefLayout L = ref_layout(p, D, TT);
   float *qr = reinterpret_cast<float *>(lds + L.qr);
   float *sp = reinterpret_cast<float *>(lds + L.sp);
   float *pw = reinterpret_cast<float *>(lds + L.pw);
@@ -299,12 +300,19 @@ __global__ __launch_bounds__(kBlock) void decode_split_kernel(const DecodeParams
   const float qscale = k_packed ? kLog2e / static_cast<float>(D) : kLog2e / sqrtf(static_cast<float>(D));
   for (int i = tid; i < gn * D; i += kBlock) qr[i] *= qscale;
 
-  // score lanes: position stok, coordinates [part * D/8, (part + 1) * D/8)
-  const int stok = tid % kTile, part = tid / kTile;
-  constexpr int kCpl = D / kScoreParts;
-  // softmax lanes: half-wave sh handles head sh, lane stok position stok
-  const int sh = part;
-  float m_run = -INFINITY, l_run = 0.0f;
+  // score lanes: position stok, coordinates [part, part + 1) * D / kParts
+  constexpr int kParts = kBlock / TT;
+  const int stok = tid % TT, part = tid / TT;
+  constexpr int kCpl = D / kParts;
+  // softmax lanes: in pass ps, the TT lanes of group `part` handle head
+  // part + ps * kParts, lane stok position stok
+  constexpr int kPasses = (HB * TT + kBlock - 1) / kBlock;
+  float m_run[kPasses], l_run[kPasses];
+#pragma unroll
+  for (int ps = 0; ps < kPasses; ++ps) {
+    m_run[ps] = -INFINITY;
+    l_run[ps] = 0.0f;
+  }
   // value lanes: coordinate vj, every TS-th position from vsub
   constexpr int TS = kBlock / D;
   const int vj = tid % D, vsub = tid / D;
@@ -312,15 +320,15 @@ __global__ __launch_bounds__(kBlock) void decode_split_kernel(const DecodeParams
 #pragma unroll
   for (int h = 0; h < HB; ++h) acc_rot[h] = acc_plain[h] = 0.0f;
 
-  Stager<D, GW> st;
+  Stager<D, GW, TT> st;
   st.init(L);
   __syncthreads();
-  if (t0 < t1) st.load(p, L, bk, t0, min(kTile, t1 - t0), hot_start);
-  for (int tb = t0; tb < t1; tb += kTile) {
-    const int nt = min(kTile, t1 - tb);
+  if (t0 < t1) st.load(p, L, bk, t0, min(TT, t1 - t0), hot_start);
+  for (int tb = t0; tb < t1; tb += TT) {
+    const int nt = min(TT, t1 - tb);
     st.store(p, L, bk, hot_start, lds);
     __syncthreads();
-    if (tb + kTile < t1) st.load(p, L, bk, tb + kTile, min(kTile, t1 - tb - kTile), hot_start);
+    if (tb + TT < t1) st.load(p, L, bk, tb + TT, min(TT, t1 - tb - TT), hot_start);
 
     // scores: partial dot products of one position over a slice of the
     // coordinates, for every head
@@ -362,34 +370,38 @@ __global__ __launch_bounds__(kBlock) void decode_split_kernel(const DecodeParams
         }
       }
 #pragma unroll
-      for (int h = 0; h < HB; ++h) sp[(part * HB + h) * kTile + stok] = acc[h];
+      for (int h = 0; h < HB; ++h) sp[(part * HB + h) * TT + stok] = acc[h];
     }
     __syncthreads();
 
-    // online softmax, one half-wave per head
-    if (sh < HB) {
-      if (sh < gn) {
-        float s = -INFINITY;
-        if (stok < nt) {
-          float a = 0.0f;
+    // online softmax, TT lanes per head
 #pragma unroll
-          for (int q = 0; q < kScoreParts; ++q) a += sp[(q * HB + sh) * kTile + stok];
-          s = a * kn[stok];
-          if (p.scores) p.scores[(hq0 + sh) * p.length + tb + stok] = s * kLn2;
+    for (int ps = 0; ps < kPasses; ++ps) {
+      const int sh = part + ps * kParts;
+      if (sh < HB) {
+        if (sh < gn) {
+          float s = -INFINITY;
+          if (stok < nt) {
+            float a = 0.0f;
+#pragma unroll
+            for (int q = 0; q < kParts; ++q) a += sp[(q * HB + sh) * TT + stok];
+            s = a * kn[stok];
+            if (p.scores) p.scores[(hq0 + sh) * p.length + tb + stok] = s * kLn2;
+          }
+          const float m_new = fmaxf(m_run[ps], group_max<TT>(s));
+          const float alpha = (m_run[ps] == -INFINITY) ? 0.0f : exp2f(m_run[ps] - m_new);
+          float w = (stok < nt && m_new != -INFINITY) ? exp2f(s - m_new) : 0.0f;
+          l_run[ps] = l_run[ps] * alpha + group_sum<TT>(w);
+          m_run[ps] = m_new;
+          // sparse-V: drop the value of a position whose weight, relative to
+          // the running maximum, is below the threshold (it stays in the sum)
+          if (p.sparse_lg != -INFINITY && !(s - m_new >= p.sparse_lg)) w = 0.0f;
+          pw[stok * HB + sh] = stok < nt ? w * vn[stok] : 0.0f;
+          if (stok == 0) al[sh] = alpha;
+        } else {
+          pw[stok * HB + sh] = 0.0f;
+          if (stok == 0) al[sh] = 0.0f;
         }
-        const float m_new = fmaxf(m_run, group_max<32>(s));
-        const float alpha = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - m_new);
-        float w = (stok < nt && m_new != -INFINITY) ? exp2f(s - m_new) : 0.0f;
-        l_run = l_run * alpha + group_sum<32>(w);
-        m_run = m_new;
-        // sparse-V: drop the value of a position whose weight, relative to
-        // the running maximum, is below the threshold (it stays in the sum)
-        if (p.sparse_lg != -INFINITY && !(s - m_new >= p.sparse_lg)) w = 0.0f;
-        pw[stok * HB + sh] = stok < nt ? w * vn[stok] : 0.0f;
-        if (stok == 0) al[sh] = alpha;
-      } else {
-        pw[stok * HB + sh] = 0.0f;
-        if (stok == 0) al[sh] = 0.0f;
       }
     }
     __syncthreads();
@@ -417,9 +429,13 @@ __global__ __launch_bounds__(kBlock) void decode_split_kernel(const DecodeParams
   float *ml = reinterpret_cast<float *>(reinterpret_cast<char *>(p.ws) + lay.ml_off);
   float *orot = reinterpret_cast<float *>(reinterpret_cast<char *>(p.ws) + lay.orot_off);
   float *ohot = reinterpret_cast<float *>(reinterpret_cast<char *>(p.ws) + lay.ohot_off);
-  if (sh < gn && stok == 0) {
-    ml[((hq0 + sh) * p.n_splits + split) * 2 + 0] = m_run;
-    ml[((hq0 + sh) * p.n_splits + split) * 2 + 1] = l_run;
+#pragma unroll
+  for (int ps = 0; ps < kPasses; ++ps) {
+    const int sh = part + ps * kParts;
+    if (sh < gn && stok == 0) {
+      ml[((hq0 + sh) * p.n_splits + split) * 2 + 0] = m_run[ps];
+      ml[((hq0 + sh) * p.n_splits + split) * 2 + 1] = l_run[ps];
+    }
   }
   // sum the TS lane groups' value sums (through LDS), then write them
   float *red = sp;  // [TS][HB][D]
@@ -483,28 +499,34 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const DecodeParams p)
   p.out[bh * D + j] = (L > 0.0f) ? (o + plain) / L : 0.0f;
 }
 
-template <int D, int GW>
+template <int D, int GW, int TT>
 void launch_hb(int hb, dim3 grid, size_t smem, hipStream_t stream, const DecodeParams &p) {
   switch (hb) {
-    case 1: hipLaunchKernelGGL((decode_split_kernel<D, GW, 1>), grid, dim3(kBlock), smem, stream, p); break;
-    case 2: hipLaunchKernelGGL((decode_split_kernel<D, GW, 2>), grid, dim3(kBlock), smem, stream, p); break;
-    case 4: hipLaunchKernelGGL((decode_split_kernel<D, GW, 4>), grid, dim3(kBlock), smem, stream, p); break;
-    default: hipLaunchKernelGGL((decode_split_kernel<D, GW, 8>), grid, dim3(kBlock), smem, stream, p); break;
+    case 1: hipLaunchKernelGGL((decode_split_kernel<D, GW, 1, TT>), grid, dim3(kBlock), smem, stream, p); break;
+    case 2: hipLaunchKernelGGL((decode_split_kernel<D, GW, 2, TT>), grid, dim3(kBlock), smem, stream, p); break;
+    case 4: hipLaunchKernelGGL((decode_split_kernel<D, GW, 4, TT>), grid, dim3(kBlock), smem, stream, p); break;
+    default: hipLaunchKernelGGL((decode_split_kernel<D, GW, 8, TT>), grid, dim3(kBlock), smem, stream, p); break;
   }
 }
 
 template <int D>
 hipError_t launch_d(const DecodeParams &p, hipStream_t stream) {
-  const RefLayout L = ref_layout(p, D);
-  const size_t smem = sizeof(uint32_t) * static_cast<size_t>(L.total);
+  const RefLayout L32 = ref_layout(p, D, 32);
   auto a16 = [](const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; };
-  const bool vec = L.kw % 4 == 0 && L.vw_cold % 4 == 0 && L.vw_hot % 4 == 0 && a16(p.k.codes) && a16(p.k.fp16) &&
-                   a16(p.v.codes) && a16(p.v.fp16);
+  const bool vec = L32.kw % 4 == 0 && L32.vw_cold % 4 == 0 && L32.vw_hot % 4 == 0 && a16(p.k.codes) &&
+                   a16(p.k.fp16) && a16(p.v.codes) && a16(p.v.fp16);
+  // 64-position tiles when their 16-byte pieces fit four per lane
+  const int vmax = L32.vw_cold > L32.vw_hot ? L32.vw_cold : L32.vw_hot;
+  const bool t64 = vec && 64 * (L32.kw / 4 + vmax / 4) <= 4 * kBlock;
+  const RefLayout L = t64 ? ref_layout(p, D, 64) : L32;
+  const size_t smem = sizeof(uint32_t) * static_cast<size_t>(L.total);
   const dim3 grid(p.n_splits, p.batch * p.kv_heads, L.ngroups);
-  if (vec) {
-    launch_hb<D, 4>(L.hb, grid, smem, stream, p);
+  if (t64) {
+    launch_hb<D, 4, 64>(L.hb, grid, smem, stream, p);
+  } else if (vec) {
+    launch_hb<D, 4, 32>(L.hb, grid, smem, stream, p);
   } else {
-    launch_hb<D, 1>(L.hb, grid, smem, stream, p);
+    launch_hb<D, 1, 32>(L.hb, grid, smem, stream, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
