@@ -105,6 +105,26 @@ def test_int8_decode(kspec, vspec, length):
     assert ok, f"out: worst {worst}"
 
 
+@pytest.mark.parametrize("H,Hq,d", [(4, 4, 128), (1, 8, 128), (2, 16, 64), (1, 3, 256)],
+                         ids=["g1_d128", "g8_d128", "g8_d64", "g3_d256"])
+def test_int8_decode_group_sizes(H, Hq, d):
+    # query groups of one, three and eight heads per KV head: eight heads on
+    # 64-position tiles take two softmax passes; d = 256 rows fall back to
+    # 32-position tiles
+    B, cap, length = 1, 700, 613
+    k, v = synth.kv_numpy(72, B, H, length, d, dist="channel", outlier_frac=0.01)
+    cache = tq.TQCache(B, H, d, cap, S("int8"), S("int8"))
+    cache.quantize_append(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), 0)
+    q = synth.q_numpy(73, B, Hq, d)
+    out, sc = cache.decode_attention(torch.from_numpy(q).cuda(), length, scores=True)
+    torch.cuda.synchronize()
+    ref, s_ref = oracle.decode_attention(q, _rows(cache, "k", length), _rows(cache, "v", length))
+    ok, worst = rows_close(sc.cpu().numpy(), s_ref)
+    assert ok, f"scores: worst {worst}"
+    ok, worst = rows_close(out.cpu().numpy(), ref)
+    assert ok, f"out: worst {worst}"
+
+
 def test_int8_paged_matches_contiguous():
     B, H, Hq, d, cap, bs = 2, 2, 8, 128, 512, 64
     k, v = synth.kv_numpy(80, B, H, 450, d)
