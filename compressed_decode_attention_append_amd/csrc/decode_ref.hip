@@ -114,12 +114,13 @@ __device__ __forceinline__ const uint32_t *piece_src(const DecodeParams &p, cons
 
 // Copy of one tile's K and V rows from HBM to LDS.  The tile is cut into
 // GW-word pieces, K rows first; lane l owns pieces l + 256 u.  For the first
-// four (u < 4, every piece of a tile at head_dim <= 128 with 16-byte loads)
-// the row, the piece and the LDS offset are the same for every tile, so they
-// are worked out once, and the loads of the next tile are issued before the
-// current one is scored and stored after it, so HBM latency overlaps
-// compute.  Pieces beyond those (fp16 rows at head_dim 256, 4-byte loads)
-// are copied when the tile is stored.
+// four (u < 4: every piece of a 32-position tile at head_dim <= 128 with
+// 16-byte loads, and of the 64-position tiles the host picks) the row, the
+// piece and the LDS offset are the same for every tile, so they are worked
+// out once, and the loads of the next tile are issued before the current
+// one is scored and stored after it, so HBM latency overlaps compute.
+// Pieces beyond those (fp16 rows at head_dim 256, 4-byte loads) are copied
+// when the tile is stored.
 template <int D, int GW, int TT>
 struct Stager {
   static constexpr int kSlots = 4;
@@ -129,7 +130,7 @@ struct Stager {
   int dst[kSlots];      // LDS word offset
   bool is_k[kSlots];
   bool live[kSlots];    // the piece was loaded for the current tile
-  float norm;           // lanes 0..31: K norm, 64..95: V norm of the tile row
+  float norm;           // lanes 0..TT-1: K norm, 64..63+TT: V norm of the tile row
   int norm_dst;         // LDS word offset of that norm, -1 = none
   int kg, vg;           // pieces per K row, per V row (the longer kind)
   int tb, nt;           // the loaded tile
