@@ -148,10 +148,13 @@ def test_shared_prefix_blocks():
 
 
 @pytest.mark.parametrize("ns", [3, 7])
-def test_paged_split_counts_match_contiguous(ns):
+@pytest.mark.parametrize("case", [CASES[4], ("tq35_d128_bs32", 2, 2, 8, 128, 32, S("packed", 3), S("packed", 4))],
+                         ids=["tq35_d64", "tq35_d128_bs32"])
+def test_paged_split_counts_match_contiguous(case, ns, monkeypatch):
     # explicit split counts give split lengths off the 32-position grid, so
-    # the plain kernel's tiles (d = 64 runs it) cross block boundaries
-    case = CASES[4]
+    # the plain kernel's tiles cross block boundaries: 32-position tiles at
+    # d = 64, and 64-position tiles over 32-position blocks at d = 128
+    monkeypatch.setenv("TQ_DECODE_VARIANT", "ref")
     contig, paged = _pair(case, 2024 + ns)
     for length in LENGTHS:
         q = torch.from_numpy(synth.q_numpy(78, case[1], case[3], case[4])).cuda()
