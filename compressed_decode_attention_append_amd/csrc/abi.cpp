@@ -102,9 +102,9 @@ void copy_levels(const tq_side &s, const float *src, int n, float *dst) {
 }
 
 // Context split of the plain decode.  A block walks its range in tiles of 32
-// positions for up to eight query heads; the automatic split aims at about
-// 2048 blocks (eight per compute unit) in whole tiles.  Any split length
-// fits the block's LDS.
+// or 64 positions for up to eight query heads; the automatic split aims at
+// about 2048 blocks (eight per compute unit) in multiples of 32 positions.
+// Any split length fits the block's LDS.
 bool choose_split(const tq_cache *c, int q_heads, int length, int n_splits, int *ns, int *sl) {
   constexpr long kTargetBlocks = 2048;
   constexpr int kTile = 32;
