@@ -17,3 +17,52 @@ def test_source_digest_ignores_comments_only(tmp_path):
     assert bench.source_digest(str(a)) == bench.source_digest(str(b))
     assert bench.source_digest(str(a)) != bench.source_digest(str(c))
 
+
+def _record(path, kernel, src, traffic):
+    path.write_text(f"# header\nkernel: {kernel}\nsource_sha256: {bench.source_digest(str(src))}\n"
+                    f"traffic_bytes_per_launch: {traffic}\n")
+
+
+def test_recorded_traffic_per_kernel(tmp_path, monkeypatch):
+    # a record is found under either decode kernel's name, is voided by a
+    # change to that kernel's source, and is not used while a decode
+    # variant is forced through the environment
+    src_m = tmp_path / "m.hip"
+    src_m.write_text("int m() { return 1; }\n")
+    src_s = tmp_path / "s.hip"
+    src_s.write_text("int s() { return 2; }\n")
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "DECODE_SOURCES", {"decode_mfma": str(src_m), "decode_split": str(src_s)})
+    monkeypatch.delenv("TQ_DECODE_VARIANT", raising=False)
+    _record(prof / "decode_mfma_wa_hbm_traffic.txt", "decode_mfma_kernel", src_m, 1000)
+    _record(prof / "decode_split_wb_hbm_traffic.txt", "decode_split_kernel", src_s, 2000)
+    assert bench.recorded_traffic("wa") == 1000
+    assert bench.recorded_traffic("wb") == 2000
+    assert bench.recorded_traffic("wc") is None
+    monkeypatch.setenv("TQ_DECODE_VARIANT", "ref")
+    assert bench.recorded_traffic("wa") is None
+    monkeypatch.delenv("TQ_DECODE_VARIANT")
+    src_s.write_text("int s() { return 3; }\n")
+    assert bench.recorded_traffic("wb") is None
+    assert bench.recorded_traffic("wa") == 1000
+
+
+def test_committed_traffic_records_parse():
+    # every committed counter summary names its kernel's source and carries
+    # the fields the bench reads
+    prof = os.path.join(ROOT, "profiles")
+    for name in sorted(os.listdir(prof)):
+        if not name.endswith("_hbm_traffic.txt"):
+            continue
+        fields = {}
+        with open(os.path.join(prof, name)) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    fields[k.strip()] = v.strip()
+        assert name.split("_")[0] + "_" + name.split("_")[1] in bench.DECODE_SOURCES, name
+        assert len(fields["source_sha256"]) == 64, name
+        assert int(float(fields["traffic_bytes_per_launch"])) > 0, name
+        assert float(fields["traffic_over_algorithmic"]) < 1.5, name
