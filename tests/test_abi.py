@@ -253,3 +253,23 @@ def test_int8_side_arguments():
     assert _qa(c, f, n=0) == tq.TQ_ERR_ARG
     # delegated stays V-only; INT8 K with a delegated V is fine
     assert _qa(_desc(f, kmode=3, vmode=2), f, n=0) == tq.TQ_OK
+
+
+def test_decode_workspace_any_group_size():
+    # the plain kernel takes any query group (eight heads a block, more
+    # blocks per KV head beyond that) and any split count: the workspace is
+    # the partials' size, counters first
+    f = _Fake()
+    for d, Hkv, Hq in ((256, 1, 256), (128, 2, 96), (32, 1, 3)):
+        c = _desc(f, d=d, B=1, H=Hkv, kb=2, vb=2)
+        for ns in (0, 1, 5, 300):
+            got = tq.lib().tq_decode_workspace_bytes(ctypes.byref(c), Hq, 1000, ns)
+            assert got > 0, (d, Hq, ns)
+            if ns:
+                # max/sum plus two d-wide accumulators per (query head, split),
+                # each region 256-byte aligned, after 256 KiB of counters
+                units = Hq * ns
+                want = 65536 * 4
+                for n in (units * 2, units * d, units * d):
+                    want += (n * 4 + 255) // 256 * 256
+                assert got == want, (d, Hq, ns, got, want)
