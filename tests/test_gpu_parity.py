@@ -226,6 +226,8 @@ DECODE_CASES = [
     ("g3_d64", 1, 2, 6, 64, 250, ("fp16", 0), ("packed", 2), "iid"),
     ("g12_d128", 1, 1, 12, 128, 200, ("packed", 4), ("packed", 4), "iid"),
     ("fp16_d256", 1, 1, 2, 256, 150, ("fp16", 0), ("fp16", 0), "iid"),
+    # 96 query heads on one KV head: twelve head blocks of eight
+    ("g96_d128", 1, 1, 96, 128, 150, ("packed", 2), ("packed", 2), "iid"),
 ]
 
 
