@@ -103,10 +103,11 @@ void copy_levels(const tq_side &s, const float *src, int n, float *dst) {
 
 // Context split of the plain decode.  A block walks its range in tiles of 32
 // or 64 positions for up to eight query heads; the automatic split aims at
-// about 2048 blocks (eight per compute unit) in multiples of 32 positions.
-// Any split length fits the block's LDS.
+// about 1024 blocks (four per compute unit, one round at the kernel's usual
+// occupancy) in multiples of 32 positions.  Any split length fits the
+// block's LDS.
 bool choose_split(const tq_cache *c, int q_heads, int length, int n_splits, int *ns, int *sl) {
-  constexpr long kTargetBlocks = 2048;
+  constexpr long kTargetBlocks = 1024;
   constexpr int kTile = 32;
   const int G = q_heads / c->kv_heads;
   int split;
