@@ -103,7 +103,8 @@ struct Lay {
   static constexpr int qwork = table_words<KB>();    // [GP][D + 4] rotated query
   static constexpr int red = qwork + GP * qstride;     // flag
   static constexpr int prog = red + 4;                 // [kMaxWaves] chunks done per wave
-  static constexpr int tail = red + 16;
+  static constexpr int qinv = red + 16;                // [8] per head: the score's query scale
+  static constexpr int tail = red + 24;
   // Merge slots of the main loop's waves: an area of their own when it fits
   // (a wave then writes its slot as soon as its own loop ends), else over
   // the tables once every wave is done with them.
@@ -298,9 +299,12 @@ struct Wave {
   Paging pg;           // PG: where the unit's rows live
   int unit;
   float sparse_lg;     // sparse-V threshold (log2), -inf = exact
+  float qinv;          // the lane's head (compact layout): the power of two
+                       // that undoes the query's scaling in B (see the prologue)
   float chunk_max;     // the last softmax's chunk maximum of the lane's head
-  float vscale;        // power of two, n vscale <= 32 for every norm seen, so
-                       // p n vscale < 2^13 fits fp16 (lowered as norms grow)
+  float vscale;        // per head (compact layout, the lane's head): a power
+                       // of two keeping the value weights p n vscale in fp16's
+                       // range (see softmax)
   // running state (compact layout: head col % GP)
   float m_run, l_run;
   float4_t accv[8];    // D layout: head col, coordinates of tile q
@@ -525,10 +529,23 @@ struct Wave {
 
   // Online softmax on compact scores (base-2 logits; -inf = masked).  The
   // accumulators are only rescaled when the running maximum grows by more
-  // than 2^8.  Returns the value MFMA's A operand: p n vscale as hi and lo
-  // fp16 rows.
-  template <bool TAIL>
-  __device__ __forceinline__ half8_t softmax(const float (&c)[NV], const float (&vn)[NV]) {
+  // than 2^8.  Returns the value MFMA's A operand: P = p n vscale as hi and lo
+  // fp16 rows (n: the positions' V norms, 1 for fp16 rows).
+  //
+  // The value scale (SCALED): P must fit fp16 (below 2^16) and the largest
+  // terms of a head must stay far above fp16's subnormal range, whatever the
+  // spread of the norms.  vscale is a power of two per head, so dividing it
+  // out at the end is exact.  It is lowered when a weight-times-norm of the
+  // chunk would give P > 2^13 (to 2^12 / the head's largest p n, rounded up
+  // to a power of two), and raised by 2^floor(growth) when the head's
+  // running maximum grows (its earlier terms shrink by 2^-growth), up to
+  // 2^40.  The largest term of a head therefore stays within [2^8, 2^13],
+  // where hi and lo carry full precision, unless the head's largest weights
+  // fall on rows of zero norm and every other weight is below 2^-30 of them;
+  // a row whose V norm is tiny next to others does not force the scale down
+  // unless its weight is large too.
+  template <bool TAIL, bool SCALED>
+  __device__ __forceinline__ half8_t softmax(const float (&c)[NV], const float (&n)[NV]) {
     float cmax = c[0];
 #pragma unroll
     for (int j = 1; j < NV; ++j) cmax = fmaxf(cmax, c[j]);
@@ -538,39 +555,46 @@ struct Wave {
     if (__ballot(grow)) {
       const float m_new = grow ? cmax : m_run;
       const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+      float f = alpha;
+      if (SCALED && grow) {
+        // raise the scale by the power of two the maximum grew by (a first
+        // maximum, m_run = -inf, leaves it at its initial 2^40)
+        const float up = fminf(ldexpf(1.0f, static_cast<int>(fminf(m_new - m_run, 64.0f))), kVscaleMax / vscale);
+        vscale *= up;
+        f *= up;
+      }
       m_run = m_new;
       l_run *= alpha;
-      scale_heads(alpha);
+      scale_heads(f);
+    }
+    float p[NV], P[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      p[j] = __builtin_amdgcn_exp2f(c[j] - m_run);
+      if (TAIL) p[j] = (c[j] == -INFINITY) ? 0.0f : p[j];
+      l_run += p[j];
+      P[j] = p[j] * n[j];
+    }
+    if (SCALED) {
+      float lm = P[0];
+#pragma unroll
+      for (int j = 1; j < NV; ++j) lm = fmaxf(lm, P[j]);
+      if (__ballot(lm * vscale > 8192.0f)) {
+        // lower the scale of the heads whose largest p n asks for it (the
+        // whole wave runs this, as scale_heads reads other lanes)
+        const float hm = head_max<GP>(lm);
+        const float vs = (hm * vscale > 8192.0f) ? 4096.0f / pow2_ceil(hm) : vscale;
+        const float f = vs / vscale;
+        vscale = vs;
+        scale_heads(f);
+      }
+#pragma unroll
+      for (int j = 0; j < NV; ++j) P[j] *= vscale;
     }
     uint32_t wh[NV / 2], wl[NV / 2];
 #pragma unroll
-    for (int j = 0; j < NV; j += 2) {
-      float p0 = __builtin_amdgcn_exp2f(c[j] - m_run);
-      float p1 = __builtin_amdgcn_exp2f(c[j + 1] - m_run);
-      if (TAIL) {
-        p0 = (c[j] == -INFINITY) ? 0.0f : p0;
-        p1 = (c[j + 1] == -INFINITY) ? 0.0f : p1;
-      }
-      l_run += p0 + p1;
-      split_pair(p0 * vn[j], p1 * vn[j + 1], wh[j / 2], wl[j / 2]);
-    }
+    for (int j = 0; j < NV; j += 2) split_pair(P[j], P[j + 1], wh[j / 2], wl[j / 2]);
     return weights_operand(wh, wl);
-  }
-
-  // Keep n vscale <= 32 for the norms of this chunk: if a larger norm shows
-  // up, lower vscale (a power of two) and the accumulators with it.
-  __device__ __forceinline__ void fit_vscale(const float (&vraw)[NV]) {
-    float lm = vraw[0];
-#pragma unroll
-    for (int j = 1; j < NV; ++j) lm = fmaxf(lm, vraw[j]);
-    if (__ballot(lm * vscale > 32.0f)) {
-      for (int m = 32; m >= 1; m >>= 1) lm = fmaxf(lm, __shfl_xor(lm, m));
-      const float nv = fminf(32.0f / pow2_ceil(lm), kVscaleMax);
-      const float f = nv / vscale;
-      vscale = nv;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) accv[i] *= f;
-    }
   }
 
   // Optional raw scores (natural-log units) of the real heads.
@@ -632,18 +656,16 @@ struct Wave {
   template <bool TAIL>
   __device__ __forceinline__ void cold_chunk(int t0, int we, const ChunkData<KB, GP> &c, float *scores,
                                              long score_row0, int length) {
-    float s[8], cs[NV], vn[NV];
+    float s[8], cs[NV];
     score(c, s);
     compact(s, cs);
-    fit_vscale(c.vn);
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      if (KB) cs[j] *= c.kn[j];
-      vn[j] = c.vn[j] * vscale;
+      cs[j] *= KB ? c.kn[j] * qinv : qinv;
       if (TAIL && t0 + cpos + j >= we) cs[j] = -INFINITY;
     }
     if (scores) store_scores<TAIL>(t0, we, cs, scores, score_row0, length);
-    const half8_t ap = softmax<TAIL>(cs, vn);
+    const half8_t ap = softmax<TAIL, true>(cs, c.vn);
     // sparse-V: every weight of the chunk, for every head, below the
     // threshold times the running maximum (which never exceeds the final
     // one): the chunk's values are skipped; its weights stay in the sum
@@ -662,7 +684,7 @@ struct Wave {
     compact(s, cs);
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      if (KB) cs[j] *= c.kn[j];
+      cs[j] *= KB ? c.kn[j] * qinv : qinv;
       vn[j] = 1.0f;
       const int t = t0 + cpos + j;
       if (t < wb || t >= we) cs[j] = -INFINITY;
@@ -674,7 +696,7 @@ struct Wave {
         if (t >= wb && t < we) scores[(score_row0 + col % GP) * length + t] = cs[j] * kLn2;
       }
     }
-    const half8_t ap = softmax<true>(cs, vn);
+    const half8_t ap = softmax<true, false>(cs, vn);
     // fp16 ring rows: tile q covers coordinates 16 q + col
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
@@ -976,18 +998,32 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   // coordinates 2 j, 2 j + 1 (hi at [0, 64), lo at [64, 128) of the row).
   // Even lanes pair their qa with the odd neighbour's, odd lanes their qb
   // with the even neighbour's.
+  // The head's B column is also scaled by a power of two 2^e that puts its
+  // largest element in [128, 256): hi and lo then carry full precision
+  // whatever the query's magnitude (fp16 ranges from 2^-24 to 65504), and
+  // the scores are multiplied by the exact 2^-e (qinv).
   uint32_t *qhl = reinterpret_cast<uint32_t *>(qw);
+  float *qinvs = reinterpret_cast<float *>(lds + L::qinv);
   if (wave < G) {
     const float qscale = k_packed ? kLog2e / static_cast<float>(D) : kLog2e / sqrtf(static_cast<float>(D));
+    float amax = fmaxf(fabsf(qa), fabsf(qb));
+    for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+    amax *= qscale;
+    int ex = 0;
+    if (amax > 0.0f) (void)frexpf(amax, &ex);       // amax = f 2^ex, f in [0.5, 1)
+    const float qs = ldexpf(qscale, 8 - ex);
     const float pa = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(qa), 0xb1, 0xf, 0xf, false));
     const float pb = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(qb), 0xb1, 0xf, 0xf, false));
     const bool odd = lane & 1;
     const float x0 = odd ? pb : qa, x1 = odd ? qb : pa;
     uint32_t h, l;
-    split_pair(x0 * qscale, x1 * qscale, h, l);
+    split_pair(x0 * qs, x1 * qs, h, l);
     const int j = (odd ? 32 : 0) + (lane >> 1);
     qhl[wave * L::qstride + j] = h;
     qhl[wave * L::qstride + 64 + j] = l;
+    if (lane == 0) qinvs[wave] = ldexpf(1.0f, ex - 8);
+  } else if (wave < GP && lane == 0) {
+    qinvs[wave] = 1.0f;
   }
   if (lane == 0) prog[wave] = 0;
   __syncthreads();  // tables, rotated query and progress counters complete
@@ -997,6 +1033,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
     // products, which the score adds (column h + GP into column h)
     const int hsel = W.col < GP ? W.col : W.col - GP;
     const bool live = W.col < 2 * GP && hsel < G;
+    W.qinv = qinvs[W.col % GP];
     const uint32_t *row = qhl + (live ? hsel : 0) * L::qstride + (W.col < GP ? 0 : 64) + 16 * W.grp;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {

@@ -72,9 +72,14 @@ __device__ __forceinline__ void encode_row(const float (&x)[4], int t,
 }
 
 // INT8 per-token absmax (mlxcel "TurboQuant KV cache", "Available modes"):
-// scale = max|x| / 127, code = x / scale rounded to the nearest integer
-// (ties to even), clamped to [-127, 127]; float32 throughout.  Lane t writes
-// word t of the row (its four codes, coordinate 4 t + e in byte e).
+// a = max|x|, code = 127 x / a rounded to the nearest integer (ties to even),
+// taken exactly; the stored scale is a / 127 in float32.  127 x is exact in
+// float32 (an fp16 significand times 7 bits), so the correctly rounded
+// quotient is within one code of the answer, and the sign of 2 (127 x) -
+// (2 k +- 1) a, computed by one fma (an exact product, one rounding, which
+// keeps the sign and zero), says on which side of k +- 1/2 the exact
+// quotient lies.  Lane t writes word t of the row (its four codes,
+// coordinate 4 t + e in byte e).
 template <int D>
 __device__ __forceinline__ void encode_int8(const float (&x)[4], int t, bool write, uint32_t *row_out,
                                             float *scale_out) {
@@ -85,8 +90,20 @@ __device__ __forceinline__ void encode_int8(const float (&x)[4], int t, bool wri
   uint32_t w = 0;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const float v = scale > 0.0f ? x[e] / scale : 0.0f;
-    const int c = min(127, max(-127, static_cast<int>(rintf(v))));
+    int c = 0;
+    if (a > 0.0f) {
+      const float y2 = 254.0f * x[e];  // 2 (127 x), exact
+      float k = rintf(0.5f * y2 / a);
+      const float up = fmaf(-(2.0f * k + 1.0f), a, y2);  // sign of 127 x / a - (k + 1/2)
+      const float dn = fmaf(-(2.0f * k - 1.0f), a, y2);  // sign of 127 x / a - (k - 1/2)
+      const bool odd = (static_cast<int>(k) & 1) != 0;
+      if (up > 0.0f || (up == 0.0f && odd)) {
+        k += 1.0f;
+      } else if (dn < 0.0f || (dn == 0.0f && odd)) {
+        k -= 1.0f;
+      }
+      c = min(127, max(-127, static_cast<int>(k)));
+    }
     w |= (static_cast<uint32_t>(c) & 0xffu) << (8 * e);
   }
   if (write) {

@@ -61,7 +61,7 @@ __all__ = [
     "row_words", "bytes_per_token_head", "quantize", "pack_codes",
     "unpack_codes", "codes_from_rotated", "dequantize", "attention", "PackedSide", "DelegatedSide",
     "decode_attention", "sparse_v_bound", "sparse_v_attention",
-    "int8_quantize", "int8_dequantize", "int8_bytes_per_token_head",
+    "int8_quantize", "int8_levels", "int8_dequantize", "int8_bytes_per_token_head",
 ]
 
 
@@ -416,22 +416,30 @@ def sparse_v_attention(q, k, v, tau):
 # modes": int8 is per-token INT8 absmax quantization, ~2x)
 # ---------------------------------------------------------------------------
 
+def int8_levels(x):
+    """The quantity each INT8 code rounds: v_j = 127 x_j / max_i |x_i| per
+    row, in float64 (0 for a zero row).  fp16 inputs are exact in float64,
+    127 x_j is exact, and the one rounding of the division cannot move v
+    across a half-integer: v is a ratio of fp16 multiples whose distance from
+    any half-integer, when not zero, is far above the float64 rounding."""
+    x64 = np.asarray(x).astype(np.float64)
+    a = np.max(np.abs(x64), axis=-1)
+    safe = np.where(a > 0, a, 1.0)
+    return np.where(a[..., None] > 0, 127.0 * x64 / safe[..., None], 0.0)
+
+
 def int8_quantize(x):
-    """Per row (one token of one head): a = max_j |x_j|, scale = a / 127 and
-    code_j = x_j / scale rounded to the nearest integer (ties to even),
-    clamped to [-127, 127]; a zero row has scale 0 and codes 0.  The scale
-    and the division are float32 (the codes are integers decided by float
-    arithmetic, so the reference takes the decision in the precision the
-    kernels use: fp16 inputs are exact in float32, and float32 division and
-    round-to-nearest-even are IEEE operations).  Returns (codes int8
+    """Per row (one token of one head): a = max_j |x_j|, code_j = the integer
+    nearest to 127 x_j / a (ties to even), which lies in [-127, 127] by
+    construction; the stored scale is a / 127 rounded to float32 (the
+    storage format keeps a float32 scale, and the dequantized row is code x
+    scale).  A zero row has scale 0 and codes 0.  The decision is the exact
+    definition, taken in float64 (see ``int8_levels``).  Returns (codes int8
     [..., d], scales float32 [...])."""
-    x32 = np.asarray(x).astype(np.float32)
-    a = np.max(np.abs(x32), axis=-1)
-    scale = (a / np.float32(127.0)).astype(np.float32)
-    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
-    v = (x32 / safe[..., None]).astype(np.float32)
-    codes = np.clip(np.rint(v), -127, 127)
-    codes = np.where(scale[..., None] > 0, codes, 0).astype(np.int8)
+    x64 = np.asarray(x).astype(np.float64)
+    a = np.max(np.abs(x64), axis=-1)
+    codes = np.rint(int8_levels(x)).astype(np.int8)
+    scale = (a / 127.0).astype(np.float32)
     return codes, scale
 
 

@@ -6,9 +6,17 @@ sampled parts it can compute in seconds:
 
 * the codes and norms of a slice of rows of sampled (batch, KV head) units,
   against the oracle's quantization of the same fp16 rows;
-* every query head of sampled units: the decode output against float64
-  attention over the rows the oracle rebuilds from what the GPU wrote
-  (dequantized packed rows, fp16 rows as stored, the delegated ring).
+* every query head of sampled units: the decode output and the scaled
+  logits against float64 attention over the rows the oracle rebuilds from
+  what the GPU wrote (dequantized packed rows, INT8 rows, fp16 rows as
+  stored, the delegated ring).  The outputs come from the call the bench
+  times (no score output); a second call with the score output must give
+  bit-identical outputs.
+
+Two configurations state their K/V distribution as "the same as config 1",
+which reads either as the i.i.d. N(0, 1) rows of the first configuration or
+as the log-normal channel scales of the second; both readings run here at the
+asymmetric 16K and the 3.5-bit 32K shapes.
 """
 import numpy as np
 import pytest
@@ -27,8 +35,12 @@ import compressed_decode_attention_append_amd as tq  # noqa: E402
 FULL = {
     "c2_sym4_4k": (1, 8, 32, 128, 4096, ("packed", 4), ("packed", 4), 0, "channel", 0.01, 0),
     "c3_asym_16k": (8, 8, 32, 128, 16384, ("fp16", 0), ("packed", 4), 0, "channel", 0.01, 1),
+    "c3_asym_16k_iid": (8, 8, 32, 128, 16384, ("fp16", 0), ("packed", 4), 0, "iid", 0.0, 1),
     "c4_tq35_32k": (4, 8, 32, 128, 32768, ("packed", 3), ("packed", 4), 0, "channel", 0.01, 8192),
+    "c4_tq35_32k_iid": (4, 8, 32, 128, 32768, ("packed", 3), ("packed", 4), 0, "iid", 0.0, 8192),
     "c5_delegated_64k": (16, 4, 32, 128, 65536, ("fp16", 0), ("delegated", 4), 256, "channel", 0.0, 0),
+    # the pages' int8 mode at the asymmetric shape (a comparison workload)
+    "c3_int8_16k": (8, 8, 32, 128, 16384, ("int8", 0), ("int8", 0), 0, "channel", 0.01, 1),
 }
 
 
@@ -39,6 +51,9 @@ def _unit_rows(cache, side, b, h, length):
     d = cache.head_dim
     if spec.mode == "fp16":
         return cache.tensors[side + "_fp16"][b, h, :length].cpu().numpy().astype(np.float64)
+    if spec.mode == "int8":
+        codes = cache.tensors[side + "_codes"][b, h, :length].cpu().numpy().view(np.int8)
+        return oracle.int8_dequantize(codes, cache.tensors[side + "_norms"][b, h, :length].cpu().numpy())
     R = oracle.rotation_matrix(cache.seed, d)
     c, _ = oracle.lloyd_max(d, spec.bits)
     n_cold = length if spec.mode == "packed" else max(0, length - spec.hot)
@@ -81,13 +96,22 @@ def test_full_size_sampled(name):
                 samples[(b, h, "new")] = (base, k[b, h, :512].cpu().numpy(), v[b, h, :512].cpu().numpy())
         del k, v
     q = synth.q_torch(77, B, Hq, d, device="cuda:0")
-    out = cache.decode_attention(q, T)
+    out = cache.decode_attention(q, T)                   # as the bench calls it
+    out2, sc = cache.decode_attention(q, T, scores=True)  # the same, with the logits
     torch.cuda.synchronize()
+    assert torch.equal(out, out2)
 
     # codes and norms of sampled rows
     for key, (start, krows, vrows) in samples.items():
         b, h = key[0], key[1]
         for side, spec, rows in (("k", kspec, krows), ("v", vspec, vrows)):
+            if spec.mode == "int8":
+                c_o, s_o = oracle.int8_quantize(rows)
+                got = cache.tensors[side + "_codes"][b, h, start:start + rows.shape[0]].cpu().numpy().view(np.int8)
+                sc_got = cache.tensors[side + "_norms"][b, h, start:start + rows.shape[0]].cpu().numpy()
+                assert np.array_equal(got, c_o), f"{name} {side} ({b},{h}): {int(np.sum(got != c_o))} codes differ"
+                assert np.array_equal(sc_got, s_o)
+                continue
             if spec.mode != "packed":
                 continue
             R = oracle.rotation_matrix(0, d)
@@ -100,14 +124,17 @@ def test_full_size_sampled(name):
             norms = cache.tensors[side + "_norms"][b, h, start:start + rows.shape[0]].cpu().numpy()
             assert np.all(np.abs(norms - n_o[0, 0]) <= 1e-6 * n_o[0, 0] + 1e-30)
 
-    # decode outputs of every query head of the sampled units
+    # decode outputs and logits of every query head of the sampled units
     qn = q.cpu().numpy()
     got = out.cpu().numpy()
     for (b, h) in pick:
         kr = _unit_rows(cache, "k", b, h, T)[None, None]
         vr = _unit_rows(cache, "v", b, h, T)[None, None]
         heads = slice(h * G, (h + 1) * G)
-        o_ref, _ = oracle.decode_attention(qn[b:b + 1, heads], kr, vr)
+        o_ref, s_ref = oracle.decode_attention(qn[b:b + 1, heads], kr, vr)
+        ok, worst = rows_close(sc[b, heads].cpu().numpy(), s_ref[0])
+        print(f"{name} unit ({b},{h}): scores worst rel {worst:.3e}")
+        assert ok, f"{name} unit ({b},{h}): scores worst {worst}"
         ok, worst = rows_close(got[b, heads], o_ref[0])
         print(f"{name} unit ({b},{h}): out worst rel {worst:.3e}")
         assert ok, f"{name} unit ({b},{h}): worst {worst}"

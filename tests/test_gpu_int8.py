@@ -1,6 +1,6 @@
 """GPU parity of the INT8 per-token absmax cache (mlxcel "TurboQuant KV
-cache", "Available modes": int8) against the oracle: codes bit-exact and
-scales equal (both sides decide in float32), dequantized rows, decode over
+cache", "Available modes": int8) against the oracle: codes bit-exact against
+the exact definition round(127 x / max|x|) and scales equal, dequantized rows, decode over
 the GPU-written rows (the plain split kernel), paged storage, and the
 policy's int8 mode."""
 import numpy as np
@@ -66,6 +66,27 @@ def test_int8_codes_and_scales(d, dist):
         pos += n
     # untouched rows stay zero
     assert int(cache.tensors["k_codes"][:, :, pos:].abs().sum()) == 0
+
+
+def test_int8_codes_on_exact_half_steps():
+    # rows whose elements sit exactly on half steps of the code grid (127 x /
+    # max|x| = k + 1/2) or next to them: the encoder must round as the exact
+    # definition does (ties to even), where dividing by the float32 scale
+    # would not; 8192 rows through the encoder
+    rng = np.random.default_rng(11)
+    B, H, n, d = 1, 2, 4096, 128
+    x = (rng.standard_normal((B, H, n, d)) * rng.uniform(0.01, 300.0, (B, H, n, 1))).astype(np.float16)
+    x[:, :, :, 0] = np.float16(127.0)
+    x[:, :, ::2, 1:40] = (rng.integers(-126, 126, (B, H, n // 2, 39)) + 0.5).astype(np.float16)
+    x[:, :, 7, :8] = np.array([-34.6, 53.6, 39.16, 51.62, 23.88, -64.8, 92.9, -103.25], np.float16)
+    cache = tq.TQCache(B, H, d, n, S("int8"), S("int8"))
+    xt = torch.from_numpy(x).cuda()
+    cache.quantize_append(xt, xt, 0)
+    torch.cuda.synchronize()
+    c, s = _int8_rows(cache, "k", 0, n)
+    c_o, s_o = oracle.int8_quantize(x)
+    assert np.array_equal(c, c_o), f"{int(np.sum(c != c_o))} codes differ"
+    assert np.array_equal(s, s_o)
 
 
 def test_int8_zero_rows_and_dequantize():

@@ -228,6 +228,12 @@ DECODE_CASES = [
     ("fp16_d256", 1, 1, 2, 256, 150, ("fp16", 0), ("fp16", 0), "iid"),
     # 96 query heads on one KV head: twelve head blocks of eight
     ("g96_d128", 1, 1, 96, 128, 150, ("packed", 2), ("packed", 2), "iid"),
+    # the i.i.d. reading of the 3.5-bit and asymmetric workloads' "same K/V
+    # distribution as config 1" (the most diffuse softmax) on the matrix-core
+    # kernel's shapes
+    ("tq35_d128_iid", 2, 2, 8, 128, 2100, ("packed", 3), ("packed", 4), "iid"),
+    ("asym_d128_iid", 2, 2, 8, 128, 1337, ("fp16", 0), ("packed", 4), "iid"),
+    ("sym4_d128_iid", 1, 8, 32, 128, 1500, ("packed", 4), ("packed", 4), "iid"),
 ]
 
 
