@@ -64,6 +64,7 @@ class tq_cache(ctypes.Structure):
         ("block_table", ctypes.c_void_p),
         ("block_size", ctypes.c_int),
         ("max_blocks", ctypes.c_int),
+        ("num_blocks", ctypes.c_int),
     ]
 
 
@@ -91,6 +92,8 @@ def lib():
         L.tq_quantize_append.restype = I
         L.tq_decode_workspace_bytes.argtypes = [ctypes.POINTER(tq_cache), I, I, I]
         L.tq_decode_workspace_bytes.restype = ctypes.c_size_t
+        L.tq_decode_workspace_init.argtypes = [P, ctypes.c_size_t, P]
+        L.tq_decode_workspace_init.restype = I
         L.tq_decode_attention.argtypes = [ctypes.POINTER(tq_cache), P, I, I, I, P, P, P,
                                           ctypes.c_size_t, P]
         L.tq_decode_attention.restype = I
@@ -179,6 +182,16 @@ def _stream_handle(stream) -> int:
     return int(s.cuda_stream)
 
 
+WORKSPACE_COUNTER_BYTES = 256 * 1024
+
+
+def decode_workspace_init(workspace, stream=None) -> None:
+    """Zero the counter region of a device workspace tensor (tq.h:
+    tq_decode_workspace_init); needed once before its first decode."""
+    _check(lib().tq_decode_workspace_init(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                          _stream_handle(stream)), "tq_decode_workspace_init")
+
+
 def read_probe(buf, sink, stream=None) -> None:
     """Stream-read the device tensor `buf` (a multiple of 16 bytes, 16-byte
     aligned) with the library's probe kernel and write the xor of its 32-bit
@@ -227,12 +240,20 @@ class TQCache:
             bs = int(block_size)
             if bs <= 0 or self.capacity % bs:
                 raise ValueError("paged cache: capacity must be a multiple of block_size")
-            table = block_table.to(device=device, dtype=torch.int32).contiguous()
-            if tuple(table.shape) != (self.batch, self.capacity // bs):
+            if tuple(block_table.shape) != (self.batch, self.capacity // bs):
                 raise ValueError(f"block_table must be [{self.batch}][{self.capacity // bs}]")
+            if int(num_blocks) < 1:
+                raise ValueError("paged cache: num_blocks must be at least 1")
+            # the table is at hand here, so its entries are range-checked on
+            # the host (the library itself only guards them on the device)
+            host = block_table.detach().to("cpu", torch.int64)
+            if host.numel() and (int(host.min()) < 0 or int(host.max()) >= int(num_blocks)):
+                raise ValueError(f"block_table entries must lie in [0, {int(num_blocks)})")
+            table = block_table.to(device=device, dtype=torch.int32).contiguous()
             self.block_table, self.block_size, self.num_blocks = table, bs, int(num_blocks)
             self.desc.block_table = _ptr(table)
             self.desc.block_size, self.desc.max_blocks = bs, self.capacity // bs
+            self.desc.num_blocks = self.num_blocks
         for name, spec, side in (("k", k, self.desc.k), ("v", v, self.desc.v)):
             side.mode = _MODES[spec.mode]
             side.bits = int(spec.bits) if spec.mode in ("packed", "delegated") else 0
@@ -292,7 +313,8 @@ class TQCache:
         if need == 0:
             raise TQError(TQ_ERR_ARG, "tq_decode_workspace_bytes")
         if self._ws is None or self._ws.numel() < need:
-            self._ws = torch.zeros(need, dtype=torch.uint8, device=self.device)
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+            decode_workspace_init(self._ws)
         return self._ws
 
     def decode_attention(self, q, length: int, n_splits: int = 0, out=None, scores=False,
@@ -354,5 +376,6 @@ class TQCache:
 __all__ = [
     "TQError", "tq_side", "tq_cache", "lib", "status_string", "split_bits", "row_words",
     "sign_words", "build_codebook", "Codebook", "SideSpec", "TQCache", "SIDE_FP16",
+    "decode_workspace_init", "WORKSPACE_COUNTER_BYTES",
     "SIDE_PACKED", "SIDE_DELEGATED",
 ]

@@ -61,7 +61,7 @@ int check_cache(const tq_cache *c) {
   if (c->block_table) {
     // paged: whole 32-position chunks per block, and the table covers the
     // capacity exactly
-    if (c->block_size < 32 || c->block_size % 32 || c->max_blocks < 1) return TQ_ERR_ARG;
+    if (c->block_size < 32 || c->block_size % 32 || c->max_blocks < 1 || c->num_blocks < 1) return TQ_ERR_ARG;
     if (static_cast<long long>(c->block_size) * c->max_blocks != c->capacity) return TQ_ERR_ARG;
   }
   int r = check_side(c->k, false);
@@ -75,6 +75,7 @@ tq::Paging paging_of(const tq_cache *c) {
   pg.bs = c->block_table ? c->block_size : 0;
   pg.max_blocks = c->block_table ? c->max_blocks : 0;
   pg.kv_heads = c->kv_heads;
+  pg.num_blocks = c->block_table ? c->num_blocks : 0;
   return pg;
 }
 
@@ -125,8 +126,8 @@ bool choose_split(const tq_cache *c, int q_heads, int length, int n_splits, int 
 }
 
 // Which decode runs: the matrix-core kernel when it supports the shape,
-// else the plain one.  TQ_DECODE_VARIANT=ref|mfma forces one (for A/B
-// measurements); forcing mfma on an unsupported shape falls back to ref.
+// else the plain one.  TQ_DECODE_VARIANT=ref forces the plain kernel (A/B
+// measurements and the cross-check tests).
 enum Variant { kRef, kMfma };
 
 Variant pick_variant(const tq::DecodeParams &p) {
@@ -322,6 +323,14 @@ int tq_decode_attention_sparse(const tq_cache *cache, const void *q, int q_heads
   p.ws_part_off = tq::kCounterBytes;
   const hipError_t e = (v == kMfma) ? tq::launch_decode_mfma(p, static_cast<hipStream_t>(hip_stream))
                                     : tq::launch_decode_ref(p, static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
+int tq_decode_workspace_init(void *workspace, size_t workspace_bytes, void *hip_stream) {
+  if (!workspace) return TQ_ERR_ARG;
+  if (workspace_bytes < tq::kCounterBytes || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return TQ_ERR_WORKSPACE;
+  const hipError_t e = tq::launch_zero_fill(workspace, tq::kCounterBytes, static_cast<hipStream_t>(hip_stream));
   return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
 

@@ -318,8 +318,9 @@ struct Wave {
 
   // First storage row of the chunk at t0.  Paged: t0 is a multiple of 32
   // and a block a multiple of 32 positions, so the chunk's rows are
-  // consecutive rows of one block.  (A wave past the end of its split may
-  // ask for t0 >= capacity: it reads nothing, and the table is not read.)
+  // consecutive rows of one block; -1 when the block lies outside the pools.
+  // (A wave past the end of its split may ask for t0 >= capacity: it reads
+  // nothing, and the table is not read.)
   __device__ __forceinline__ long row_of(int t0) const {
     if (!PG) return t0;
     return t0 < capacity ? cache_row(pg, unit, t0, capacity) : 0L;
@@ -337,16 +338,18 @@ struct Wave {
   __device__ __forceinline__ long row_from(uint32_t blk, int t0) const {
     if (!PG) return t0;
     const int kv = unit % pg.kv_heads;
-    const long bl = static_cast<long>(__builtin_amdgcn_readfirstlane(blk));
-    return (bl * pg.kv_heads + kv) * pg.bs + t0 % pg.bs;
+    const long bl = valid_block(pg, static_cast<int>(__builtin_amdgcn_readfirstlane(blk)));
+    return bl < 0 ? -1L : (bl * pg.kv_heads + kv) * pg.bs + t0 % pg.bs;
   }
 
   __device__ __forceinline__ void load(int t0, ChunkData<KB, GP> &c) const { load_row(row_of(t0), t0, c); }
 
   // rows [t0, t0 + 32) at most, from storage row row0 on; rows past the
-  // unit's capacity read 0
+  // unit's capacity, and every row of an out-of-range block (row0 = -1),
+  // read 0
   __device__ __forceinline__ void load_row(long row0, int t0, ChunkData<KB, GP> &c) const {
-    const int rows = min(capacity - t0, kChunk);
+    const int rows = row0 < 0 ? 0 : min(capacity - t0, kChunk);
+    row0 = row0 < 0 ? 0L : row0;
     const auto rk = rsrc(kbase + row0 * kRowBytes, rows * kRowBytes);
     const auto rkn = rsrc(knbase + row0 * 4, rows * 4);
     const auto rv = rsrc(vbase + row0 * 64, rows * 64);

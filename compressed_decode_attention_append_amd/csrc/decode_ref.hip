@@ -3,7 +3,8 @@
 // Cache Quantization Works": scores from the compressed representation; FAQ
 // on dequantization: the stored rotation and codebooks).  It serves every
 // cache layout the matrix-core kernel does not: head_dim other than 128,
-// INT8 sides, paged delegated caches.
+// INT8 sides, code widths other than 3 or 4 bits for K and 4 for V, more
+// than eight query heads per KV head.
 //
 // Grid (n_splits, B * Hkv, head groups); one block handles up to eight query
 // heads of one KV head over one contiguous range of positions:
@@ -91,23 +92,30 @@ __device__ __forceinline__ int v_hot_start(const DecodeParams &p) {
 }
 
 // Start of piece `piece` (GW words) of the stored row of position t, or null
-// where that row kind is shorter (the cold rows of a delegated V).
+// where that row kind is shorter (the cold rows of a delegated V).  A
+// position in a block outside the paged pools reads the zero row.
 template <int D, int GW>
 __device__ __forceinline__ const uint32_t *piece_src(const DecodeParams &p, const RefLayout &L, long bk, int t,
                                                      bool is_k, int piece, int hot_start) {
   const uint32_t *src;
   if (is_k) {
-    src = p.k.mode == TQ_SIDE_FP16
-              ? reinterpret_cast<const uint32_t *>(p.k.fp16 + cache_row(p.pg, bk, t, p.capacity) * D)
-              : p.k.codes + cache_row(p.pg, bk, t, p.capacity) * p.k.words;
+    const long r = cache_row(p.pg, bk, t, p.capacity);
+    if (r < 0) return kZeroRow + piece * GW;
+    src = p.k.mode == TQ_SIDE_FP16 ? reinterpret_cast<const uint32_t *>(p.k.fp16 + r * D) : p.k.codes + r * p.k.words;
   } else if (t >= hot_start) {
     if (piece * GW >= L.vw_hot) return nullptr;
-    src = p.v.mode == TQ_SIDE_FP16
-              ? reinterpret_cast<const uint32_t *>(p.v.fp16 + cache_row(p.pg, bk, t, p.capacity) * D)
-              : reinterpret_cast<const uint32_t *>(p.v.fp16 + (bk * p.v.hot + t % p.v.hot) * D);
+    if (p.v.mode == TQ_SIDE_FP16) {
+      const long r = cache_row(p.pg, bk, t, p.capacity);
+      if (r < 0) return kZeroRow + piece * GW;
+      src = reinterpret_cast<const uint32_t *>(p.v.fp16 + r * D);
+    } else {
+      src = reinterpret_cast<const uint32_t *>(p.v.fp16 + (bk * p.v.hot + t % p.v.hot) * D);
+    }
   } else {
     if (piece * GW >= L.vw_cold) return nullptr;
-    src = p.v.codes + cache_row(p.pg, bk, t, p.capacity) * p.v.words;
+    const long r = cache_row(p.pg, bk, t, p.capacity);
+    if (r < 0) return kZeroRow + piece * GW;
+    src = p.v.codes + r * p.v.words;
   }
   return src + piece * GW;
 }
@@ -178,9 +186,13 @@ struct Stager {
     }
     norm = 1.0f;
     if (tid < n) {
-      if (p.k.mode != TQ_SIDE_FP16) norm = p.k.norms[cache_row(p.pg, bk, t + tid, p.capacity)];
+      if (p.k.mode != TQ_SIDE_FP16) {
+        const long r = cache_row(p.pg, bk, t + tid, p.capacity);
+        norm = r < 0 ? 0.0f : p.k.norms[r];
+      }
     } else if (tid >= 64 && tid < 64 + n && t + tid - 64 < hot_start) {
-      norm = p.v.norms[cache_row(p.pg, bk, t + tid - 64, p.capacity)];
+      const long r = cache_row(p.pg, bk, t + tid - 64, p.capacity);
+      norm = r < 0 ? 0.0f : p.v.norms[r];
     }
   }
 

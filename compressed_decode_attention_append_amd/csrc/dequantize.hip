@@ -26,11 +26,14 @@ __global__ __launch_bounds__(kBlock) void dequantize_kernel(const DequantParams 
   const long r = live ? task : 0;
   const long bh = r / p.count;
   const int pos = p.start + static_cast<int>(r % p.count);
-  const uint32_t *row = p.s.codes + cache_row(p.pg, bh, pos, p.capacity) * p.s.words;
+  // a position in a block outside the paged pools reads the zero row
+  const long sr = cache_row(p.pg, bh, pos, p.capacity);
+  const uint32_t *row = sr < 0 ? kZeroRow : p.s.codes + sr * p.s.words;
+  const float n = sr < 0 ? 0.0f : p.s.norms[sr];
   if (p.s.mode == TQ_SIDE_INT8) {
     // INT8 rows: code times the row's scale, no rotation
     const uint32_t w = row[t];
-    const float sc = p.s.norms[cache_row(p.pg, bh, pos, p.capacity)];
+    const float sc = n;
     if (live) {
       const float4 o = make_float4(int8_at(w, 0) * sc, int8_at(w, 1) * sc, int8_at(w, 2) * sc, int8_at(w, 3) * sc);
       *reinterpret_cast<float4 *>(p.out + r * D + 4 * t) = o;
@@ -41,7 +44,6 @@ __global__ __launch_bounds__(kBlock) void dequantize_kernel(const DequantParams 
 #pragma unroll
   for (int e = 0; e < 4; ++e) v[e] = cent[extract_code(row, p.s.bits, 4 * t + e)];
   fwht_group4<TPR>(v, t);
-  const float n = p.s.norms[cache_row(p.pg, bh, pos, p.capacity)];
   const float scale = n / sqrtf(static_cast<float>(D));
   if (live) {
     float4 o;

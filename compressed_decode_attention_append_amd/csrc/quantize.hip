@@ -152,19 +152,22 @@ __global__ __launch_bounds__(kBlock) void quantize_append_kernel(const QuantizeP
   const SideDev &s = side ? p.v : p.k;
   const uint16_t *src = (side ? p.v_new : p.k_new) + (bh * p.n_new + i) * D;
   const float *th = thr[side];
+  // the storage row; a position in a block outside the paged pools is not
+  // written (-1)
+  const long srow = cache_row(p.pg, bh, pos, p.capacity);
+  const bool put = live && srow >= 0;
+  const long orow = srow < 0 ? 0L : srow;
 
   if (s.mode == TQ_SIDE_INT8) {
     float x[4];
     load4<D>(src, t, x);
-    encode_int8<D>(x, t, live, s.codes + cache_row(p.pg, bh, pos, p.capacity) * s.words,
-                   s.norms + cache_row(p.pg, bh, pos, p.capacity));
+    encode_int8<D>(x, t, put, s.codes + orow * s.words, s.norms + orow);
   } else if (s.mode == TQ_SIDE_PACKED) {
     float x[4];
     load4<D>(src, t, x);
-    encode_row<D>(x, t, p.sign, th, s.bits, s.words, live,
-                  s.codes + cache_row(p.pg, bh, pos, p.capacity) * s.words, s.norms + cache_row(p.pg, bh, pos, p.capacity));
+    encode_row<D>(x, t, p.sign, th, s.bits, s.words, put, s.codes + orow * s.words, s.norms + orow);
   } else if (s.mode == TQ_SIDE_FP16) {
-    if (live) copy4(src, s.fp16 + cache_row(p.pg, bh, pos, p.capacity) * D, t);
+    if (put) copy4(src, s.fp16 + orow * D, t);
   } else {  // TQ_SIDE_DELEGATED (V only)
     const int hot = s.hot;
     const int end = p.offset + p.n_new;
@@ -172,8 +175,7 @@ __global__ __launch_bounds__(kBlock) void quantize_append_kernel(const QuantizeP
       // Already older than the newest `hot` positions: straight to cold.
       float x[4];
       load4<D>(src, t, x);
-      encode_row<D>(x, t, p.sign, th, s.bits, s.words, live,
-                    s.codes + cache_row(p.pg, bh, pos, p.capacity) * s.words, s.norms + cache_row(p.pg, bh, pos, p.capacity));
+      encode_row<D>(x, t, p.sign, th, s.bits, s.words, put, s.codes + orow * s.words, s.norms + orow);
     } else {
       // Last new position of its ring slot: evict the slot's old occupant
       // (the position o < offset with o = pos mod hot) into the cold rows,
@@ -183,9 +185,9 @@ __global__ __launch_bounds__(kBlock) void quantize_append_kernel(const QuantizeP
       uint16_t *ring = s.fp16 + (bh * hot + slot) * D;
       float x[4];
       load4<D>(ring, t, x);
-      encode_row<D>(x, t, p.sign, th, s.bits, s.words, live && o >= 0,
-                    s.codes + cache_row(p.pg, bh, o >= 0 ? o : 0, p.capacity) * s.words,
-                    s.norms + cache_row(p.pg, bh, o >= 0 ? o : 0, p.capacity));
+      const long erow = cache_row(p.pg, bh, o >= 0 ? o : 0, p.capacity);
+      encode_row<D>(x, t, p.sign, th, s.bits, s.words, live && o >= 0 && erow >= 0,
+                    s.codes + (erow < 0 ? 0L : erow) * s.words, s.norms + (erow < 0 ? 0L : erow));
       if (live) copy4(src, ring, t);
     }
   }

@@ -221,12 +221,13 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_mfma_kernel(const Quanti
     const unsigned ubs = static_cast<unsigned>(p.pg.bs), blkf = tf / ubs;
     const int within = static_cast<int>(tf - blkf * ubs);
     const int sqf = wrapf ? sq1 : sq0, hdf = wrapf ? hd1 : hd0;
-    rw[0] = (static_cast<long>(p.pg.table[sqf * p.pg.max_blocks + static_cast<int>(blkf)]) * p.pg.kv_heads + hdf) *
-                p.pg.bs + within;
+    // (-1: a block outside the pools, whose rows are not written)
+    const long ef = valid_block(p.pg, p.pg.table[sqf * p.pg.max_blocks + static_cast<int>(blkf)]);
+    rw[0] = ef < 0 ? -1L : (ef * p.pg.kv_heads + hdf) * p.pg.bs + within;
     const bool run = 4 * g + 3 <= lf - 1 && (j0 + 4 * g + 3 >= p.n_new) == wrapf && within + 3 < p.pg.bs;
     if (run) {
 #pragma unroll
-      for (int r = 1; r < 4; ++r) rw[r] = rw[0] + r;
+      for (int r = 1; r < 4; ++r) rw[r] = ef < 0 ? -1L : rw[0] + r;
     } else {
 #pragma unroll
       for (int r = 1; r < 4; ++r) {
@@ -325,7 +326,7 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_mfma_kernel(const Quanti
     if (paged) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        if (4 * g + r >= left) continue;
+        if (4 * g + r >= left || prow[r] < 0) continue;
         if (n < W) sd.codes[prow[r] * W + n] = word[r];
         if (n == r) sd.norms[prow[r]] = nrm[r];
       }

@@ -31,18 +31,27 @@ struct SideDev {
 struct Paging {
   const int32_t *table;  // [B][max_blocks] or null
   int bs, max_blocks, kv_heads;
+  int num_blocks;        // blocks in each pool: table entries in [0, num_blocks) are valid
 };
 
-// Paged row of position t of (sequence b, KV head kv).  Unsigned 32-bit
-// arithmetic for the divisions: positions and bh = b Hkv + kv (at most 65535)
-// fit, and a 64-bit division costs tens of instructions.
+// Block index a table entry names, or -1 when the entry lies outside the
+// pools (such a block reads as zero rows and takes no writes).
+__host__ __device__ inline long valid_block(const Paging &pg, int entry) {
+  return static_cast<unsigned>(entry) < static_cast<unsigned>(pg.num_blocks) ? static_cast<long>(entry) : -1L;
+}
+
+// Paged row of position t of (sequence b, KV head kv), or -1 in an
+// out-of-range block.  Unsigned 32-bit arithmetic for the divisions:
+// positions and bh = b Hkv + kv (at most 65535) fit, and a 64-bit division
+// costs tens of instructions.
 __host__ __device__ inline long paged_row(const Paging &pg, int b, int kv, int t) {
   const unsigned ut = static_cast<unsigned>(t), ubs = static_cast<unsigned>(pg.bs);
   const unsigned blk = ut / ubs;
-  return (static_cast<long>(pg.table[b * pg.max_blocks + static_cast<int>(blk)]) * pg.kv_heads + kv) * pg.bs +
-         static_cast<int>(ut - blk * ubs);
+  const long e = valid_block(pg, pg.table[b * pg.max_blocks + static_cast<int>(blk)]);
+  return e < 0 ? -1L : (e * pg.kv_heads + kv) * pg.bs + static_cast<int>(ut - blk * ubs);
 }
 
+// Storage row of position t of unit bh; -1 in an out-of-range block.
 __host__ __device__ inline long cache_row(const Paging &pg, long bh, int t, int capacity) {
   if (!pg.table) return bh * capacity + t;
   const unsigned u = static_cast<unsigned>(bh), kvh = static_cast<unsigned>(pg.kv_heads);
@@ -101,6 +110,7 @@ struct DecodeParams {
 // Workspace: a fixed region of per-unit counters (zero on entry, left zero
 // on exit), then the partial results of whichever variant runs.
 constexpr size_t kCounterBytes = size_t(65536) * sizeof(unsigned);
+static_assert(kCounterBytes == TQ_WORKSPACE_COUNTER_BYTES, "tq.h states the counter region's size");
 
 // Plain variant's partials (floats, each region 256-byte aligned):
 //   ml   [B*Hq][n_splits][2]   running max (log2 domain) and sum
@@ -142,6 +152,8 @@ float quantize_lut_scale(const float *thr, int bits);
 constexpr int kQuantLutMaxScale = 512;
 hipError_t launch_dequantize(const DequantParams &p, hipStream_t stream);
 hipError_t launch_read_probe(const void *buf, size_t bytes, unsigned *sink, hipStream_t stream);
+// Zero `bytes` (a multiple of 16) of device memory at a 16-byte aligned `buf`.
+hipError_t launch_zero_fill(void *buf, size_t bytes, hipStream_t stream);
 hipError_t launch_decode_ref(const DecodeParams &p, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeParams &p, hipStream_t stream);
 bool decode_mfma_supported(const DecodeParams &p);

@@ -40,7 +40,8 @@ import math
 from dataclasses import dataclass
 from typing import List, Optional, Sequence, Tuple, Union
 
-from . import SideSpec, TQCache
+from . import SideSpec, TQCache, TQError
+from . import split_bits as _lib_split_bits
 
 DEFAULT_HOT = 256
 
@@ -84,14 +85,15 @@ def split_flags_mode(cache_type_k: str, cache_type_v: str) -> str:
 
 def split_bits(bits: float) -> Tuple[int, int]:
     """floor(bits) to K, ceil(bits) to V (a whole number gives both sides
-    the same width); each side must land in [1, 8]."""
+    the same width); each side must land in [1, 8].  The split is the
+    library's (tq_split_bits); a budget it rejects raises ValueError."""
     b = float(bits)
     if not math.isfinite(b):
         raise ValueError(f"bit budget {bits!r} is not finite")
-    kb, vb = math.floor(b), math.ceil(b)
-    if kb < 1 or vb > 8:
-        raise ValueError(f"bit budget {bits!r} splits to K{kb}/V{vb}, outside 1..8 bits per side")
-    return kb, vb
+    try:
+        return _lib_split_bits(b)
+    except TQError as e:
+        raise ValueError(f"bit budget {bits!r} splits outside 1..8 bits per side ({e})") from None
 
 
 def mode_sides(mode: Union[str, float, int], hot: int = DEFAULT_HOT) -> Sides:

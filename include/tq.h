@@ -118,8 +118,8 @@ typedef struct tq_side {
   int hot;                 /* DELEGATED: ring length (>= 1)                   */
 } tq_side;
 
-/* One layer's cache.  K may be FP16 or PACKED; V may be FP16, PACKED or
- * DELEGATED.  `seed` selects the rotation shared by both sides.
+/* One layer's cache.  K may be FP16, PACKED or INT8; V may be FP16, PACKED,
+ * DELEGATED or INT8.  `seed` selects the rotation shared by both sides.
  *
  * Paged storage (mlxcel "TurboQuant KV cache", "Paged cache and server
  * batching": TurboQuant modes in a block-table decode layout).  With
@@ -131,15 +131,20 @@ typedef struct tq_side {
  * and position t of sequence b sits in block block_table[b][t / block_size]
  * at row t % block_size.  The DELEGATED hot ring stays [B][Hkv][hot][d].
  *   block_table: DEVICE int32 [B][max_blocks]; entries are block indices of
- *                the pools (each in [0, num_blocks); not checked -- the
- *                library does not read device memory on the host).  Blocks
- *                may be shared between sequences for positions they share;
- *                an append must not write different rows into a shared block
- *                (copy it first).
+ *                the pools.  The library does not read device memory on the
+ *                host, so entries are checked on the device: an entry
+ *                outside [0, num_blocks) makes its positions read as zero
+ *                rows (score 0, value 0; they still count in the softmax)
+ *                and an append to them writes nothing, so a bad entry never
+ *                reaches memory outside the pools.  Blocks may be shared
+ *                between sequences for positions they share; an append must
+ *                not write different rows into a shared block (copy it
+ *                first).
  *   block_size:  positions per block, a multiple of 32.
  *   max_blocks:  table row length; capacity must equal max_blocks * block_size.
- * Errors: TQ_ERR_ARG if block_size or max_blocks is invalid or capacity does
- * not match. */
+ *   num_blocks:  blocks in each pool (>= 1).
+ * Errors: TQ_ERR_ARG if block_size, max_blocks or num_blocks is invalid or
+ * capacity does not match. */
 typedef struct tq_cache {
   int batch;
   int kv_heads;
@@ -151,6 +156,7 @@ typedef struct tq_cache {
   const int32_t *block_table; /* NULL: contiguous sides */
   int block_size;
   int max_blocks;
+  int num_blocks;
 } tq_cache;
 
 /* Quantize-append ("update_and_fetch" of the TurboQuantKVCache; one launch
@@ -173,21 +179,45 @@ int tq_quantize_append(const tq_cache *cache, const void *k_new,
                        void *hip_stream);
 
 /* Bytes of workspace tq_decode_attention needs for this shape (0 on invalid
- * arguments).  n_splits = 0 picks the library's split of the context. */
+ * arguments).  n_splits = 0 picks the library's split of the context.  The
+ * size is at least TQ_WORKSPACE_COUNTER_BYTES. */
 size_t tq_decode_workspace_bytes(const tq_cache *cache, int q_heads,
                                  int length, int n_splits);
+
+/* The decode workspace starts with TQ_WORKSPACE_COUNTER_BYTES of per-unit
+ * arrival counters (the last block of a (batch, KV head) unit to finish
+ * merges the context splits).  They must read zero before the workspace's
+ * first decode; every successful decode leaves them zero again, so one
+ * set-up serves every later call, whatever its shape.  A workspace whose
+ * counters are not zero gives undefined output (a merge may run early or
+ * not at all).  Zero them with tq_decode_workspace_init or any zero fill. */
+#define TQ_WORKSPACE_COUNTER_BYTES (256u * 1024u)
+
+/* Zero the counter region of a decode workspace on `hip_stream` (a store
+ * kernel, no memset, so it may be recorded into a HIP graph).
+ *   workspace: DEVICE, 256-byte aligned, workspace_bytes >=
+ *              TQ_WORKSPACE_COUNTER_BYTES (else TQ_ERR_WORKSPACE).
+ * Errors: TQ_ERR_ARG on a null workspace. */
+int tq_decode_workspace_init(void *workspace, size_t workspace_bytes,
+                             void *hip_stream);
 
 /* Decode attention over positions [0, length) straight from the packed cache
  * ("How TurboQuant KV Cache Quantization Works": scores from the compressed
  * representation).  Packed K is scored as n_i <R q, c[code_i]>; packed V is
  * accumulated in the rotated domain and rotated back once per output head.
+ * A DELEGATED V is attended as "the newest `hot` positions from the ring,
+ * older ones packed", with newest meaning the last `length` positions: the
+ * ring holds the newest `hot` positions appended, so length must equal the
+ * number of positions appended (a shorter length reads ring slots that later
+ * appends have overwritten).
  *   q:      DEVICE fp16 [B][q_heads][d]; q_heads a multiple of kv_heads.
  *   out:    DEVICE fp32 [B][q_heads][d].
  *   scores: DEVICE fp32 [B][q_heads][length] or NULL; when given, receives
  *           the scaled logits q . k~ / sqrt(d).
- *   workspace: DEVICE, >= tq_decode_workspace_bytes(...), 256-byte aligned.
- *           It holds per-split partial results; calls that share a workspace
- *           must not overlap.
+ *   workspace: DEVICE, >= tq_decode_workspace_bytes(...), 256-byte aligned,
+ *           its counters zero before its first use (see
+ *           TQ_WORKSPACE_COUNTER_BYTES).  It holds per-split partial
+ *           results; calls that share a workspace must not overlap.
  *   n_splits: 0 = automatic, else the number of context splits (>= 1).
  * length = 0 writes zeros to out. */
 int tq_decode_attention(const tq_cache *cache, const void *q, int q_heads,

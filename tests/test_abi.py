@@ -209,18 +209,19 @@ def test_read_probe_argument_errors():
 
 
 def test_paged_descriptor_errors():
-    # paged storage: block_size a multiple of 32, max_blocks >= 1 and
-    # capacity == max_blocks * block_size; checked before any launch
+    # paged storage: block_size a multiple of 32, max_blocks >= 1, num_blocks
+    # >= 1 and capacity == max_blocks * block_size; checked before any launch
     f = _Fake()
     table = np.zeros(64, np.int32)
 
-    def paged(bs, mb, cap):
+    def paged(bs, mb, cap, nb=16):
         c = _desc(f, cap=cap)
-        c.block_table, c.block_size, c.max_blocks = table.ctypes.data, bs, mb
+        c.block_table, c.block_size, c.max_blocks, c.num_blocks = table.ctypes.data, bs, mb, nb
         return c
 
-    for bs, mb, cap in ((48, 4, 192), (16, 8, 128), (0, 4, 0), (64, 0, 0), (64, 4, 192), (64, 4, 320)):
-        c = paged(bs, mb, cap)
+    for bs, mb, cap, nb in ((48, 4, 192, 16), (16, 8, 128, 16), (0, 4, 0, 16), (64, 0, 0, 16), (64, 4, 192, 16),
+                            (64, 4, 320, 16), (64, 4, 256, 0), (64, 4, 256, -3)):
+        c = paged(bs, mb, cap, nb)
         assert _qa(c, f, n=0) == tq.TQ_ERR_ARG, (bs, mb, cap)
         assert tq.lib().tq_decode_workspace_bytes(ctypes.byref(c), 8, 0, 0) == 0
         assert tq.lib().tq_dequantize(ctypes.byref(c), 1, 0, 0, None, None) == tq.TQ_ERR_ARG
@@ -228,6 +229,44 @@ def test_paged_descriptor_errors():
     assert _qa(ok, f, n=0) == tq.TQ_OK
     assert tq.lib().tq_decode_workspace_bytes(ctypes.byref(ok), 8, 256, 0) > 0
     assert _qa(ok, f, n=4, off=253) == tq.TQ_ERR_CAPACITY
+
+
+def test_workspace_init_errors():
+    # the counter-region set-up: a null, short or misaligned workspace is
+    # refused before any launch
+    L = tq.lib()
+    fake = np.zeros(1 << 20, np.uint8)
+    base = (fake.ctypes.data + 255) & ~255
+    assert tq.WORKSPACE_COUNTER_BYTES == 256 * 1024
+    assert L.tq_decode_workspace_init(None, 1 << 20, None) == tq.TQ_ERR_ARG
+    assert L.tq_decode_workspace_init(ctypes.c_void_p(base), 256 * 1024 - 16, None) == tq.TQ_ERR_WORKSPACE
+    assert L.tq_decode_workspace_init(ctypes.c_void_p(base + 16), 1 << 19, None) == tq.TQ_ERR_WORKSPACE
+
+
+def test_workspace_bytes_cover_the_counters():
+    f = _Fake()
+    for kmode, vmode, d, Hq in ((1, 1, 128, 8), (0, 1, 128, 8), (1, 1, 64, 4), (3, 3, 128, 8)):
+        c = _desc(f, kmode=kmode, vmode=vmode, d=d)
+        for length in (0, 1, 1000):
+            assert tq.lib().tq_decode_workspace_bytes(ctypes.byref(c), Hq, length, 0) >= tq.WORKSPACE_COUNTER_BYTES
+
+
+def test_cache_checks_its_block_table_on_the_host():
+    # the binding holds the table when it builds the descriptor, so it
+    # refuses entries outside [0, num_blocks) there (the library guards them
+    # on the device)
+    torch = pytest.importorskip("torch")
+    S = tq.SideSpec
+    good = torch.arange(8, dtype=torch.int32).reshape(2, 4)
+    c = tq.TQCache(2, 2, 64, 256, S("packed", 3), S("packed", 4), device="cpu", block_table=good, block_size=64,
+                   num_blocks=8)
+    assert c.desc.num_blocks == 8 and c.desc.max_blocks == 4 and c.desc.block_size == 64
+    for bad, nb in ((torch.tensor([[0, 1, 2, 3], [4, 5, 6, 8]], dtype=torch.int32), 8),
+                    (torch.tensor([[0, 1, 2, 3], [4, 5, -1, 7]], dtype=torch.int32), 8),
+                    (good, 0)):
+        with pytest.raises(ValueError):
+            tq.TQCache(2, 2, 64, 256, S("packed", 3), S("packed", 4), device="cpu", block_table=bad, block_size=64,
+                       num_blocks=nb)
 
 
 def test_sparse_v_threshold_errors():

@@ -18,12 +18,12 @@ def _flat(s):
 
 
 # "Quantization Codecs and Bit Splitting": floor to K, ceil to V; the pages'
-# own example budget is 3.5 bits, and reading 11 of the design takes other
-# fractions literally (4.2 -> K4 / V5)
+# own example budget is 3.5 bits, and other fractions are split literally
+# (4.2 -> K4 / V5).  The policy's split is the library's tq_split_bits.
 @pytest.mark.parametrize("bits,k,v", [(3.5, 3, 4), (3, 3, 3), (4, 4, 4), (4.2, 4, 5), (1.5, 1, 2), (7.5, 7, 8),
                                       (2.0, 2, 2)])
 def test_split_bits(bits, k, v):
-    assert P.split_bits(bits) == (k, v)
+    assert P.split_bits(bits) == (k, v) == P._lib_split_bits(bits)
     assert _flat(P.mode_sides(bits)) == _sides("packed", k, "packed", v)
 
 
