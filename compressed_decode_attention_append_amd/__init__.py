@@ -25,6 +25,7 @@ TQ_ERR_CAPACITY = -4
 TQ_ERR_WORKSPACE = -5
 TQ_ERR_MODE = -6
 TQ_ERR_HIP = -7
+TQ_ERR_SCRATCH = -8
 
 SIDE_FP16 = 0
 SIDE_PACKED = 1
@@ -100,6 +101,8 @@ def lib():
         L.tq_decode_attention_sparse.argtypes = [ctypes.POINTER(tq_cache), P, I, I, I, ctypes.c_float, P, P,
                                                  P, ctypes.c_size_t, P]
         L.tq_decode_attention_sparse.restype = I
+        L.tq_decode_attention_noalloc.argtypes = [ctypes.POINTER(tq_cache), P, I, I, I, P, P, P]
+        L.tq_decode_attention_noalloc.restype = I
         L.tq_dequantize.argtypes = [ctypes.POINTER(tq_cache), I, I, I, P, P]
         L.tq_dequantize.restype = I
         L.tq_status_string.argtypes = [I]
@@ -183,6 +186,7 @@ def _stream_handle(stream) -> int:
 
 
 WORKSPACE_COUNTER_BYTES = 256 * 1024
+TQ_NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024
 
 
 def decode_workspace_init(workspace, stream=None) -> None:
@@ -343,6 +347,24 @@ class TQCache:
                                              int(n_splits), _ptr(out), _ptr(sc), _ptr(ws),
                                              ws.numel() * ws.element_size(), _stream_handle(stream)),
                    "tq_decode_attention")
+        return (out, sc[:, :, :length]) if scores else out
+
+    def decode_attention_noalloc(self, q, length: int, n_splits: int = 0, out=None, scores=False, stream=None):
+        """decode_attention through tq_decode_attention_noalloc: the library's
+        fixed per-GPU scratch instead of a workspace (for callers that cannot
+        allocate; overlapping calls on one GPU race)."""
+        import torch
+        if q.dtype != torch.float16 or not q.is_contiguous() or q.dim() != 3:
+            raise ValueError("q must be contiguous fp16 [B, Hq, d]")
+        B, Hq, d = q.shape
+        if B != self.batch or d != self.head_dim:
+            raise ValueError("q shape does not match the cache")
+        if out is None:
+            out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+        sc = torch.empty((B, Hq, max(int(length), 1)), dtype=torch.float32, device=q.device) if scores else None
+        _check(lib().tq_decode_attention_noalloc(ctypes.byref(self.desc), _ptr(q), int(Hq), int(length),
+                                                 int(n_splits), _ptr(out), _ptr(sc), _stream_handle(stream)),
+               "tq_decode_attention_noalloc")
         return (out, sc[:, :, :length]) if scores else out
 
     def dequantize(self, side: str, start: int, count: int, stream=None):

@@ -222,6 +222,7 @@ const char *tq_status_string(int status) {
     case TQ_ERR_WORKSPACE: return "workspace missing or too small";
     case TQ_ERR_MODE: return "unsupported side mode";
     case TQ_ERR_HIP: return "HIP launch error";
+    case TQ_ERR_SCRATCH: return "the decode needs more than the fixed 16 MiB scratch";
     default: return "unknown status";
   }
 }
@@ -324,6 +325,25 @@ int tq_decode_attention_sparse(const tq_cache *cache, const void *q, int q_heads
   const hipError_t e = (v == kMfma) ? tq::launch_decode_mfma(p, static_cast<hipStream_t>(hip_stream))
                                     : tq::launch_decode_ref(p, static_cast<hipStream_t>(hip_stream));
   return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
+int tq_decode_attention_noalloc(const tq_cache *cache, const void *q, int q_heads, int length, int n_splits,
+                                float *out, float *scores, void *hip_stream) {
+  int r = check_cache(cache);
+  if (r != TQ_OK) return r;
+  if (!q || !out) return TQ_ERR_ARG;
+  if (q_heads < cache->kv_heads || q_heads % cache->kv_heads) return TQ_ERR_ARG;
+  if (n_splits < 0) return TQ_ERR_ARG;
+  if (length < 0 || length > cache->capacity) return TQ_ERR_CAPACITY;
+  tq::DecodeParams p;
+  Variant v;
+  const size_t need = workspace_need(cache, q_heads, length, n_splits, &p, &v);
+  if (need == 0) return TQ_ERR_ARG;
+  if (need > tq::kScratchBytes) return TQ_ERR_SCRATCH;
+  void *ws = nullptr;
+  if (tq::scratch_workspace(static_cast<hipStream_t>(hip_stream), &ws) != hipSuccess) return TQ_ERR_HIP;
+  return tq_decode_attention_sparse(cache, q, q_heads, length, n_splits, 0.0f, out, scores, ws, tq::kScratchBytes,
+                                    hip_stream);
 }
 
 int tq_decode_workspace_init(void *workspace, size_t workspace_bytes, void *hip_stream) {

@@ -154,6 +154,11 @@ hipError_t launch_dequantize(const DequantParams &p, hipStream_t stream);
 hipError_t launch_read_probe(const void *buf, size_t bytes, unsigned *sink, hipStream_t stream);
 // Zero `bytes` (a multiple of 16) of device memory at a 16-byte aligned `buf`.
 hipError_t launch_zero_fill(void *buf, size_t bytes, hipStream_t stream);
+// Size of the fixed per-device decode scratch (tq_decode_attention_noalloc),
+// and its device address on the device `stream` runs on (set up on first use).
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static_assert(kScratchBytes == TQ_NOALLOC_SCRATCH_BYTES, "tq.h states the scratch size");
+hipError_t scratch_workspace(hipStream_t stream, void **ptr);
 hipError_t launch_decode_ref(const DecodeParams &p, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeParams &p, hipStream_t stream);
 bool decode_mfma_supported(const DecodeParams &p);

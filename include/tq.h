@@ -54,7 +54,9 @@ enum {
   TQ_ERR_CAPACITY = -4,  /* rows outside [0, capacity)                      */
   TQ_ERR_WORKSPACE = -5, /* workspace missing or smaller than required      */
   TQ_ERR_MODE = -6,      /* unsupported side mode or mode combination       */
-  TQ_ERR_HIP = -7        /* the HIP runtime reported a launch error         */
+  TQ_ERR_HIP = -7,       /* the HIP runtime reported a launch error         */
+  TQ_ERR_SCRATCH = -8    /* tq_decode_attention_noalloc: the call needs more
+                            than TQ_NOALLOC_SCRATCH_BYTES of workspace      */
 };
 
 /* How one side (K or V) of a cache is stored ("Available modes": fp16 K with
@@ -241,6 +243,22 @@ int tq_decode_attention_sparse(const tq_cache *cache, const void *q, int q_heads
                                int length, int n_splits, float sparse_v, float *out,
                                float *scores, void *workspace, size_t workspace_bytes,
                                void *hip_stream);
+
+/* tq_decode_attention without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The workspace is a fixed static device
+ * array of TQ_NOALLOC_SCRATCH_BYTES per GPU, which the library holds until
+ * the process ends; nothing is allocated or freed.  The first call on a
+ * device looks the array up and clears its counters on `hip_stream`.  Every
+ * call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (concurrent streams, threads) race and must be serialised by the caller.
+ * Results are those of tq_decode_attention (the same kernels and splits).
+ * Errors: as tq_decode_attention; TQ_ERR_SCRATCH (nothing launched) when
+ * tq_decode_workspace_bytes for the call exceeds TQ_NOALLOC_SCRATCH_BYTES. */
+#define TQ_NOALLOC_SCRATCH_BYTES (16u * 1024u * 1024u)
+int tq_decode_attention_noalloc(const tq_cache *cache, const void *q,
+                                int q_heads, int length, int n_splits,
+                                float *out, float *scores, void *hip_stream);
 
 /* Dequantize packed rows [start, start + count) of one side (0 = K, 1 = V;
  * for a DELEGATED V this reads the packed cold rows) into DEVICE fp32

@@ -38,7 +38,7 @@ def test_missing_library_raises_tq_error(monkeypatch):
 
 
 def test_status_strings():
-    for s in range(0, -8, -1):
+    for s in range(0, -9, -1):
         assert tq.status_string(s) not in ("", "unknown status")
     assert tq.status_string(-99) == "unknown status"
 
@@ -229,6 +229,31 @@ def test_paged_descriptor_errors():
     assert _qa(ok, f, n=0) == tq.TQ_OK
     assert tq.lib().tq_decode_workspace_bytes(ctypes.byref(ok), 8, 256, 0) > 0
     assert _qa(ok, f, n=4, off=253) == tq.TQ_ERR_CAPACITY
+
+
+def test_noalloc_decode_errors():
+    # the allocation-free decode validates like tq_decode_attention and
+    # refuses a call whose workspace would exceed its fixed scratch, all
+    # before any launch or device set-up
+    f = _Fake()
+    L = tq.lib()
+
+    def na(c, Hq=8, length=100, ns=0, q=True, out=True):
+        return L.tq_decode_attention_noalloc(ctypes.byref(c), f.p(4096) if q else None, Hq, length, ns,
+                                             f.p(8192) if out else None, None, None)
+
+    assert na(_desc(f, d=96)) == tq.TQ_ERR_HEAD_DIM
+    assert na(_desc(f), q=False) == tq.TQ_ERR_ARG
+    assert na(_desc(f), out=False) == tq.TQ_ERR_ARG
+    assert na(_desc(f), Hq=6) == tq.TQ_ERR_ARG
+    assert na(_desc(f), ns=-1) == tq.TQ_ERR_ARG
+    assert na(_desc(f), length=2000) == tq.TQ_ERR_CAPACITY
+    # the plain kernel's partials at 2000 splits of 64 query heads, d = 256:
+    # far beyond 16 MiB
+    big = _desc(f, d=256, kb=4, vb=5, cap=1 << 20, B=2, H=4)
+    assert L.tq_decode_workspace_bytes(ctypes.byref(big), 64, 100000, 2000) > tq.TQ_NOALLOC_SCRATCH_BYTES
+    assert na(big, Hq=64, length=100000, ns=2000) == tq.TQ_ERR_SCRATCH
+    assert "16 MiB" in tq.status_string(tq.TQ_ERR_SCRATCH)
 
 
 def test_workspace_init_errors():
