@@ -261,6 +261,98 @@ def stats_summary(stats_csv: str, workload: str, cmds: list):
     return "\n".join(out) + "\n"
 
 
+# per-dispatch counters the --pmc-summary mode explains, and the ratios it derives
+PMC_RATIOS = [
+    ("valu issue share of wave time", "SQ_ACTIVE_INST_VALU", "SQ_WAVE_CYCLES"),
+    ("lds issue share of wave time", "SQ_ACTIVE_INST_LDS", "SQ_WAVE_CYCLES"),
+    ("share of wave time waiting on any instruction", "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES"),
+    ("share of wave time waiting on LDS", "SQ_WAIT_INST_LDS", "SQ_WAVE_CYCLES"),
+    ("lds bank-conflict cycles per LDS issue cycle", "SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_LDS"),
+]
+
+
+def pmc_summary(csvs: list, workload: str, cmds: list, title: str):
+    """Summarise rocprofv3 --pmc runs (any counters, one or more CSV files)
+    of this script: each counter's average per dispatch for each of the
+    library's kernels, divided by the workload's (batch, KV head, 32-position)
+    chunks for the decode kernels, and a few ratios of cycle counters."""
+    import collections
+    import csv
+    w = WORKLOADS[workload]
+    chunks = w["batch"] * w["kv_heads"] * w["tokens"] // 32
+    acc = collections.defaultdict(lambda: collections.defaultdict(list))
+    for path in csvs:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                name = r["Kernel_Name"]
+                if "tq::" not in name:
+                    continue
+                short = name.replace("void ", "").replace("tq::(anonymous namespace)::", "").split("(tq::")[0]
+                acc[short][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    out = [f"# rocprofv3 hardware counters ({title}), workload {workload}: batch {w['batch']}, "
+           f"{w['kv_heads']} KV heads, {w['q_heads']} query heads, head_dim {w['head_dim']}, context {w['tokens']}",
+           "# commands (from the repository root):"]
+    out += [f"#   {c}" for c in cmds]
+    out += [f"# values are averages per dispatch; 'per chunk' divides by the {chunks} (batch, KV head, "
+            "32-position) chunks of one decode", ""]
+    for short in sorted(acc):
+        cs = acc[short]
+        n = max(len(v) for v in cs.values())
+        out.append(f"kernel: {short} ({n} dispatches)")
+        is_decode = "decode" in short
+        for c in sorted(cs):
+            avg = sum(cs[c]) / len(cs[c])
+            extra = f"   per chunk {avg / chunks:10.2f}" if is_decode and c.startswith("SQ_INSTS") else ""
+            out.append(f"  {c:32s} {avg:18.1f}{extra}")
+        for label, a, b in PMC_RATIOS:
+            if a in cs and b in cs and sum(cs[b]) > 0:
+                out.append(f"  ratio {a} / {b} = {sum(cs[a]) / sum(cs[b]):.4f}   ({label})")
+        out.append("")
+    return "\n".join(out) + "\n"
+
+
+def trace_summary(trace_csv: str, workload: str, last: int, cmds: list, n_new: int = 0):
+    """Per-kernel durations from a rocprofv3 --kernel-trace CSV of this
+    script, over each kernel's last `last` dispatches only (the timed steps:
+    steps x layers), so the cache fill and the warm-up do not enter the
+    averages; with the decode and quantize-append throughput they imply."""
+    import collections
+    import csv
+    w = dict(WORKLOADS[workload])
+    per = collections.defaultdict(list)
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"]
+            if "tq::" not in name:
+                continue
+            short = name.replace("void ", "").replace("tq::(anonymous namespace)::", "").split("(tq::")[0]
+            per[short].append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    out = [f"# rocprofv3 kernel trace, workload {workload}: batch {w['batch']}, {w['kv_heads']} KV heads, "
+           f"{w['q_heads']} query heads, head_dim {w['head_dim']}, context {w['tokens']}, "
+           f"K {w['k'][0]}{w['k'][1] or ''}, V {w['v'][0]}{w['v'][1] or ''}",
+           "# commands (from the repository root):"]
+    out += [f"#   {c}" for c in cmds]
+    out += [f"# each kernel's last {last} dispatches (the timed steps); durations in microseconds",
+            f"# decode algorithmic bytes per launch: {decode_bytes(w)}"]
+    if n_new:
+        out.append(f"# quantize-append: {n_new} new positions per sequence per launch, "
+                   f"algorithmic bytes per launch {append_bytes(w, n_new)}")
+    out += ["", f"{'kernel':44s} {'calls':>6s} {'avg_us':>9s} {'median':>9s} {'min_us':>9s} {'max_us':>9s}"]
+    for short in sorted(per):
+        d = [x[1] / 1e3 for x in sorted(per[short])[-last:]]
+        d_sorted = sorted(d)
+        avg = sum(d) / len(d)
+        out.append(f"{short:44s} {len(d):6d} {avg:9.2f} {d_sorted[len(d) // 2]:9.2f} {d_sorted[0]:9.2f} "
+                   f"{d_sorted[-1]:9.2f}")
+        if "decode_mfma" in short or "decode_split" in short:
+            out.append(f"#   -> {decode_bytes(w) / (avg * 1e-6) / 1e9:.1f} GB/s over the algorithmic bytes, "
+                       f"{decode_bytes(w) / (avg * 1e-6) / 1e9 / HBM_PEAK_GBS:.4f} of {HBM_PEAK_GBS:.0f} GB/s")
+        if n_new and "quantize" in short:
+            out.append(f"#   -> {w['batch'] * n_new / (avg * 1e-6) / 1e6:.1f} Mtok/s, "
+                       f"{append_bytes(w, n_new) / (avg * 1e-6) / 1e9:.1f} GB/s over the algorithmic bytes")
+    return "\n".join(out) + "\n"
+
+
 def attainable_read_gbs(stream, nbytes=4 << 30, reps=10) -> float:
     """HBM read bandwidth of the library's streaming-read probe over a fresh
     `nbytes` buffer (the attainable ceiling the decode can be read against;
@@ -312,7 +404,22 @@ def main():
                     help="with --counter-summary: a command line to record in the summary")
     ap.add_argument("--stats-summary", metavar="KERNEL_STATS_CSV",
                     help="format a rocprofv3 --stats kernel table of this script's run; runs nothing")
+    ap.add_argument("--pmc-summary", nargs="+", metavar="COUNTER_CSV",
+                    help="summarise rocprofv3 --pmc runs (any counters) of this script; runs nothing")
+    ap.add_argument("--title", default="", help="with --pmc-summary: what the counters were taken of")
+    ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
+                    help="per-kernel durations of the timed steps (--steps x layers last dispatches) from a "
+                         "rocprofv3 --kernel-trace CSV of this script; runs nothing")
     args = ap.parse_args()
+    if args.trace_summary:
+        w = WORKLOADS[args.workload]
+        layers = args.layers or w["layers"]
+        sys.stdout.write(trace_summary(args.trace_summary, args.workload, args.steps * layers, args.command,
+                                       w.get("prefill", 0) or w.get("append", 0)))
+        return
+    if args.pmc_summary:
+        sys.stdout.write(pmc_summary(args.pmc_summary, args.workload, args.command, args.title))
+        return
     if args.stats_summary:
         sys.stdout.write(stats_summary(args.stats_summary, args.workload, args.command))
         return

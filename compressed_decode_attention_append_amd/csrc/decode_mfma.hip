@@ -536,23 +536,28 @@ struct Wave {
   // fp16 rows (n: the positions' V norms, 1 for fp16 rows).
   //
   // The value scale (SCALED): P must fit fp16 (below 2^16) and the largest
-  // terms of a head must stay far above fp16's subnormal range, whatever the
-  // spread of the norms.  vscale is a power of two per head, so dividing it
-  // out at the end is exact.  It is lowered when a weight-times-norm of the
-  // chunk would give P > 2^13 (to 2^12 / the head's largest p n, rounded up
-  // to a power of two), and raised by 2^floor(growth) when the head's
-  // running maximum grows (its earlier terms shrink by 2^-growth), up to
-  // 2^40.  The largest term of a head therefore stays within [2^8, 2^13],
-  // where hi and lo carry full precision, unless the head's largest weights
-  // fall on rows of zero norm and every other weight is below 2^-30 of them;
-  // a row whose V norm is tiny next to others does not force the scale down
-  // unless its weight is large too.
+  // terms of a head must stay far above fp16's subnormal range (2^-14),
+  // whatever the spread of the norms.  vscale is a power of two per head, so
+  // dividing it out at the end is exact.  It is lowered when a
+  // weight-times-norm of the chunk would give P > 2^15 (to 16 / the head's
+  // largest p n, rounded up to a power of two, so that term lands in
+  // (8, 16]), and raised by 2^floor(growth) when the head's running maximum
+  // grows (its earlier terms shrink by 2^-growth), up to 2^40.  The 2^11
+  // headroom above 16 exceeds the 2^8 by which a weight may outgrow the lazily
+  // updated maximum, so lowering is rare.  The largest term of a head
+  // therefore stays within [2^2, 2^15], where hi and lo carry full
+  // precision, unless the head's largest weights fall on rows of zero norm
+  // and every other weight is below 2^-30 of them; a row whose V norm is
+  // tiny next to others does not force the scale down unless its weight is
+  // large too.
   template <bool TAIL, bool SCALED>
   __device__ __forceinline__ half8_t softmax(const float (&c)[NV], const float (&n)[NV]) {
+    // c holds the logits before the query's power-of-two scale qinv (> 0),
+    // which commutes with the maximum and enters the exponent by an fma
     float cmax = c[0];
 #pragma unroll
     for (int j = 1; j < NV; ++j) cmax = fmaxf(cmax, c[j]);
-    cmax = head_max<GP>(cmax);
+    cmax = head_max<GP>(cmax) * qinv;
     chunk_max = cmax;
     const bool grow = cmax > m_run + kRescale;
     if (__ballot(grow)) {
@@ -573,7 +578,7 @@ struct Wave {
     float p[NV], P[NV];
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      p[j] = __builtin_amdgcn_exp2f(c[j] - m_run);
+      p[j] = __builtin_amdgcn_exp2f(fmaf(c[j], qinv, -m_run));
       if (TAIL) p[j] = (c[j] == -INFINITY) ? 0.0f : p[j];
       l_run += p[j];
       P[j] = p[j] * n[j];
@@ -582,11 +587,11 @@ struct Wave {
       float lm = P[0];
 #pragma unroll
       for (int j = 1; j < NV; ++j) lm = fmaxf(lm, P[j]);
-      if (__ballot(lm * vscale > 8192.0f)) {
+      if (__ballot(lm * vscale > 32768.0f)) {
         // lower the scale of the heads whose largest p n asks for it (the
         // whole wave runs this, as scale_heads reads other lanes)
         const float hm = head_max<GP>(lm);
-        const float vs = (hm * vscale > 8192.0f) ? 4096.0f / pow2_ceil(hm) : vscale;
+        const float vs = (hm * vscale > 32768.0f) ? 16.0f / pow2_ceil(hm) : vscale;
         const float f = vs / vscale;
         vscale = vs;
         scale_heads(f);
@@ -609,7 +614,7 @@ struct Wave {
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
         const int t = t0 + cpos + j;
-        if (!TAIL || t < we) scores[(score_row0 + h) * length + t] = c[j] * kLn2;
+        if (!TAIL || t < we) scores[(score_row0 + h) * length + t] = c[j] * qinv * kLn2;
       }
     }
   }
@@ -664,7 +669,7 @@ struct Wave {
     compact(s, cs);
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      cs[j] *= KB ? c.kn[j] * qinv : qinv;
+      if (KB) cs[j] *= c.kn[j];
       if (TAIL && t0 + cpos + j >= we) cs[j] = -INFINITY;
     }
     if (scores) store_scores<TAIL>(t0, we, cs, scores, score_row0, length);
@@ -687,7 +692,7 @@ struct Wave {
     compact(s, cs);
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      cs[j] *= KB ? c.kn[j] * qinv : qinv;
+      if (KB) cs[j] *= c.kn[j];
       vn[j] = 1.0f;
       const int t = t0 + cpos + j;
       if (t < wb || t >= we) cs[j] = -INFINITY;
@@ -696,7 +701,7 @@ struct Wave {
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
         const int t = t0 + cpos + j;
-        if (t >= wb && t < we) scores[(score_row0 + col % GP) * length + t] = cs[j] * kLn2;
+        if (t >= wb && t < we) scores[(score_row0 + col % GP) * length + t] = cs[j] * qinv * kLn2;
       }
     }
     const half8_t ap = softmax<true, false>(cs, vn);
@@ -848,7 +853,7 @@ struct Balance {
   }
 };
 
-template <int KB, int GP, bool PG>
+template <int KB, int GP, bool PG, bool SC>
 __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(const DecodeParams p) {
   constexpr int kWaves = waves_of<KB>();
   constexpr int kThreads = 64 * kWaves;
@@ -863,6 +868,9 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   // positions, the buffer descriptors) then stays in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = p.q_heads / p.kv_heads;
+  // SC: the launch writes the scaled logits (parity runs); otherwise their
+  // address arithmetic is compiled out
+  float *const scores = SC ? p.scores : nullptr;
   float *qw = reinterpret_cast<float *>(lds + L::qwork);
   int *flag = reinterpret_cast<int *>(lds + L::red);
   int *prog = reinterpret_cast<int *>(lds + L::prog);
@@ -1065,9 +1073,9 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
       nblk = nblk2;
       asm volatile("" ::: "memory");
       if (c < n_full) {
-        W.template cold_chunk<false>(s0 + c * kChunk, s1, A, p.scores, hq0, p.length);
+        W.template cold_chunk<false>(s0 + c * kChunk, s1, A, scores, hq0, p.length);
       } else {
-        W.template cold_chunk<true>(s0 + c * kChunk, s1, A, p.scores, hq0, p.length);
+        W.template cold_chunk<true>(s0 + c * kChunk, s1, A, scores, hq0, p.length);
       }
       bal.step(wave, lane);
       c = cn;
@@ -1079,9 +1087,9 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
       nblk = nblk2;
       asm volatile("" ::: "memory");
       if (c < n_full) {
-        W.template cold_chunk<false>(s0 + c * kChunk, s1, B, p.scores, hq0, p.length);
+        W.template cold_chunk<false>(s0 + c * kChunk, s1, B, scores, hq0, p.length);
       } else {
-        W.template cold_chunk<true>(s0 + c * kChunk, s1, B, p.scores, hq0, p.length);
+        W.template cold_chunk<true>(s0 + c * kChunk, s1, B, scores, hq0, p.length);
       }
       bal.step(wave, lane);
       c = cn;
@@ -1105,7 +1113,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
       W.load_row(W.row_from(nblk, s0 + min(cn, last) * kChunk), s0 + min(cn, last) * kChunk, B);
       nblk = nblk2;
       asm volatile("" ::: "memory");
-      W.template cold_chunk<false>(s0 + c * kChunk, s1, A, p.scores, hq0, p.length);
+      W.template cold_chunk<false>(s0 + c * kChunk, s1, A, scores, hq0, p.length);
       bal.step(wave, lane);
       c = cn;
       if (c >= n_full) {
@@ -1118,15 +1126,15 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
       W.load_row(W.row_from(nblk, s0 + min(cn, last) * kChunk), s0 + min(cn, last) * kChunk, A);
       nblk = nblk2;
       asm volatile("" ::: "memory");
-      W.template cold_chunk<false>(s0 + c * kChunk, s1, B, p.scores, hq0, p.length);
+      W.template cold_chunk<false>(s0 + c * kChunk, s1, B, scores, hq0, p.length);
       bal.step(wave, lane);
       c = cn;
     }
     if (c < n_chunks) {
       if (in_b) {
-        W.template cold_chunk<true>(s0 + c * kChunk, s1, B, p.scores, hq0, p.length);
+        W.template cold_chunk<true>(s0 + c * kChunk, s1, B, scores, hq0, p.length);
       } else {
-        W.template cold_chunk<true>(s0 + c * kChunk, s1, A, p.scores, hq0, p.length);
+        W.template cold_chunk<true>(s0 + c * kChunk, s1, A, scores, hq0, p.length);
       }
     }
   }
@@ -1176,7 +1184,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
     W.vscale = 1.0f;
     for (int t0 = hs; t0 < he; t0 += kChunk) {
       W.load(t0, A);
-      W.hot_chunk(t0, h0, he, A, p.scores, hq0, p.length);
+      W.hot_chunk(t0, h0, he, A, scores, hq0, p.length);
     }
     W.to_slot(work + wave * GP * kPS, true);
     __syncthreads();
@@ -1303,12 +1311,21 @@ bool decode_mfma_supported(const DecodeParams &p) {
 
 int decode_mfma_max_splits() { return kMaxSplits; }
 
+template <int KB, int GP, bool SC>
+void launch_sc(const DecodeParams &p, dim3 grid, hipStream_t stream) {
+  if (p.pg.table) {
+    hipLaunchKernelGGL((decode_mfma_kernel<KB, GP, true, SC>), grid, dim3(64 * waves_of<KB>()), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((decode_mfma_kernel<KB, GP, false, SC>), grid, dim3(64 * waves_of<KB>()), 0, stream, p);
+  }
+}
+
 template <int KB, int GP>
 void launch_gp(const DecodeParams &p, dim3 grid, hipStream_t stream) {
-  if (p.pg.table) {
-    hipLaunchKernelGGL((decode_mfma_kernel<KB, GP, true>), grid, dim3(64 * waves_of<KB>()), 0, stream, p);
+  if (p.scores) {
+    launch_sc<KB, GP, true>(p, grid, stream);
   } else {
-    hipLaunchKernelGGL((decode_mfma_kernel<KB, GP, false>), grid, dim3(64 * waves_of<KB>()), 0, stream, p);
+    launch_sc<KB, GP, false>(p, grid, stream);
   }
 }
 
