@@ -83,55 +83,136 @@ def append_bytes(w, n_new: int) -> int:
     return units * n_new * per
 
 
-def cpu_baseline(w, budget_s: float = 12.0):
-    """Time the oracle (float64 NumPy) on a bounded sample of the decode:
-    whole (batch, KV head) units over the full context, until ~budget_s."""
+def _oracle_side(w, mode, bits, x, R):
+    """Storage of one side as the oracle builds it (set-up, not timed)."""
     import numpy as np
+
+    import oracle
+    d = w["head_dim"]
+    if mode == "fp16":
+        return ("fp16", x)
+    if mode == "int8":
+        return ("int8",) + oracle.int8_quantize(x)
+    c, t = oracle.lloyd_max(d, bits)
+    codes, n, _ = oracle.quantize(x, R, t)
+    return ("packed", oracle.pack_codes(codes, bits), n.astype(np.float32), c, bits)
+
+
+def _oracle_rows(w, st, R):
+    """Rows the decode reads, rebuilt from the storage (timed)."""
+    import oracle
+    if st[0] == "fp16":
+        return st[1].astype("float64")
+    if st[0] == "int8":
+        return oracle.int8_dequantize(st[1], st[2])
+    _, words, n, c, bits = st
+    return oracle.dequantize(oracle.unpack_codes(words, bits, w["head_dim"]), n, R, c)
+
+
+def _oracle_decode_unit(w, seed):
+    """One (batch, KV head) unit of one layer's decode through the oracle:
+    storage built untimed, then unpack + dequantize + float64 attention timed.
+    Returns (seconds, algorithmic bytes of the unit)."""
+    import oracle
+    import synth
+    d, T, G = w["head_dim"], w["tokens"], w["q_heads"] // w["kv_heads"]
+    R = oracle.rotation_matrix(0, d)
+    k, v = synth.kv_numpy(seed, 1, 1, T, d, dist=w["dist"], outlier_frac=w["outlier_frac"])
+    q = synth.q_numpy(seed, 1, G, d)
+    ks, vs = _oracle_side(w, w["k"][0], w["k"][1], k, R), _oracle_side(w, w["v"][0], w["v"][1], v, R)
+    t0 = time.perf_counter()
+    oracle.decode_attention(q, _oracle_rows(w, ks, R), _oracle_rows(w, vs, R))
+    dt = time.perf_counter() - t0
+    nbytes = (side_bytes_per_token(w["k"][0], w["k"][1], d) + side_bytes_per_token(w["v"][0], w["v"][1], d)) * T
+    return dt, nbytes
+
+
+def _pool_worker(args):
+    """All-cores leg: one unit per process with single-threaded BLAS; the
+    processes start their timed part together (barrier)."""
+    w, seed = args
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):
+        _oracle_decode_unit(w, seed + 50000)  # warm the imports and caches (untimed)
+        _POOL_BARRIER.wait()
+        return _oracle_decode_unit(w, seed)
+
+
+def _pool_init(barrier):
+    global _POOL_BARRIER
+    _POOL_BARRIER = barrier
+
+
+def cpu_baseline(w, budget_s: float = 8.0, max_workers: int = 16):
+    """Time the oracle (float64 NumPy, as it stands) on bounded samples of the
+    workload on this host's cores: the decode with one core (BLAS pinned to
+    one thread) over whole (batch, KV head) units until ~budget_s, the decode
+    with all cores (one unit per process, up to max_workers processes, the
+    box's CPU share), and the prefill quantize-append (norm, rotation,
+    threshold count, packing) of one unit's new rows for K and V."""
+    import multiprocessing as mp
+    import numpy as np
+    from threadpoolctl import threadpool_limits
 
     import oracle
     import synth
 
+    nproc = os.cpu_count() or 1
+    model = ""
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        cores = 1
-    d, T, G = w["head_dim"], w["tokens"], w["q_heads"] // w["kv_heads"]
-    kb, vb = w["k"][1], w["v"][1]
-    R = oracle.rotation_matrix(0, d)
-    units, spent, nbytes = 0, 0.0, 0
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
+    d, T = w["head_dim"], w["tokens"]
     total_units = w["batch"] * w["kv_heads"]
-    def prepare(mode, bits, x):
-        """Storage of one side, built outside the timed part."""
-        if mode == "fp16":
-            return ("fp16", x)
-        if mode == "int8":
-            return ("int8",) + oracle.int8_quantize(x)
-        c, t = oracle.lloyd_max(d, bits)
-        codes, n, _ = oracle.quantize(x, R, t)
-        return ("packed", oracle.pack_codes(codes, bits), n.astype(np.float32), c, bits)
 
-    def rows(st):
-        """Rows the decode reads, rebuilt from the storage (timed)."""
-        if st[0] == "fp16":
-            return st[1].astype(np.float64)
-        if st[0] == "int8":
-            return oracle.int8_dequantize(st[1], st[2])
-        _, words, n, c, bits = st
-        return oracle.dequantize(oracle.unpack_codes(words, bits, d), n, R, c)
+    # one core
+    units, spent, nbytes = 0, 0.0, 0
+    with threadpool_limits(1):
+        while spent < budget_s and units < total_units:
+            dt, nb = _oracle_decode_unit(w, 1000 + units)
+            spent, nbytes, units = spent + dt, nbytes + nb, units + 1
+    one = {"value": nbytes / spent / 1e9, "unit": "GB/s", "cores": 1,
+           "sample": f"{units} of {total_units} (batch, KV head) units of one layer's decode at context {T} "
+                     f"(unpack + dequantize + float64 attention), {spent:.1f} s"}
 
-    while spent < budget_s and units < total_units:
-        k, v = synth.kv_numpy(1000 + units, 1, 1, T, d, dist=w["dist"], outlier_frac=w["outlier_frac"])
-        q = synth.q_numpy(1000 + units, 1, G, d)
-        ks, vs = prepare(w["k"][0], kb, k), prepare(w["v"][0], vb, v)
-        t0 = time.perf_counter()
-        oracle.decode_attention(q, rows(ks), rows(vs))
-        spent += time.perf_counter() - t0
-        units += 1
-        nbytes += (side_bytes_per_token(w["k"][0], kb, d) + side_bytes_per_token(w["v"][0], vb, d)) * T
-    return {"value": nbytes / spent / 1e9, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{units} of {total_units} (batch, KV head) units of one layer's "
-                      f"decode at context {T} (unpack + dequantize + float64 attention), {spent:.1f} s"}
+    # all cores: one unit per process, timed together
+    workers = max(1, min(nproc, max_workers, total_units))
+    barrier = mp.get_context("fork").Barrier(workers)
+    with mp.get_context("fork").Pool(workers, initializer=_pool_init, initargs=(barrier,)) as pool:
+        res = pool.map(_pool_worker, [(w, 2000 + i) for i in range(workers)])
+    wall = max(r[0] for r in res)
+    allc = {"value": sum(r[1] for r in res) / wall / 1e9, "unit": "GB/s", "cores": workers,
+            "sample": f"{workers} (batch, KV head) units of one layer's decode at context {T}, one per process "
+                      f"(BLAS single-threaded), timed together: {wall:.1f} s"}
+
+    # prefill quantize-append: one unit's new rows of K and V
+    qa = None
+    n_new = w.get("prefill", 0) or w.get("append", 0)
+    if n_new:
+        R = oracle.rotation_matrix(0, d)
+        k, v = synth.kv_numpy(3000, 1, 1, n_new, d, dist=w["dist"], outlier_frac=w["outlier_frac"])
+        with threadpool_limits(1):
+            t0 = time.perf_counter()
+            for (mode, bits), x in ((w["k"], k), (w["v"], v)):
+                if mode in ("packed", "delegated"):
+                    _, th = oracle.lloyd_max(d, bits)
+                    codes, n, _ = oracle.quantize(x, R, th)
+                    oracle.pack_codes(codes, bits)
+                    n.astype(np.float32)
+                elif mode == "int8":
+                    oracle.int8_quantize(x)
+            dt = time.perf_counter() - t0
+        # positions per second with every KV head of a sequence (the metric's unit)
+        qa = {"value": n_new / (dt * w["kv_heads"]) / 1e6, "unit": "Mtok/s", "cores": 1,
+              "sample": f"one (batch, KV head) unit's {n_new} new rows of K and V quantized and packed, "
+                        f"{dt:.2f} s, scaled to {w['kv_heads']} KV heads per position"}
+    out = {"value": allc["value"], "unit": "GB/s", "cores": workers, "kind": "oracle",
+           "sample": allc["sample"], "one_core": one, "all_cores": allc, "nproc": nproc, "cpu_model": model}
+    if qa:
+        out["quantize_append"] = qa
+    return out
 
 
 # the decode kernels whose counters can be recorded, by name prefix, with the
@@ -281,7 +362,10 @@ def pmc_summary(csvs: list, workload: str, cmds: list, title: str):
     w = WORKLOADS[workload]
     chunks = w["batch"] * w["kv_heads"] * w["tokens"] // 32
     acc = collections.defaultdict(lambda: collections.defaultdict(list))
+    # ratios only between counters of the same file (one profiled run)
+    ratio = collections.defaultdict(lambda: collections.defaultdict(float))
     for path in csvs:
+        one = collections.defaultdict(lambda: collections.defaultdict(float))
         with open(path) as f:
             for r in csv.DictReader(f):
                 name = r["Kernel_Name"]
@@ -289,6 +373,12 @@ def pmc_summary(csvs: list, workload: str, cmds: list, title: str):
                     continue
                 short = name.replace("void ", "").replace("tq::(anonymous namespace)::", "").split("(tq::")[0]
                 acc[short][r["Counter_Name"]].append(float(r["Counter_Value"]))
+                one[short][r["Counter_Name"]] += float(r["Counter_Value"])
+        for short, cs in one.items():
+            for _, a, b in PMC_RATIOS:
+                if a in cs and b in cs:
+                    ratio[short][a] += cs[a]
+                    ratio[short][(a, b)] += cs[b]
     out = [f"# rocprofv3 hardware counters ({title}), workload {workload}: batch {w['batch']}, "
            f"{w['kv_heads']} KV heads, {w['q_heads']} query heads, head_dim {w['head_dim']}, context {w['tokens']}",
            "# commands (from the repository root):"]
@@ -305,8 +395,9 @@ def pmc_summary(csvs: list, workload: str, cmds: list, title: str):
             extra = f"   per chunk {avg / chunks:10.2f}" if is_decode and c.startswith("SQ_INSTS") else ""
             out.append(f"  {c:32s} {avg:18.1f}{extra}")
         for label, a, b in PMC_RATIOS:
-            if a in cs and b in cs and sum(cs[b]) > 0:
-                out.append(f"  ratio {a} / {b} = {sum(cs[a]) / sum(cs[b]):.4f}   ({label})")
+            num, den = ratio[short].get(a, 0.0), ratio[short].get((a, b), 0.0)
+            if den > 0:
+                out.append(f"  ratio {a} / {b} = {num / den:.4f}   ({label}; both from the same runs)")
         out.append("")
     return "\n".join(out) + "\n"
 
@@ -442,6 +533,9 @@ def main():
     if args.tokens:
         w["tokens"] = args.tokens
         w["prefill"] = min(w.get("prefill", 0), args.tokens)
+    # the oracle's CPU baseline runs first, before anything touches the GPU
+    # (its all-cores leg forks worker processes)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w)
     dev = "cuda:0"
     torch.cuda.set_device(0)
     B, Hkv, Hq, d, T, Lyr = w["batch"], w["kv_heads"], w["q_heads"], w["head_dim"], w["tokens"], w["layers"]
@@ -500,7 +594,16 @@ def main():
     # launches by kind changes no work; it lets one event pair per group time
     # the back-to-back launches of each kernel (per-launch average = group
     # time / layers) without an event between every two kernels.
+    # A step whose working set fits the caches (the 256 MB Infinity Cache and
+    # the L2s) would be served from them on the next step: such workloads
+    # overwrite a 1 GiB scratch buffer before every step, outside the event
+    # pairs that time the kernels (ms_per_step includes it).
+    working = Lyr * (decode_bytes(w) + (append_bytes(w, n_new) if n_new else 0))
+    flush = torch.empty(1 << 28, dtype=torch.int32, device=dev) if working < (1 << 30) else None
+
     def step(record):
+        if flush is not None:
+            flush.fill_(len(record) if record is not None else -1)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)] if record is not None else None
         if ev:
             ev[0].record(stream)
@@ -549,7 +652,8 @@ def main():
         "config": {"workload": args.workload, "batch": B, "kv_heads": Hkv, "q_heads": Hq,
                    "head_dim": d, "context": T, "layers": Lyr,
                    "k": f"{w['k'][0]}{w['k'][1] or ''}", "v": f"{w['v'][0]}{w['v'][1] or ''}",
-                   "append_per_layer": n_new, "block_size": bsz, "sparse_v": args.sparse_v},
+                   "append_per_layer": n_new, "block_size": bsz, "sparse_v": args.sparse_v,
+                   "cache_flush_gib_per_step": 1 if flush is not None else 0},
         "hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4),
         "decode_us_per_layer": round(dec_avg_s * 1e6, 2),
         "decode_bytes_per_layer": dbytes,
@@ -567,8 +671,8 @@ def main():
         res["quantize_append_mtok_s"] = round(B * n_new / app_avg_s / 1e6, 2)
         res["quantize_append_us_per_layer"] = round(app_avg_s * 1e6, 2)
         res["quantize_append_gbs"] = round(append_bytes(w, n_new) / app_avg_s / 1e9, 1)
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w)
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
 
 

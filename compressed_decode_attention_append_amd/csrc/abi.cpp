@@ -130,10 +130,20 @@ bool choose_split(const tq_cache *c, int q_heads, int length, int n_splits, int 
 // measurements and the cross-check tests).
 enum Variant { kRef, kMfma };
 
+// The shapes the matrix-core decode takes (tq_common.h states the rule).
+bool decode_mfma_supported(const tq::DecodeParams &p) {
+  const int G = p.q_heads / p.kv_heads;
+  if (p.head_dim != 128 || G > 8) return false;
+  if (!(p.v.mode == TQ_SIDE_PACKED || p.v.mode == TQ_SIDE_DELEGATED) || p.v.bits != 4) return false;
+  if (p.k.mode == TQ_SIDE_FP16) return true;
+  if (p.k.mode != TQ_SIDE_PACKED || p.v.mode != TQ_SIDE_PACKED) return false;
+  return p.k.bits == 3 || (p.k.bits == 4 && p.share_lut);  // 4-bit K shares V's codebook table
+}
+
 Variant pick_variant(const tq::DecodeParams &p) {
   const char *env = getenv("TQ_DECODE_VARIANT");
   if (env && strcmp(env, "ref") == 0) return kRef;
-  return tq::decode_mfma_supported(p) ? kMfma : kRef;
+  return decode_mfma_supported(p) ? kMfma : kRef;
 }
 
 // Splits of the matrix-core kernel: the packed positions of a unit in
@@ -145,7 +155,7 @@ void mfma_splits(const tq_cache *c, int length, int n_splits, tq::DecodeParams *
   constexpr int kTargetBlocks = 256, kMinPerBlock = 512, kQuantum = 256;
   const int units = c->batch * c->kv_heads;
   const int cold = (c->v.mode == TQ_SIDE_DELEGATED) ? std::max(0, length - c->v.hot) : length;
-  const int cap = tq::decode_mfma_max_splits();
+  const int cap = tq::kMfmaMaxSplits;
   int ncold = 1, clen = 1;
   if (cold > 0) {
     if (n_splits > 0) {

@@ -66,7 +66,7 @@ constexpr int waves_of() { return KB == 0 ? 8 : 12; }
 constexpr int kMaxWaves = 12;
 constexpr int kChunk = 32;
 constexpr int kRep = 32;          // pair-table replicas, one per LDS bank
-constexpr int kMaxSplits = 256;   // splits per unit (bounded by the host)
+constexpr int kMaxSplits = kMfmaMaxSplits;  // splits per unit (bounded by the host)
 constexpr float kRescale = 8.0f;  // lazy rescaling threshold (log2 units)
 constexpr float kVscaleMax = 1099511627776.0f;  // 2^40: start and ceiling of the V scale
 
@@ -1290,26 +1290,6 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
 }
 
 }  // namespace
-
-bool decode_mfma_supported(const DecodeParams &p) {
-  const int G = p.q_heads / p.kv_heads;
-  if (p.head_dim != D || G > 8) return false;
-  if (!(p.v.mode == TQ_SIDE_PACKED || p.v.mode == TQ_SIDE_DELEGATED) || p.v.bits != 4) return false;
-  int kb;
-  if (p.k.mode == TQ_SIDE_FP16) {
-    kb = 0;
-  } else if (p.k.mode == TQ_SIDE_PACKED && p.k.bits == 3 && p.v.mode == TQ_SIDE_PACKED) {
-    kb = 3;
-  } else if (p.k.mode == TQ_SIDE_PACKED && p.k.bits == 4 && p.share_lut && p.v.mode == TQ_SIDE_PACKED) {
-    kb = 4;  // K and V share one 4-bit codebook table
-  } else {
-    return false;
-  }
-  (void)kb;
-  return true;
-}
-
-int decode_mfma_max_splits() { return kMaxSplits; }
 
 template <int KB, int GP, bool SC>
 void launch_sc(const DecodeParams &p, dim3 grid, hipStream_t stream) {

@@ -160,8 +160,12 @@ constexpr size_t kScratchBytes = size_t(16) << 20;
 static_assert(kScratchBytes == TQ_NOALLOC_SCRATCH_BYTES, "tq.h states the scratch size");
 hipError_t scratch_workspace(hipStream_t stream, void **ptr);
 hipError_t launch_decode_ref(const DecodeParams &p, hipStream_t stream);
+// The matrix-core decode takes head_dim 128, up to 8 query heads per KV
+// head, a packed or delegated 4-bit V, and K as fp16, packed 3-bit, or
+// packed 4-bit sharing V's codebook; at most kMfmaMaxSplits context splits
+// per (batch, KV head) unit.  (The host picks it by this rule; the launcher
+// checks it again.)
 hipError_t launch_decode_mfma(const DecodeParams &p, hipStream_t stream);
-bool decode_mfma_supported(const DecodeParams &p);
-int decode_mfma_max_splits();
+constexpr int kMfmaMaxSplits = 256;
 
 }  // namespace tq

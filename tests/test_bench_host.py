@@ -66,3 +66,39 @@ def test_committed_traffic_records_parse():
         assert len(fields["source_sha256"]) == 64, name
         assert int(float(fields["traffic_bytes_per_launch"])) > 0, name
         assert float(fields["traffic_over_algorithmic"]) < 1.5, name
+
+
+def test_trace_summary_keeps_the_timed_dispatches(tmp_path):
+    # six decode dispatches: two warm-up ones of 100 us, then four of 30 us;
+    # with steps 2 and layers 2 only the last four enter the average
+    import bench
+    path = tmp_path / "trace.csv"
+    name = "void tq::(anonymous namespace)::decode_mfma_kernel<3, 4, false, false>(tq::DecodeParams)"
+    with open(path, "w") as f:
+        f.write("Kernel_Name,Start_Timestamp,End_Timestamp\n")
+        t = 0
+        for dur in (100000, 100000, 30000, 30000, 30000, 30000):
+            f.write(f"\"{name}\",{t},{t + dur}\n")
+            t += dur + 1000
+    out = bench.trace_summary(str(path), "c4_tq35_32k", 4, ["cmd"])
+    line = next(ln for ln in out.splitlines() if ln.startswith("decode_mfma_kernel"))
+    calls, avg = line.split()[-5], float(line.split()[-4])
+    assert calls == "4" and avg == 30.0
+    gbs = bench.decode_bytes(bench.WORKLOADS["c4_tq35_32k"]) / 30e-6 / 1e9
+    assert f"{gbs:.1f} GB/s" in out
+
+
+def test_pmc_summary_per_chunk(tmp_path):
+    import bench
+    path = tmp_path / "pmc.csv"
+    name = "void tq::(anonymous namespace)::decode_mfma_kernel<3, 4, false, false>(tq::DecodeParams)"
+    chunks = 4 * 8 * 32768 // 32
+    with open(path, "w") as f:
+        f.write("Kernel_Name,Counter_Name,Counter_Value\n")
+        for v in (2.0, 4.0):
+            f.write(f"\"{name}\",SQ_INSTS_VALU,{v * chunks}\n")
+            f.write(f"\"{name}\",SQ_WAVE_CYCLES,{10 * v * chunks}\n")
+            f.write(f"\"{name}\",SQ_ACTIVE_INST_VALU,{v * chunks}\n")
+    out = bench.pmc_summary([str(path)], "c4_tq35_32k", ["cmd"], "test")
+    assert "per chunk       3.00" in out
+    assert "SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES = 0.1000" in out
