@@ -44,6 +44,11 @@ WORKLOADS = {
     "c3_int8_16k": dict(batch=8, kv_heads=8, q_heads=32, head_dim=128, tokens=16384, layers=36,
                         k=("int8", 0), v=("int8", 0), prefill=0, append=1, dist="channel",
                         outlier_frac=0.01),
+    # the 32K workload with a peaked softmax (heavy-hitter keys at the first
+    # 4 positions of every 512; the sparse-V comparison)
+    "c4_tq35_32k_peaked": dict(batch=4, kv_heads=8, q_heads=32, head_dim=128, tokens=32768, layers=36,
+                               k=("packed", 3), v=("packed", 4), prefill=8192, dist="channel",
+                               outlier_frac=0.01, peaked=(512, 4, 9.0)),
     "c5_delegated_64k": dict(batch=16, kv_heads=4, q_heads=32, head_dim=128, tokens=65536, layers=48,
                              k=("fp16", 0), v=("delegated", 4), prefill=0, dist="channel",
                              outlier_frac=0.0, hot=256),
@@ -559,20 +564,25 @@ def main():
             perm = torch.randperm(nb, generator=torch.Generator().manual_seed(li)).to(torch.int32)
             paging = dict(block_table=perm.reshape(B, T // bsz), block_size=bsz, num_blocks=nb)
         cache = tq.TQCache(B, Hkv, d, T, kspec, vspec, seed=0, device=dev, **paging)
+        q = synth.q_torch(31 + li, B, Hq, d, device=dev)
+        peak = w.get("peaked")
         # fill positions [0, base) with the layer's own synthetic rows
         chunk = 4096
         for s in range(0, base, chunk):
             n = min(chunk, base - s)
             k, v = synth.kv_torch(7919 * li + s, B, Hkv, n, d, dist=w["dist"],
                                   outlier_frac=w["outlier_frac"], device=dev)
+            if peak:
+                synth.peak_keys_torch(k, q, s, *peak)
             cache.quantize_append(k, v, s)
             del k, v
         if n_new:
             kn, vn = synth.kv_torch(104729 + li, B, Hkv, n_new, d, dist=w["dist"],
                                     outlier_frac=w["outlier_frac"], device=dev)
+            if peak:
+                synth.peak_keys_torch(kn, q, base, *peak)
         else:
             kn = vn = None
-        q = synth.q_torch(31 + li, B, Hq, d, device=dev)
         out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
         ws = cache.workspace(Hq, T, args.splits)
         layers.append((cache, kn, vn, q, out, ws))

@@ -104,7 +104,8 @@ struct Lay {
   static constexpr int red = qwork + GP * qstride;     // flag
   static constexpr int prog = red + 4;                 // [kMaxWaves] chunks done per wave
   static constexpr int qinv = red + 16;                // [8] per head: the score's query scale
-  static constexpr int tail = red + 24;
+  static constexpr int bmax = red + 24;                // sparse-V: [8 heads][16 waves] published maxima
+  static constexpr int tail = red + 152;
   // Merge slots of the main loop's waves: an area of their own when it fits
   // (a wave then writes its slot as soon as its own loop ends), else over
   // the tables once every wave is done with them.
@@ -266,6 +267,7 @@ struct ChunkData {
   float kn[nv];        // K norms of the lane's compact positions
   uint32_t v[8];       // V code word `col` of the 8 positions of this lane group
   float vn[nv];        // V norms of the compact positions
+  bool vskip;          // sparse-V: the V codes were not loaded (predicted skippable)
 };
 
 // Lane roles.  MFMA layouts (v_mfma_f32_16x16x32_f16): A lane l holds row
@@ -288,6 +290,8 @@ struct Wave {
   uint32_t rep4v;       // 4 r + the V table's byte offset
   uint32_t koff, knoff, voff;   // lane byte offsets inside a chunk
   const uint32_t *lds;
+  uint32_t bmax_at;     // sparse-V: LDS byte address of the published maxima [8 heads][16 waves]
+  int wave_id;
   half8_t bq[4];         // R q: column h < GP hi, column GP + h lo of head h
   // per-unit bases
   const char *kbase;   // K codes or fp16 rows of this unit
@@ -299,6 +303,10 @@ struct Wave {
   Paging pg;           // PG: where the unit's rows live
   int unit;
   float sparse_lg;     // sparse-V threshold (log2), -inf = exact
+  float block_ref;     // sparse-V: the largest running maximum the block's waves
+                       // have published for the lane's head (-inf: none)
+  bool pred_skip;      // sparse-V: the wave's last chunk was skippable, so the
+                       // next chunk's V codes are not loaded up front
   float qinv;          // the lane's head (compact layout): the power of two
                        // that undoes the query's scaling in B (see the prologue)
   float chunk_max;     // the last softmax's chunk maximum of the lane's head
@@ -347,13 +355,18 @@ struct Wave {
   // rows [t0, t0 + 32) at most, from storage row row0 on; rows past the
   // unit's capacity, and every row of an out-of-range block (row0 = -1),
   // read 0
-  __device__ __forceinline__ void load_row(long row0, int t0, ChunkData<KB, GP> &c) const {
+  // vskip (sparse-V): the V codes go through an empty buffer resource, which
+  // reads nothing and returns zeros (the same loads are issued, so the
+  // wave's waits stay static); the chunk notes it, and reloads them if its
+  // weights turn out to need them.
+  __device__ __forceinline__ void load_row(long row0, int t0, ChunkData<KB, GP> &c, bool vskip = false) const {
     const int rows = row0 < 0 ? 0 : min(capacity - t0, kChunk);
     row0 = row0 < 0 ? 0L : row0;
     const auto rk = rsrc(kbase + row0 * kRowBytes, rows * kRowBytes);
     const auto rkn = rsrc(knbase + row0 * 4, rows * 4);
-    const auto rv = rsrc(vbase + row0 * 64, rows * 64);
+    const auto rv = rsrc(vbase + row0 * 64, vskip ? 0 : rows * 64);
     const auto rvn = rsrc(vnbase + row0 * 4, rows * 4);
+    c.vskip = vskip;
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const int mo = m * 16 * kRowBytes;
@@ -386,6 +399,10 @@ struct Wave {
 #pragma unroll
       for (int j = 0; j < NV; ++j) c.vn[j] = __uint_as_float(b[j]);
     }
+    load_v(rv, c);
+  }
+
+  __device__ __forceinline__ void load_v(__amdgpu_buffer_rsrc_t rv, ChunkData<KB, GP> &c) const {
 #pragma unroll
     for (int s8 = 0; s8 < 8; ++s8)
       c.v[s8] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff + (16 * (s8 >> 2) + (s8 & 3)) * 64, 0, 0);
@@ -623,11 +640,11 @@ struct Wave {
   // byte per coordinate pair index), then per tile q one table lookup per
   // slot pair and one MFMA: D[(head, hi/lo)][coordinate 8 col + q] +=
   // P[(head, hi/lo)][slot] * c[code of slot, coordinate].
-  __device__ __forceinline__ void values(const ChunkData<KB, GP> &c, const half8_t ap) {
+  __device__ __forceinline__ void values(const uint32_t (&cv)[8], const half8_t ap) {
     uint32_t ev[4], od[4];  // bytes j: coordinates 8 col + 2 j (ev) and 8 col + 2 j + 1 (od)
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2) {
-      const uint32_t x0 = c.v[2 * s2], x1 = c.v[2 * s2 + 1];
+      const uint32_t x0 = cv[2 * s2], x1 = cv[2 * s2 + 1];
       ev[s2] = bfi(0x0f0f0f0fu, x0, x1 << 4);
       od[s2] = bfi(0x0f0f0f0fu, x0 >> 4, x1);
     }
@@ -661,7 +678,7 @@ struct Wave {
   }
 
   // One chunk of packed positions [t0, t0 + 32); positions >= we are masked.
-  template <bool TAIL>
+  template <bool TAIL, bool SP>
   __device__ __forceinline__ void cold_chunk(int t0, int we, const ChunkData<KB, GP> &c, float *scores,
                                              long score_row0, int length) {
     float s[8], cs[NV];
@@ -674,11 +691,45 @@ struct Wave {
     }
     if (scores) store_scores<TAIL>(t0, we, cs, scores, score_row0, length);
     const half8_t ap = softmax<TAIL, true>(cs, c.vn);
-    // sparse-V: every weight of the chunk, for every head, below the
-    // threshold times the running maximum (which never exceeds the final
-    // one): the chunk's values are skipped; its weights stay in the sum
-    if (sparse_lg != -INFINITY && !__ballot(chunk_max - m_run >= sparse_lg)) return;
-    values(c, ap);
+    if (!SP) {
+      // exact decode: a threshold never set (kept as a runtime test: the
+      // branch keeps the value phase out of the score phase's schedule)
+      if (sparse_lg != -INFINITY && !__ballot(chunk_max - m_run >= sparse_lg)) return;
+    } else {
+      // sparse-V: every weight of the chunk, for every real head, below the
+      // threshold times the larger of the wave's running maximum and the
+      // block's published one (neither exceeds the final maximum): the
+      // chunk's values are skipped; its weights stay in the sum.  The block
+      // maximum is what the block's waves have published in LDS, and this
+      // wave publishes its own.
+      typedef __attribute__((address_space(3))) const volatile u32x4_t lds_v4;
+      typedef __attribute__((address_space(3))) volatile float lds_f;
+      float r = m_run;
+#pragma unroll
+      for (int i = 0; i < kMaxWaves / 4; ++i) {
+        // head h's maxima are floats 16 h .. 16 h + 15 (one per wave)
+        const u32x4_t m = *reinterpret_cast<lds_v4 *>(bmax_at + 64u * (col % GP) + 16u * i);
+        r = fmaxf(r, fmaxf(fmaxf(__uint_as_float(m[0]), __uint_as_float(m[1])),
+                           fmaxf(__uint_as_float(m[2]), __uint_as_float(m[3]))));
+      }
+      const bool skip = !__ballot(col % GP < G && chunk_max - r >= sparse_lg);
+      if (col < GP && grp == 0) *reinterpret_cast<lds_f *>(bmax_at + 4u * (16u * col + wave_id)) = m_run;
+      pred_skip = skip;
+      if (skip) return;
+      if (c.vskip) {
+        // predicted skippable, but needed: load the V codes now
+        const long row0 = row_of(t0);
+        const int rows = row0 < 0 ? 0 : min(capacity - t0, kChunk);
+        const auto rv = rsrc(vbase + (row0 < 0 ? 0L : row0) * 64, rows * 64);
+        uint32_t vv[8];
+#pragma unroll
+        for (int s8 = 0; s8 < 8; ++s8)
+          vv[s8] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff + (16 * (s8 >> 2) + (s8 & 3)) * 64, 0, 0);
+        values(vv, ap);
+        return;
+      }
+    }
+    values(c.v, ap);
   }
 
   // One chunk of the fp16 hot window (delegated V), positions >= we masked.
@@ -853,7 +904,7 @@ struct Balance {
   }
 };
 
-template <int KB, int GP, bool PG, bool SC>
+template <int KB, int GP, bool PG, bool SC, bool SP>
 __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(const DecodeParams p) {
   constexpr int kWaves = waves_of<KB>();
   constexpr int kThreads = 64 * kWaves;
@@ -923,6 +974,9 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   W.ring = (p.v.mode == TQ_SIDE_DELEGATED) ? p.v.fp16 + static_cast<long>(unit) * p.v.hot * D : nullptr;
   W.vscale = kVscaleMax;
   W.sparse_lg = p.sparse_lg;
+  W.pred_skip = false;
+  W.bmax_at = 4u * L::bmax;
+  W.wave_id = wave;
   W.reset();
 
   // ---- the query, then the first chunk, in flight while the block builds
@@ -1037,6 +1091,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
     qinvs[wave] = 1.0f;
   }
   if (lane == 0) prog[wave] = 0;
+  if (SP && threadIdx.x < 128) reinterpret_cast<float *>(lds + L::bmax)[threadIdx.x] = -INFINITY;
   __syncthreads();  // tables, rotated query and progress counters complete
   {
     // B operand of the score: column h < G the hi half of head h's query,
@@ -1069,13 +1124,13 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
       int cn = c + kWaves;
       uint32_t nblk2 = W.blk_fetch(s0 + min(cn + kWaves, last) * kChunk);
       if (PG) asm volatile("" ::: "memory");
-      W.load_row(W.row_from(nblk, s0 + min(cn, last) * kChunk), s0 + min(cn, last) * kChunk, B);
+      W.load_row(W.row_from(nblk, s0 + min(cn, last) * kChunk), s0 + min(cn, last) * kChunk, B, SP && W.pred_skip);
       nblk = nblk2;
       asm volatile("" ::: "memory");
       if (c < n_full) {
-        W.template cold_chunk<false>(s0 + c * kChunk, s1, A, scores, hq0, p.length);
+        W.template cold_chunk<false, SP>(s0 + c * kChunk, s1, A, scores, hq0, p.length);
       } else {
-        W.template cold_chunk<true>(s0 + c * kChunk, s1, A, scores, hq0, p.length);
+        W.template cold_chunk<true, SP>(s0 + c * kChunk, s1, A, scores, hq0, p.length);
       }
       bal.step(wave, lane);
       c = cn;
@@ -1083,13 +1138,13 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
       cn = c + kWaves;
       nblk2 = W.blk_fetch(s0 + min(cn + kWaves, last) * kChunk);
       if (PG) asm volatile("" ::: "memory");
-      W.load_row(W.row_from(nblk, s0 + min(cn, last) * kChunk), s0 + min(cn, last) * kChunk, A);
+      W.load_row(W.row_from(nblk, s0 + min(cn, last) * kChunk), s0 + min(cn, last) * kChunk, A, SP && W.pred_skip);
       nblk = nblk2;
       asm volatile("" ::: "memory");
       if (c < n_full) {
-        W.template cold_chunk<false>(s0 + c * kChunk, s1, B, scores, hq0, p.length);
+        W.template cold_chunk<false, SP>(s0 + c * kChunk, s1, B, scores, hq0, p.length);
       } else {
-        W.template cold_chunk<true>(s0 + c * kChunk, s1, B, scores, hq0, p.length);
+        W.template cold_chunk<true, SP>(s0 + c * kChunk, s1, B, scores, hq0, p.length);
       }
       bal.step(wave, lane);
       c = cn;
@@ -1110,10 +1165,10 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
       int cn = c + kWaves;
       uint32_t nblk2 = W.blk_fetch(s0 + min(cn + kWaves, last) * kChunk);
       if (PG) asm volatile("" ::: "memory");
-      W.load_row(W.row_from(nblk, s0 + min(cn, last) * kChunk), s0 + min(cn, last) * kChunk, B);
+      W.load_row(W.row_from(nblk, s0 + min(cn, last) * kChunk), s0 + min(cn, last) * kChunk, B, SP && W.pred_skip);
       nblk = nblk2;
       asm volatile("" ::: "memory");
-      W.template cold_chunk<false>(s0 + c * kChunk, s1, A, scores, hq0, p.length);
+      W.template cold_chunk<false, SP>(s0 + c * kChunk, s1, A, scores, hq0, p.length);
       bal.step(wave, lane);
       c = cn;
       if (c >= n_full) {
@@ -1123,18 +1178,18 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
       cn = c + kWaves;
       nblk2 = W.blk_fetch(s0 + min(cn + kWaves, last) * kChunk);
       if (PG) asm volatile("" ::: "memory");
-      W.load_row(W.row_from(nblk, s0 + min(cn, last) * kChunk), s0 + min(cn, last) * kChunk, A);
+      W.load_row(W.row_from(nblk, s0 + min(cn, last) * kChunk), s0 + min(cn, last) * kChunk, A, SP && W.pred_skip);
       nblk = nblk2;
       asm volatile("" ::: "memory");
-      W.template cold_chunk<false>(s0 + c * kChunk, s1, B, scores, hq0, p.length);
+      W.template cold_chunk<false, SP>(s0 + c * kChunk, s1, B, scores, hq0, p.length);
       bal.step(wave, lane);
       c = cn;
     }
     if (c < n_chunks) {
       if (in_b) {
-        W.template cold_chunk<true>(s0 + c * kChunk, s1, B, scores, hq0, p.length);
+        W.template cold_chunk<true, SP>(s0 + c * kChunk, s1, B, scores, hq0, p.length);
       } else {
-        W.template cold_chunk<true>(s0 + c * kChunk, s1, A, scores, hq0, p.length);
+        W.template cold_chunk<true, SP>(s0 + c * kChunk, s1, A, scores, hq0, p.length);
       }
     }
   }
@@ -1291,12 +1346,22 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
 
 }  // namespace
 
+template <int KB, int GP, bool SC, bool SP>
+void launch_sp(const DecodeParams &p, dim3 grid, hipStream_t stream) {
+  if (p.pg.table) {
+    hipLaunchKernelGGL((decode_mfma_kernel<KB, GP, true, SC, SP>), grid, dim3(64 * waves_of<KB>()), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((decode_mfma_kernel<KB, GP, false, SC, SP>), grid, dim3(64 * waves_of<KB>()), 0, stream, p);
+  }
+}
+
+// SP: sparse-V (a threshold is set); the exact decode compiles it out
 template <int KB, int GP, bool SC>
 void launch_sc(const DecodeParams &p, dim3 grid, hipStream_t stream) {
-  if (p.pg.table) {
-    hipLaunchKernelGGL((decode_mfma_kernel<KB, GP, true, SC>), grid, dim3(64 * waves_of<KB>()), 0, stream, p);
+  if (p.sparse_lg != -INFINITY) {
+    launch_sp<KB, GP, SC, true>(p, grid, stream);
   } else {
-    hipLaunchKernelGGL((decode_mfma_kernel<KB, GP, false, SC>), grid, dim3(64 * waves_of<KB>()), 0, stream, p);
+    launch_sp<KB, GP, SC, false>(p, grid, stream);
   }
 }
 

@@ -114,6 +114,23 @@ def q_torch(seed: int, batch: int, q_heads: int, head_dim: int,
                        dtype=torch.float32, device=device).to(torch.float16)
 
 
+def peak_keys_torch(k, q, start: int, period: int = 512, count: int = 4, gain: float = 9.0):
+    """Heavy-hitter keys for a peaked softmax: in the K rows k [B, H, n, d]
+    (positions start .. start + n - 1), the positions t with t mod period <
+    count are replaced by gain times the mean of the KV head's query group
+    (q [B, Hq, d]); every other row is left as drawn.  With N(0, 1) queries
+    those positions' logits lie far above the rest."""
+    import torch
+    B, H, n, d = k.shape
+    G = q.shape[1] // H
+    qbar = q.float().reshape(B, H, G, d).mean(dim=2)                   # [B, H, d]
+    t = torch.arange(start, start + n, device=k.device)
+    hot = (t % period) < count
+    if bool(hot.any()):
+        k[:, :, hot] = (gain * qbar)[:, :, None, :].to(k.dtype)
+    return k
+
+
 # The five workload shapes.  ``dist`` / ``outliers`` give the input recipe;
 # ``append`` is the number of tokens appended per sequence inside one step
 # ("prefill" = the chunk size of the prefill quantize-append).

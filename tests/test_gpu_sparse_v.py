@@ -117,3 +117,46 @@ def test_zero_threshold_is_the_exact_call():
     torch.cuda.synchronize()
     assert r == tq.TQ_OK
     assert torch.equal(out, exact)
+
+
+def _periodic(B, H, Hq, d, T, period, seed):
+    """Heavy hitters at the first two positions of every ``period``: the
+    chunks between them are skippable and the chunk holding the next pair
+    is not, so a decode that predicts a skip from the chunk before must
+    still fetch that chunk's values."""
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal((B, H, d))
+    u /= np.linalg.norm(u, axis=-1, keepdims=True)
+    k = rng.standard_normal((B, H, T, d))
+    hot = (np.arange(T) % period) < 2
+    k[:, :, hot] = 8.0 * u[:, :, None, :] + 0.5 * rng.standard_normal((B, H, int(hot.sum()), d))
+    v = rng.standard_normal((B, H, T, d))
+    G = Hq // H
+    q = 32.0 * np.repeat(u, G, axis=1) + 0.1 * rng.standard_normal((B, Hq, d))
+    return k.astype(np.float16), v.astype(np.float16), q.astype(np.float16)
+
+
+@pytest.mark.parametrize("case", CASES[:2], ids=[c[0] for c in CASES[:2]])
+@pytest.mark.parametrize("period", [96, 384])
+def test_sparse_v_periodic_peaks(case, period, dvariant):
+    name, ks, vs = case
+    B, H, Hq, d, T = 2, 2, 8, 128, 5000
+    k, v, q = _periodic(B, H, Hq, d, T, period, 11)
+    cache = tq.TQCache(B, H, d, T, ks, vs)
+    cache.quantize_append(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), 0)
+    qd = torch.from_numpy(q).cuda()
+    tau = 1e-3
+    exact = cache.decode_attention(qd, T)
+    sparse = cache.decode_attention(qd, T, sparse_v=tau)
+    torch.cuda.synchronize()
+    exact, sparse = exact.cpu().numpy().astype(np.float64), sparse.cpu().numpy().astype(np.float64)
+    kr, vr = _rows(cache, "k", T), _rows(cache, "v", T)
+    bound = oracle.sparse_v_bound(q, kr, vr, tau)
+    scale = np.max(np.abs(exact), axis=-1, keepdims=True)
+    assert np.all(np.abs(sparse - exact) <= bound * (1 + 1e-3) + 1e-5 * scale)
+    assert not np.array_equal(sparse, exact)
+    # the heavy hitters' values dominate: dropping any of them would move the
+    # output by far more than the bound
+    ref, _ = oracle.decode_attention(q, kr, vr)
+    ok, worst = rows_close(sparse, ref, rel=2e-3 + float(np.max(bound / scale)))
+    assert ok, f"worst {worst}"
