@@ -91,31 +91,34 @@ __device__ __forceinline__ int v_hot_start(const DecodeParams &p) {
   return 0x7fffffff;
 }
 
+// fp16 row r of a side, or the zero row where r < 0 (a block outside the pools)
+template <int D>
+__device__ __forceinline__ const uint32_t *fp16_row_or_zero(const uint16_t *base, long r) {
+  return r < 0 ? kZeroRow : reinterpret_cast<const uint32_t *>(base + r * D);
+}
+
 // Start of piece `piece` (GW words) of the stored row of position t, or null
 // where that row kind is shorter (the cold rows of a delegated V).  A
-// position in a block outside the paged pools reads the zero row.
+// position in a block outside the paged pools reads the zero row where the
+// row is fp16; a code row (packed or INT8) is read from the pool's row 0
+// instead, and its norm (scale) reads 0 (Stager::load), so the row still
+// contributes exactly nothing.  (This shape keeps the kernel at the register
+// count of the unguarded one.)
 template <int D, int GW>
 __device__ __forceinline__ const uint32_t *piece_src(const DecodeParams &p, const RefLayout &L, long bk, int t,
                                                      bool is_k, int piece, int hot_start) {
   const uint32_t *src;
   if (is_k) {
-    const long r = cache_row(p.pg, bk, t, p.capacity);
-    if (r < 0) return kZeroRow + piece * GW;
-    src = p.k.mode == TQ_SIDE_FP16 ? reinterpret_cast<const uint32_t *>(p.k.fp16 + r * D) : p.k.codes + r * p.k.words;
+    src = p.k.mode == TQ_SIDE_FP16 ? fp16_row_or_zero<D>(p.k.fp16, cache_row(p.pg, bk, t, p.capacity))
+                                   : p.k.codes + max(cache_row(p.pg, bk, t, p.capacity), 0L) * p.k.words;
   } else if (t >= hot_start) {
     if (piece * GW >= L.vw_hot) return nullptr;
-    if (p.v.mode == TQ_SIDE_FP16) {
-      const long r = cache_row(p.pg, bk, t, p.capacity);
-      if (r < 0) return kZeroRow + piece * GW;
-      src = reinterpret_cast<const uint32_t *>(p.v.fp16 + r * D);
-    } else {
-      src = reinterpret_cast<const uint32_t *>(p.v.fp16 + (bk * p.v.hot + t % p.v.hot) * D);
-    }
+    src = p.v.mode == TQ_SIDE_FP16
+              ? fp16_row_or_zero<D>(p.v.fp16, cache_row(p.pg, bk, t, p.capacity))
+              : reinterpret_cast<const uint32_t *>(p.v.fp16 + (bk * p.v.hot + t % p.v.hot) * D);
   } else {
     if (piece * GW >= L.vw_cold) return nullptr;
-    const long r = cache_row(p.pg, bk, t, p.capacity);
-    if (r < 0) return kZeroRow + piece * GW;
-    src = p.v.codes + r * p.v.words;
+    src = p.v.codes + max(cache_row(p.pg, bk, t, p.capacity), 0L) * p.v.words;
   }
   return src + piece * GW;
 }

@@ -7,8 +7,12 @@
 namespace tq {
 
 // 512 zero bytes (the longest stored row: fp16 at head_dim 256).  A position
-// in a block outside the paged pools reads its row from here.
-static __device__ const uint32_t kZeroRow[128] = {};
+// in a block outside the paged pools reads its row from here.  Global memory
+// on purpose, not const: a const array lands in the constant address space,
+// and a pointer that may point there or into the cache turns the kernels'
+// row loads into flat loads, which the LDS waits then also wait for.  Never
+// written.
+static __device__ uint32_t kZeroRow[128] = {};
 
 __device__ __forceinline__ float h2f(uint16_t bits) {
   return static_cast<float>(__builtin_bit_cast(_Float16, bits));
