@@ -134,6 +134,7 @@ enum Variant { kRef, kMfma };
 bool decode_mfma_supported(const tq::DecodeParams &p) {
   const int G = p.q_heads / p.kv_heads;
   if (p.head_dim != 128 || G > 8) return false;
+  if (p.k.mode == TQ_SIDE_INT8 || p.v.mode == TQ_SIDE_INT8) return p.k.mode == p.v.mode;  // INT8 on both sides
   if (!(p.v.mode == TQ_SIDE_PACKED || p.v.mode == TQ_SIDE_DELEGATED) || p.v.bits != 4) return false;
   if (p.k.mode == TQ_SIDE_FP16) return true;
   if (p.k.mode != TQ_SIDE_PACKED || p.v.mode != TQ_SIDE_PACKED) return false;

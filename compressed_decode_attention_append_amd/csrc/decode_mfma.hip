@@ -58,11 +58,20 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int D = 128;
-// Waves per block: 12 for packed K (about 160 registers a lane, so three
-// waves a SIMD), 8 for fp16 K rows (about 250 registers, two a SIMD).  One
-// block per compute unit either way.
+// KB selects the K storage: 3 or 4 (packed codes, rotated domain), 0 (fp16
+// rows), kInt8 (INT8 absmax: one signed byte a coordinate and a float scale
+// a row, on both sides; original domain, no codebook).
+constexpr int kInt8 = 8;
 template <int KB>
-constexpr int waves_of() { return KB == 0 ? 8 : 12; }
+constexpr bool rotated_k() { return KB == 3 || KB == 4; }
+// V bytes a row: 4-bit codes, or INT8 bytes
+template <int KB>
+constexpr int v_row_bytes() { return KB == kInt8 ? D : D / 2; }
+// Waves per block: 12 for packed K (about 160 registers a lane, so three
+// waves a SIMD), 8 for fp16 K rows and for INT8 (about 200-250 registers,
+// two a SIMD).  One block per compute unit either way.
+template <int KB>
+constexpr int waves_of() { return (KB == 0 || KB == kInt8) ? 8 : 12; }
 constexpr int kMaxWaves = 12;
 constexpr int kChunk = 32;
 constexpr int kRep = 32;          // pair-table replicas, one per LDS bank
@@ -134,6 +143,32 @@ __device__ __forceinline__ void split_pair(float x0, float x1, uint32_t &hi, uin
   const float h0 = h2f(f2h(x0)), h1 = h2f(f2h(x1));
   hi = pack_half2(h0, h1);
   lo = pack_half2(x0 - h0, x1 - h1);
+}
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+// Two signed bytes of an INT8 K row as an exact fp16 pair.  w holds four
+// bytes already offset by 128 (x ^ 0x80 = x + 128 as an unsigned byte);
+// bytes B and B + 1 are placed under the exponent byte 0x64, which reads as
+// 1024 + (x + 128), and 1152 is subtracted (exact: every value involved is
+// an integer below 2048).
+template <int B>
+__device__ __forceinline__ uint32_t i8_pair_exact(uint32_t w) {
+  const uint32_t e = __builtin_amdgcn_perm(0x64646464u, w, 0x04000400u | ((B + 1) << 16) | B);
+  const half2_t h = __builtin_bit_cast(half2_t, e) - half2_t{1152.0f16, 1152.0f16};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// One byte from each of two INT8 V rows (byte B of a and of b, both offset
+// by 128) as an fp16 pair x_a 2^-10, x_b 2^-10: the byte as the low bits of
+// an fp16 is the subnormal (x + 128) 2^-24; times 2^14 minus 2^-3 is x 2^-10
+// exactly (one packed fused multiply-add; fp16 subnormals are kept).
+template <int B>
+__device__ __forceinline__ uint32_t i8_cross_pair(uint32_t a, uint32_t b) {
+  const uint32_t e = __builtin_amdgcn_perm(b, a, 0x0c000c00u | ((4 + B) << 16) | B);
+  const half2_t h = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, e), half2_t{16384.0f16, 16384.0f16},
+                                              half2_t{-0.125f16, -0.125f16});
+  return __builtin_bit_cast(uint32_t, h);
 }
 
 // LDS word at byte address `addr` plus a compile-time byte offset.
@@ -261,12 +296,14 @@ __device__ __forceinline__ float xor_butterfly(float x, int lane) {
 // Global-memory data of one chunk of 32 positions for one lane.
 template <int KB, int GP>
 struct ChunkData {
-  static constexpr int kw = KB == 0 ? 16 : (KB == 4 ? 4 : 3);  // K dwords per M-tile
+  static constexpr int kw = KB == 0 ? 16 : (KB == kInt8 ? 8 : (KB == 4 ? 4 : 3));  // K dwords per M-tile
+  static constexpr int kvw = KB == kInt8 ? 16 : 8;             // V dwords
   static constexpr int nv = GP / 2;                            // compact values per lane
-  uint32_t k[2][kw];   // K words (packed) or fp16 row piece, M-tiles 0 and 1
-  float kn[nv];        // K norms of the lane's compact positions
-  uint32_t v[8];       // V code word `col` of the 8 positions of this lane group
-  float vn[nv];        // V norms of the compact positions
+  uint32_t k[2][kw];   // K words (packed), fp16 or INT8 row piece, M-tiles 0 and 1
+  float kn[nv];        // K norms (INT8: scales) of the lane's compact positions
+  uint32_t v[kvw];     // V: code word `col` (INT8: bytes 8 col .. 8 col + 7) of the
+                       // 8 positions of this lane group
+  float vn[nv];        // V norms (INT8: scales) of the compact positions
   bool vskip;          // sparse-V: the V codes were not loaded (predicted skippable)
 };
 
@@ -283,7 +320,8 @@ struct ChunkData {
 template <int KB, int GP, bool PG>
 struct Wave {
   static constexpr int NV = GP / 2;
-  static constexpr int kRowBytes = KB == 0 ? 2 * D : (KB == 4 ? 64 : 48);
+  static constexpr int kRowBytes = KB == 0 ? 2 * D : (KB == kInt8 ? D : (KB == 4 ? 64 : 48));
+  static constexpr int kVRow = v_row_bytes<KB>();
   // per-lane constants
   int col, grp, cpos;   // cpos: chunk position of the lane's first compact slot
   uint32_t rep4;        // 4 r: the lane's replica
@@ -364,7 +402,7 @@ struct Wave {
     row0 = row0 < 0 ? 0L : row0;
     const auto rk = rsrc(kbase + row0 * kRowBytes, rows * kRowBytes);
     const auto rkn = rsrc(knbase + row0 * 4, rows * 4);
-    const auto rv = rsrc(vbase + row0 * 64, vskip ? 0 : rows * 64);
+    const auto rv = rsrc(vbase + row0 * kVRow, vskip ? 0 : rows * kVRow);
     const auto rvn = rsrc(vnbase + row0 * 4, rows * 4);
     c.vskip = vskip;
 #pragma unroll
@@ -399,13 +437,23 @@ struct Wave {
 #pragma unroll
       for (int j = 0; j < NV; ++j) c.vn[j] = __uint_as_float(b[j]);
     }
-    load_v(rv, c);
+    load_v(rv, c.v);
   }
 
-  __device__ __forceinline__ void load_v(__amdgpu_buffer_rsrc_t rv, ChunkData<KB, GP> &c) const {
+  // The V data of the lane's 8 position slots: one code word, or (INT8) the
+  // 8 bytes of coordinates 8 col .. 8 col + 7.
+  __device__ __forceinline__ void load_v(__amdgpu_buffer_rsrc_t rv, uint32_t (&v)[ChunkData<KB, GP>::kvw]) const {
 #pragma unroll
-    for (int s8 = 0; s8 < 8; ++s8)
-      c.v[s8] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff + (16 * (s8 >> 2) + (s8 & 3)) * 64, 0, 0);
+    for (int s8 = 0; s8 < 8; ++s8) {
+      const uint32_t off = voff + (16 * (s8 >> 2) + (s8 & 3)) * kVRow;
+      if (KB == kInt8) {
+        const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(rv, off, 0, 0);
+        v[2 * s8] = w[0];
+        v[2 * s8 + 1] = w[1];
+      } else {
+        v[s8] = __builtin_amdgcn_raw_buffer_load_b32(rv, off, 0, 0);
+      }
+    }
   }
 
   // Scores of the chunk in D layout (lane: slots 4 m + r, head col).
@@ -417,6 +465,16 @@ struct Wave {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const half8_t a = as_half8(c.k[m][4 * q], c.k[m][4 * q + 1], c.k[m][4 * q + 2], c.k[m][4 * q + 3]);
+          acc = mma(a, bq[q], acc);
+        }
+      } else if (KB == kInt8) {
+        // the lane's 32 bytes are coordinates 32 grp .. 32 grp + 31; step q
+        // takes 8 of them, widened exactly to fp16 (one MFMA: exact A)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t w0 = c.k[m][2 * q] ^ 0x80808080u, w1 = c.k[m][2 * q + 1] ^ 0x80808080u;
+          const half8_t a = as_half8(i8_pair_exact<0>(w0), i8_pair_exact<2>(w0), i8_pair_exact<0>(w1),
+                                     i8_pair_exact<2>(w1));
           acc = mma(a, bq[q], acc);
         }
       } else if (KB == 3) {
@@ -640,7 +698,31 @@ struct Wave {
   // byte per coordinate pair index), then per tile q one table lookup per
   // slot pair and one MFMA: D[(head, hi/lo)][coordinate 8 col + q] +=
   // P[(head, hi/lo)][slot] * c[code of slot, coordinate].
-  __device__ __forceinline__ void values(const uint32_t (&cv)[8], const half8_t ap) {
+  __device__ __forceinline__ void values(const uint32_t (&cv)[ChunkData<KB, GP>::kvw], const half8_t ap) {
+    if (KB == kInt8) {
+      // INT8: slot s holds bytes 8 col .. 8 col + 7 in words 2 s, 2 s + 1;
+      // tile q takes byte q % 4 of word q / 4 of every slot, two slots an
+      // operand word, as x 2^-10 (the merge multiplies by 2^10)
+      uint32_t x[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[i] = cv[i] ^ 0x80808080u;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        uint32_t a4[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t a = x[4 * u + (q >> 2)], b = x[4 * u + 2 + (q >> 2)];
+          switch (q & 3) {
+            case 0: a4[u] = i8_cross_pair<0>(a, b); break;
+            case 1: a4[u] = i8_cross_pair<1>(a, b); break;
+            case 2: a4[u] = i8_cross_pair<2>(a, b); break;
+            default: a4[u] = i8_cross_pair<3>(a, b); break;
+          }
+        }
+        accv[q] = mma(ap, as_half8(a4[0], a4[1], a4[2], a4[3]), accv[q]);
+      }
+      return;
+    }
     uint32_t ev[4], od[4];  // bytes j: coordinates 8 col + 2 j (ev) and 8 col + 2 j + 1 (od)
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2) {
@@ -720,11 +802,9 @@ struct Wave {
         // predicted skippable, but needed: load the V codes now
         const long row0 = row_of(t0);
         const int rows = row0 < 0 ? 0 : min(capacity - t0, kChunk);
-        const auto rv = rsrc(vbase + (row0 < 0 ? 0L : row0) * 64, rows * 64);
-        uint32_t vv[8];
-#pragma unroll
-        for (int s8 = 0; s8 < 8; ++s8)
-          vv[s8] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff + (16 * (s8 >> 2) + (s8 & 3)) * 64, 0, 0);
+        const auto rv = rsrc(vbase + (row0 < 0 ? 0L : row0) * kVRow, rows * kVRow);
+        uint32_t vv[ChunkData<KB, GP>::kvw];
+        load_v(rv, vv);
         values(vv, ap);
         return;
       }
@@ -943,8 +1023,9 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   const int n_chunks = (span + kChunk - 1) / kChunk;
   const int n_full = span / kChunk;
 
-  constexpr bool k_packed = KB != 0;
+  constexpr bool k_rot = rotated_k<KB>();
   constexpr int kRowBytes = WaveT::kRowBytes;
+  constexpr int kVRow = WaveT::kVRow;
   WaveT W;
   W.col = lane & 15;
   W.grp = lane >> 4;
@@ -964,11 +1045,11 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   W.kbase = KB ? reinterpret_cast<const char *>(p.k.codes) + rowbase * kRowBytes
                : reinterpret_cast<const char *>(p.k.fp16) + rowbase * kRowBytes;
   W.knbase = KB ? reinterpret_cast<const char *>(p.k.norms + rowbase) : W.kbase;
-  W.vbase = reinterpret_cast<const char *>(p.v.codes) + rowbase * 64;
+  W.vbase = reinterpret_cast<const char *>(p.v.codes) + rowbase * kVRow;
   W.vnbase = reinterpret_cast<const char *>(p.v.norms + rowbase);
   W.koff = static_cast<uint32_t>(W.col * kRowBytes + W.grp * (kRowBytes / 4));
   W.knoff = static_cast<uint32_t>(4 * W.cpos);
-  W.voff = static_cast<uint32_t>(W.grp * 4 * 64 + W.col * 4);
+  W.voff = static_cast<uint32_t>(W.grp * 4 * kVRow + W.col * (kVRow / 16));
   W.capacity = p.capacity;
   W.hot_len = p.v.hot > 0 ? p.v.hot : 1;
   W.ring = (p.v.mode == TQ_SIDE_DELEGATED) ? p.v.fp16 + static_cast<long>(unit) * p.v.hot * D : nullptr;
@@ -997,8 +1078,8 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   float kc = 0.0f, vc = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    if (KB) kc = (lane == i) ? p.k_cent[i] : kc;
-    vc = (lane == i) ? p.v_cent[i] : vc;
+    if (k_rot) kc = (lane == i) ? p.k_cent[i] : kc;
+    if (KB != kInt8) vc = (lane == i) ? p.v_cent[i] : vc;
   }
   // Tables, written four replicas (16 bytes) at a time: the value table
   // (for KB = 4 also the K lo table; for KB = 3 also the K hi and lo
@@ -1006,7 +1087,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   // Every loop below runs whole waves (the counts are multiples of 64), as
   // the shuffles need.
   constexpr int kVWord = v_table_byte<KB>() / 4;
-  for (int i = threadIdx.x; i < 256 * (kRep / 4); i += kThreads) {
+  for (int i = threadIdx.x; KB != kInt8 && i < 256 * (kRep / 4); i += kThreads) {
     const int e = i >> 3, r4 = 4 * (i & 7);
     const uint32_t w = pack_half2(__shfl(vc, e & 15), __shfl(vc, e >> 4));
     *reinterpret_cast<u32x4_t *>(lds + kVWord + e * 64 + r4) = u32x4_t{w, w, w, w};
@@ -1037,7 +1118,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
     out_sign = wsel == 2 ? p.sign[2] : out_sign;
     out_sign = wsel == 3 ? p.sign[3] : out_sign;
   }
-  if (k_packed && wave < G) {
+  if (k_rot && wave < G) {
     // signs of coordinates lane and lane + 64 (uniform words, per-lane select)
     const uint32_t sa = lane < 32 ? p.sign[0] : p.sign[1];
     const uint32_t sb = lane < 32 ? p.sign[2] : p.sign[3];
@@ -1070,7 +1151,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   uint32_t *qhl = reinterpret_cast<uint32_t *>(qw);
   float *qinvs = reinterpret_cast<float *>(lds + L::qinv);
   if (wave < G) {
-    const float qscale = k_packed ? kLog2e / static_cast<float>(D) : kLog2e / sqrtf(static_cast<float>(D));
+    const float qscale = k_rot ? kLog2e / static_cast<float>(D) : kLog2e / sqrtf(static_cast<float>(D));
     float amax = fmaxf(fabsf(qa), fabsf(qb));
     for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
     amax *= qscale;
@@ -1311,6 +1392,18 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
       }
     }
   }
+  float4 o;
+  const float inv = (Lt > 0.0f) ? __builtin_amdgcn_rcpf(Lt) : 0.0f;  // within 1 ulp
+  if (KB == kInt8) {
+    // original domain; the value operands were x 2^-10
+    o.x = r4[0] * 1024.0f * inv;
+    o.y = r4[1] * 1024.0f * inv;
+    o.z = r4[2] * 1024.0f * inv;
+    o.w = r4[3] * 1024.0f * inv;
+    *reinterpret_cast<float4 *>(orow) = o;
+    if (threadIdx.x == 0) __hip_atomic_store(p.counters + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
   // inverse rotation diag(s) H / sqrt(d): butterflies at strides 1 and 2
   // inside the thread, strides 4 .. 64 across the head's 32 lanes
   {
@@ -1329,8 +1422,6 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
     r4[e] = xor_butterfly<16>(r4[e], lane);
   }
   const float rs = 1.0f / sqrtf(static_cast<float>(D));
-  const float inv = (Lt > 0.0f) ? __builtin_amdgcn_rcpf(Lt) : 0.0f;  // within 1 ulp
-  float4 o;
   const uint32_t sbits = out_sign >> (jj & 31);
   o.x = ((sbits & 1u) ? -r4[0] : r4[0]) * rs;
   o.y = ((sbits & 2u) ? -r4[1] : r4[1]) * rs;
@@ -1386,7 +1477,8 @@ void launch_kb(const DecodeParams &p, dim3 grid, hipStream_t stream) {
 
 hipError_t launch_decode_mfma(const DecodeParams &p, hipStream_t stream) {
   const int G = p.q_heads / p.kv_heads;
-  const int kb = p.k.mode == TQ_SIDE_PACKED ? p.k.bits : 0;
+  const int kb = p.k.mode == TQ_SIDE_PACKED ? p.k.bits : (p.k.mode == TQ_SIDE_INT8 ? kInt8 : 0);
+  if ((kb == kInt8) != (p.v.mode == TQ_SIDE_INT8)) return hipErrorInvalidValue;
   if (G < 1 || G > 8 || p.head_dim != D) return hipErrorInvalidValue;
   const int nsplit = p.n_cold_splits;
   if (nsplit < 1 || nsplit > kMaxSplits || p.n_hot_splits != 0) return hipErrorInvalidValue;
@@ -1395,6 +1487,7 @@ hipError_t launch_decode_mfma(const DecodeParams &p, hipStream_t stream) {
     case 0: launch_kb<0>(p, grid, stream); break;
     case 3: launch_kb<3>(p, grid, stream); break;
     case 4: launch_kb<4>(p, grid, stream); break;
+    case kInt8: launch_kb<kInt8>(p, grid, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -8,7 +8,8 @@ oracle's float64 attention over the rows it rebuilds from what the GPU wrote:
   chunk, for K and V independently and with one factor per position, so a
   head's weight can fall on rows whose value norm is far below the largest
   one seen;
-* large logits (a peaked softmax).
+* large logits (a peaked softmax);
+* the same rows in INT8 caches (both sides).
 
 The tolerance is the parity tests' own: per row, ||x - ref||_inf <= 2e-3
 ||ref||_inf, for the scaled logits and for the outputs.
@@ -51,6 +52,9 @@ def _rows(cache, side, length):
     d = cache.head_dim
     if spec.mode == "fp16":
         return cache.tensors[side + "_fp16"][:, :, :length].cpu().numpy().astype(np.float64)
+    if spec.mode == "int8":
+        codes = cache.tensors[side + "_codes"][:, :, :length].cpu().numpy().view(np.int8)  # byte j = coordinate j
+        return oracle.int8_dequantize(codes, cache.tensors[side + "_norms"][:, :, :length].cpu().numpy())
     R = oracle.rotation_matrix(cache.seed, d)
     c, _ = oracle.lloyd_max(d, spec.bits)
     n_cold = length if spec.mode == "packed" else max(0, length - spec.hot)
@@ -108,11 +112,14 @@ def _case(name):
         ks = ("fp16", 0)
     if name.endswith("_delegated"):
         ks, vs = ("fp16", 0), ("delegated", 4)
+    if name.endswith("_int8"):
+        ks, vs = ("int8", 0), ("int8", 0)
     return k.astype(np.float16), v.astype(np.float16), q.astype(np.float16), ks, vs
 
 
 CASES = ["zero_rows", "zero_rows_asym", "fp16_max", "fp16_max_asym", "norm_decades", "norm_decades_asym",
-         "norm_decades_delegated", "norm_decades_shared", "large_logits", "large_logits_asym"]
+         "norm_decades_delegated", "norm_decades_shared", "large_logits", "large_logits_asym",
+         "zero_rows_int8", "fp16_max_int8", "norm_decades_int8", "large_logits_int8"]
 
 
 @pytest.mark.parametrize("name", CASES)

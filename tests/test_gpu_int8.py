@@ -1,8 +1,11 @@
 """GPU parity of the INT8 per-token absmax cache (mlxcel "TurboQuant KV
 cache", "Available modes": int8) against the oracle: codes bit-exact against
 the exact definition round(127 x / max|x|) and scales equal, dequantized rows, decode over
-the GPU-written rows (the plain split kernel), paged storage, and the
-policy's int8 mode."""
+the GPU-written rows (both decode kernels: the matrix-core one takes INT8 on
+both sides at head_dim 128, the plain split kernel every mix), paged
+storage, and the policy's int8 mode."""
+import os
+
 import numpy as np
 import pytest
 
@@ -23,6 +26,17 @@ S = tq.SideSpec
 def _gpu():
     assert torch.cuda.is_available(), "GPU tests need a ROCm device"
     tq.lib()
+
+
+@pytest.fixture(params=["auto", "ref"])
+def variant(request):
+    old = os.environ.get("TQ_DECODE_VARIANT")
+    os.environ["TQ_DECODE_VARIANT"] = request.param
+    yield request.param
+    if old is None:
+        os.environ.pop("TQ_DECODE_VARIANT", None)
+    else:
+        os.environ["TQ_DECODE_VARIANT"] = old
 
 
 def _int8_rows(cache, side, lo, hi, logical=False):
@@ -111,7 +125,7 @@ def test_int8_zero_rows_and_dequantize():
                                          (S("int8"), S("packed", 4)), (S("packed", 3), S("int8"))],
                          ids=["int8-int8", "fp16-int8", "int8-packed4", "packed3-int8"])
 @pytest.mark.parametrize("length", [1, 65, 777])
-def test_int8_decode(kspec, vspec, length):
+def test_int8_decode(kspec, vspec, length, variant):
     B, H, Hq, d, cap = 2, 2, 8, 128, 800
     k, v = synth.kv_numpy(70, B, H, length, d, dist="channel", outlier_frac=0.01)
     cache = tq.TQCache(B, H, d, cap, kspec, vspec)
@@ -128,7 +142,7 @@ def test_int8_decode(kspec, vspec, length):
 
 @pytest.mark.parametrize("H,Hq,d", [(4, 4, 128), (1, 8, 128), (2, 16, 64), (1, 3, 256)],
                          ids=["g1_d128", "g8_d128", "g8_d64", "g3_d256"])
-def test_int8_decode_group_sizes(H, Hq, d):
+def test_int8_decode_group_sizes(H, Hq, d, variant):
     # query groups of one, three and eight heads per KV head: eight heads on
     # 64-position tiles take two softmax passes; d = 256 rows fall back to
     # 32-position tiles
@@ -146,7 +160,7 @@ def test_int8_decode_group_sizes(H, Hq, d):
     assert ok, f"out: worst {worst}"
 
 
-def test_int8_paged_matches_contiguous():
+def test_int8_paged_matches_contiguous(variant):
     B, H, Hq, d, cap, bs = 2, 2, 8, 128, 512, 64
     k, v = synth.kv_numpy(80, B, H, 450, d)
     perm = torch.from_numpy(np.random.default_rng(1).permutation(B * cap // bs).astype(np.int32).reshape(B, -1))

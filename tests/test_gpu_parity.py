@@ -55,6 +55,9 @@ def _oracle_rows(cache, side, length):
     d = cache.head_dim
     if spec.mode == "fp16":
         return cache.tensors[side + "_fp16"][:, :, :length].cpu().numpy().astype(np.float64)
+    if spec.mode == "int8":
+        codes = cache.tensors[side + "_codes"][:, :, :length].cpu().numpy().view(np.int8)  # byte j = coordinate j
+        return oracle.int8_dequantize(codes, cache.tensors[side + "_norms"][:, :, :length].cpu().numpy())
     R = oracle.rotation_matrix(cache.seed, d)
     c, _ = oracle.lloyd_max(d, spec.bits)
 
@@ -234,6 +237,12 @@ DECODE_CASES = [
     ("tq35_d128_iid", 2, 2, 8, 128, 2100, ("packed", 3), ("packed", 4), "iid"),
     ("asym_d128_iid", 2, 2, 8, 128, 1337, ("fp16", 0), ("packed", 4), "iid"),
     ("sym4_d128_iid", 1, 8, 32, 128, 1500, ("packed", 4), ("packed", 4), "iid"),
+    # INT8 on both sides (the matrix-core kernel's original-domain mode):
+    # groups of one, four and eight heads, both readings
+    ("int8_d128", 2, 2, 8, 128, 1900, ("int8", 0), ("int8", 0), "channel"),
+    ("int8_d128_iid", 1, 8, 32, 128, 1500, ("int8", 0), ("int8", 0), "iid"),
+    ("int8_mha", 2, 4, 4, 128, 300, ("int8", 0), ("int8", 0), "channel"),
+    ("int8_g8", 1, 1, 8, 128, 613, ("int8", 0), ("int8", 0), "iid"),
 ]
 
 
@@ -279,7 +288,10 @@ def test_decode_attention(case, variant):
     assert ok, f"out: worst {worst}"
 
 
-@pytest.mark.parametrize("case", DECODE_CASES[1:5], ids=[c[0] for c in DECODE_CASES[1:5]])
+SPLIT_CASES = DECODE_CASES[1:5] + [c for c in DECODE_CASES if c[0] == "int8_d128"]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])
 def test_decode_split_counts_agree(case, variant):
     cache, k, v, q = _build(case)
     T = k.shape[2]
@@ -289,7 +301,7 @@ def test_decode_split_counts_agree(case, variant):
         assert ok, worst
 
 
-@pytest.mark.parametrize("case", DECODE_CASES[1:5], ids=[c[0] for c in DECODE_CASES[1:5]])
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])
 def test_decode_variants_agree(case):
     cache, k, v, q = _build(case)
     T = k.shape[2]
