@@ -242,6 +242,12 @@ def source_digest(path=DECODE_SOURCE) -> str:
     return hashlib.sha256(text.encode()).hexdigest()
 
 
+def traffic_key(workload: str, sparse_v: float = 0.0) -> str:
+    """Name under which a decode's byte counters are recorded: the workload,
+    and the sparse-V threshold when one is set (a skip changes the bytes)."""
+    return f"{workload}_sparse_v{sparse_v:g}" if sparse_v else workload
+
+
 def traffic_file(workload: str, kernel: str = "decode_mfma") -> str:
     return os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_traffic.txt")
 
@@ -272,23 +278,33 @@ def recorded_traffic(workload: str):
     return None
 
 
-def counter_summary(fetch_csv: str, write_csv: str, workload: str, copy_mib: int, cmds: list):
+def counter_summary(fetch_csv: str, write_csv: str, workload: str, copy_mib: int, cmds: list,
+                    append_last: int = 0):
     """Summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per
     dispatch) of `bench.py --copy-mib N`: the plain copy kernel of known size
-    calibrates each counter, the decode kernel's per-launch HBM bytes follow."""
+    calibrates each counter, the decode kernel's per-launch HBM bytes follow.
+    With append_last > 0, the quantize-append kernel's bytes too, over its
+    last append_last dispatches (the step's appends, not the cache fill)."""
     import csv
     import collections
 
-    def read(path, counter):
+    def read(path, counter, last_of=None, last=0):
         acc = collections.defaultdict(list)
         with open(path) as f:
             for r in csv.DictReader(f):
                 if r["Counter_Name"] == counter:
-                    acc[r["Kernel_Name"]].append(float(r["Counter_Value"]))
-        return {k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
+                    acc[r["Kernel_Name"]].append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+        lastid = {}
+        for k in acc:
+            acc[k].sort()
+            lastid[k] = acc[k][-1][0]
+            if last_of and last_of in k and last:
+                acc[k] = acc[k][-last:]
+        return ({k: sum(x[1] for x in v) / len(v) for k, v in acc.items()},
+                {k: len(v) for k, v in acc.items()}, lastid)
 
-    fetch, nf = read(fetch_csv, "FETCH_SIZE")
-    write, nw = read(write_csv, "WRITE_SIZE")
+    fetch, nf, last_f = read(fetch_csv, "FETCH_SIZE", "quantize", append_last)
+    write, nw, _ = read(write_csv, "WRITE_SIZE", "quantize", append_last)
     copy_name = next(k for k in fetch if "neg_kernel" in k)
     dec_name = next(k for k in fetch if "decode_mfma_kernel" in k or "decode_split_kernel" in k)
     src = DECODE_SOURCES["decode_mfma" if "decode_mfma_kernel" in dec_name else "decode_split"]
@@ -316,6 +332,25 @@ def counter_summary(fetch_csv: str, write_csv: str, workload: str, copy_mib: int
             f"traffic_bytes_per_launch: {traffic:.0f}",
             f"algorithmic_bytes_per_launch: {decode_bytes(w)}",
             f"traffic_over_algorithmic: {traffic / decode_bytes(w):.4f}"]
+    n_new = w.get("prefill", 0) or w.get("append", 0)
+    # the encoder of the step's appends: the quantize kernel dispatched last
+    # (the cache fill may use the other encoder)
+    q_names = [k for k in fetch if "quantize" in k and k in write]
+    q_name = max(q_names, key=lambda k: last_f[k]) if q_names else None
+    if append_last and n_new and q_name:
+        qshort = q_name.replace("void ", "").replace("tq::(anonymous namespace)::", "").split("(tq::")[0]
+        q_traffic = (fetch[q_name] * f_fetch + write[q_name] * f_write) * 1024.0
+        ab = append_bytes(w, n_new)
+        out += ["#",
+                f"# {qshort}: its last {nf[q_name]} dispatches (the appends of {n_new} positions per "
+                f"sequence); FETCH_SIZE {fetch[q_name]:.1f} KiB, WRITE_SIZE {write[q_name]:.1f} KiB per "
+                "dispatch (raw)",
+                f"append_kernel: {qshort}",
+                f"append_fetch_bytes_per_launch: {fetch[q_name] * f_fetch * 1024.0:.0f}",
+                f"append_write_bytes_per_launch: {write[q_name] * f_write * 1024.0:.0f}",
+                f"append_traffic_bytes_per_launch: {q_traffic:.0f}",
+                f"append_algorithmic_bytes_per_launch: {ab}",
+                f"append_traffic_over_algorithmic: {q_traffic / ab:.4f}"]
     return "\n".join(out) + "\n"
 
 
@@ -520,8 +555,10 @@ def main():
         sys.stdout.write(stats_summary(args.stats_summary, args.workload, args.command))
         return
     if args.counter_summary:
+        w = WORKLOADS[args.workload]
         sys.stdout.write(counter_summary(args.counter_summary[0], args.counter_summary[1], args.workload,
-                                         args.copy_mib or 256, args.command))
+                                         args.copy_mib or 256, args.command,
+                                         (args.warmup + args.steps) * (args.layers or w["layers"])))
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}), flush=True)
@@ -670,7 +707,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                      # counters were taken on contiguous caches
-                     "traffic": None if bsz else recorded_traffic(args.workload)},
+                     "traffic": None if bsz else recorded_traffic(traffic_key(args.workload, args.sparse_v))},
         # context for the roofline: what a plain streaming-read kernel attains
         "attainable_read": {"gbs": round(attain, 1), "bytes": 4 << 30,
                             "kernel": "tq_read_probe: 16-byte loads, 256 blocks of 768 threads",
