@@ -15,7 +15,8 @@
 //       popcount(i & j) = popcount(n & (4 q + g)) + popcount(t & s): each
 //       entry is a per-lane sign times a fixed 8 x 8 Hadamard pattern.  B is
 //       built once per block into LDS (16 KB) and read per tile, which keeps
-//       the wave at about 120 registers: four waves per SIMD.
+//       the wave at 80 registers: six waves per SIMD on contiguous caches
+//       (paged ones keep a prefetch buffer: four).
 //   D   lane (g = l / 16, n = l % 16) holds rows 4 g + r (r = 0..3),
 //       coordinates 8 n .. 8 n + 7, as 8 N-tiles of 4 values.
 //
@@ -146,8 +147,12 @@ __device__ __forceinline__ void encode_tile(const float4_t (&acc)[8], const floa
   }
 }
 
-__global__ __launch_bounds__(kThreads, 4) void quantize_mfma_kernel(const QuantizeParams p, int tiles_k,
-                                                                    int tiles_total) {
+// PG: paged storage.  Contiguous caches run six waves a SIMD (80 registers)
+// with no prefetch buffer, the waves hiding each other's load latency; paged
+// ones keep the next tile's operands and storage rows in flight (four waves).
+template <bool PG>
+__global__ __launch_bounds__(kThreads, PG ? 4 : 6) void quantize_mfma_kernel(const QuantizeParams p, int tiles_k,
+                                                                             int tiles_total) {
   __shared__ LutEntry lut[2][kLutCells];
   __shared__ u32x4_t bsh[16][64];  // B operands [4 t + q][lane] for the N-tiles t < 4
   const int lane = threadIdx.x & 63;
@@ -237,108 +242,118 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_mfma_kernel(const Quanti
       }
     }
   };
-  const bool paged = p.pg.table != nullptr;
-  half8_t a[4], an[4];
-  long prow[4] = {0, 0, 0, 0}, prow_n[4] = {0, 0, 0, 0};
+  // encode tile `tile` from its A operands (and, paged, its storage rows)
+  auto encode = [&](int tile, const half8_t (&a)[4], const long (&prow)[4]) {
+      const int side = tile < tiles_k ? 0 : 1;
+      const SideDev &sd = side ? p.v : p.k;
+      const float scale = side ? p.v_lut_scale : p.k_lut_scale;
+      const long r0 = static_cast<long>(side ? tile - tiles_k : tile) * kTileRows;
+      const long left = rows - r0;
+
+      // squared norm of row n: fp16 products are exact, sums in fp32
+      float ss = 0.0f;
+  #pragma unroll
+      for (int q = 0; q < 4; ++q) {
+  #pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const half2_t h = {a[q][e], a[q][e + 1]};
+          ss = __builtin_amdgcn_fdot2(h, h, ss, false);
+        }
+      }
+      ss = sum_rows(ss);
+
+      float4_t acc[8];
+  #pragma unroll
+      for (int t = 0; t < 8; ++t) acc[t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      asm volatile("" ::: "memory");  // B is read from LDS per tile, not kept in registers
+  #pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        u32x4_t af = __builtin_bit_cast(u32x4_t, a[q]);
+        af[2] ^= 0x80008000u;
+        af[3] ^= 0x80008000u;
+        const half8_t a_flip = as_half8(af);
+  #pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const u32x4_t b = bsh[4 * t + q][lane];
+          acc[t] = mma(a[q], as_half8(b), acc[t]);
+          acc[t + 4] = mma(a_flip, as_half8(b), acc[t + 4]);
+        }
+      }
+
+      // rows 4 g + r of this lane: norm and 1 / (n sqrt(d)) times the table
+      // scale (a power of two, so the scaling is exact)
+      float nrm[4], inv_s[4];
+  #pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float s2 = __shfl(ss, 4 * g + r);
+        nrm[r] = __builtin_amdgcn_sqrtf(s2);  // v_sqrt_f32: within 1 ulp
+        inv_s[r] = nrm[r] > 0.0f ? scale * (rsd * __builtin_amdgcn_rcpf(nrm[r])) : 0.0f;
+      }
+
+      uint32_t word[4];
+      const LutEntry *lut0 = lut[side] + static_cast<int>(scale) + 1;
+      switch (sd.bits) {
+        case 1: encode_tile<1>(acc, inv_s, lut0, lane, word); break;
+        case 2: encode_tile<2>(acc, inv_s, lut0, lane, word); break;
+        case 3: encode_tile<3>(acc, inv_s, lut0, lane, word); break;
+        default: encode_tile<4>(acc, inv_s, lut0, lane, word); break;
+      }
+
+      // output rows: tile row tr = 4 g + r is input row r0 + tr = (bh, i).
+      // n_new >= 16, so the tile crosses at most one (batch, head) boundary;
+      // crossing it skips the capacity - n_new rows the append leaves alone.
+      // (32-bit division when the rows allow: a 64-bit one costs about a
+      // hundred scalar instructions per tile)
+      const long bh0 = rows <= 0x7fffffffL ? static_cast<long>(static_cast<uint32_t>(r0) / static_cast<uint32_t>(p.n_new))
+                                           : r0 / p.n_new;
+      const int i0 = static_cast<int>(r0 - bh0 * p.n_new);
+      const int W = sd.words;
+      uint32_t *codes0 = sd.codes + (bh0 * p.capacity + p.offset + i0) * W;
+      float *norms0 = sd.norms + bh0 * p.capacity + p.offset + i0;
+      const int skip = p.capacity - p.n_new;
+      if (PG) {
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (4 * g + r >= left || prow[r] < 0) continue;
+          if (n < W) sd.codes[prow[r] * W + n] = word[r];
+          if (n == r) sd.norms[prow[r]] = nrm[r];
+        }
+        return;
+      }
+  #pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tr = 4 * g + r;
+        if (tr >= left) continue;
+        const int rel = tr + (i0 + tr >= p.n_new ? skip : 0);
+        if (n < W) codes0[rel * W + n] = word[r];
+        if (n == r) norms0[rel] = nrm[r];
+      }
+  };
   int tile = blockIdx.x * kWaves + wave;
-  if (tile < tiles_total) {
-    load_tile(tile, an);
-    if (paged) paged_rows(tile, prow_n);
-  }
-  for (; tile < tiles_total; tile += stride) {
+  if (PG) {
+    half8_t a[4], an[4];
+    long prow[4], prow_n[4];
+    if (tile < tiles_total) {
+      load_tile(tile, an);
+      paged_rows(tile, prow_n);
+    }
+    for (; tile < tiles_total; tile += stride) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) a[q] = an[q];
-    if (paged) {
+      for (int q = 0; q < 4; ++q) a[q] = an[q];
 #pragma unroll
       for (int r = 0; r < 4; ++r) prow[r] = prow_n[r];
-    }
-    if (tile + stride < tiles_total) {
-      load_tile(tile + stride, an);
-      if (paged) paged_rows(tile + stride, prow_n);
-    }
-    const int side = tile < tiles_k ? 0 : 1;
-    const SideDev &sd = side ? p.v : p.k;
-    const float scale = side ? p.v_lut_scale : p.k_lut_scale;
-    const long r0 = static_cast<long>(side ? tile - tiles_k : tile) * kTileRows;
-    const long left = rows - r0;
-
-    // squared norm of row n: fp16 products are exact, sums in fp32
-    float ss = 0.0f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const half2_t h = {a[q][e], a[q][e + 1]};
-        ss = __builtin_amdgcn_fdot2(h, h, ss, false);
+      if (tile + stride < tiles_total) {
+        load_tile(tile + stride, an);
+        paged_rows(tile + stride, prow_n);
       }
+      encode(tile, a, prow);
     }
-    ss = sum_rows(ss);
-
-    float4_t acc[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) acc[t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    asm volatile("" ::: "memory");  // B is read from LDS per tile, not kept in registers
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      u32x4_t af = __builtin_bit_cast(u32x4_t, a[q]);
-      af[2] ^= 0x80008000u;
-      af[3] ^= 0x80008000u;
-      const half8_t a_flip = as_half8(af);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const u32x4_t b = bsh[4 * t + q][lane];
-        acc[t] = mma(a[q], as_half8(b), acc[t]);
-        acc[t + 4] = mma(a_flip, as_half8(b), acc[t + 4]);
-      }
-    }
-
-    // rows 4 g + r of this lane: norm and 1 / (n sqrt(d)) times the table
-    // scale (a power of two, so the scaling is exact)
-    float nrm[4], inv_s[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float s2 = __shfl(ss, 4 * g + r);
-      nrm[r] = __builtin_amdgcn_sqrtf(s2);  // v_sqrt_f32: within 1 ulp
-      inv_s[r] = nrm[r] > 0.0f ? scale * (rsd * __builtin_amdgcn_rcpf(nrm[r])) : 0.0f;
-    }
-
-    uint32_t word[4];
-    const LutEntry *lut0 = lut[side] + static_cast<int>(scale) + 1;
-    switch (sd.bits) {
-      case 1: encode_tile<1>(acc, inv_s, lut0, lane, word); break;
-      case 2: encode_tile<2>(acc, inv_s, lut0, lane, word); break;
-      case 3: encode_tile<3>(acc, inv_s, lut0, lane, word); break;
-      default: encode_tile<4>(acc, inv_s, lut0, lane, word); break;
-    }
-
-    // output rows: tile row tr = 4 g + r is input row r0 + tr = (bh, i).
-    // n_new >= 16, so the tile crosses at most one (batch, head) boundary;
-    // crossing it skips the capacity - n_new rows the append leaves alone.
-    // (32-bit division when the rows allow: a 64-bit one costs about a
-    // hundred scalar instructions per tile)
-    const long bh0 = rows <= 0x7fffffffL ? static_cast<long>(static_cast<uint32_t>(r0) / static_cast<uint32_t>(p.n_new))
-                                         : r0 / p.n_new;
-    const int i0 = static_cast<int>(r0 - bh0 * p.n_new);
-    const int W = sd.words;
-    uint32_t *codes0 = sd.codes + (bh0 * p.capacity + p.offset + i0) * W;
-    float *norms0 = sd.norms + bh0 * p.capacity + p.offset + i0;
-    const int skip = p.capacity - p.n_new;
-    if (paged) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (4 * g + r >= left || prow[r] < 0) continue;
-        if (n < W) sd.codes[prow[r] * W + n] = word[r];
-        if (n == r) sd.norms[prow[r]] = nrm[r];
-      }
-      continue;
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int tr = 4 * g + r;
-      if (tr >= left) continue;
-      const int rel = tr + (i0 + tr >= p.n_new ? skip : 0);
-      if (n < W) codes0[rel * W + n] = word[r];
-      if (n == r) norms0[rel] = nrm[r];
+  } else {
+    const long none[4] = {0, 0, 0, 0};
+    for (; tile < tiles_total; tile += stride) {
+      half8_t a[4];
+      load_tile(tile, a);
+      encode(tile, a, none);
     }
   }
 }
@@ -376,9 +391,16 @@ hipError_t launch_quantize_mfma(const QuantizeParams &p, hipStream_t stream) {
   const long tiles_total = tiles_k + (v_on ? tiles_side : 0);
   if (tiles_total == 0) return hipSuccess;
   if (tiles_total > 0x7fffffffL) return hipErrorInvalidValue;
-  const long blocks = std::min<long>((tiles_total + kWaves - 1) / kWaves, 1024);  // up to four per CU
-  hipLaunchKernelGGL(quantize_mfma_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, p,
-                     static_cast<int>(tiles_k), static_cast<int>(tiles_total));
+  // up to one round at the kernel's occupancy: six (paged: four) blocks per CU
+  const long cap = p.pg.table ? 1024 : 1536;
+  const long blocks = std::min<long>((tiles_total + kWaves - 1) / kWaves, cap);
+  if (p.pg.table) {
+    hipLaunchKernelGGL(quantize_mfma_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, p,
+                       static_cast<int>(tiles_k), static_cast<int>(tiles_total));
+  } else {
+    hipLaunchKernelGGL(quantize_mfma_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
+                       p, static_cast<int>(tiles_k), static_cast<int>(tiles_total));
+  }
   return hipGetLastError();
 }
 

@@ -147,9 +147,13 @@ hipError_t launch_quantize_append(const QuantizeParams &p, hipStream_t stream);
 // p.side_mask.
 hipError_t launch_quantize_mfma(const QuantizeParams &p, hipStream_t stream);
 // Power-of-two code-table scale for the matrix-core encoder (0 when the
-// thresholds are too close for a table of at most kQuantLutMax cells).
+// thresholds are too close for a scale of at most kQuantLutMaxScale; such a
+// side goes to the plain encoder).  The Lloyd-Max codebooks at head_dim 128
+// need 1, 16, 32 and 64 for 1..4 bits (smallest threshold gaps 2, 0.087,
+// 0.044, 0.023), so the table holds at most 131 cells a side and leaves the
+// LDS to the kernel's occupancy.
 float quantize_lut_scale(const float *thr, int bits);
-constexpr int kQuantLutMaxScale = 512;
+constexpr int kQuantLutMaxScale = 64;
 hipError_t launch_dequantize(const DequantParams &p, hipStream_t stream);
 hipError_t launch_read_probe(const void *buf, size_t bytes, unsigned *sink, hipStream_t stream);
 // Zero `bytes` (a multiple of 16) of device memory at a 16-byte aligned `buf`.
