@@ -481,6 +481,8 @@ def trace_summary(trace_csv: str, workload: str, last: int, cmds: list, n_new: i
         if n_new and "quantize" in short:
             out.append(f"#   -> {w['batch'] * n_new / (avg * 1e-6) / 1e6:.1f} Mtok/s, "
                        f"{append_bytes(w, n_new) / (avg * 1e-6) / 1e9:.1f} GB/s over the algorithmic bytes")
+        elif "quantize" in short:
+            out.append("#   (the cache fill before the timed steps: this workload's step appends nothing)")
     return "\n".join(out) + "\n"
 
 
