@@ -252,9 +252,9 @@ __global__ __launch_bounds__(kThreads, PG ? 4 : 6) void quantize_mfma_kernel(con
 
       // squared norm of row n: fp16 products are exact, sums in fp32
       float ss = 0.0f;
-  #pragma unroll
+#pragma unroll
       for (int q = 0; q < 4; ++q) {
-  #pragma unroll
+#pragma unroll
         for (int e = 0; e < 8; e += 2) {
           const half2_t h = {a[q][e], a[q][e + 1]};
           ss = __builtin_amdgcn_fdot2(h, h, ss, false);
@@ -263,16 +263,16 @@ __global__ __launch_bounds__(kThreads, PG ? 4 : 6) void quantize_mfma_kernel(con
       ss = sum_rows(ss);
 
       float4_t acc[8];
-  #pragma unroll
+#pragma unroll
       for (int t = 0; t < 8; ++t) acc[t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
       asm volatile("" ::: "memory");  // B is read from LDS per tile, not kept in registers
-  #pragma unroll
+#pragma unroll
       for (int q = 0; q < 4; ++q) {
         u32x4_t af = __builtin_bit_cast(u32x4_t, a[q]);
         af[2] ^= 0x80008000u;
         af[3] ^= 0x80008000u;
         const half8_t a_flip = as_half8(af);
-  #pragma unroll
+#pragma unroll
         for (int t = 0; t < 4; ++t) {
           const u32x4_t b = bsh[4 * t + q][lane];
           acc[t] = mma(a[q], as_half8(b), acc[t]);
@@ -283,7 +283,7 @@ __global__ __launch_bounds__(kThreads, PG ? 4 : 6) void quantize_mfma_kernel(con
       // rows 4 g + r of this lane: norm and 1 / (n sqrt(d)) times the table
       // scale (a power of two, so the scaling is exact)
       float nrm[4], inv_s[4];
-  #pragma unroll
+#pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float s2 = __shfl(ss, 4 * g + r);
         nrm[r] = __builtin_amdgcn_sqrtf(s2);  // v_sqrt_f32: within 1 ulp
@@ -312,7 +312,7 @@ __global__ __launch_bounds__(kThreads, PG ? 4 : 6) void quantize_mfma_kernel(con
       float *norms0 = sd.norms + bh0 * p.capacity + p.offset + i0;
       const int skip = p.capacity - p.n_new;
       if (PG) {
-  #pragma unroll
+#pragma unroll
         for (int r = 0; r < 4; ++r) {
           if (4 * g + r >= left || prow[r] < 0) continue;
           if (n < W) sd.codes[prow[r] * W + n] = word[r];
@@ -320,7 +320,7 @@ __global__ __launch_bounds__(kThreads, PG ? 4 : 6) void quantize_mfma_kernel(con
         }
         return;
       }
-  #pragma unroll
+#pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tr = 4 * g + r;
         if (tr >= left) continue;
