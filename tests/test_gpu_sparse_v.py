@@ -160,3 +160,42 @@ def test_sparse_v_periodic_peaks(case, period, dvariant):
     ref, _ = oracle.decode_attention(q, kr, vr)
     ok, worst = rows_close(sparse, ref, rel=2e-3 + float(np.max(bound / scale)))
     assert ok, f"worst {worst}"
+
+
+@pytest.mark.parametrize("case", CASES[:2] + CASES[3:], ids=[c[0] for c in CASES[:2] + CASES[3:]])
+def test_sparse_v_paged_within_bound(case, dvariant):
+    # the skips and the reload of a predicted-skippable chunk's values go
+    # through the block table (blocks in a shuffled order): the paged sparse
+    # decode stays within the oracle bound of the exact attention, and skips
+    name, ks, vs = case
+    B, H, Hq, d, T, bs = 2, 2, 8, 128, 3000, 64
+    cap = 3008
+    k, v, q = _periodic(B, H, Hq, d, T, 160, 13)
+    nb = B * cap // bs
+    table = torch.from_numpy(np.random.default_rng(5).permutation(nb).astype(np.int32).reshape(B, cap // bs))
+    paged = tq.TQCache(B, H, d, cap, ks, vs, block_table=table, block_size=bs, num_blocks=nb)
+    paged.quantize_append(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), 0)
+    qd = torch.from_numpy(q).cuda()
+    tau = 1e-3
+    exact = paged.decode_attention(qd, T)
+    sparse = paged.decode_attention(qd, T, sparse_v=tau)
+    torch.cuda.synchronize()
+    exact, sparse = exact.cpu().numpy().astype(np.float64), sparse.cpu().numpy().astype(np.float64)
+    logical = {}
+    for side in ("k", "v"):
+        spec = ks if side == "k" else vs
+        if spec.mode == "fp16":
+            logical[side] = paged.logical(side + "_fp16")[:, :, :T].cpu().numpy().astype(np.float64)
+        elif spec.mode == "int8":
+            codes = paged.logical(side + "_codes")[:, :, :T].cpu().numpy().view(np.int8)
+            logical[side] = oracle.int8_dequantize(codes, paged.logical(side + "_norms")[:, :, :T].cpu().numpy())
+        else:
+            R = oracle.rotation_matrix(paged.seed, d)
+            c, _ = oracle.lloyd_max(d, spec.bits)
+            words = paged.logical(side + "_codes")[:, :, :T].cpu().numpy()
+            norms = paged.logical(side + "_norms")[:, :, :T].cpu().numpy().astype(np.float64)
+            logical[side] = oracle.dequantize(words_to_codes(words, spec.bits, d), norms, R, c)
+    bound = oracle.sparse_v_bound(q, logical["k"], logical["v"], tau)
+    scale = np.max(np.abs(exact), axis=-1, keepdims=True)
+    assert np.all(np.abs(sparse - exact) <= bound * (1 + 1e-3) + 1e-5 * scale)
+    assert not np.array_equal(sparse, exact)
