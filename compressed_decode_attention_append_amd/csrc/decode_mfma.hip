@@ -113,7 +113,7 @@ struct Lay {
   static constexpr int red = qwork + GP * qstride;     // flag
   static constexpr int prog = red + 4;                 // [kMaxWaves] chunks done per wave
   static constexpr int qinv = red + 16;                // [8] per head: the score's query scale
-  static constexpr int bmax = red + 24;                // sparse-V: [8 heads][16 waves] published maxima
+  static constexpr int bmax = red + 24;                // sparse-V: [8 heads][16 waves] exchanged maxima
   static constexpr int tail = red + 152;
   // Merge slots of the main loop's waves: an area of their own when it fits
   // (a wave then writes its slot as soon as its own loop ends), else over
@@ -328,7 +328,7 @@ struct Wave {
   uint32_t rep4v;       // 4 r + the V table's byte offset
   uint32_t koff, knoff, voff;   // lane byte offsets inside a chunk
   const uint32_t *lds;
-  uint32_t bmax_at;     // sparse-V: LDS byte address of the published maxima [8 heads][16 waves]
+  uint32_t bmax_at;     // sparse-V: LDS byte address of the exchanged maxima [8 heads][16 waves]
   int wave_id;
   half8_t bq[4];         // R q: column h < GP hi, column GP + h lo of head h
   // per-unit bases
@@ -341,8 +341,8 @@ struct Wave {
   Paging pg;           // PG: where the unit's rows live
   int unit;
   float sparse_lg;     // sparse-V threshold (log2), -inf = exact
-  float block_ref;     // sparse-V: the largest running maximum the block's waves
-                       // have published for the lane's head (-inf: none)
+  float block_ref;     // sparse-V: the largest running maximum of the lane's head
+                       // the block's waves had after their first chunk (-inf: none)
   bool pred_skip;      // sparse-V: the wave's last chunk was skippable, so the
                        // next chunk's V codes are not loaded up front
   float qinv;          // the lane's head (compact layout): the power of two
@@ -780,22 +780,11 @@ struct Wave {
     } else {
       // sparse-V: every weight of the chunk, for every real head, below the
       // threshold times the larger of the wave's running maximum and the
-      // block's published one (neither exceeds the final maximum): the
-      // chunk's values are skipped; its weights stay in the sum.  The block
-      // maximum is what the block's waves have published in LDS, and this
-      // wave publishes its own.
-      typedef __attribute__((address_space(3))) const volatile u32x4_t lds_v4;
-      typedef __attribute__((address_space(3))) volatile float lds_f;
-      float r = m_run;
-#pragma unroll
-      for (int i = 0; i < kMaxWaves / 4; ++i) {
-        // head h's maxima are floats 16 h .. 16 h + 15 (one per wave)
-        const u32x4_t m = *reinterpret_cast<lds_v4 *>(bmax_at + 64u * (col % GP) + 16u * i);
-        r = fmaxf(r, fmaxf(fmaxf(__uint_as_float(m[0]), __uint_as_float(m[1])),
-                           fmaxf(__uint_as_float(m[2]), __uint_as_float(m[3]))));
-      }
+      // block maximum after the first round of chunks (neither exceeds the
+      // final maximum, and both are the same on every call): the chunk's
+      // values are skipped; its weights stay in the sum
+      const float r = fmaxf(m_run, block_ref);
       const bool skip = !__ballot(col % GP < G && chunk_max - r >= sparse_lg);
-      if (col < GP && grp == 0) *reinterpret_cast<lds_f *>(bmax_at + 4u * (16u * col + wave_id)) = m_run;
       pred_skip = skip;
       if (skip) return;
       if (c.vskip) {
@@ -810,6 +799,25 @@ struct Wave {
       }
     }
     values(c.v, ap);
+  }
+
+  // sparse-V: the waves' running maxima after their first chunk, exchanged
+  // at a block barrier (every wave has a first chunk when this is called)
+  __device__ __forceinline__ void exchange_max() {
+    typedef __attribute__((address_space(3))) const volatile u32x4_t lds_v4;
+    typedef __attribute__((address_space(3))) volatile float lds_f;
+    const uint32_t base = bmax_at;
+    if (col < GP && grp == 0) *reinterpret_cast<lds_f *>(base + 4u * (16u * col + wave_id)) = m_run;
+    __syncthreads();
+    float r = block_ref;
+#pragma unroll
+    for (int i = 0; i < kMaxWaves / 4; ++i) {
+      // head h's maxima are floats 16 h .. 16 h + 15 (one per wave)
+      const u32x4_t m = *reinterpret_cast<lds_v4 *>(base + 64u * (col % GP) + 16u * i);
+      r = fmaxf(r, fmaxf(fmaxf(__uint_as_float(m[0]), __uint_as_float(m[1])),
+                         fmaxf(__uint_as_float(m[2]), __uint_as_float(m[3]))));
+    }
+    block_ref = r;
   }
 
   // One chunk of the fp16 hot window (delegated V), positions >= we masked.
@@ -1058,6 +1066,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   W.pred_skip = false;
   W.bmax_at = 4u * L::bmax;
   W.wave_id = wave;
+  W.block_ref = -INFINITY;
   W.reset();
 
   // ---- the query, then the first chunk, in flight while the block builds
@@ -1195,6 +1204,15 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   // into the other of two register buffers (ping-pong, so nothing is
   // copied).  Only the split's last chunk can be partial.
   Balance<kWaves, 4u * L::prog> bal;
+  // sparse-V: after the first round of chunks (chunk c = wave), when every
+  // wave has a full chunk in it, the waves exchange their running maxima at
+  // one block barrier.  A decision from the other waves' maxima at any other
+  // time would depend on how far they had got; this one is the same on
+  // every call.  (More exchanges measured slower: each barrier waits for
+  // the slowest wave.)
+  auto exchange = [&](int cc) {
+    if (cc == wave && kWaves <= n_full) W.exchange_max();
+  };
   if (KB == 0) {
     // fp16 K rows (32 dwords a buffer): the masked variant stays inside the
     // loop, which keeps this shape within its registers
@@ -1214,6 +1232,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
         W.template cold_chunk<true, SP>(s0 + c * kChunk, s1, A, scores, hq0, p.length);
       }
       bal.step(wave, lane);
+      if (SP) exchange(c);
       c = cn;
       if (c >= n_chunks) break;
       cn = c + kWaves;
@@ -1228,6 +1247,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
         W.template cold_chunk<true, SP>(s0 + c * kChunk, s1, B, scores, hq0, p.length);
       }
       bal.step(wave, lane);
+      if (SP) exchange(c);
       c = cn;
     }
   } else {
@@ -1251,6 +1271,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
       asm volatile("" ::: "memory");
       W.template cold_chunk<false, SP>(s0 + c * kChunk, s1, A, scores, hq0, p.length);
       bal.step(wave, lane);
+      if (SP) exchange(c);
       c = cn;
       if (c >= n_full) {
         in_b = true;
@@ -1264,6 +1285,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
       asm volatile("" ::: "memory");
       W.template cold_chunk<false, SP>(s0 + c * kChunk, s1, B, scores, hq0, p.length);
       bal.step(wave, lane);
+      if (SP) exchange(c);
       c = cn;
     }
     if (c < n_chunks) {

@@ -237,10 +237,10 @@ int tq_decode_attention(const tq_cache *cache, const void *q, int q_heads,
  * a running maximum that never exceeds the final one.  So each dropped
  * position i has p_i < sparse_v (p relative to the largest weight), and
  * every output element moves by at most sum over such i of p_i |v_i| / sum p.
- * In the matrix-core kernel that maximum includes what the block's other
- * waves have seen so far, read without waiting for them: which groups are
- * dropped, and so the low bits of the result, may differ from call to call
- * (the bound holds for every call).  The exact decode is bit-reproducible.
+ * In the matrix-core kernel that maximum also includes what the block's
+ * other waves saw in their first chunks (exchanged at one barrier), so
+ * which groups are dropped depends only on the data: results are
+ * bit-reproducible, as are the exact decode's.
  *   sparse_v: in [0, 1); 0 is exactly tq_decode_attention.
  * Errors: as tq_decode_attention; TQ_ERR_ARG if sparse_v is outside [0, 1). */
 int tq_decode_attention_sparse(const tq_cache *cache, const void *q, int q_heads,

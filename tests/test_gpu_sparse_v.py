@@ -199,3 +199,27 @@ def test_sparse_v_paged_within_bound(case, dvariant):
     scale = np.max(np.abs(exact), axis=-1, keepdims=True)
     assert np.all(np.abs(sparse - exact) <= bound * (1 + 1e-3) + 1e-5 * scale)
     assert not np.array_equal(sparse, exact)
+
+
+@pytest.mark.parametrize("case", CASES[:2] + CASES[3:], ids=[c[0] for c in CASES[:2] + CASES[3:]])
+def test_sparse_v_deterministic_and_layout_independent(case, dvariant):
+    # which chunks are skipped depends only on the data and the fixed chunk
+    # order: repeated calls give the same bits, and a paged cache (shuffled
+    # blocks) gives the bits of a contiguous one
+    name, ks, vs = case
+    B, H, Hq, d, T, bs = 2, 2, 8, 128, 3000, 64
+    cap = 3008
+    k, v, q = _periodic(B, H, Hq, d, T, 160, 17)
+    nb = B * cap // bs
+    table = torch.from_numpy(np.random.default_rng(6).permutation(nb).astype(np.int32).reshape(B, cap // bs))
+    contig = tq.TQCache(B, H, d, cap, ks, vs)
+    paged = tq.TQCache(B, H, d, cap, ks, vs, block_table=table, block_size=bs, num_blocks=nb)
+    for c in (contig, paged):
+        c.quantize_append(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), 0)
+    qd = torch.from_numpy(q).cuda()
+    runs = [contig.decode_attention(qd, T, sparse_v=1e-3, scores=True) for _ in range(5)]
+    op, sp_ = paged.decode_attention(qd, T, sparse_v=1e-3, scores=True)
+    torch.cuda.synchronize()
+    for o, sc in runs[1:]:
+        assert torch.equal(o, runs[0][0]) and torch.equal(sc, runs[0][1])
+    assert torch.equal(op, runs[0][0]) and torch.equal(sp_, runs[0][1])
