@@ -1210,6 +1210,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   // time would depend on how far they had got; this one is the same on
   // every call.  (More exchanges measured slower: each barrier waits for
   // the slowest wave.)
+  // (chunk c = wave is always the first half of a loop iteration)
   auto exchange = [&](int cc) {
     if (cc == wave && kWaves <= n_full) W.exchange_max();
   };
@@ -1247,7 +1248,6 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
         W.template cold_chunk<true, SP>(s0 + c * kChunk, s1, B, scores, hq0, p.length);
       }
       bal.step(wave, lane);
-      if (SP) exchange(c);
       c = cn;
     }
   } else {
@@ -1285,7 +1285,6 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
       asm volatile("" ::: "memory");
       W.template cold_chunk<false, SP>(s0 + c * kChunk, s1, B, scores, hq0, p.length);
       bal.step(wave, lane);
-      if (SP) exchange(c);
       c = cn;
     }
     if (c < n_chunks) {

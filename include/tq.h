@@ -173,7 +173,11 @@ typedef struct tq_cache {
  *                new positions that are already older than the newest `hot`
  *                go straight to the cold rows.  Positions must be appended
  *                in order (offset = current length) for the ring to hold the
- *                newest tokens.
+ *                newest tokens;
+ *   INT8      -> per row, scale = fp32(max|x| / 127) in `norms` and code_j =
+ *                round(127 x_j / max|x|) (to nearest, ties to even; the exact
+ *                value, not a float32 approximation of it) in `codes`; a zero
+ *                row stores scale 0 and codes 0.
  * Errors: TQ_ERR_CAPACITY if offset < 0 or offset + n_new > capacity.
  * n_new = 0 is a no-op returning TQ_OK. */
 int tq_quantize_append(const tq_cache *cache, const void *k_new,
@@ -207,6 +211,7 @@ int tq_decode_workspace_init(void *workspace, size_t workspace_bytes,
  * ("How TurboQuant KV Cache Quantization Works": scores from the compressed
  * representation).  Packed K is scored as n_i <R q, c[code_i]>; packed V is
  * accumulated in the rotated domain and rotated back once per output head.
+ * INT8 rows are used as scale_i code_i, in the original domain.
  * A DELEGATED V is attended as "the newest `hot` positions from the ring,
  * older ones packed", with newest meaning the last `length` positions: the
  * ring holds the newest `hot` positions appended, so length must equal the
