@@ -243,6 +243,10 @@ DECODE_CASES = [
     ("int8_d128_iid", 1, 8, 32, 128, 1500, ("int8", 0), ("int8", 0), "iid"),
     ("int8_mha", 2, 4, 4, 128, 300, ("int8", 0), ("int8", 0), "channel"),
     ("int8_g8", 1, 1, 8, 128, 613, ("int8", 0), ("int8", 0), "iid"),
+    # query groups that leave padding columns in the matrix-core kernel's
+    # head layouts (three of four, five of eight)
+    ("int8_g3", 1, 2, 6, 128, 700, ("int8", 0), ("int8", 0), "iid"),
+    ("int8_g5", 1, 1, 5, 128, 500, ("int8", 0), ("int8", 0), "channel"),
 ]
 
 

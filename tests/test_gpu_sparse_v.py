@@ -223,3 +223,25 @@ def test_sparse_v_deterministic_and_layout_independent(case, dvariant):
     for o, sc in runs[1:]:
         assert torch.equal(o, runs[0][0]) and torch.equal(sc, runs[0][1])
     assert torch.equal(op, runs[0][0]) and torch.equal(sp_, runs[0][1])
+
+
+@pytest.mark.parametrize("Hq", [6, 16], ids=["g3", "g8"])
+def test_sparse_v_group_sizes(Hq, dvariant):
+    # groups of three (padding heads in the four-head layout) and eight query
+    # heads per KV head: the skip test and the block maxima cover the real
+    # heads only
+    B, H, d, T = 1, 2, 128, 4000
+    k, v, q = _periodic(B, H, Hq, d, T, 256, 19)
+    cache = tq.TQCache(B, H, d, T, S("packed", 3), S("packed", 4))
+    cache.quantize_append(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), 0)
+    qd = torch.from_numpy(q).cuda()
+    tau = 1e-3
+    exact = cache.decode_attention(qd, T)
+    sparse = cache.decode_attention(qd, T, sparse_v=tau)
+    torch.cuda.synchronize()
+    exact, sparse = exact.cpu().numpy().astype(np.float64), sparse.cpu().numpy().astype(np.float64)
+    kr, vr = _rows(cache, "k", T), _rows(cache, "v", T)
+    bound = oracle.sparse_v_bound(q, kr, vr, tau)
+    scale = np.max(np.abs(exact), axis=-1, keepdims=True)
+    assert np.all(np.abs(sparse - exact) <= bound * (1 + 1e-3) + 1e-5 * scale)
+    assert not np.array_equal(sparse, exact)
