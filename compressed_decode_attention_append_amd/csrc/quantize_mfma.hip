@@ -16,7 +16,8 @@
 //       entry is a per-lane sign times a fixed 8 x 8 Hadamard pattern.  B is
 //       built once per block into LDS (16 KB) and read per tile, which keeps
 //       the wave at 80 registers: six waves per SIMD on contiguous caches
-//       (paged ones keep a prefetch buffer: four).
+//       and on paged ones with an append aligned to the tile (general paged
+//       appends keep a prefetch buffer: four).
 //   D   lane (g = l / 16, n = l % 16) holds rows 4 g + r (r = 0..3),
 //       coordinates 8 n .. 8 n + 7, as 8 N-tiles of 4 values.
 //
@@ -147,10 +148,15 @@ __device__ __forceinline__ void encode_tile(const float4_t (&acc)[8], const floa
   }
 }
 
-// PG: paged storage.  Contiguous caches run six waves a SIMD (80 registers)
-// with no prefetch buffer, the waves hiding each other's load latency; paged
-// ones keep the next tile's operands and storage rows in flight (four waves).
-template <bool PG>
+// PG: paged storage, any append.  Contiguous caches run six waves a SIMD (80
+// registers) with no prefetch buffer, the waves hiding each other's load
+// latency; the general paged kernel keeps the next tile's operands and
+// storage rows in flight (four waves).  AL (with PG false): paged storage
+// and an aligned append (offset and n_new multiples of 16), so each tile's
+// 16 rows are consecutive positions of one unit inside one block: one table
+// entry per tile gives their storage rows, and the tile runs as on a
+// contiguous cache.
+template <bool PG, bool AL>
 __global__ __launch_bounds__(kThreads, PG ? 4 : 6) void quantize_mfma_kernel(const QuantizeParams p, int tiles_k,
                                                                              int tiles_total) {
   __shared__ LutEntry lut[2][kLutCells];
@@ -243,12 +249,31 @@ __global__ __launch_bounds__(kThreads, PG ? 4 : 6) void quantize_mfma_kernel(con
     }
   };
   // encode tile `tile` from its A operands (and, paged, its storage rows)
-  auto encode = [&](int tile, const half8_t (&a)[4], const long (&prow)[4]) {
+  // AL: the storage row of the tile's first row (-1: a block outside the
+  // pools, whose rows are not written).  The table entry is read with a
+  // vector load issued after the tile's operands, so waiting for the
+  // operands does not wait for it.
+  auto aligned_row = [&](int tl) -> long {
+    const int sd_ = tl < tiles_k ? 0 : 1;
+    const unsigned q0 = static_cast<unsigned>(sd_ ? tl - tiles_k : tl) * kTileRows;
+    const unsigned un = static_cast<unsigned>(p.n_new), uh = static_cast<unsigned>(p.heads);
+    const unsigned bh = q0 / un, i0 = q0 - bh * un;
+    const unsigned b = bh / uh, kv = bh - b * uh;
+    const unsigned t = static_cast<unsigned>(p.offset) + i0, ubs = static_cast<unsigned>(p.pg.bs);
+    const unsigned blk = t / ubs;
+    const auto rt = rsrc(p.pg.table + static_cast<long>(b) * p.pg.max_blocks, 4L * p.pg.max_blocks);
+    const int entry = __builtin_amdgcn_readfirstlane(
+        static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(rt, 4 * blk, 0, 0)));
+    const long e = valid_block(p.pg, entry);
+    return e < 0 ? -1L : (e * p.pg.kv_heads + kv) * p.pg.bs + static_cast<long>(t - blk * ubs);
+  };
+  auto encode = [&](int tile, const half8_t (&a)[4], const long (&prow)[4], long al_row) {
       const int side = tile < tiles_k ? 0 : 1;
       const SideDev &sd = side ? p.v : p.k;
       const float scale = side ? p.v_lut_scale : p.k_lut_scale;
       const long r0 = static_cast<long>(side ? tile - tiles_k : tile) * kTileRows;
-      const long left = rows - r0;
+      // rows of this tile that exist (the last tile may be short)
+      const int left = rows - r0 < kTileRows ? static_cast<int>(rows - r0) : kTileRows;
 
       // squared norm of row n: fp16 products are exact, sums in fp32
       float ss = 0.0f;
@@ -308,8 +333,11 @@ __global__ __launch_bounds__(kThreads, PG ? 4 : 6) void quantize_mfma_kernel(con
                                            : r0 / p.n_new;
       const int i0 = static_cast<int>(r0 - bh0 * p.n_new);
       const int W = sd.words;
-      uint32_t *codes0 = sd.codes + (bh0 * p.capacity + p.offset + i0) * W;
-      float *norms0 = sd.norms + bh0 * p.capacity + p.offset + i0;
+      // AL: the tile's rows start at al_row and never cross a unit
+      if (AL && al_row < 0) return;
+      const long row0 = AL ? al_row : bh0 * p.capacity + p.offset + i0;
+      uint32_t *codes0 = sd.codes + row0 * W;
+      float *norms0 = sd.norms + row0;
       const int skip = p.capacity - p.n_new;
       if (PG) {
 #pragma unroll
@@ -346,14 +374,14 @@ __global__ __launch_bounds__(kThreads, PG ? 4 : 6) void quantize_mfma_kernel(con
         load_tile(tile + stride, an);
         paged_rows(tile + stride, prow_n);
       }
-      encode(tile, a, prow);
+      encode(tile, a, prow, 0L);
     }
   } else {
     const long none[4] = {0, 0, 0, 0};
     for (; tile < tiles_total; tile += stride) {
       half8_t a[4];
       load_tile(tile, a);
-      encode(tile, a, none);
+      encode(tile, a, none, AL ? aligned_row(tile) : 0L);
     }
   }
 }
@@ -391,15 +419,24 @@ hipError_t launch_quantize_mfma(const QuantizeParams &p, hipStream_t stream) {
   const long tiles_total = tiles_k + (v_on ? tiles_side : 0);
   if (tiles_total == 0) return hipSuccess;
   if (tiles_total > 0x7fffffffL) return hipErrorInvalidValue;
-  // up to one round at the kernel's occupancy: six (paged: four) blocks per CU
-  const long cap = p.pg.table ? 1024 : 1536;
+  // a paged append whose offset and length are multiples of the tile keeps
+  // every tile inside one block (blocks are multiples of 32 positions)
+  const bool aligned = p.pg.table && p.offset % kTileRows == 0 && p.n_new % kTileRows == 0 && p.pg.bs % kTileRows == 0;
+  const bool general = p.pg.table && !aligned;
+  // up to one round at the kernel's occupancy: six (general paged: four)
+  // blocks per CU
+  const long cap = general ? 1024 : 1536;
   const long blocks = std::min<long>((tiles_total + kWaves - 1) / kWaves, cap);
-  if (p.pg.table) {
-    hipLaunchKernelGGL(quantize_mfma_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, p,
-                       static_cast<int>(tiles_k), static_cast<int>(tiles_total));
+  const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
+  if (general) {
+    hipLaunchKernelGGL((quantize_mfma_kernel<true, false>), grid, block, 0, stream, p, static_cast<int>(tiles_k),
+                       static_cast<int>(tiles_total));
+  } else if (aligned) {
+    hipLaunchKernelGGL((quantize_mfma_kernel<false, true>), grid, block, 0, stream, p, static_cast<int>(tiles_k),
+                       static_cast<int>(tiles_total));
   } else {
-    hipLaunchKernelGGL(quantize_mfma_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
-                       p, static_cast<int>(tiles_k), static_cast<int>(tiles_total));
+    hipLaunchKernelGGL((quantize_mfma_kernel<false, false>), grid, block, 0, stream, p, static_cast<int>(tiles_k),
+                       static_cast<int>(tiles_total));
   }
   return hipGetLastError();
 }

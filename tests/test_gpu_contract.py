@@ -65,15 +65,19 @@ def test_workspace_init_clears_garbage_counters(variant):
         _restore("TQ_DECODE_VARIANT", old)
 
 
+# 500 positions: an append whose length is not a multiple of 16 (the general
+# paged encoder); 512: one that is (the encoder's aligned path, one table
+# entry per 16-row tile)
+@pytest.mark.parametrize("T", [500, 512], ids=["unaligned", "aligned"])
 @pytest.mark.parametrize("qvariant", ["auto", "plain"])
 @pytest.mark.parametrize("variant", ["auto", "ref"])
 @pytest.mark.parametrize("ks,vs", [(("packed", 3), ("packed", 4)), (("fp16", 0), ("packed", 4)),
                                    (("int8", 0), ("int8", 0))], ids=["tq35", "asym", "int8"])
-def test_out_of_range_blocks_read_zero_and_take_no_writes(ks, vs, variant, qvariant):
+def test_out_of_range_blocks_read_zero_and_take_no_writes(ks, vs, variant, qvariant, T):
     old_d = _env("TQ_DECODE_VARIANT", variant)
     old_q = _env("TQ_QUANTIZE_VARIANT", qvariant)
     try:
-        B, H, Hq, d, bs, cap, T = 2, 2, 8, 128, 64, 512, 500
+        B, H, Hq, d, bs, cap = 2, 2, 8, 128, 64, 512
         nb = B * cap // bs
         table = torch.from_numpy(np.random.default_rng(2).permutation(nb).astype(np.int32).reshape(B, cap // bs))
         paged = tq.TQCache(B, H, d, cap, S(*ks), S(*vs), block_table=table, block_size=bs, num_blocks=nb)

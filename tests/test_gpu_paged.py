@@ -93,6 +93,37 @@ def test_paged_storage_and_decode_match_contiguous(case, dvariant):
         assert torch.equal(oc, op), f"outputs differ at length {length}"
 
 
+# appends whose offset and length are multiples of 16 take the matrix-core
+# encoder's aligned paged path (one table entry per 16-row tile); the short
+# and odd ones after them take the general path and the plain encoder
+APPENDS_ALIGNED = [(0, 256), (256, 48), (304, 16), (320, 1), (321, 31)]
+
+
+@pytest.mark.parametrize("case", [c for c in CASES if c[4] == 128], ids=[c[0] for c in CASES if c[4] == 128])
+def test_paged_aligned_appends_match_contiguous(case):
+    name, B, H, Hq, d, bs, k, v = case
+    seed = 3000 + CASES.index(case)
+    contig = tq.TQCache(B, H, d, CAP, k, v, device="cuda")
+    table, n = _table(B, CAP // bs, seed)
+    paged = tq.TQCache(B, H, d, CAP, k, v, device="cuda", block_table=table, block_size=bs, num_blocks=n)
+    for i, (off, rows) in enumerate(APPENDS_ALIGNED):
+        kx, vx = synth.kv_numpy(seed + i, B, H, rows, d, dist="channel", outlier_frac=0.01)
+        kd, vd = torch.from_numpy(kx).cuda(), torch.from_numpy(vx).cuda()
+        contig.quantize_append(kd, vd, off)
+        paged.quantize_append(kd, vd, off)
+    torch.cuda.synchronize()
+    for nm in contig.tensors:
+        assert torch.equal(contig.tensors[nm], paged.logical(nm)), nm
+    q = torch.from_numpy(synth.q_numpy(78, B, Hq, d)).cuda()
+    # a delegated V is decoded at its appended length only (its ring holds
+    # the newest positions appended)
+    for length in ((352,) if v.mode == "delegated" else (320, 352)):
+        oc, sc = contig.decode_attention(q, length, scores=True)
+        op, sp = paged.decode_attention(q, length, scores=True)
+        torch.cuda.synchronize()
+        assert torch.equal(sc, sp) and torch.equal(oc, op), length
+
+
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_paged_dequantize_matches_contiguous(case):
     contig, paged = _pair(case, 2000 + CASES.index(case))
