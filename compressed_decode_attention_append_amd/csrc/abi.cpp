@@ -150,18 +150,22 @@ Variant pick_variant(const tq::DecodeParams &p) {
 // Splits of the matrix-core kernel: the packed positions of a unit in
 // n_cold splits of a multiple of 256 positions (8 waves x 32), aiming at one
 // block per compute unit (256 blocks) with at least 512 positions per block.
-// The fp16 hot window of a delegated V is attended by the block that
-// finishes its unit last, so it needs no split of its own.
+// An explicit split count still gives splits of a multiple of 32 positions:
+// the kernel reads 32-position chunks from each split's start, and a paged
+// chunk must lie in one block (blocks are multiples of 32 positions), so
+// every split starts on that grid.  The fp16 hot window of a delegated V is
+// attended by the block that finishes its unit last, so it needs no split
+// of its own.
 void mfma_splits(const tq_cache *c, int length, int n_splits, tq::DecodeParams *p) {
   constexpr int kTargetBlocks = 256, kMinPerBlock = 512, kQuantum = 256;
   const int units = c->batch * c->kv_heads;
   const int cold = (c->v.mode == TQ_SIDE_DELEGATED) ? std::max(0, length - c->v.hot) : length;
   const int cap = tq::kMfmaMaxSplits;
-  int ncold = 1, clen = 1;
+  int ncold = 1, clen = tq::kMfmaChunk;
   if (cold > 0) {
     if (n_splits > 0) {
       ncold = std::min(std::min(n_splits, cold), cap);
-      clen = (cold + ncold - 1) / ncold;
+      clen = ((cold + ncold - 1) / ncold + tq::kMfmaChunk - 1) / tq::kMfmaChunk * tq::kMfmaChunk;
     } else {
       const int want = std::max(1, std::min(std::min((kTargetBlocks + units - 1) / units,
                                                      (cold + kMinPerBlock - 1) / kMinPerBlock),

@@ -73,7 +73,7 @@ constexpr int v_row_bytes() { return KB == kInt8 ? D : D / 2; }
 template <int KB>
 constexpr int waves_of() { return (KB == 0 || KB == kInt8) ? 8 : 12; }
 constexpr int kMaxWaves = 12;
-constexpr int kChunk = 32;
+constexpr int kChunk = kMfmaChunk;
 constexpr int kRep = 32;          // pair-table replicas, one per LDS bank
 constexpr int kMaxSplits = kMfmaMaxSplits;  // splits per unit (bounded by the host)
 constexpr float kRescale = 8.0f;  // lazy rescaling threshold (log2 units)
@@ -1503,6 +1503,8 @@ hipError_t launch_decode_mfma(const DecodeParams &p, hipStream_t stream) {
   if (G < 1 || G > 8 || p.head_dim != D) return hipErrorInvalidValue;
   const int nsplit = p.n_cold_splits;
   if (nsplit < 1 || nsplit > kMaxSplits || p.n_hot_splits != 0) return hipErrorInvalidValue;
+  // every split starts on the chunk grid (a paged chunk lies in one block)
+  if (p.cold_split_len < 1 || p.cold_split_len % kChunk) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(p.batch * p.kv_heads * nsplit));
   switch (kb) {
     case 0: launch_kb<0>(p, grid, stream); break;

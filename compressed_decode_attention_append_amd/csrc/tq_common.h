@@ -168,9 +168,10 @@ hipError_t launch_decode_ref(const DecodeParams &p, hipStream_t stream);
 // head, and either INT8 on both sides or a packed or delegated 4-bit V with
 // K as fp16, packed 3-bit, or packed 4-bit sharing V's codebook; at most
 // kMfmaMaxSplits context splits
-// per (batch, KV head) unit.  (The host picks it by this rule; the launcher
-// checks it again.)
+// per (batch, KV head) unit, each a multiple of kMfmaChunk positions long.
+// (The host picks it by this rule; the launcher checks it again.)
 hipError_t launch_decode_mfma(const DecodeParams &p, hipStream_t stream);
 constexpr int kMfmaMaxSplits = 256;
+constexpr int kMfmaChunk = 32;  // positions the matrix-core decode reads as one chunk
 
 }  // namespace tq

@@ -178,16 +178,22 @@ def test_shared_prefix_blocks():
     assert ok, f"out: worst {worst}"
 
 
-@pytest.mark.parametrize("ns", [3, 7])
-@pytest.mark.parametrize("case", [CASES[4], ("tq35_d128_bs32", 2, 2, 8, 128, 32, S("packed", 3), S("packed", 4))],
-                         ids=["tq35_d64", "tq35_d128_bs32"])
-def test_paged_split_counts_match_contiguous(case, ns, monkeypatch):
-    # explicit split counts give split lengths off the 32-position grid, so
-    # the plain kernel's tiles cross block boundaries: 32-position tiles at
-    # d = 64, and 64-position tiles over 32-position blocks at d = 128
-    monkeypatch.setenv("TQ_DECODE_VARIANT", "ref")
+@pytest.mark.parametrize("variant", ["auto", "ref"])
+@pytest.mark.parametrize("ns", [2, 3, 7])
+@pytest.mark.parametrize("case", [CASES[4], ("tq35_d128_bs32", 2, 2, 8, 128, 32, S("packed", 3), S("packed", 4)),
+                                  ("asym_d128_bs64", 2, 3, 15, 128, 64, S("fp16", 0), S("packed", 4))],
+                         ids=["tq35_d64", "tq35_d128_bs32", "asym_d128_bs64"])
+def test_paged_split_counts_match_contiguous(case, ns, variant, monkeypatch):
+    # explicit split counts: the plain kernel's split lengths are off the
+    # 32-position grid, so its tiles cross block boundaries (32-position
+    # tiles at d = 64, 64-position tiles over 32-position blocks at d = 128);
+    # the matrix-core kernel rounds its split lengths up to that grid, since
+    # each of its 32-position chunks must lie in one block (length 574 over
+    # 2 splits once started a split at 287, and those chunks read across
+    # block boundaries)
+    monkeypatch.setenv("TQ_DECODE_VARIANT", variant)
     contig, paged = _pair(case, 2024 + ns)
-    for length in LENGTHS:
+    for length in LENGTHS + [574]:
         q = torch.from_numpy(synth.q_numpy(78, case[1], case[3], case[4])).cuda()
         oc, sc = contig.decode_attention(q, length, n_splits=ns, scores=True)
         op, sp = paged.decode_attention(q, length, n_splits=ns, scores=True)
