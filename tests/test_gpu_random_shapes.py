@@ -14,7 +14,10 @@ Checks, as in the fixed-case parity tests:
   there); norms within 1e-6; INT8 sides: codes and scales equal the exact
   definition; fp16 sides: the rows themselves;
 * decode (both kernels): scores and outputs against the oracle's attention
-  over the rows the GPU wrote, within 2e-3 of each row's largest magnitude.
+  over the rows the GPU wrote, within 2e-3 of each row's largest magnitude;
+* sparse-V (both kernels, a threshold per case): within the oracle's bound
+  of the exact output;
+* the allocation-free entry point: the same output as the workspace call.
 """
 import os
 
@@ -166,18 +169,31 @@ def test_random_configuration(seed):
         pos += n
     T = c["length"]
     q = synth.q_numpy(9000 + seed, B, Hq, d)
-    o_ref, s_ref = oracle.decode_attention(q, _rows(cache, "k", c["k"], T), _rows(cache, "v", c["v"], T))
+    kr, vr = _rows(cache, "k", c["k"], T), _rows(cache, "v", c["v"], T)
+    o_ref, s_ref = oracle.decode_attention(q, kr, vr)
+    tau = (1e-4, 1e-3, 1e-2)[seed % 3]
+    bound = oracle.sparse_v_bound(q, kr, vr, tau)
+    qd = torch.from_numpy(q).cuda()
     old = os.environ.get("TQ_DECODE_VARIANT")
     try:
         for variant in ("auto", "ref"):
             os.environ["TQ_DECODE_VARIANT"] = variant
-            out, sc = cache.decode_attention(torch.from_numpy(q).cuda(), T, n_splits=c["splits"], scores=True)
+            out, sc = cache.decode_attention(qd, T, n_splits=c["splits"], scores=True)
+            sparse = cache.decode_attention(qd, T, n_splits=c["splits"], sparse_v=tau)
             torch.cuda.synchronize()
             ok_s, worst_s = rows_close(sc.cpu().numpy(), s_ref)
             ok_o, worst_o = rows_close(out.cpu().numpy(), o_ref)
             print(f"  {variant}: scores {worst_s:.2e}, out {worst_o:.2e}", flush=True)
             assert ok_s, f"{desc} [{variant}]: scores worst {worst_s}"
             assert ok_o, f"{desc} [{variant}]: out worst {worst_o}"
+            exact = out.cpu().numpy().astype(np.float64)
+            scale = np.max(np.abs(exact), axis=-1, keepdims=True)
+            moved = np.abs(sparse.cpu().numpy().astype(np.float64) - exact)
+            assert np.all(moved <= bound * (1 + 1e-3) + 1e-5 * scale), f"{desc} [{variant}]: sparse-V tau {tau}"
+            if variant == "auto":
+                free = cache.decode_attention_noalloc(qd, T, n_splits=c["splits"])
+                torch.cuda.synchronize()
+                assert torch.equal(free, out), f"{desc}: allocation-free call differs"
     finally:
         if old is None:
             os.environ.pop("TQ_DECODE_VARIANT", None)
