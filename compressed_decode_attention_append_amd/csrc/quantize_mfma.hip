@@ -421,7 +421,9 @@ hipError_t launch_quantize_mfma(const QuantizeParams &p, hipStream_t stream) {
   if (tiles_total > 0x7fffffffL) return hipErrorInvalidValue;
   // a paged append whose offset and length are multiples of the tile keeps
   // every tile inside one block (blocks are multiples of 32 positions)
-  const bool aligned = p.pg.table && p.offset % kTileRows == 0 && p.n_new % kTileRows == 0 && p.pg.bs % kTileRows == 0;
+  // (and its row indices fit the aligned path's 32-bit arithmetic)
+  const bool aligned = p.pg.table && p.offset % kTileRows == 0 && p.n_new % kTileRows == 0 &&
+                       p.pg.bs % kTileRows == 0 && rows <= 0x7fffffffL;
   const bool general = p.pg.table && !aligned;
   // up to one round at the kernel's occupancy: six (general paged: four)
   // blocks per CU
