@@ -225,7 +225,11 @@ int tq_decode_workspace_init(void *workspace, size_t workspace_bytes,
  *           its counters zero before its first use (see
  *           TQ_WORKSPACE_COUNTER_BYTES).  It holds per-split partial
  *           results; calls that share a workspace must not overlap.
- *   n_splits: 0 = automatic, else the number of context splits (>= 1).
+ *   n_splits: 0 = automatic, else the number of context splits asked
+ *           for (>= 1): pieces of equal length.  The matrix-core kernel
+ *           rounds each piece up to a multiple of 32 positions (what it
+ *           reads as one chunk), so it may use fewer splits than asked,
+ *           never more.
  * length = 0 writes zeros to out. */
 int tq_decode_attention(const tq_cache *cache, const void *q, int q_heads,
                         int length, int n_splits, float *out, float *scores,
