@@ -17,7 +17,10 @@ Checks, as in the fixed-case parity tests:
   over the rows the GPU wrote, within 2e-3 of each row's largest magnitude;
 * sparse-V (both kernels, a threshold per case): within the oracle's bound
   of the exact output;
-* the allocation-free entry point: the same output as the workspace call.
+* the allocation-free entry point: the same output as the workspace call;
+* dequantize of the packed and INT8 sides over a range of positions: the
+  oracle's dequantization of the same codes, within 1e-5 of each row's
+  largest magnitude.
 """
 import os
 
@@ -194,6 +197,15 @@ def test_random_configuration(seed):
                 free = cache.decode_attention_noalloc(qd, T, n_splits=c["splits"])
                 torch.cuda.synchronize()
                 assert torch.equal(free, out), f"{desc}: allocation-free call differs"
+        rng = np.random.default_rng(seed + 77)
+        for side, spec, rows in (("k", c["k"], kr), ("v", c["v"], vr)):
+            if spec.mode in ("packed", "int8"):
+                st = int(rng.integers(0, T))
+                cnt = int(rng.integers(1, T - st + 1))
+                dq = cache.dequantize(side, st, cnt)
+                torch.cuda.synchronize()
+                ok, worst = rows_close(dq.cpu().numpy(), rows[:, :, st:st + cnt], 1e-5)
+                assert ok, f"{desc}: dequantize {side} [{st}, {st + cnt}) worst {worst}"
     finally:
         if old is None:
             os.environ.pop("TQ_DECODE_VARIANT", None)
