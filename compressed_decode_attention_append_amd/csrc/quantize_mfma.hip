@@ -161,6 +161,9 @@ __global__ __launch_bounds__(kThreads, PG ? 4 : 6) void quantize_mfma_kernel(con
                                                                              int tiles_total) {
   __shared__ LutEntry lut[2][kLutCells];
   __shared__ u32x4_t bsh[16][64];  // B operands [4 t + q][lane] for the N-tiles t < 4
+  // contiguous stores: each wave's tile of code words (16 rows of up to 16
+  // words) and norms, gathered in row order
+  __shared__ u32x4_t stage[PG ? 1 : kWaves][68];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
@@ -346,6 +349,29 @@ __global__ __launch_bounds__(kThreads, PG ? 4 : 6) void quantize_mfma_kernel(con
           if (n < W) sd.codes[prow[r] * W + n] = word[r];
           if (n == r) sd.norms[prow[r]] = nrm[r];
         }
+        return;
+      }
+      // (AL: always; n_new is a multiple of 16 there)
+      if (AL || (left == kTileRows && i0 + kTileRows <= p.n_new)) {
+        // the tile's 16 rows are consecutive storage rows: gather them in
+        // row order in LDS, then write the 16 W words with one 16-byte
+        // store per lane (16 W is a multiple of 4: W = 4 bits) and the 16
+        // norms with one word store per lane
+        uint32_t *st = reinterpret_cast<uint32_t *>(&stage[PG ? 0 : wave][0]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (n < W) st[(4 * g + r) * W + n] = word[r];
+          if (n == r) st[256 + 4 * g + r] = __float_as_uint(nrm[r]);
+        }
+        __builtin_amdgcn_wave_barrier();
+        // the lane index recomputed here: offsets derived from the kernel's
+        // copy would be kept in registers across the whole loop
+        uint32_t lid;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lid));
+        if (4 * lid < static_cast<uint32_t>(kTileRows * W))
+          *reinterpret_cast<u32x4_t *>(codes0 + 4 * lid) = *reinterpret_cast<const u32x4_t *>(st + 4 * lid);
+        if (lid < kTileRows) norms0[lid] = __uint_as_float(st[256 + lid]);
+        __builtin_amdgcn_wave_barrier();  // the stage is read before the next tile writes it
         return;
       }
 #pragma unroll
