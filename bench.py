@@ -44,6 +44,10 @@ WORKLOADS = {
     "c3_int8_16k": dict(batch=8, kv_heads=8, q_heads=32, head_dim=128, tokens=16384, layers=36,
                         k=("int8", 0), v=("int8", 0), prefill=0, append=1, dist="channel",
                         outlier_frac=0.01),
+    # the pages' turbo3-asym mode (fp16 K, 3-bit V) at the same shape
+    "c3_turbo3_asym_16k": dict(batch=8, kv_heads=8, q_heads=32, head_dim=128, tokens=16384, layers=36,
+                               k=("fp16", 0), v=("packed", 3), prefill=0, append=1, dist="channel",
+                               outlier_frac=0.01),
     # the 32K workload with a peaked softmax (heavy-hitter keys at the first
     # 4 positions of every 512; the sparse-V comparison)
     "c4_tq35_32k_peaked": dict(batch=4, kv_heads=8, q_heads=32, head_dim=128, tokens=32768, layers=36,

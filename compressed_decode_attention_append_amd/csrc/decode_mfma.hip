@@ -5,8 +5,8 @@
 // "TurboQuant KV cache", "Available modes": fp16 K with TurboQuant V and the
 // delegated hot/cold V split).
 //
-// head_dim 128, 4-bit V codes, K packed (3 or 4 bits) or fp16, up to 8 query
-// heads per KV head.  Grid = (B * Hkv units) x splits, about one block per
+// head_dim 128, 3- or 4-bit V codes, K packed (3 or 4 bits) or fp16, up to 8
+// query heads per KV head (and INT8 on both sides).  Grid = (B * Hkv units) x splits, about one block per
 // compute unit (12 waves for packed K, 8 for fp16 K).  A block issues its first
 // loads, builds its lookup tables and rotated query while they are in
 // flight, then each wave walks its share of the split in chunks of 32
@@ -22,12 +22,14 @@
 //           is the base-2 logit.
 //   softmax online per query head; the accumulators are only rescaled when
 //           the running maximum grows by more than 2^8.
-//   value   the same MFMA with M = 16 coordinates, N = 16 heads, K = 32
-//           positions.  Each lane loads one code word of 8 positions and
-//           transposes the 8 x 8 nibbles in registers, so it then holds one
-//           coordinate of 8 positions; B holds p_i n_i times a power of two
-//           that keeps fp16 in range (lowered lazily when a larger norm
-//           arrives).  The sum stays in the rotated domain.
+//   value   the same MFMA with M = 16 (the hi and lo weights of the G
+//           heads, rest padding), N = 16 coordinates, K = 32 positions.  A
+//           holds p_i n_i times a power of two that keeps fp16 in range
+//           (lowered lazily when a larger norm arrives).  Each lane loads the
+//           codes of 8 coordinates of 8 positions and pairs the codes of two
+//           positions at one coordinate in registers, so B (one coordinate
+//           of 8 positions a lane) comes from pair-table reads.  The sum
+//           stays in the rotated domain.
 //   precision  fp16 operands carry 11 bits, and the output of a diffuse
 //           softmax is much smaller than the rows it averages, so plain fp16
 //           leaves output errors near 1e-3.  Each fp16 operand that is not
@@ -64,9 +66,10 @@ constexpr int D = 128;
 constexpr int kInt8 = 8;
 template <int KB>
 constexpr bool rotated_k() { return KB == 3 || KB == 4; }
-// V bytes a row: 4-bit codes, or INT8 bytes
-template <int KB>
-constexpr int v_row_bytes() { return KB == kInt8 ? D : D / 2; }
+// VB selects the packed V storage: 3 or 4 bits a code (kInt8 with INT8 K:
+// INT8 bytes).  V bytes a row:
+template <int VB>
+constexpr int v_row_bytes() { return D * VB / 8; }
 // Waves per block: 12 for packed K (about 160 registers a lane, so three
 // waves a SIMD), 8 for fp16 K rows and for INT8 (about 200-250 registers,
 // two a SIMD).  One block per compute unit either way.
@@ -93,12 +96,19 @@ constexpr float kVscaleMax = 1099511627776.0f;  // 2^40: start and ceiling of th
 //               (the top 2 bits are ignored, so every pair is read straight
 //               from a byte of the code stream shifted by 0, 6, 12, ...);
 //               V hi in the first half of entries 256..511
+//   KB = 4, VB = 3   as KB = 3, with 4-bit K pairs (a whole byte)
+// A 3-bit V table is indexed the same way: low 6 bits = the codes of two
+// positions at one coordinate, the top 2 bits ignored.
 // After the main loop the table area is reused for the merges.
 constexpr int kTableWords = 256 * 64;  // one 256-entry region (64 KB)
-template <int KB>
-constexpr int table_words() { return KB == 3 ? 2 * kTableWords : kTableWords; }
-template <int KB>
-constexpr uint32_t v_table_byte() { return KB == 3 ? 4u * kTableWords : 0u; }
+// K hi / K lo in the first region and V in the second whenever K's pairs
+// need tables of their own: 3-bit K, and 4-bit K beside 3-bit V
+template <int KB, int VB>
+constexpr bool two_tables() { return KB == 3 || (KB == 4 && VB == 3); }
+template <int KB, int VB>
+constexpr int table_words() { return two_tables<KB, VB>() ? 2 * kTableWords : kTableWords; }
+template <int KB, int VB>
+constexpr uint32_t v_table_byte() { return two_tables<KB, VB>() ? 4u * kTableWords : 0u; }
 // A partial result (merge slot, workspace partial) of one query head: max,
 // sum, two pad words, then the D accumulator values, so the values start
 // 16-byte aligned.
@@ -106,10 +116,10 @@ constexpr int kPS = D + 4;
 constexpr int kPV = 4;
 constexpr int kKloOff = 128;  // byte offset of the K lo table from the K hi / V one
 
-template <int KB, int GP>
+template <int KB, int VB, int GP>
 struct Lay {
-  static constexpr int qstride = D + 4;              // padded row: fewer bank conflicts
-  static constexpr int qwork = table_words<KB>();    // [GP][D + 4] rotated query
+  static constexpr int qstride = D + 4;                  // padded row: fewer bank conflicts
+  static constexpr int qwork = table_words<KB, VB>();    // [GP][D + 4] rotated query
   static constexpr int red = qwork + GP * qstride;     // flag
   static constexpr int prog = red + 4;                 // [kMaxWaves] chunks done per wave
   static constexpr int qinv = red + 16;                // [8] per head: the score's query scale
@@ -294,15 +304,16 @@ __device__ __forceinline__ float xor_butterfly(float x, int lane) {
 }
 
 // Global-memory data of one chunk of 32 positions for one lane.
-template <int KB, int GP>
+template <int KB, int VB, int GP>
 struct ChunkData {
   static constexpr int kw = KB == 0 ? 16 : (KB == kInt8 ? 8 : (KB == 4 ? 4 : 3));  // K dwords per M-tile
-  static constexpr int kvw = KB == kInt8 ? 16 : 8;             // V dwords
+  static constexpr int kvw = VB == 4 ? 8 : 16;                 // V dwords
   static constexpr int nv = GP / 2;                            // compact values per lane
   uint32_t k[2][kw];   // K words (packed), fp16 or INT8 row piece, M-tiles 0 and 1
   float kn[nv];        // K norms (INT8: scales) of the lane's compact positions
-  uint32_t v[kvw];     // V: code word `col` (INT8: bytes 8 col .. 8 col + 7) of the
-                       // 8 positions of this lane group
+  uint32_t v[kvw];     // V: code word `col` (3-bit: the two dwords holding the
+                       // 24 bits of coordinates 8 col .. 8 col + 7; INT8: bytes
+                       // 8 col .. 8 col + 7) of the 8 positions of this lane group
   float vn[nv];        // V norms (INT8: scales) of the compact positions
   bool vskip;          // sparse-V: the V codes were not loaded (predicted skippable)
 };
@@ -317,16 +328,18 @@ struct ChunkData {
 // nv kc .. nv kc + nv - 1 (nv = GP / 2 consecutive positions), moved there
 // from lane (grp, h) with DPP row shifts, and moved back the same way for the
 // value MFMA's B operand.
-template <int KB, int GP, bool PG>
+template <int KB, int VB, int GP, bool PG>
 struct Wave {
   static constexpr int NV = GP / 2;
   static constexpr int kRowBytes = KB == 0 ? 2 * D : (KB == kInt8 ? D : (KB == 4 ? 64 : 48));
-  static constexpr int kVRow = v_row_bytes<KB>();
+  static constexpr int kVRow = v_row_bytes<VB>();
   // per-lane constants
   int col, grp, cpos;   // cpos: chunk position of the lane's first compact slot
   uint32_t rep4;        // 4 r: the lane's replica
   uint32_t rep4v;       // 4 r + the V table's byte offset
   uint32_t koff, knoff, voff;   // lane byte offsets inside a chunk
+  uint32_t vsh;         // 3-bit V: bit offset of the lane's 24 bits in its first dword
+  bool vlast;           // 3-bit V: lane column 15, whose bits all lie in its second dword
   const uint32_t *lds;
   uint32_t bmax_at;     // sparse-V: LDS byte address of the exchanged maxima [8 heads][16 waves]
   int wave_id;
@@ -388,7 +401,7 @@ struct Wave {
     return bl < 0 ? -1L : (bl * pg.kv_heads + kv) * pg.bs + t0 % pg.bs;
   }
 
-  __device__ __forceinline__ void load(int t0, ChunkData<KB, GP> &c) const { load_row(row_of(t0), t0, c); }
+  __device__ __forceinline__ void load(int t0, ChunkData<KB, VB, GP> &c) const { load_row(row_of(t0), t0, c); }
 
   // rows [t0, t0 + 32) at most, from storage row row0 on; rows past the
   // unit's capacity, and every row of an out-of-range block (row0 = -1),
@@ -397,7 +410,7 @@ struct Wave {
   // reads nothing and returns zeros (the same loads are issued, so the
   // wave's waits stay static); the chunk notes it, and reloads them if its
   // weights turn out to need them.
-  __device__ __forceinline__ void load_row(long row0, int t0, ChunkData<KB, GP> &c, bool vskip = false) const {
+  __device__ __forceinline__ void load_row(long row0, int t0, ChunkData<KB, VB, GP> &c, bool vskip = false) const {
     const int rows = row0 < 0 ? 0 : min(capacity - t0, kChunk);
     row0 = row0 < 0 ? 0L : row0;
     const auto rk = rsrc(kbase + row0 * kRowBytes, rows * kRowBytes);
@@ -414,7 +427,7 @@ struct Wave {
         c.k[m][0] = w[0]; c.k[m][1] = w[1]; c.k[m][2] = w[2];
       } else {
 #pragma unroll
-        for (int i = 0; i < ChunkData<KB, GP>::kw; i += 4) {
+        for (int i = 0; i < ChunkData<KB, VB, GP>::kw; i += 4) {
           const u32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(rk, koff + mo + 4 * i, 0, 0);
           c.k[m][i] = w[0]; c.k[m][i + 1] = w[1]; c.k[m][i + 2] = w[2]; c.k[m][i + 3] = w[3];
         }
@@ -440,13 +453,14 @@ struct Wave {
     load_v(rv, c.v);
   }
 
-  // The V data of the lane's 8 position slots: one code word, or (INT8) the
-  // 8 bytes of coordinates 8 col .. 8 col + 7.
-  __device__ __forceinline__ void load_v(__amdgpu_buffer_rsrc_t rv, uint32_t (&v)[ChunkData<KB, GP>::kvw]) const {
+  // The V data of the lane's 8 position slots: one code word, (3-bit) the
+  // two dwords holding the 24 bits of coordinates 8 col .. 8 col + 7, or
+  // (INT8) the 8 bytes of those coordinates.
+  __device__ __forceinline__ void load_v(__amdgpu_buffer_rsrc_t rv, uint32_t (&v)[ChunkData<KB, VB, GP>::kvw]) const {
 #pragma unroll
     for (int s8 = 0; s8 < 8; ++s8) {
       const uint32_t off = voff + (16 * (s8 >> 2) + (s8 & 3)) * kVRow;
-      if (KB == kInt8) {
+      if (VB != 4) {
         const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(rv, off, 0, 0);
         v[2 * s8] = w[0];
         v[2 * s8 + 1] = w[1];
@@ -457,7 +471,7 @@ struct Wave {
   }
 
   // Scores of the chunk in D layout (lane: slots 4 m + r, head col).
-  __device__ __forceinline__ void score(const ChunkData<KB, GP> &c, float (&s)[8]) const {
+  __device__ __forceinline__ void score(const ChunkData<KB, VB, GP> &c, float (&s)[8]) const {
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       float4_t acc = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -698,7 +712,7 @@ struct Wave {
   // byte per coordinate pair index), then per tile q one table lookup per
   // slot pair and one MFMA: D[(head, hi/lo)][coordinate 8 col + q] +=
   // P[(head, hi/lo)][slot] * c[code of slot, coordinate].
-  __device__ __forceinline__ void values(const uint32_t (&cv)[ChunkData<KB, GP>::kvw], const half8_t ap) {
+  __device__ __forceinline__ void values(const uint32_t (&cv)[ChunkData<KB, VB, GP>::kvw], const half8_t ap) {
     if (KB == kInt8) {
       // INT8: slot s holds bytes 8 col .. 8 col + 7 in words 2 s, 2 s + 1;
       // tile q takes byte q % 4 of word q / 4 of every slot, two slots an
@@ -723,6 +737,33 @@ struct Wave {
       }
       return;
     }
+    if (VB == 3) {
+      // 3-bit codes: the lane's 24 bits of each slot (coordinate 8 col + k
+      // at bit 3 k), then per slot pair the 6-bit pairs (slot 2 s2 low,
+      // slot 2 s2 + 1 high) of the even coordinates at bits 0, 6, 12, 18
+      // (ev) and of the odd ones (od); pair j is byte 0 of the word shifted
+      // right by 6 j, and the table ignores the byte's top 2 bits
+      uint32_t ev[4], od[4];
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) {
+        const uint32_t fa = __builtin_amdgcn_alignbit(cv[4 * s2 + 1], vlast ? cv[4 * s2 + 1] : cv[4 * s2], vsh);
+        const uint32_t fb = __builtin_amdgcn_alignbit(cv[4 * s2 + 3], vlast ? cv[4 * s2 + 3] : cv[4 * s2 + 2], vsh);
+        ev[s2] = bfi(0x1c71c7u, fa, fb << 3);
+        od[s2] = bfi(0x1c71c7u, fa >> 3, fb);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const uint32_t *src = (q & 1) ? od : ev;
+        uint32_t a4[4];
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+          const uint32_t w = src[s2] >> (6 * (q >> 1));
+          a4[s2] = lds_at<0>(lds, two_tables<KB, VB>() ? baddr_hi<0>(w, rep4v) : baddr<0>(w, rep4));
+        }
+        accv[q] = mma(ap, as_half8(a4[0], a4[1], a4[2], a4[3]), accv[q]);
+      }
+      return;
+    }
     uint32_t ev[4], od[4];  // bytes j: coordinates 8 col + 2 j (ev) and 8 col + 2 j + 1 (od)
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2) {
@@ -738,7 +779,7 @@ struct Wave {
       for (int s2 = 0; s2 < 4; ++s2) {
         const uint32_t w = src[s2];
         uint32_t ad;
-        if (KB == 3) {
+        if (two_tables<KB, VB>()) {
           switch (q >> 1) {
             case 0: ad = baddr_hi<0>(w, rep4v); break;
             case 1: ad = baddr_hi<1>(w, rep4v); break;
@@ -761,7 +802,7 @@ struct Wave {
 
   // One chunk of packed positions [t0, t0 + 32); positions >= we are masked.
   template <bool TAIL, bool SP>
-  __device__ __forceinline__ void cold_chunk(int t0, int we, const ChunkData<KB, GP> &c, float *scores,
+  __device__ __forceinline__ void cold_chunk(int t0, int we, const ChunkData<KB, VB, GP> &c, float *scores,
                                              long score_row0, int length) {
     float s[8], cs[NV];
     score(c, s);
@@ -792,7 +833,7 @@ struct Wave {
         const long row0 = row_of(t0);
         const int rows = row0 < 0 ? 0 : min(capacity - t0, kChunk);
         const auto rv = rsrc(vbase + (row0 < 0 ? 0L : row0) * kVRow, rows * kVRow);
-        uint32_t vv[ChunkData<KB, GP>::kvw];
+        uint32_t vv[ChunkData<KB, VB, GP>::kvw];
         load_v(rv, vv);
         values(vv, ap);
         return;
@@ -824,7 +865,7 @@ struct Wave {
   // Chunk [t0, t0 + 32) of the fp16 hot window [wb, we): t0 is on the
   // 32-position grid (a paged chunk then lies in one block), and positions
   // outside the window are masked.
-  __device__ __forceinline__ void hot_chunk(int t0, int wb, int we, const ChunkData<KB, GP> &c, float *scores,
+  __device__ __forceinline__ void hot_chunk(int t0, int wb, int we, const ChunkData<KB, VB, GP> &c, float *scores,
                                             long score_row0, int length) {
     float s[8], cs[NV], vn[NV];
     score(c, s);
@@ -992,12 +1033,12 @@ struct Balance {
   }
 };
 
-template <int KB, int GP, bool PG, bool SC, bool SP>
+template <int KB, int VB, int GP, bool PG, bool SC, bool SP>
 __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(const DecodeParams p) {
   constexpr int kWaves = waves_of<KB>();
   constexpr int kThreads = 64 * kWaves;
-  using L = Lay<KB, GP>;
-  using WaveT = Wave<KB, GP, PG>;
+  using L = Lay<KB, VB, GP>;
+  using WaveT = Wave<KB, VB, GP, PG>;
   constexpr int NV = WaveT::NV;
   // Static LDS: its base address is a compile-time constant, so table reads
   // fold the table offset into the instruction.
@@ -1042,7 +1083,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
     W.cpos = 16 * (i0 >> 2) + 4 * W.grp + (i0 & 3);
   }
   W.rep4 = (lane & 31) * 4u;
-  W.rep4v = W.rep4 + v_table_byte<KB>();
+  W.rep4v = W.rep4 + v_table_byte<KB, VB>();
   W.lds = lds;
   W.G = G;
   // contiguous: the unit's rows start at unit * capacity; paged: load()
@@ -1057,7 +1098,13 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   W.vnbase = reinterpret_cast<const char *>(p.v.norms + rowbase);
   W.koff = static_cast<uint32_t>(W.col * kRowBytes + W.grp * (kRowBytes / 4));
   W.knoff = static_cast<uint32_t>(4 * W.cpos);
-  W.voff = static_cast<uint32_t>(W.grp * 4 * kVRow + W.col * (kVRow / 16));
+  // 3-bit V: the lane's 24 bits start at byte 3 col of the row, in dword
+  // 3 col / 4 at bit 8 (3 col % 4); lane 15 reads dwords 10 and 11 (the
+  // row's last two) and takes its bits from the second
+  W.voff = static_cast<uint32_t>(W.grp * 4 * kVRow +
+                                 (VB == 3 ? 4 * min(3 * W.col / 4, 10) : W.col * (kVRow / 16)));
+  W.vsh = 8u * ((3u * W.col) & 3u);
+  W.vlast = W.col == 15;
   W.capacity = p.capacity;
   W.hot_len = p.v.hot > 0 ? p.v.hot : 1;
   W.ring = (p.v.mode == TQ_SIDE_DELEGATED) ? p.v.fp16 + static_cast<long>(unit) * p.v.hot * D : nullptr;
@@ -1078,7 +1125,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   // waves past the split read an empty range, which returns zeros.)
   uint32_t qa_raw = p.q[(hq0 + min(wave, G - 1)) * D + lane];  // fp16 bits
   uint32_t qb_raw = p.q[(hq0 + min(wave, G - 1)) * D + lane + 64];
-  ChunkData<KB, GP> A, B;
+  ChunkData<KB, VB, GP> A, B;
   W.load(s0 + wave * kChunk, A);
   // The 16 (V) and up to 16 (K) centroids the tables need: every wave reads
   // them with uniform indices (scalar loads of the kernel arguments) into
@@ -1091,14 +1138,15 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
     if (KB != kInt8) vc = (lane == i) ? p.v_cent[i] : vc;
   }
   // Tables, written four replicas (16 bytes) at a time: the value table
-  // (for KB = 4 also the K lo table; for KB = 3 also the K hi and lo
-  // tables).  Built while the query and the first chunk are in flight.
-  // Every loop below runs whole waves (the counts are multiples of 64), as
-  // the shuffles need.
-  constexpr int kVWord = v_table_byte<KB>() / 4;
+  // (for KB = 4 also the K lo table, and the K hi table beside 3-bit V; for
+  // KB = 3 also the K hi and lo tables).  Built while the query and the
+  // first chunk are in flight.  Every loop below runs whole waves (the
+  // counts are multiples of 64), as the shuffles need.
+  constexpr int kVWord = v_table_byte<KB, VB>() / 4;
   for (int i = threadIdx.x; KB != kInt8 && i < 256 * (kRep / 4); i += kThreads) {
     const int e = i >> 3, r4 = 4 * (i & 7);
-    const uint32_t w = pack_half2(__shfl(vc, e & 15), __shfl(vc, e >> 4));
+    const uint32_t w = VB == 4 ? pack_half2(__shfl(vc, e & 15), __shfl(vc, e >> 4))
+                               : pack_half2(__shfl(vc, e & 7), __shfl(vc, (e >> 3) & 7));
     *reinterpret_cast<u32x4_t *>(lds + kVWord + e * 64 + r4) = u32x4_t{w, w, w, w};
     if (KB) {
       uint32_t h, l;
@@ -1106,8 +1154,8 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
         split_pair(__shfl(kc, e & 15), __shfl(kc, e >> 4), h, l);
       } else {
         split_pair(__shfl(kc, e & 7), __shfl(kc, (e >> 3) & 7), h, l);
-        *reinterpret_cast<u32x4_t *>(lds + e * 64 + r4) = u32x4_t{h, h, h, h};
       }
+      if (two_tables<KB, VB>()) *reinterpret_cast<u32x4_t *>(lds + e * 64 + r4) = u32x4_t{h, h, h, h};
       *reinterpret_cast<u32x4_t *>(lds + e * 64 + 32 + r4) = u32x4_t{l, l, l, l};
     }
   }
@@ -1458,41 +1506,41 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
 
 }  // namespace
 
-template <int KB, int GP, bool SC, bool SP>
+template <int KB, int VB, int GP, bool SC, bool SP>
 void launch_sp(const DecodeParams &p, dim3 grid, hipStream_t stream) {
   if (p.pg.table) {
-    hipLaunchKernelGGL((decode_mfma_kernel<KB, GP, true, SC, SP>), grid, dim3(64 * waves_of<KB>()), 0, stream, p);
+    hipLaunchKernelGGL((decode_mfma_kernel<KB, VB, GP, true, SC, SP>), grid, dim3(64 * waves_of<KB>()), 0, stream, p);
   } else {
-    hipLaunchKernelGGL((decode_mfma_kernel<KB, GP, false, SC, SP>), grid, dim3(64 * waves_of<KB>()), 0, stream, p);
+    hipLaunchKernelGGL((decode_mfma_kernel<KB, VB, GP, false, SC, SP>), grid, dim3(64 * waves_of<KB>()), 0, stream, p);
   }
 }
 
 // SP: sparse-V (a threshold is set); the exact decode compiles it out
-template <int KB, int GP, bool SC>
+template <int KB, int VB, int GP, bool SC>
 void launch_sc(const DecodeParams &p, dim3 grid, hipStream_t stream) {
   if (p.sparse_lg != -INFINITY) {
-    launch_sp<KB, GP, SC, true>(p, grid, stream);
+    launch_sp<KB, VB, GP, SC, true>(p, grid, stream);
   } else {
-    launch_sp<KB, GP, SC, false>(p, grid, stream);
+    launch_sp<KB, VB, GP, SC, false>(p, grid, stream);
   }
 }
 
-template <int KB, int GP>
+template <int KB, int VB, int GP>
 void launch_gp(const DecodeParams &p, dim3 grid, hipStream_t stream) {
   if (p.scores) {
-    launch_sc<KB, GP, true>(p, grid, stream);
+    launch_sc<KB, VB, GP, true>(p, grid, stream);
   } else {
-    launch_sc<KB, GP, false>(p, grid, stream);
+    launch_sc<KB, VB, GP, false>(p, grid, stream);
   }
 }
 
-template <int KB>
+template <int KB, int VB>
 void launch_kb(const DecodeParams &p, dim3 grid, hipStream_t stream) {
   const int G = p.q_heads / p.kv_heads;
   if (G <= 4) {
-    launch_gp<KB, 4>(p, grid, stream);
+    launch_gp<KB, VB, 4>(p, grid, stream);
   } else {
-    launch_gp<KB, 8>(p, grid, stream);
+    launch_gp<KB, VB, 8>(p, grid, stream);
   }
 }
 
@@ -1506,11 +1554,21 @@ hipError_t launch_decode_mfma(const DecodeParams &p, hipStream_t stream) {
   // every split starts on the chunk grid (a paged chunk lies in one block)
   if (p.cold_split_len < 1 || p.cold_split_len % kChunk) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(p.batch * p.kv_heads * nsplit));
-  switch (kb) {
-    case 0: launch_kb<0>(p, grid, stream); break;
-    case 3: launch_kb<3>(p, grid, stream); break;
-    case 4: launch_kb<4>(p, grid, stream); break;
-    case kInt8: launch_kb<kInt8>(p, grid, stream); break;
+  if (kb == kInt8) {
+    launch_kb<kInt8, kInt8>(p, grid, stream);
+    return hipGetLastError();
+  }
+  // packed or delegated V at 3 or 4 bits; 4-bit K beside 4-bit V reads the
+  // V table for its hi half, so it needs the same codebook
+  const int vb = p.v.bits;
+  if ((vb != 3 && vb != 4) || (kb == 4 && vb == 4 && !p.share_lut)) return hipErrorInvalidValue;
+  switch (kb * 16 + vb) {
+    case 3: launch_kb<0, 3>(p, grid, stream); break;
+    case 4: launch_kb<0, 4>(p, grid, stream); break;
+    case 3 * 16 + 3: launch_kb<3, 3>(p, grid, stream); break;
+    case 3 * 16 + 4: launch_kb<3, 4>(p, grid, stream); break;
+    case 4 * 16 + 3: launch_kb<4, 3>(p, grid, stream); break;
+    case 4 * 16 + 4: launch_kb<4, 4>(p, grid, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

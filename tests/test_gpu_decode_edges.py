@@ -9,7 +9,8 @@ oracle's float64 attention over the rows it rebuilds from what the GPU wrote:
   head's weight can fall on rows whose value norm is far below the largest
   one seen;
 * large logits (a peaked softmax);
-* the same rows in INT8 caches (both sides).
+* the same rows in INT8 caches (both sides), and with 3-bit V codes (beside
+  fp16 K and beside 3-bit K).
 
 The tolerance is the parity tests' own: per row, ||x - ref||_inf <= 2e-3
 ||ref||_inf, for the scaled logits and for the outputs.
@@ -114,12 +115,17 @@ def _case(name):
         ks, vs = ("fp16", 0), ("delegated", 4)
     if name.endswith("_int8"):
         ks, vs = ("int8", 0), ("int8", 0)
+    if name.endswith("_asym3"):
+        ks, vs = ("fp16", 0), ("packed", 3)
+    if name.endswith("_k3v3"):
+        ks, vs = ("packed", 3), ("packed", 3)
     return k.astype(np.float16), v.astype(np.float16), q.astype(np.float16), ks, vs
 
 
 CASES = ["zero_rows", "zero_rows_asym", "fp16_max", "fp16_max_asym", "norm_decades", "norm_decades_asym",
          "norm_decades_delegated", "norm_decades_shared", "large_logits", "large_logits_asym",
-         "zero_rows_int8", "fp16_max_int8", "norm_decades_int8", "large_logits_int8"]
+         "zero_rows_int8", "fp16_max_int8", "norm_decades_int8", "large_logits_int8",
+         "zero_rows_k3v3", "fp16_max_asym3", "norm_decades_asym3", "large_logits_k3v3"]
 
 
 @pytest.mark.parametrize("name", CASES)

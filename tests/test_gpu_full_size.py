@@ -41,6 +41,8 @@ FULL = {
     "c5_delegated_64k": (16, 4, 32, 128, 65536, ("fp16", 0), ("delegated", 4), 256, "channel", 0.0, 0),
     # the pages' int8 mode at the asymmetric shape (a comparison workload)
     "c3_int8_16k": (8, 8, 32, 128, 16384, ("int8", 0), ("int8", 0), 0, "channel", 0.01, 1),
+    # the pages' turbo3-asym mode (fp16 K, 3-bit V) at the same shape
+    "c3_turbo3_asym_16k": (8, 8, 32, 128, 16384, ("fp16", 0), ("packed", 3), 0, "channel", 0.01, 1),
 }
 
 

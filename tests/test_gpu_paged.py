@@ -31,6 +31,8 @@ CASES = [
     ("delegated_d128", 2, 2, 16, 128, 64, S("fp16", 0), S("delegated", 4, 64)),
     ("tq35_d64", 1, 2, 4, 64, 32, S("packed", 3), S("packed", 4)),
     ("fp16v_d128", 1, 2, 8, 128, 32, S("packed", 3), S("fp16", 0)),
+    ("asym3_d128", 2, 2, 8, 128, 64, S("fp16", 0), S("packed", 3)),
+    ("k3v3_d128", 1, 2, 8, 128, 32, S("packed", 3), S("packed", 3)),
 ]
 CAP = 640
 APPENDS = [(0, 300), (300, 1), (301, 216)]   # (offset, rows)

@@ -247,6 +247,15 @@ DECODE_CASES = [
     # head layouts (three of four, five of eight)
     ("int8_g3", 1, 2, 6, 128, 700, ("int8", 0), ("int8", 0), "iid"),
     ("int8_g5", 1, 1, 5, 128, 500, ("int8", 0), ("int8", 0), "channel"),
+    # 3-bit V on the matrix-core kernel: fp16 K (the turbo3-asym mode), 3-bit
+    # K (3.0 bits), 4-bit K beside it (K tables of their own), a delegated
+    # 3-bit cold tail, eight and five heads a group
+    ("asym3_d128", 2, 2, 8, 128, 1337, ("fp16", 0), ("packed", 3), "channel"),
+    ("asym3_d128_iid", 1, 8, 32, 128, 1500, ("fp16", 0), ("packed", 3), "iid"),
+    ("k3v3_d128", 2, 2, 8, 128, 2100, ("packed", 3), ("packed", 3), "iid"),
+    ("k4v3_d128", 1, 2, 16, 128, 900, ("packed", 4), ("packed", 3), "channel"),
+    ("delegated3", 2, 2, 16, 128, 900, ("fp16", 0), ("delegated", 3), "channel"),
+    ("k3v3_g5", 1, 1, 5, 128, 500, ("packed", 3), ("packed", 3), "channel"),
 ]
 
 
@@ -292,7 +301,7 @@ def test_decode_attention(case, variant):
     assert ok, f"out: worst {worst}"
 
 
-SPLIT_CASES = DECODE_CASES[1:5] + [c for c in DECODE_CASES if c[0] == "int8_d128"]
+SPLIT_CASES = DECODE_CASES[1:5] + [c for c in DECODE_CASES if c[0] in ("int8_d128", "asym3_d128", "k3v3_d128")]
 
 
 @pytest.mark.parametrize("case", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])

@@ -25,6 +25,7 @@ CASES = [
     ("asym", S("fp16", 0), S("packed", 4)),
     ("delegated", S("fp16", 0), S("delegated", 4, 128)),
     ("int8", S("int8", 0), S("int8", 0)),
+    ("asym3", S("fp16", 0), S("packed", 3)),
 ]
 
 
