@@ -48,6 +48,11 @@ WORKLOADS = {
     "c3_turbo3_asym_16k": dict(batch=8, kv_heads=8, q_heads=32, head_dim=128, tokens=16384, layers=36,
                                k=("fp16", 0), v=("packed", 3), prefill=0, append=1, dist="channel",
                                outlier_frac=0.01),
+    # 2.5 bits (2-bit K, 3-bit V: the lower end of the pages' 2-4 bit range)
+    # at the 32K shape
+    "c4_tq25_32k": dict(batch=4, kv_heads=8, q_heads=32, head_dim=128, tokens=32768, layers=36,
+                        k=("packed", 2), v=("packed", 3), prefill=8192, dist="channel",
+                        outlier_frac=0.01),
     # the 32K workload with a peaked softmax (heavy-hitter keys at the first
     # 4 positions of every 512; the sparse-V comparison)
     "c4_tq35_32k_peaked": dict(batch=4, kv_heads=8, q_heads=32, head_dim=128, tokens=32768, layers=36,

@@ -135,11 +135,13 @@ bool decode_mfma_supported(const tq::DecodeParams &p) {
   const int G = p.q_heads / p.kv_heads;
   if (p.head_dim != 128 || G > 8) return false;
   if (p.k.mode == TQ_SIDE_INT8 || p.v.mode == TQ_SIDE_INT8) return p.k.mode == p.v.mode;  // INT8 on both sides
-  if (!(p.v.mode == TQ_SIDE_PACKED || p.v.mode == TQ_SIDE_DELEGATED) || (p.v.bits != 3 && p.v.bits != 4)) return false;
+  if (!(p.v.mode == TQ_SIDE_PACKED || p.v.mode == TQ_SIDE_DELEGATED) || p.v.bits < 2 || p.v.bits > 4) return false;
   if (p.k.mode == TQ_SIDE_FP16) return true;
   if (p.k.mode != TQ_SIDE_PACKED || p.v.mode != TQ_SIDE_PACKED) return false;
-  // 4-bit K beside 4-bit V shares V's codebook table
-  return p.k.bits == 3 || (p.k.bits == 4 && (p.v.bits == 3 || p.share_lut));
+  // the floor/ceil splits of 2 to 4 bits, and 4-bit K beside 3-bit V; 4-bit
+  // K beside 4-bit V shares V's codebook table
+  const int kb = p.k.bits, vb = p.v.bits;
+  return (kb == 2 && vb <= 3) || (kb == 3 && vb >= 3) || (kb == 4 && (vb == 3 || (vb == 4 && p.share_lut)));
 }
 
 Variant pick_variant(const tq::DecodeParams &p) {

@@ -5,8 +5,8 @@
 // "TurboQuant KV cache", "Available modes": fp16 K with TurboQuant V and the
 // delegated hot/cold V split).
 //
-// head_dim 128, 3- or 4-bit V codes, K packed (3 or 4 bits) or fp16, up to 8
-// query heads per KV head (and INT8 on both sides).  Grid = (B * Hkv units) x splits, about one block per
+// head_dim 128, V codes of 2 to 4 bits, K packed (2 to 4 bits) or fp16, up
+// to 8 query heads per KV head (and INT8 on both sides).  Grid = (B * Hkv units) x splits, about one block per
 // compute unit (12 waves for packed K, 8 for fp16 K).  A block issues its first
 // loads, builds its lookup tables and rotated query while they are in
 // flight, then each wave walks its share of the split in chunks of 32
@@ -60,14 +60,14 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int D = 128;
-// KB selects the K storage: 3 or 4 (packed codes, rotated domain), 0 (fp16
-// rows), kInt8 (INT8 absmax: one signed byte a coordinate and a float scale
-// a row, on both sides; original domain, no codebook).
+// KB selects the K storage: 2, 3 or 4 (packed codes, rotated domain), 0
+// (fp16 rows), kInt8 (INT8 absmax: one signed byte a coordinate and a float
+// scale a row, on both sides; original domain, no codebook).
 constexpr int kInt8 = 8;
 template <int KB>
-constexpr bool rotated_k() { return KB == 3 || KB == 4; }
-// VB selects the packed V storage: 3 or 4 bits a code (kInt8 with INT8 K:
-// INT8 bytes).  V bytes a row:
+constexpr bool rotated_k() { return KB == 2 || KB == 3 || KB == 4; }
+// VB selects the packed V storage: 2, 3 or 4 bits a code (kInt8 with INT8
+// K: INT8 bytes).  V bytes a row:
 template <int VB>
 constexpr int v_row_bytes() { return D * VB / 8; }
 // Waves per block: 12 for packed K (about 160 registers a lane, so three
@@ -97,14 +97,17 @@ constexpr float kVscaleMax = 1099511627776.0f;  // 2^40: start and ceiling of th
 //               from a byte of the code stream shifted by 0, 6, 12, ...);
 //               V hi in the first half of entries 256..511
 //   KB = 4, VB = 3   as KB = 3, with 4-bit K pairs (a whole byte)
-// A 3-bit V table is indexed the same way: low 6 bits = the codes of two
-// positions at one coordinate, the top 2 bits ignored.
+//   KB = 2      as KB = 3, indexed by a byte whose low 4 bits hold a pair of
+//               2-bit codes (the top 4 bits ignored: nibble n of a word is
+//               byte n / 2 of the word, or of the word shifted right by 4)
+// 3- and 2-bit V tables are indexed the same way: the low 6 or 4 bits hold
+// the codes of two positions at one coordinate, the rest is ignored.
 // After the main loop the table area is reused for the merges.
 constexpr int kTableWords = 256 * 64;  // one 256-entry region (64 KB)
 // K hi / K lo in the first region and V in the second whenever K's pairs
-// need tables of their own: 3-bit K, and 4-bit K beside 3-bit V
+// need tables of their own: 2- and 3-bit K, and 4-bit K beside 3-bit V
 template <int KB, int VB>
-constexpr bool two_tables() { return KB == 3 || (KB == 4 && VB == 3); }
+constexpr bool two_tables() { return KB == 2 || KB == 3 || (KB == 4 && VB == 3); }
 template <int KB, int VB>
 constexpr int table_words() { return two_tables<KB, VB>() ? 2 * kTableWords : kTableWords; }
 template <int KB, int VB>
@@ -306,14 +309,15 @@ __device__ __forceinline__ float xor_butterfly(float x, int lane) {
 // Global-memory data of one chunk of 32 positions for one lane.
 template <int KB, int VB, int GP>
 struct ChunkData {
-  static constexpr int kw = KB == 0 ? 16 : (KB == kInt8 ? 8 : (KB == 4 ? 4 : 3));  // K dwords per M-tile
-  static constexpr int kvw = VB == 4 ? 8 : 16;                 // V dwords
+  static constexpr int kw = KB == 0 ? 16 : (KB == kInt8 ? 8 : KB);  // K dwords per M-tile
+  static constexpr int kvw = (VB == 4 || VB == 2) ? 8 : 16;    // V dwords
   static constexpr int nv = GP / 2;                            // compact values per lane
   uint32_t k[2][kw];   // K words (packed), fp16 or INT8 row piece, M-tiles 0 and 1
   float kn[nv];        // K norms (INT8: scales) of the lane's compact positions
-  uint32_t v[kvw];     // V: code word `col` (3-bit: the two dwords holding the
-                       // 24 bits of coordinates 8 col .. 8 col + 7; INT8: bytes
-                       // 8 col .. 8 col + 7) of the 8 positions of this lane group
+  uint32_t v[kvw];     // V: code word `col` (2-bit: the dword holding the 16 bits
+                       // of coordinates 8 col .. 8 col + 7; 3-bit: the two dwords
+                       // holding their 24 bits; INT8: bytes 8 col .. 8 col + 7)
+                       // of the 8 positions of this lane group
   float vn[nv];        // V norms (INT8: scales) of the compact positions
   bool vskip;          // sparse-V: the V codes were not loaded (predicted skippable)
 };
@@ -331,14 +335,15 @@ struct ChunkData {
 template <int KB, int VB, int GP, bool PG>
 struct Wave {
   static constexpr int NV = GP / 2;
-  static constexpr int kRowBytes = KB == 0 ? 2 * D : (KB == kInt8 ? D : (KB == 4 ? 64 : 48));
+  static constexpr int kRowBytes = KB == 0 ? 2 * D : (KB == kInt8 ? D : D * KB / 8);
   static constexpr int kVRow = v_row_bytes<VB>();
   // per-lane constants
   int col, grp, cpos;   // cpos: chunk position of the lane's first compact slot
   uint32_t rep4;        // 4 r: the lane's replica
   uint32_t rep4v;       // 4 r + the V table's byte offset
   uint32_t koff, knoff, voff;   // lane byte offsets inside a chunk
-  uint32_t vsh;         // 3-bit V: bit offset of the lane's 24 bits in its first dword
+  uint32_t vsh;         // 3-bit V: bit offset of the lane's 24 bits in its first
+                        // dword; 2-bit V: v_perm selector of its 16 bits
   bool vlast;           // 3-bit V: lane column 15, whose bits all lie in its second dword
   const uint32_t *lds;
   uint32_t bmax_at;     // sparse-V: LDS byte address of the exchanged maxima [8 heads][16 waves]
@@ -425,6 +430,9 @@ struct Wave {
         typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
         const u32x3_t w = __builtin_amdgcn_raw_buffer_load_b96(rk, koff + mo, 0, 0);
         c.k[m][0] = w[0]; c.k[m][1] = w[1]; c.k[m][2] = w[2];
+      } else if (KB == 2) {
+        const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(rk, koff + mo, 0, 0);
+        c.k[m][0] = w[0]; c.k[m][1] = w[1];
       } else {
 #pragma unroll
         for (int i = 0; i < ChunkData<KB, VB, GP>::kw; i += 4) {
@@ -453,14 +461,14 @@ struct Wave {
     load_v(rv, c.v);
   }
 
-  // The V data of the lane's 8 position slots: one code word, (3-bit) the
-  // two dwords holding the 24 bits of coordinates 8 col .. 8 col + 7, or
-  // (INT8) the 8 bytes of those coordinates.
+  // The V data of the lane's 8 position slots: one code word, (2-bit) the
+  // dword holding the 16 bits of coordinates 8 col .. 8 col + 7, (3-bit) the
+  // two dwords holding their 24 bits, or (INT8) their 8 bytes.
   __device__ __forceinline__ void load_v(__amdgpu_buffer_rsrc_t rv, uint32_t (&v)[ChunkData<KB, VB, GP>::kvw]) const {
 #pragma unroll
     for (int s8 = 0; s8 < 8; ++s8) {
       const uint32_t off = voff + (16 * (s8 >> 2) + (s8 & 3)) * kVRow;
-      if (VB != 4) {
+      if (VB == 3 || VB == kInt8) {
         const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(rv, off, 0, 0);
         v[2 * s8] = w[0];
         v[2 * s8 + 1] = w[1];
@@ -490,6 +498,29 @@ struct Wave {
           const half8_t a = as_half8(i8_pair_exact<0>(w0), i8_pair_exact<2>(w0), i8_pair_exact<0>(w1),
                                      i8_pair_exact<2>(w1));
           acc = mma(a, bq[q], acc);
+        }
+      } else if (KB == 2) {
+        // the lane's 32 coordinates are 64 bits; step q takes coordinates
+        // 8 q .. 8 q + 7, the four nibbles (code pairs) 4 (q & 1) .. + 3 of
+        // word q / 2, each the low nibble of a byte of the word or of the
+        // word shifted right by 4
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t w = c.k[m][q >> 1], ws = w >> 4;
+          uint32_t ad[4];
+          if (q & 1) {
+            ad[0] = baddr<2>(w, rep4); ad[1] = baddr<2>(ws, rep4);
+            ad[2] = baddr<3>(w, rep4); ad[3] = baddr<3>(ws, rep4);
+          } else {
+            ad[0] = baddr<0>(w, rep4); ad[1] = baddr<0>(ws, rep4);
+            ad[2] = baddr<1>(w, rep4); ad[3] = baddr<1>(ws, rep4);
+          }
+          const half8_t ah = as_half8(lds_at<0>(lds, ad[0]), lds_at<0>(lds, ad[1]), lds_at<0>(lds, ad[2]),
+                                      lds_at<0>(lds, ad[3]));
+          const half8_t al = as_half8(lds_at_sep<kKloOff>(lds, ad[0]), lds_at_sep<kKloOff>(lds, ad[1]),
+                                      lds_at_sep<kKloOff>(lds, ad[2]), lds_at_sep<kKloOff>(lds, ad[3]));
+          acc = mma(ah, bq[q], acc);
+          acc = mma(al, bq[q], acc);
         }
       } else if (KB == 3) {
         // byte addresses of the 16 code pairs of the lane's 32 coordinates:
@@ -732,6 +763,43 @@ struct Wave {
             case 2: a4[u] = i8_cross_pair<2>(a, b); break;
             default: a4[u] = i8_cross_pair<3>(a, b); break;
           }
+        }
+        accv[q] = mma(ap, as_half8(a4[0], a4[1], a4[2], a4[3]), accv[q]);
+      }
+      return;
+    }
+    if (VB == 2) {
+      // 2-bit codes: per slot pair, the 4-bit pairs (slot 2 s2 low) of the
+      // even coordinates of both 16-bit halves of the words (ev) and of the
+      // odd ones (od); the lane's half of each goes into one word (even
+      // coordinates in bytes 0, 1, odd in bytes 2, 3), where coordinate
+      // 8 col + q is nibble q / 2 (q even) or 4 + q / 2 (q odd): the low
+      // nibble of a byte of the word, or of the word shifted right by 4
+      uint32_t pw[4], ps[4];
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) {
+        const uint32_t x0 = cv[2 * s2], x1 = cv[2 * s2 + 1];
+        const uint32_t ev = bfi(0x33333333u, x0, x1 << 2), od = bfi(0x33333333u, x0 >> 2, x1);
+        pw[s2] = __builtin_amdgcn_perm(od, ev, vsh);
+        ps[s2] = pw[s2] >> 4;
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        // nibble n = q / 2 + 4 (q & 1): byte n / 2 of pw (n even) or ps (n odd)
+        const int n = (q >> 1) + 4 * (q & 1);
+        const uint32_t *src = (n & 1) ? ps : pw;
+        uint32_t a4[4];
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+          const uint32_t w = src[s2];
+          uint32_t ad;
+          switch (n >> 1) {
+            case 0: ad = two_tables<KB, VB>() ? baddr_hi<0>(w, rep4v) : baddr<0>(w, rep4); break;
+            case 1: ad = two_tables<KB, VB>() ? baddr_hi<1>(w, rep4v) : baddr<1>(w, rep4); break;
+            case 2: ad = two_tables<KB, VB>() ? baddr_hi<2>(w, rep4v) : baddr<2>(w, rep4); break;
+            default: ad = two_tables<KB, VB>() ? baddr_hi<3>(w, rep4v) : baddr<3>(w, rep4); break;
+          }
+          a4[s2] = lds_at<0>(lds, ad);
         }
         accv[q] = mma(ap, as_half8(a4[0], a4[1], a4[2], a4[3]), accv[q]);
       }
@@ -1101,9 +1169,11 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   // 3-bit V: the lane's 24 bits start at byte 3 col of the row, in dword
   // 3 col / 4 at bit 8 (3 col % 4); lane 15 reads dwords 10 and 11 (the
   // row's last two) and takes its bits from the second
+  // 2-bit V: its 16 bits are half h = col % 2 of dword col / 2, picked
+  // after the pairing by a v_perm selector (bytes 2 h, 2 h + 1 of each word)
   W.voff = static_cast<uint32_t>(W.grp * 4 * kVRow +
-                                 (VB == 3 ? 4 * min(3 * W.col / 4, 10) : W.col * (kVRow / 16)));
-  W.vsh = 8u * ((3u * W.col) & 3u);
+                                 (VB == 3 ? 4 * min(3 * W.col / 4, 10) : VB == 2 ? 4 * (W.col / 2) : W.col * (kVRow / 16)));
+  W.vsh = VB == 2 ? ((W.col & 1) ? 0x07060302u : 0x05040100u) : 8u * ((3u * W.col) & 3u);
   W.vlast = W.col == 15;
   W.capacity = p.capacity;
   W.hot_len = p.v.hot > 0 ? p.v.hot : 1;
@@ -1145,15 +1215,18 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   constexpr int kVWord = v_table_byte<KB, VB>() / 4;
   for (int i = threadIdx.x; KB != kInt8 && i < 256 * (kRep / 4); i += kThreads) {
     const int e = i >> 3, r4 = 4 * (i & 7);
-    const uint32_t w = VB == 4 ? pack_half2(__shfl(vc, e & 15), __shfl(vc, e >> 4))
-                               : pack_half2(__shfl(vc, e & 7), __shfl(vc, (e >> 3) & 7));
+    const uint32_t w = VB == 4   ? pack_half2(__shfl(vc, e & 15), __shfl(vc, e >> 4))
+                       : VB == 3 ? pack_half2(__shfl(vc, e & 7), __shfl(vc, (e >> 3) & 7))
+                                 : pack_half2(__shfl(vc, e & 3), __shfl(vc, (e >> 2) & 3));
     *reinterpret_cast<u32x4_t *>(lds + kVWord + e * 64 + r4) = u32x4_t{w, w, w, w};
     if (KB) {
       uint32_t h, l;
       if (KB == 4) {
         split_pair(__shfl(kc, e & 15), __shfl(kc, e >> 4), h, l);
-      } else {
+      } else if (KB == 3) {
         split_pair(__shfl(kc, e & 7), __shfl(kc, (e >> 3) & 7), h, l);
+      } else {
+        split_pair(__shfl(kc, e & 3), __shfl(kc, (e >> 2) & 3), h, l);
       }
       if (two_tables<KB, VB>()) *reinterpret_cast<u32x4_t *>(lds + e * 64 + r4) = u32x4_t{h, h, h, h};
       *reinterpret_cast<u32x4_t *>(lds + e * 64 + 32 + r4) = u32x4_t{l, l, l, l};
@@ -1558,13 +1631,16 @@ hipError_t launch_decode_mfma(const DecodeParams &p, hipStream_t stream) {
     launch_kb<kInt8, kInt8>(p, grid, stream);
     return hipGetLastError();
   }
-  // packed or delegated V at 3 or 4 bits; 4-bit K beside 4-bit V reads the
-  // V table for its hi half, so it needs the same codebook
+  // packed or delegated V at 2, 3 or 4 bits; 4-bit K beside 4-bit V reads
+  // the V table for its hi half, so it needs the same codebook
   const int vb = p.v.bits;
-  if ((vb != 3 && vb != 4) || (kb == 4 && vb == 4 && !p.share_lut)) return hipErrorInvalidValue;
+  if (kb == 4 && vb == 4 && !p.share_lut) return hipErrorInvalidValue;
   switch (kb * 16 + vb) {
+    case 2: launch_kb<0, 2>(p, grid, stream); break;
     case 3: launch_kb<0, 3>(p, grid, stream); break;
     case 4: launch_kb<0, 4>(p, grid, stream); break;
+    case 2 * 16 + 2: launch_kb<2, 2>(p, grid, stream); break;
+    case 2 * 16 + 3: launch_kb<2, 3>(p, grid, stream); break;
     case 3 * 16 + 3: launch_kb<3, 3>(p, grid, stream); break;
     case 3 * 16 + 4: launch_kb<3, 4>(p, grid, stream); break;
     case 4 * 16 + 3: launch_kb<4, 3>(p, grid, stream); break;

@@ -165,11 +165,10 @@ static_assert(kScratchBytes == TQ_NOALLOC_SCRATCH_BYTES, "tq.h states the scratc
 hipError_t scratch_workspace(hipStream_t stream, void **ptr);
 hipError_t launch_decode_ref(const DecodeParams &p, hipStream_t stream);
 // The matrix-core decode takes head_dim 128, up to 8 query heads per KV
-// head, and either INT8 on both sides or a packed or delegated V of 3 or 4
-// bits with K as fp16, or packed K (V packed too) of 3 bits, or of 4 bits
-// (beside 4-bit V only with V's codebook); at most kMfmaMaxSplits context
-// splits per (batch, KV head) unit, each a multiple of kMfmaChunk positions
-// long.
+// head, and either INT8 on both sides, or a packed or delegated V of 2 to 4
+// bits with fp16 K, or packed K and V as 2/2, 2/3, 3/3, 3/4, 4/3 bits, or
+// 4/4 with one codebook; at most kMfmaMaxSplits context splits per (batch,
+// KV head) unit, each a multiple of kMfmaChunk positions long.
 // (The host picks it by this rule; the launcher checks it again.)
 hipError_t launch_decode_mfma(const DecodeParams &p, hipStream_t stream);
 constexpr int kMfmaMaxSplits = 256;

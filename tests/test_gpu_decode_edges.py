@@ -9,8 +9,8 @@ oracle's float64 attention over the rows it rebuilds from what the GPU wrote:
   head's weight can fall on rows whose value norm is far below the largest
   one seen;
 * large logits (a peaked softmax);
-* the same rows in INT8 caches (both sides), and with 3-bit V codes (beside
-  fp16 K and beside 3-bit K).
+* the same rows in INT8 caches (both sides), and with 3- and 2-bit codes
+  (3-bit V beside fp16 K and beside 3-bit K; 2-bit K beside 2- and 3-bit V).
 
 The tolerance is the parity tests' own: per row, ||x - ref||_inf <= 2e-3
 ||ref||_inf, for the scaled logits and for the outputs.
@@ -119,13 +119,18 @@ def _case(name):
         ks, vs = ("fp16", 0), ("packed", 3)
     if name.endswith("_k3v3"):
         ks, vs = ("packed", 3), ("packed", 3)
+    if name.endswith("_k2v2"):
+        ks, vs = ("packed", 2), ("packed", 2)
+    if name.endswith("_k2v3"):
+        ks, vs = ("packed", 2), ("packed", 3)
     return k.astype(np.float16), v.astype(np.float16), q.astype(np.float16), ks, vs
 
 
 CASES = ["zero_rows", "zero_rows_asym", "fp16_max", "fp16_max_asym", "norm_decades", "norm_decades_asym",
          "norm_decades_delegated", "norm_decades_shared", "large_logits", "large_logits_asym",
          "zero_rows_int8", "fp16_max_int8", "norm_decades_int8", "large_logits_int8",
-         "zero_rows_k3v3", "fp16_max_asym3", "norm_decades_asym3", "large_logits_k3v3"]
+         "zero_rows_k3v3", "fp16_max_asym3", "norm_decades_asym3", "large_logits_k3v3",
+         "zero_rows_k2v2", "fp16_max_k2v3", "norm_decades_k2v2", "large_logits_k2v3"]
 
 
 @pytest.mark.parametrize("name", CASES)

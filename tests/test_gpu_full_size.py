@@ -43,6 +43,8 @@ FULL = {
     "c3_int8_16k": (8, 8, 32, 128, 16384, ("int8", 0), ("int8", 0), 0, "channel", 0.01, 1),
     # the pages' turbo3-asym mode (fp16 K, 3-bit V) at the same shape
     "c3_turbo3_asym_16k": (8, 8, 32, 128, 16384, ("fp16", 0), ("packed", 3), 0, "channel", 0.01, 1),
+    # 2.5 bits (2-bit K, 3-bit V) at the 32K shape
+    "c4_tq25_32k": (4, 8, 32, 128, 32768, ("packed", 2), ("packed", 3), 0, "channel", 0.01, 8192),
 }
 
 

@@ -33,6 +33,8 @@ CASES = [
     ("fp16v_d128", 1, 2, 8, 128, 32, S("packed", 3), S("fp16", 0)),
     ("asym3_d128", 2, 2, 8, 128, 64, S("fp16", 0), S("packed", 3)),
     ("k3v3_d128", 1, 2, 8, 128, 32, S("packed", 3), S("packed", 3)),
+    ("k2v3_d128", 2, 2, 8, 128, 32, S("packed", 2), S("packed", 3)),
+    ("asym2_d128", 1, 2, 8, 128, 64, S("fp16", 0), S("packed", 2)),
 ]
 CAP = 640
 APPENDS = [(0, 300), (300, 1), (301, 216)]   # (offset, rows)

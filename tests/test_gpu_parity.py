@@ -256,6 +256,14 @@ DECODE_CASES = [
     ("k4v3_d128", 1, 2, 16, 128, 900, ("packed", 4), ("packed", 3), "channel"),
     ("delegated3", 2, 2, 16, 128, 900, ("fp16", 0), ("delegated", 3), "channel"),
     ("k3v3_g5", 1, 1, 5, 128, 500, ("packed", 3), ("packed", 3), "channel"),
+    # 2-bit codes on the matrix-core kernel: 2.5 bits (2-bit K, 3-bit V),
+    # 2.0 bits, fp16 K beside 2-bit V, a delegated 2-bit cold tail, three
+    # heads a group
+    ("k2v3_d128", 2, 2, 8, 128, 1337, ("packed", 2), ("packed", 3), "iid"),
+    ("k2v2_d128", 1, 8, 32, 128, 1500, ("packed", 2), ("packed", 2), "channel"),
+    ("asym2_d128", 1, 2, 16, 128, 900, ("fp16", 0), ("packed", 2), "iid"),
+    ("delegated2", 1, 2, 8, 128, 700, ("fp16", 0), ("delegated", 2), "channel"),
+    ("k2v2_g3", 1, 2, 6, 128, 613, ("packed", 2), ("packed", 2), "iid"),
 ]
 
 
@@ -301,7 +309,7 @@ def test_decode_attention(case, variant):
     assert ok, f"out: worst {worst}"
 
 
-SPLIT_CASES = DECODE_CASES[1:5] + [c for c in DECODE_CASES if c[0] in ("int8_d128", "asym3_d128", "k3v3_d128")]
+SPLIT_CASES = DECODE_CASES[1:5] + [c for c in DECODE_CASES if c[0] in ("int8_d128", "asym3_d128", "k3v3_d128", "k2v3_d128")]
 
 
 @pytest.mark.parametrize("case", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])

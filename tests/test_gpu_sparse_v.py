@@ -26,6 +26,7 @@ CASES = [
     ("delegated", S("fp16", 0), S("delegated", 4, 128)),
     ("int8", S("int8", 0), S("int8", 0)),
     ("asym3", S("fp16", 0), S("packed", 3)),
+    ("k2v3", S("packed", 2), S("packed", 3)),
 ]
 
 
