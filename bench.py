@@ -53,6 +53,11 @@ WORKLOADS = {
     "c4_tq25_32k": dict(batch=4, kv_heads=8, q_heads=32, head_dim=128, tokens=32768, layers=36,
                         k=("packed", 2), v=("packed", 3), prefill=8192, dist="channel",
                         outlier_frac=0.01),
+    # the 32K workload's widths with 16 query heads per KV head (64 query
+    # heads over 4 KV heads: head groups on the matrix cores)
+    "c4_tq35_32k_g16": dict(batch=4, kv_heads=4, q_heads=64, head_dim=128, tokens=32768, layers=36,
+                            k=("packed", 3), v=("packed", 4), prefill=8192, dist="channel",
+                            outlier_frac=0.01),
     # the 32K workload with a peaked softmax (heavy-hitter keys at the first
     # 4 positions of every 512; the sparse-V comparison)
     "c4_tq35_32k_peaked": dict(batch=4, kv_heads=8, q_heads=32, head_dim=128, tokens=32768, layers=36,

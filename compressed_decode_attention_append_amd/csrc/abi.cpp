@@ -133,7 +133,9 @@ enum Variant { kRef, kMfma };
 // The shapes the matrix-core decode takes (tq_common.h states the rule).
 bool decode_mfma_supported(const tq::DecodeParams &p) {
   const int G = p.q_heads / p.kv_heads;
-  if (p.head_dim != 128 || G > 8) return false;
+  if (p.head_dim != 128) return false;
+  // more than 8 query heads a KV head: head groups of 8, one counter each
+  if (static_cast<long>(p.batch) * p.kv_heads * ((G + 7) / 8) > tq::kMfmaMaxUnits) return false;
   if (p.k.mode == TQ_SIDE_INT8 || p.v.mode == TQ_SIDE_INT8) return p.k.mode == p.v.mode;  // INT8 on both sides
   if (!(p.v.mode == TQ_SIDE_PACKED || p.v.mode == TQ_SIDE_DELEGATED) || p.v.bits < 2 || p.v.bits > 4) return false;
   if (p.k.mode == TQ_SIDE_FP16) return true;
@@ -161,7 +163,7 @@ Variant pick_variant(const tq::DecodeParams &p) {
 // of its own.
 void mfma_splits(const tq_cache *c, int length, int n_splits, tq::DecodeParams *p) {
   constexpr int kTargetBlocks = 256, kMinPerBlock = 512, kQuantum = 256;
-  const int units = c->batch * c->kv_heads;
+  const int units = c->batch * c->kv_heads * ((p->q_heads / c->kv_heads + 7) / 8);
   const int cold = (c->v.mode == TQ_SIDE_DELEGATED) ? std::max(0, length - c->v.hot) : length;
   const int cap = tq::kMfmaMaxSplits;
   int ncold = 1, clen = tq::kMfmaChunk;

@@ -1115,7 +1115,13 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   // wave index as a scalar: everything derived from it (the wave's range of
   // positions, the buffer descriptors) then stays in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int G = p.q_heads / p.kv_heads;
+  // A query group of more than 8 heads runs as head groups of 8 (the last
+  // one possibly smaller): each is a unit of its own (its splits, partials
+  // and arrival counter) that reads its KV head's rows.  G is this block's
+  // head count, Gs the partial stride (8, or the whole group when smaller).
+  const int g_all = p.q_heads / p.kv_heads;
+  const int n_hg = (g_all + 7) / 8;
+  const int Gs = min(g_all, 8);
   // SC: the launch writes the scaled logits (parity runs); otherwise their
   // address arithmetic is compiled out
   float *const scores = SC ? p.scores : nullptr;
@@ -1126,11 +1132,14 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   float *slots = reinterpret_cast<float *>(lds + L::slots);
 
   const int nsplit = p.n_cold_splits;
-  const int unit = blockIdx.x / nsplit;
+  const int vunit = blockIdx.x / nsplit;  // (KV unit, head group)
   const int split = blockIdx.x % nsplit;
+  const int unit = vunit / n_hg;          // (batch, KV head)
+  const int hgrp = vunit % n_hg;
+  const int G = min(g_all - 8 * hgrp, 8);
   const int b = unit / p.kv_heads;
   const int kv = unit % p.kv_heads;
-  const long hq0 = static_cast<long>(b) * p.q_heads + static_cast<long>(kv) * G;
+  const long hq0 = static_cast<long>(b) * p.q_heads + static_cast<long>(kv) * g_all + 8 * hgrp;
   const int s0 = split * p.cold_split_len;
   const int s1 = min(p.cold_len, s0 + p.cold_split_len);
   const int span = max(0, s1 - s0);
@@ -1423,7 +1432,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   W.to_slot(slots + wave * GP * kPS, false);
   __syncthreads();
   float *part = reinterpret_cast<float *>(reinterpret_cast<char *>(p.ws) + p.ws_part_off);
-  float *mypart = part + (static_cast<long>(unit) * nsplit + split) * G * kPS;
+  float *mypart = part + (static_cast<long>(vunit) * nsplit + split) * Gs * kPS;
   if (threadIdx.x < G * (D / 4)) {
     // thread (h, j4): head h, values 4 j4 .. 4 j4 + 3, L2-coherent stores
     const int h = threadIdx.x / (D / 4), j4 = threadIdx.x % (D / 4);
@@ -1441,7 +1450,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    const unsigned old = __hip_atomic_fetch_add(p.counters + unit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned old = __hip_atomic_fetch_add(p.counters + vunit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *flag = (old == static_cast<unsigned>(nsplit - 1)) ? 1 : 0;
   }
   __syncthreads();
@@ -1480,7 +1489,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   // coordinates 4 j4 .. 4 j4 + 3; the 32 threads of a head sit in one wave,
   // so the inverse rotation needs no block barrier.
   if (threadIdx.x >= G * (D / 4)) return;
-  const float *up = part + static_cast<long>(unit) * nsplit * G * kPS;
+  const float *up = part + static_cast<long>(vunit) * nsplit * Gs * kPS;
   const int hh = threadIdx.x / (D / 4);
   const int jj = 4 * (threadIdx.x % (D / 4));
   float *orow = p.out + (hq0 + hh) * D + jj;
@@ -1488,14 +1497,14 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   float Lt = 0.0f;
   float M = -INFINITY;
   // partials of the unit, read past the non-coherent caches (sc1)
-  const auto rp = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(up), 0, nsplit * G * kPS * 4, 0x00020000);
+  const auto rp = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(up), 0, nsplit * Gs * kPS * 4, 0x00020000);
   constexpr int kB = 8;  // splits per batch of independent loads
   for (int sp0 = 0; sp0 < nsplit; sp0 += kB) {
     float mv[kB], lv[kB], ov[kB][4];
 #pragma unroll
     for (int k = 0; k < kB; ++k) {
       const int sp = min(sp0 + k, nsplit - 1);
-      const int base = ((sp * G + hh) * kPS) * 4;
+      const int base = ((sp * Gs + hh) * kPS) * 4;
       const u32x2_t ml = __builtin_amdgcn_raw_buffer_load_b64(rp, base, 0, kCoherentLoad);
       const u32x4_t o4 = __builtin_amdgcn_raw_buffer_load_b128(rp, base + (kPV + jj) * 4, 0, kCoherentLoad);
       mv[k] = (sp0 + k < nsplit) ? __uint_as_float(ml[0]) : -INFINITY;
@@ -1543,7 +1552,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
     o.z = r4[2] * 1024.0f * inv;
     o.w = r4[3] * 1024.0f * inv;
     *reinterpret_cast<float4 *>(orow) = o;
-    if (threadIdx.x == 0) __hip_atomic_store(p.counters + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) __hip_atomic_store(p.counters + vunit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
   // inverse rotation diag(s) H / sqrt(d): butterflies at strides 1 and 2
@@ -1574,7 +1583,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   o.z = (o.z + q4[2]) * inv;
   o.w = (o.w + q4[3]) * inv;
   *reinterpret_cast<float4 *>(orow) = o;
-  if (threadIdx.x == 0) __hip_atomic_store(p.counters + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) __hip_atomic_store(p.counters + vunit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace
@@ -1621,12 +1630,15 @@ hipError_t launch_decode_mfma(const DecodeParams &p, hipStream_t stream) {
   const int G = p.q_heads / p.kv_heads;
   const int kb = p.k.mode == TQ_SIDE_PACKED ? p.k.bits : (p.k.mode == TQ_SIDE_INT8 ? kInt8 : 0);
   if ((kb == kInt8) != (p.v.mode == TQ_SIDE_INT8)) return hipErrorInvalidValue;
-  if (G < 1 || G > 8 || p.head_dim != D) return hipErrorInvalidValue;
+  if (G < 1 || p.head_dim != D) return hipErrorInvalidValue;
+  // head groups of at most 8 query heads, each a unit with its own counter
+  const long vunits = static_cast<long>(p.batch) * p.kv_heads * ((G + 7) / 8);
+  if (vunits > kMfmaMaxUnits) return hipErrorInvalidValue;
   const int nsplit = p.n_cold_splits;
   if (nsplit < 1 || nsplit > kMaxSplits || p.n_hot_splits != 0) return hipErrorInvalidValue;
   // every split starts on the chunk grid (a paged chunk lies in one block)
   if (p.cold_split_len < 1 || p.cold_split_len % kChunk) return hipErrorInvalidValue;
-  const dim3 grid(static_cast<unsigned>(p.batch * p.kv_heads * nsplit));
+  const dim3 grid(static_cast<unsigned>(vunits * nsplit));
   if (kb == kInt8) {
     launch_kb<kInt8, kInt8>(p, grid, stream);
     return hipGetLastError();

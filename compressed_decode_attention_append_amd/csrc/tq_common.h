@@ -135,10 +135,13 @@ __host__ __device__ inline DecodeWorkspace decode_workspace_layout(int batch, in
 
 // Matrix-core variant's partials: [B*Hkv][splits][G][d + 2] floats holding
 // (max, sum, accumulator[d]) per query head.
+// A query group of G > 8 heads runs as ceil(G / 8) head groups of at most 8,
+// each with partials for 8 heads.
 inline size_t decode_mfma_workspace_bytes(int batch, int kv_heads, int q_heads, int splits,
                                           int head_dim) {
   const size_t G = size_t(q_heads / kv_heads);
-  return kCounterBytes + align256(size_t(batch) * kv_heads * splits * G * (head_dim + 4) * sizeof(float));
+  const size_t groups = (G + 7) / 8, per = G < 8 ? G : 8;
+  return kCounterBytes + align256(size_t(batch) * kv_heads * groups * splits * per * (head_dim + 4) * sizeof(float));
 }
 
 hipError_t launch_quantize_append(const QuantizeParams &p, hipStream_t stream);
@@ -164,14 +167,17 @@ constexpr size_t kScratchBytes = size_t(16) << 20;
 static_assert(kScratchBytes == TQ_NOALLOC_SCRATCH_BYTES, "tq.h states the scratch size");
 hipError_t scratch_workspace(hipStream_t stream, void **ptr);
 hipError_t launch_decode_ref(const DecodeParams &p, hipStream_t stream);
-// The matrix-core decode takes head_dim 128, up to 8 query heads per KV
-// head, and either INT8 on both sides, or a packed or delegated V of 2 to 4
-// bits with fp16 K, or packed K and V as 2/2, 2/3, 3/3, 3/4, 4/3 bits, or
-// 4/4 with one codebook; at most kMfmaMaxSplits context splits per (batch,
-// KV head) unit, each a multiple of kMfmaChunk positions long.
+// The matrix-core decode takes head_dim 128, any number of query heads per
+// KV head (more than 8 as head groups of at most 8, at most kMfmaMaxUnits
+// (batch, KV head, head group) units), and either INT8 on both sides, or a
+// packed or delegated V of 2 to 4 bits with fp16 K, or packed K and V as
+// 2/2, 2/3, 3/3, 3/4, 4/3 bits, or 4/4 with one codebook; at most
+// kMfmaMaxSplits context splits per unit, each a multiple of kMfmaChunk
+// positions long.
 // (The host picks it by this rule; the launcher checks it again.)
 hipError_t launch_decode_mfma(const DecodeParams &p, hipStream_t stream);
 constexpr int kMfmaMaxSplits = 256;
+constexpr long kMfmaMaxUnits = long(kCounterBytes / sizeof(unsigned));  // one arrival counter each
 constexpr int kMfmaChunk = 32;  // positions the matrix-core decode reads as one chunk
 
 }  // namespace tq

@@ -319,13 +319,28 @@ def test_int8_side_arguments():
     assert _qa(_desc(f, kmode=3, vmode=2), f, n=0) == tq.TQ_OK
 
 
+def test_decode_workspace_head_groups():
+    # the matrix-core kernel runs a query group of G > 8 heads as ceil(G / 8)
+    # head groups, each with partials for 8 heads per split; an explicit
+    # split count gives splits of a multiple of 32 positions
+    f = _Fake()
+    for Hkv, Hq, ns, splits in ((2, 96, 1, 1), (2, 96, 5, 5), (1, 12, 7, 7), (1, 8, 3, 3), (2, 4, 300, 32)):
+        c = _desc(f, d=128, B=1, H=Hkv, kb=3, vb=4)
+        got = tq.lib().tq_decode_workspace_bytes(ctypes.byref(c), Hq, 1000, ns)
+        G = Hq // Hkv
+        groups, per = (G + 7) // 8, min(G, 8)
+        want = 65536 * 4 + (Hkv * groups * splits * per * 132 * 4 + 255) // 256 * 256
+        assert got == want, (Hkv, Hq, ns, got, want)
+
+
 def test_decode_workspace_any_group_size():
     # the plain kernel takes any query group (eight heads a block, more
     # blocks per KV head beyond that) and any split count: the workspace is
     # the partials' size, counters first
     f = _Fake()
     for d, Hkv, Hq in ((256, 1, 256), (128, 2, 96), (32, 1, 3)):
-        c = _desc(f, d=d, B=1, H=Hkv, kb=2, vb=2)
+        # (5-bit sides: the matrix-core kernel takes 2 to 4 bits at d = 128)
+        c = _desc(f, d=d, B=1, H=Hkv, kb=5, vb=5)
         for ns in (0, 1, 5, 300):
             got = tq.lib().tq_decode_workspace_bytes(ctypes.byref(c), Hq, 1000, ns)
             assert got > 0, (d, Hq, ns)

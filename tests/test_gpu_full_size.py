@@ -45,6 +45,8 @@ FULL = {
     "c3_turbo3_asym_16k": (8, 8, 32, 128, 16384, ("fp16", 0), ("packed", 3), 0, "channel", 0.01, 1),
     # 2.5 bits (2-bit K, 3-bit V) at the 32K shape
     "c4_tq25_32k": (4, 8, 32, 128, 32768, ("packed", 2), ("packed", 3), 0, "channel", 0.01, 8192),
+    # 16 query heads per KV head (head groups) at the 32K shape
+    "c4_tq35_32k_g16": (4, 4, 64, 128, 32768, ("packed", 3), ("packed", 4), 0, "channel", 0.01, 8192),
 }
 
 

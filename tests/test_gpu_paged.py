@@ -35,6 +35,7 @@ CASES = [
     ("k3v3_d128", 1, 2, 8, 128, 32, S("packed", 3), S("packed", 3)),
     ("k2v3_d128", 2, 2, 8, 128, 32, S("packed", 2), S("packed", 3)),
     ("asym2_d128", 1, 2, 8, 128, 64, S("fp16", 0), S("packed", 2)),
+    ("g16_tq35_d128", 1, 2, 32, 128, 64, S("packed", 3), S("packed", 4)),
 ]
 CAP = 640
 APPENDS = [(0, 300), (300, 1), (301, 216)]   # (offset, rows)

@@ -264,6 +264,12 @@ DECODE_CASES = [
     ("asym2_d128", 1, 2, 16, 128, 900, ("fp16", 0), ("packed", 2), "iid"),
     ("delegated2", 1, 2, 8, 128, 700, ("fp16", 0), ("delegated", 2), "channel"),
     ("k2v2_g3", 1, 2, 6, 128, 613, ("packed", 2), ("packed", 2), "iid"),
+    # query groups above 8 heads on the matrix-core kernel (head groups of
+    # 8, the last one smaller for 12, 20 and 24)
+    ("g16_tq35", 2, 2, 32, 128, 1500, ("packed", 3), ("packed", 4), "channel"),
+    ("g16_asym_iid", 1, 4, 64, 128, 1337, ("fp16", 0), ("packed", 4), "iid"),
+    ("g20_delegated", 1, 2, 40, 128, 700, ("fp16", 0), ("delegated", 4), "channel"),
+    ("g12_int8", 1, 2, 24, 128, 613, ("int8", 0), ("int8", 0), "iid"),
 ]
 
 
@@ -309,7 +315,7 @@ def test_decode_attention(case, variant):
     assert ok, f"out: worst {worst}"
 
 
-SPLIT_CASES = DECODE_CASES[1:5] + [c for c in DECODE_CASES if c[0] in ("int8_d128", "asym3_d128", "k3v3_d128", "k2v3_d128")]
+SPLIT_CASES = DECODE_CASES[1:5] + [c for c in DECODE_CASES if c[0] in ("int8_d128", "asym3_d128", "k3v3_d128", "k2v3_d128", "g16_tq35")]
 
 
 @pytest.mark.parametrize("case", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])

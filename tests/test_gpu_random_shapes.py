@@ -2,7 +2,7 @@
 oracle.
 
 Each case draws, from its own seeded generator: a shape (batch, KV heads,
-query group, head_dim), the modes of K and V (packed at several widths,
+query group of 1 to 16 heads, head_dim), the modes of K and V (packed at several widths,
 fp16, INT8, a delegated V), contiguous or paged storage (block size and a
 shuffled block table), a run of appends in order (lengths from 1 to a few
 hundred, some of them multiples of 16, so both encoders and the aligned and
@@ -51,7 +51,7 @@ def _draw(seed):
     d = int(rng.choice([64, 128], p=[0.3, 0.7]))
     B = int(rng.integers(1, 4))
     H = int(rng.integers(1, 4))
-    G = int(rng.choice([1, 2, 3, 4, 5, 6, 8]))
+    G = int(rng.choice([1, 2, 3, 4, 5, 6, 8, 12, 16], p=[0.1, 0.1, 0.1, 0.2, 0.1, 0.1, 0.16, 0.07, 0.07]))
     k_mode = str(rng.choice(["packed", "fp16", "int8"], p=[0.6, 0.25, 0.15]))
     v_mode = str(rng.choice(["packed", "fp16", "delegated", "int8"], p=[0.55, 0.1, 0.2, 0.15]))
     bits = lambda: int(rng.choice([1, 2, 3, 4, 5, 8], p=[0.05, 0.15, 0.35, 0.35, 0.05, 0.05]))  # noqa: E731
