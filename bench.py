@@ -538,6 +538,9 @@ def main():
     ap.add_argument("--sparse-v", type=float, default=0.0,
                     help="decode with tq_decode_attention_sparse at this weight threshold "
                          "(an approximation; 0 = the exact decode)")
+    ap.add_argument("--fused-append", action="store_true",
+                    help="workloads that append one position a step: each layer's append and decode "
+                         "in one tq_decode_attention_append call (timed as the decode group)")
     ap.add_argument("--splits", type=int, default=0,
                     help="context splits per (batch, KV head); 0 = the library's choice")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -602,6 +605,10 @@ def main():
     n_new = pre or app
     base = T - n_new if n_new else T
 
+    if args.fused_append and (n_new != 1 or args.sparse_v):
+        print(json.dumps({"error": "--fused-append needs a one-position append workload and the exact decode"}),
+              flush=True)
+        sys.exit(2)
     kspec = tq.SideSpec(w["k"][0], w["k"][1])
     vspec = tq.SideSpec(w["v"][0], w["v"][1], w.get("hot", 256))
     layers = []
@@ -676,14 +683,18 @@ def main():
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)] if record is not None else None
         if ev:
             ev[0].record(stream)
-        if n_new:
+        if n_new and not args.fused_append:
             for cache, kn, vn, q, out, ws in layers:
                 cache.quantize_append(kn, vn, base, stream=stream)
         if ev:
             ev[1].record(stream)
         for cache, kn, vn, q, out, ws in layers:
-            cache.decode_attention(q, T, n_splits=args.splits, out=out, workspace=ws, stream=stream,
-                                   sparse_v=args.sparse_v)
+            if args.fused_append:
+                cache.decode_attention_append(kn, vn, base, q, T, n_splits=args.splits, out=out, workspace=ws,
+                                              stream=stream)
+            else:
+                cache.decode_attention(q, T, n_splits=args.splits, out=out, workspace=ws, stream=stream,
+                                       sparse_v=args.sparse_v)
         if ev:
             ev[2].record(stream)
             record.append(ev)
@@ -721,7 +732,8 @@ def main():
         "config": {"workload": args.workload, "batch": B, "kv_heads": Hkv, "q_heads": Hq,
                    "head_dim": d, "context": T, "layers": Lyr,
                    "k": f"{w['k'][0]}{w['k'][1] or ''}", "v": f"{w['v'][0]}{w['v'][1] or ''}",
-                   "append_per_layer": n_new, "block_size": bsz, "sparse_v": args.sparse_v,
+                   "append_per_layer": n_new, "fused_append": bool(args.fused_append),
+                   "block_size": bsz, "sparse_v": args.sparse_v,
                    "cache_flush_gib_per_step": 1 if flush is not None else 0},
         "hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4),
         "decode_us_per_layer": round(dec_avg_s * 1e6, 2),
@@ -729,13 +741,14 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                      # counters were taken on contiguous caches
-                     "traffic": None if bsz else recorded_traffic(traffic_key(args.workload, args.sparse_v))},
+                     "traffic": None if (bsz or args.fused_append)
+                     else recorded_traffic(traffic_key(args.workload, args.sparse_v))},
         # context for the roofline: what a plain streaming-read kernel attains
         "attainable_read": {"gbs": round(attain, 1), "bytes": 4 << 30,
                             "kernel": "tq_read_probe: 16-byte loads, 256 blocks of 768 threads",
                             "decode_frac": round(dec_gbs / attain, 4)},
     }
-    if n_new:
+    if n_new and not args.fused_append:
         app_avg_s = app_ms / (len(rec) * Lyr) / 1e3
         res["quantize_append_mtok_s"] = round(B * n_new / app_avg_s / 1e6, 2)
         res["quantize_append_us_per_layer"] = round(app_avg_s * 1e6, 2)

@@ -101,6 +101,9 @@ def lib():
         L.tq_decode_attention_sparse.argtypes = [ctypes.POINTER(tq_cache), P, I, I, I, ctypes.c_float, P, P,
                                                  P, ctypes.c_size_t, P]
         L.tq_decode_attention_sparse.restype = I
+        L.tq_decode_attention_append.argtypes = [ctypes.POINTER(tq_cache), P, P, I, P, I, I, I, P, P, P,
+                                                 ctypes.c_size_t, P]
+        L.tq_decode_attention_append.restype = I
         L.tq_decode_attention_noalloc.argtypes = [ctypes.POINTER(tq_cache), P, I, I, I, P, P, P]
         L.tq_decode_attention_noalloc.restype = I
         L.tq_dequantize.argtypes = [ctypes.POINTER(tq_cache), I, I, I, P, P]
@@ -347,6 +350,32 @@ class TQCache:
                                              int(n_splits), _ptr(out), _ptr(sc), _ptr(ws),
                                              ws.numel() * ws.element_size(), _stream_handle(stream)),
                    "tq_decode_attention")
+        return (out, sc[:, :, :length]) if scores else out
+
+    def decode_attention_append(self, k_new, v_new, offset: int, q, length: int, n_splits: int = 0, out=None,
+                                scores=False, workspace=None, stream=None):
+        """One decode step's append-then-attend through
+        tq_decode_attention_append: the new position k_new, v_new (fp16
+        [B, Hkv, 1, d]) written at row `offset`, then attention over
+        [0, length).  Returns what decode_attention returns."""
+        import torch
+        for x in (k_new, v_new):
+            self._check_rows(x)
+        if int(k_new.shape[2]) != 1 or int(v_new.shape[2]) != 1:
+            raise ValueError("k_new and v_new hold one position")
+        if q.dtype != torch.float16 or not q.is_contiguous() or q.dim() != 3:
+            raise ValueError("q must be contiguous fp16 [B, Hq, d]")
+        B, Hq, d = q.shape
+        if B != self.batch or d != self.head_dim:
+            raise ValueError("q shape does not match the cache")
+        if out is None:
+            out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+        sc = torch.empty((B, Hq, max(int(length), 1)), dtype=torch.float32, device=q.device) if scores else None
+        ws = workspace if workspace is not None else self.workspace(Hq, length, n_splits)
+        _check(lib().tq_decode_attention_append(ctypes.byref(self.desc), _ptr(k_new), _ptr(v_new), int(offset),
+                                                _ptr(q), int(Hq), int(length), int(n_splits), _ptr(out), _ptr(sc),
+                                                _ptr(ws), ws.numel() * ws.element_size(), _stream_handle(stream)),
+               "tq_decode_attention_append")
         return (out, sc[:, :, :length]) if scores else out
 
     def decode_attention_noalloc(self, q, length: int, n_splits: int = 0, out=None, scores=False, stream=None):

@@ -205,6 +205,7 @@ void fill_decode_params(const tq_cache *cache, const void *q, int q_heads, int l
   fill_signs(cache->seed, d, p->sign);
   copy_levels(cache->k, cache->k.centroids, n_levels(cache->k), p->k_cent);
   copy_levels(cache->v, cache->v.centroids, n_levels(cache->v), p->v_cent);
+  p->ap_split = -1;  // nothing appended (tq_decode_attention_append sets it)
   p->share_lut = (cache->k.mode == TQ_SIDE_PACKED && cache->k.bits == 4 && cache->v.bits == 4 &&
                   memcmp(p->k_cent, p->v_cent, sizeof(float) * 16) == 0)
                      ? 1
@@ -344,6 +345,54 @@ int tq_decode_attention_sparse(const tq_cache *cache, const void *q, int q_heads
   p.ws_part_off = tq::kCounterBytes;
   const hipError_t e = (v == kMfma) ? tq::launch_decode_mfma(p, static_cast<hipStream_t>(hip_stream))
                                     : tq::launch_decode_ref(p, static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
+int tq_decode_attention_append(const tq_cache *cache, const void *k_new, const void *v_new, int offset,
+                               const void *q, int q_heads, int length, int n_splits, float *out, float *scores,
+                               void *workspace, size_t workspace_bytes, void *hip_stream) {
+  // every argument of both steps is checked before anything is launched
+  int r = check_cache(cache);
+  if (r != TQ_OK) return r;
+  if (!k_new || !v_new || !q || !out) return TQ_ERR_ARG;
+  if (offset < 0 || offset >= cache->capacity) return TQ_ERR_CAPACITY;
+  if (q_heads < cache->kv_heads || q_heads % cache->kv_heads) return TQ_ERR_ARG;
+  if (n_splits < 0) return TQ_ERR_ARG;
+  if (length < 0 || length > cache->capacity) return TQ_ERR_CAPACITY;
+  tq::DecodeParams p;
+  Variant v;
+  const size_t need = workspace_need(cache, q_heads, length, n_splits, &p, &v);
+  if (need == 0) return TQ_ERR_ARG;
+  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return TQ_ERR_WORKSPACE;
+  // one launch when the matrix-core kernel runs, both sides are fp16 or
+  // packed, the new position is attended and no scores are asked for; else
+  // the two calls in order
+  const auto plain = [](const tq_side &sd) { return sd.mode == TQ_SIDE_FP16 || sd.mode == TQ_SIDE_PACKED; };
+  if (v != kMfma || !plain(cache->k) || !plain(cache->v) || offset >= length || scores) {
+    r = tq_quantize_append(cache, k_new, v_new, 1, offset, hip_stream);
+    if (r != TQ_OK) return r;
+    return tq_decode_attention_sparse(cache, q, q_heads, length, n_splits, 0.0f, out, scores, workspace,
+                                      workspace_bytes, hip_stream);
+  }
+  p.q = static_cast<const uint16_t *>(q);
+  p.out = out;
+  p.scores = scores;
+  p.ws = static_cast<float *>(workspace);
+  p.counters = static_cast<unsigned *>(workspace);
+  p.sparse_lg = -INFINITY;
+  p.ws_part_off = tq::kCounterBytes;
+  p.k_new = static_cast<const uint16_t *>(k_new);
+  p.v_new = static_cast<const uint16_t *>(v_new);
+  p.ap_offset = offset;
+  p.ap_split = offset / p.cold_split_len;
+  const float *kt = cache->k.mode == TQ_SIDE_PACKED ? cache->k.thresholds : nullptr;
+  const float *vt = cache->v.mode == TQ_SIDE_PACKED ? cache->v.thresholds : nullptr;
+  for (int i = 0; i < 16; ++i) {
+    p.k_thr[i] = (kt && i < n_levels(cache->k) - 1) ? kt[i] : 0.0f;
+    p.v_thr[i] = (vt && i < n_levels(cache->v) - 1) ? vt[i] : 0.0f;
+  }
+  const hipError_t e = tq::launch_decode_mfma(p, static_cast<hipStream_t>(hip_stream));
   return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
 

@@ -126,7 +126,8 @@ struct Lay {
   static constexpr int red = qwork + GP * qstride;     // flag
   static constexpr int prog = red + 4;                 // [kMaxWaves] chunks done per wave
   static constexpr int qinv = red + 16;                // [8] per head: the score's query scale
-  static constexpr int bmax = red + 24;                // sparse-V: [8 heads][16 waves] exchanged maxima
+  static constexpr int bmax = red + 24;                // sparse-V: [8 heads][16 waves] exchanged maxima;
+                                                       // fused append (exact decode): [32] code bytes of one row
   static constexpr int tail = red + 152;
   // Merge slots of the main loop's waves: an area of their own when it fits
   // (a wave then writes its slot as soon as its own loop ends), else over
@@ -304,6 +305,78 @@ __device__ __forceinline__ float xor_butterfly(float x, int lane) {
     pt = dpp_f<kRowShr + M, 0xf ^ lo_banks>(pt, x);
   }
   return upper ? pt - x : x + pt;
+}
+
+// Fused append: the new position of one unit written at storage row `row`
+// of one side as the encoder writes it ("TurboQuant KV Cache Quantization in
+// MLX-VLM", "How TurboQuant KV Cache Quantization Works"): an fp16 row is
+// copied; a packed row is normalised, rotated by diag(s) then H, scaled by
+// 1 / (n sqrt(d)), coded as the number of thresholds below each coordinate
+// and packed LSB-first.  One wave: lane l holds coordinates l and l + 64.
+// `stage` is 32 words of this wave's LDS for the codes (a byte per
+// coordinate).  A row in an out-of-range block (row < 0) takes no writes.
+// x0, x1: the fp16 bits of coordinates lane and lane + 64 of the new row.
+// The thresholds and sign words are read with uniform indices only (scalar
+// loads of the kernel arguments): a per-lane index would make each step of
+// a search a memory round trip.
+__device__ __forceinline__ void append_side(const SideDev &s, const float (&thr)[16],
+                                            const uint32_t (&sign)[kMaxSignWords], uint16_t x0, uint16_t x1,
+                                            long row, int lane, uint32_t *stage) {
+  if (row < 0) return;
+  if (s.mode == TQ_SIDE_FP16) {
+    s.fp16[row * D + lane] = x0;
+    s.fp16[row * D + lane + 64] = x1;
+    return;
+  }
+  float a = h2f(x0), c = h2f(x1);
+  float ss = a * a + c * c;
+  for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+  const float n = sqrtf(ss);
+  const float inv = (n > 0.0f) ? 1.0f / (n * sqrtf(static_cast<float>(D))) : 0.0f;
+  const uint32_t sa = lane < 32 ? sign[0] : sign[1], sb = lane < 32 ? sign[2] : sign[3];
+  a = ((sa >> (lane & 31)) & 1u) ? -a : a;
+  c = ((sb >> (lane & 31)) & 1u) ? -c : c;
+  float y0 = a + c, y1 = a - c;
+  y0 = xor_butterfly<32>(y0, lane);
+  y1 = xor_butterfly<32>(y1, lane);
+  y0 = xor_butterfly<16>(y0, lane);
+  y1 = xor_butterfly<16>(y1, lane);
+  y0 = xor_butterfly<8>(y0, lane);
+  y1 = xor_butterfly<8>(y1, lane);
+  y0 = xor_butterfly<4>(y0, lane);
+  y1 = xor_butterfly<4>(y1, lane);
+  y0 = xor_butterfly<2>(y0, lane);
+  y1 = xor_butterfly<2>(y1, lane);
+  y0 = xor_butterfly<1>(y0, lane);
+  y1 = xor_butterfly<1>(y1, lane);
+  // code: the number of thresholds below the coordinate (ascending
+  // thresholds, 2^bits - 1 of them; at most 4 bits here)
+  const float u0 = y0 * inv, u1 = y1 * inv;
+  const int nt = (1 << s.bits) - 1;
+  int c0 = 0, c1 = 0;
+#pragma unroll
+  for (int k = 0; k < 15; ++k) {
+    if (k < nt) {
+      c0 += u0 > thr[k] ? 1 : 0;
+      c1 += u1 > thr[k] ? 1 : 0;
+    }
+  }
+  uint8_t *st8 = reinterpret_cast<uint8_t *>(stage);
+  st8[lane] = static_cast<uint8_t>(c0);
+  st8[lane + 64] = static_cast<uint8_t>(c1);
+  // the stage is this wave's own: its LDS accesses complete in order, so
+  // only the compiler has to keep the reads after the writes
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+  // word w holds bits 32 w .. 32 w + 31 of the stream, code j at bit b j
+  if (lane < s.words) {
+    const int b = s.bits;
+    const int j0 = 32 * lane / b, j1 = min((32 * lane + 31) / b, D - 1);
+    uint64_t acc = 0;
+    for (int j = j0; j <= j1; ++j) acc |= static_cast<uint64_t>(st8[j]) << (b * j - 32 * lane + 32);
+    s.codes[row * s.words + lane] = static_cast<uint32_t>(acc >> 32);
+  }
+  if (lane == 0) s.norms[row] = n;
 }
 
 // Global-memory data of one chunk of 32 positions for one lane.
@@ -1101,7 +1174,8 @@ struct Balance {
   }
 };
 
-template <int KB, int VB, int GP, bool PG, bool SC, bool SP>
+// AP: the fused append (tq_decode_attention_append; exact decode, no scores).
+template <int KB, int VB, int GP, bool PG, bool SC, bool SP, bool AP>
 __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(const DecodeParams p) {
   constexpr int kWaves = waves_of<KB>();
   constexpr int kThreads = 64 * kWaves;
@@ -1204,6 +1278,40 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
   // waves past the split read an empty range, which returns zeros.)
   uint32_t qa_raw = p.q[(hq0 + min(wave, G - 1)) * D + lane];  // fp16 bits
   uint32_t qb_raw = p.q[(hq0 + min(wave, G - 1)) * D + lane + 64];
+  // fused append: in the split holding the new position, the wave that
+  // reads the position's chunk (chunk c goes to wave c % kWaves) writes the
+  // new K and V rows first and waits for the stores, so it reads them back;
+  // no other wave reads that chunk, so nothing else waits.  Every head group
+  // of the unit writes the same rows.
+  // When the position lies in a later chunk of that wave, the wave's first
+  // chunk load goes out first and the append runs while it is in flight.
+  // The new rows' loads go out before the wave's first chunk load (so the
+  // append does not wait for the chunk).  When the position lies in a later
+  // chunk of the wave, the rows are written after the prologue (whose block
+  // barrier the append would otherwise hold up), before the main loop.
+  static_assert(!(AP && (SP || SC)), "the fused append runs the exact decode without scores");
+  const int ap_chunk = (AP && split == p.ap_split) ? (p.ap_offset - s0) / kChunk : -1;
+  const bool ap_wave = AP && ap_chunk >= 0 && wave == ap_chunk % kWaves;
+  uint16_t ax[4] = {0, 0, 0, 0};
+  if (ap_wave) {
+    const uint16_t *kx = p.k_new + static_cast<long>(unit) * D, *vx = p.v_new + static_cast<long>(unit) * D;
+    ax[0] = kx[lane];
+    ax[1] = kx[lane + 64];
+    ax[2] = vx[lane];
+    ax[3] = vx[lane + 64];
+  }
+  auto append = [&]() {
+    const long row = cache_row(p.pg, unit, p.ap_offset, p.capacity);
+    uint32_t *stage = lds + L::bmax;
+    append_side(p.k, p.k_thr, p.sign, ax[0], ax[1], row, lane, stage);
+    append_side(p.v, p.v_thr, p.sign, ax[2], ax[3], row, lane, stage);
+  };
+  if (ap_wave && ap_chunk < kWaves) {
+    append();
+    __builtin_amdgcn_s_waitcnt(0);  // the stores complete before the chunk is loaded
+    asm volatile("" ::: "memory");
+  }
+  const bool ap_late = ap_wave && ap_chunk >= kWaves;
   ChunkData<KB, VB, GP> A, B;
   W.load(s0 + wave * kChunk, A);
   // The 16 (V) and up to 16 (K) centroids the tables need: every wave reads
@@ -1328,6 +1436,14 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
       if (!live) h = u32x4_t{0u, 0u, 0u, 0u};
       W.bq[c] = __builtin_bit_cast(half8_t, h);
     }
+  }
+
+  if (ap_late) {
+    // after the prologue, which it then does not delay; the stores complete
+    // before the loop loads the position's chunk
+    append();
+    __builtin_amdgcn_s_waitcnt(0);
+    asm volatile("" ::: "memory");
   }
 
   // ---- main loop: the wave processes its chunk while its next one loads
@@ -1588,12 +1704,12 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
 
 }  // namespace
 
-template <int KB, int VB, int GP, bool SC, bool SP>
+template <int KB, int VB, int GP, bool SC, bool SP, bool AP = false>
 void launch_sp(const DecodeParams &p, dim3 grid, hipStream_t stream) {
   if (p.pg.table) {
-    hipLaunchKernelGGL((decode_mfma_kernel<KB, VB, GP, true, SC, SP>), grid, dim3(64 * waves_of<KB>()), 0, stream, p);
+    hipLaunchKernelGGL((decode_mfma_kernel<KB, VB, GP, true, SC, SP, AP>), grid, dim3(64 * waves_of<KB>()), 0, stream, p);
   } else {
-    hipLaunchKernelGGL((decode_mfma_kernel<KB, VB, GP, false, SC, SP>), grid, dim3(64 * waves_of<KB>()), 0, stream, p);
+    hipLaunchKernelGGL((decode_mfma_kernel<KB, VB, GP, false, SC, SP, AP>), grid, dim3(64 * waves_of<KB>()), 0, stream, p);
   }
 }
 
@@ -1609,6 +1725,12 @@ void launch_sc(const DecodeParams &p, dim3 grid, hipStream_t stream) {
 
 template <int KB, int VB, int GP>
 void launch_gp(const DecodeParams &p, dim3 grid, hipStream_t stream) {
+  if (p.ap_split >= 0) {
+    // fused append: exact decode, no scores (the host checks both; INT8 and
+    // delegated sides take the two separate calls instead)
+    if constexpr (KB != kInt8) launch_sp<KB, VB, GP, false, false, true>(p, grid, stream);
+    return;
+  }
   if (p.scores) {
     launch_sc<KB, VB, GP, true>(p, grid, stream);
   } else {

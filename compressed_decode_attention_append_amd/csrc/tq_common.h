@@ -105,6 +105,12 @@ struct DecodeParams {
   uint32_t sign[kMaxSignWords];
   float k_cent[kMaxLevels];
   float v_cent[kMaxLevels];
+  // fused append (matrix-core kernel): the new rows k_new / v_new (fp16
+  // [B][Hkv][1][d]) are written at position ap_offset by the blocks of split
+  // ap_split before they read them; ap_split = -1: nothing is appended.
+  const uint16_t *k_new, *v_new;
+  int ap_offset, ap_split;
+  float k_thr[16], v_thr[16];  // packed sides' thresholds (at most 4 bits here)
 };
 
 // Workspace: a fixed region of per-unit counters (zero on entry, left zero

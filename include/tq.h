@@ -257,6 +257,32 @@ int tq_decode_attention_sparse(const tq_cache *cache, const void *q, int q_heads
                                float *scores, void *workspace, size_t workspace_bytes,
                                void *hip_stream);
 
+/* One decode step's append-then-attend in one call ("TurboQuant KV Cache
+ * Quantization in MLX-VLM", "Manual Cache Operations": quantize the new K/V
+ * into the cache, then score from the compressed cache): the same results
+ * as tq_quantize_append(cache, k_new, v_new, 1, offset, stream) followed by
+ * tq_decode_attention(cache, q, q_heads, length, n_splits, out, scores,
+ * workspace, workspace_bytes, stream).
+ *   k_new, v_new: device fp16 [B][Hkv][1][d], the new position of every
+ *                 sequence; written at row `offset` (0 <= offset < capacity).
+ *   the rest: as tq_decode_attention (the same workspace size).
+ * Where the matrix-core decode takes the shape, both sides are fp16 or
+ * packed, offset < length and `scores` is NULL, this is one launch: in the
+ * split that holds `offset`, the wave that reads the position's chunk
+ * encodes and writes the new rows first, so the step pays no separate
+ * launch.  Otherwise (delegated or INT8 sides, other shapes, offset >=
+ * length, scores requested) it makes the two calls in order on
+ * `hip_stream`.  The rows written are those tq_quantize_append defines, up
+ * to rounding: the one-launch path sums the norm and the rotation in another
+ * order, so a norm may differ in its last bits and a coordinate within
+ * rounding of a threshold may take the neighbouring code.
+ * Errors: as tq_quantize_append (with n_new = 1) and tq_decode_attention,
+ * all checked before anything is launched. */
+int tq_decode_attention_append(const tq_cache *cache, const void *k_new, const void *v_new,
+                               int offset, const void *q, int q_heads, int length, int n_splits,
+                               float *out, float *scores, void *workspace, size_t workspace_bytes,
+                               void *hip_stream);
+
 /* tq_decode_attention without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation).  The workspace is a fixed static device

@@ -179,6 +179,32 @@ def test_decode_errors():
     assert _dec(_desc(f, d=100), f) == tq.TQ_ERR_HEAD_DIM
 
 
+def test_append_decode_errors():
+    # the fused append-then-attend call checks every argument of both steps
+    # before anything is launched (no GPU is touched on these paths)
+    f = _Fake()
+    c = _desc(f)
+    need = tq.lib().tq_decode_workspace_bytes(ctypes.byref(c), 8, 100, 0)
+
+    def call(k=True, v=True, offset=99, q=True, Hq=8, length=100, ns=0, out=True, ws_bytes=need, cache=c):
+        return tq.lib().tq_decode_attention_append(ctypes.byref(cache), f.p(1024) if k else None,
+                                                   f.p(2048) if v else None, offset, f.p(4096) if q else None,
+                                                   Hq, length, ns, f.p(8192) if out else None, None,
+                                                   f.p(0) if ws_bytes else None, ws_bytes, None)
+    assert call(k=False) == tq.TQ_ERR_ARG
+    assert call(v=False) == tq.TQ_ERR_ARG
+    assert call(q=False) == tq.TQ_ERR_ARG
+    assert call(out=False) == tq.TQ_ERR_ARG
+    assert call(offset=-1) == tq.TQ_ERR_CAPACITY
+    assert call(offset=1024) == tq.TQ_ERR_CAPACITY      # capacity 1024
+    assert call(Hq=6) == tq.TQ_ERR_ARG
+    assert call(length=1025) == tq.TQ_ERR_CAPACITY
+    assert call(ns=-1) == tq.TQ_ERR_ARG
+    assert call(ws_bytes=need - 1) == tq.TQ_ERR_WORKSPACE
+    assert call(cache=_desc(f, d=100)) == tq.TQ_ERR_HEAD_DIM
+    assert call(cache=_desc(f, kb=0)) == tq.TQ_ERR_BITS
+
+
 def test_decode_workspace_grows_with_splits():
     f = _Fake()
     c = _desc(f)
