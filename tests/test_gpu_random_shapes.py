@@ -18,6 +18,9 @@ Checks, as in the fixed-case parity tests:
 * sparse-V (both kernels, a threshold per case): within the oracle's bound
   of the exact output;
 * the allocation-free entry point: the same output as the workspace call;
+* the fused append-then-attend call: one more position appended and
+  attended in one call (one launch or its two-call fallback, as the shape
+  decides), the row it wrote and the output against the oracle;
 * dequantize of the packed and INT8 sides over a range of positions: the
   oracle's dequantization of the same codes, within 1e-5 of each row's
   largest magnitude.
@@ -197,6 +200,21 @@ def test_random_configuration(seed):
                 free = cache.decode_attention_noalloc(qd, T, n_splits=c["splits"])
                 torch.cuda.synchronize()
                 assert torch.equal(free, out), f"{desc}: allocation-free call differs"
+        # one more position through the fused call, attended at once
+        pos = sum(c["lens"])
+        if pos < c["cap"] and (c["v"].mode != "delegated" or T == pos):
+            kn, vn = synth.kv_numpy(8000 + seed, B, H, 1, d, dist=c["dist"], outlier_frac=0.01)
+            os.environ["TQ_DECODE_VARIANT"] = "auto"
+            out_f = cache.decode_attention_append(torch.from_numpy(kn).cuda(), torch.from_numpy(vn).cuda(), pos, qd,
+                                                  pos + 1, n_splits=c["splits"])
+            torch.cuda.synchronize()
+            _check_written(cache, "k", c["k"], kn, pos)
+            if c["v"].mode != "delegated":
+                _check_written(cache, "v", c["v"], vn, pos)
+            o_f, _ = oracle.decode_attention(q, _rows(cache, "k", c["k"], pos + 1), _rows(cache, "v", c["v"], pos + 1))
+            ok_f, worst_f = rows_close(out_f.cpu().numpy(), o_f)
+            print(f"  fused append at {pos}: out {worst_f:.2e}", flush=True)
+            assert ok_f, f"{desc}: fused append-then-attend worst {worst_f}"
         rng = np.random.default_rng(seed + 77)
         for side, spec, rows in (("k", c["k"], kr), ("v", c["v"], vr)):
             if spec.mode in ("packed", "int8"):
