@@ -38,6 +38,8 @@ def main(path):
     L.tq_decode_attention_sparse.argtypes = [ctypes.POINTER(Cache), P, I, I, I, ctypes.c_float, P, P, P,
                                              ctypes.c_size_t, P]
     L.tq_decode_attention_noalloc.argtypes = [ctypes.POINTER(Cache), P, I, I, I, P, P, P]
+    L.tq_decode_attention_append.argtypes = [ctypes.POINTER(Cache), P, P, I, P, I, I, I, P, P, P,
+                                             ctypes.c_size_t, P]
     L.tq_decode_workspace_init.argtypes = [P, ctypes.c_size_t, P]
     L.tq_dequantize.argtypes = [ctypes.POINTER(Cache), I, I, I, P, P]
     L.tq_read_probe.argtypes = [P, ctypes.c_size_t, P, P]
@@ -104,6 +106,9 @@ def main(path):
                         call(L.tq_decode_attention_sparse, ctypes.byref(cd), base, Hq, length, 0, 0.5, base, base,
                              base, max(need, 1), None)
                         call(L.tq_decode_attention_noalloc, ctypes.byref(cd), base, Hq, length, 0, base, None, None)
+                        for off, sc in ((max(length - 1, 0), None), (length, None), (max(length - 1, 0), base)):
+                            call(L.tq_decode_attention_append, ctypes.byref(cd), base, base, off, base, Hq, length, 0,
+                                 base, sc, base, ws_big, None)
                     for n_new, off in ((0, 0), (1, 0), (16, 1000), (300, 5), (2000, 0), (-1, 0)):
                         call(L.tq_quantize_append, ctypes.byref(cd), base, base, n_new, off, None)
                     for side in (0, 1, 2):
@@ -114,6 +119,12 @@ def main(path):
     assert call(L.tq_decode_attention_sparse, ctypes.byref(cd), base, 8, 100, 0, 1.5, base, None, base, ws_big,
                 None) == ARG
     assert call(L.tq_decode_attention, ctypes.byref(cd), base, 8, 100, 0, base, None, base, ws_big, None) == HIP
+    assert call(L.tq_decode_attention_append, ctypes.byref(cd), base, base, 99, base, 8, 100, 0, base, None, base,
+                ws_big, None) == HIP
+    assert call(L.tq_decode_attention_append, ctypes.byref(cd), None, base, 99, base, 8, 100, 0, base, None, base,
+                ws_big, None) == ARG
+    assert call(L.tq_decode_attention_append, ctypes.byref(cd), base, base, 1024, base, 8, 100, 0, base, None, base,
+                ws_big, None) == CAP
     big = desc(d=256, kbits=4, vbits=5, cap=1 << 20, B=2, H=4)
     assert call(L.tq_decode_attention_noalloc, ctypes.byref(big), base, 64, 100000, 2000, base, None, None) == SCR
     assert call(L.tq_decode_workspace_init, None, 1 << 20, None) == ARG
