@@ -365,10 +365,12 @@ int tq_decode_attention_append(const tq_cache *cache, const void *k_new, const v
   if (need == 0) return TQ_ERR_ARG;
   if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u))
     return TQ_ERR_WORKSPACE;
-  // one launch when the matrix-core kernel runs, both sides are fp16 or
-  // packed, the new position is attended and no scores are asked for; else
-  // the two calls in order
-  const auto plain = [](const tq_side &sd) { return sd.mode == TQ_SIDE_FP16 || sd.mode == TQ_SIDE_PACKED; };
+  // one launch when the matrix-core kernel runs, no side is delegated, the
+  // new position is attended and no scores are asked for; else the two
+  // calls in order
+  const auto plain = [](const tq_side &sd) {
+    return sd.mode == TQ_SIDE_FP16 || sd.mode == TQ_SIDE_PACKED || sd.mode == TQ_SIDE_INT8;
+  };
   if (v != kMfma || !plain(cache->k) || !plain(cache->v) || offset >= length || scores) {
     r = tq_quantize_append(cache, k_new, v_new, 1, offset, hip_stream);
     if (r != TQ_OK) return r;

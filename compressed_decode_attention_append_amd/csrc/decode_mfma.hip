@@ -310,7 +310,8 @@ __device__ __forceinline__ float xor_butterfly(float x, int lane) {
 // Fused append: the new position of one unit written at storage row `row`
 // of one side as the encoder writes it ("TurboQuant KV Cache Quantization in
 // MLX-VLM", "How TurboQuant KV Cache Quantization Works"): an fp16 row is
-// copied; a packed row is normalised, rotated by diag(s) then H, scaled by
+// copied; an INT8 row coded by its absmax; a packed row is normalised,
+// rotated by diag(s) then H, scaled by
 // 1 / (n sqrt(d)), coded as the number of thresholds below each coordinate
 // and packed LSB-first.  One wave: lane l holds coordinates l and l + 64.
 // `stage` is 32 words of this wave's LDS for the codes (a byte per
@@ -329,6 +330,17 @@ __device__ __forceinline__ void append_side(const SideDev &s, const float (&thr)
     return;
   }
   float a = h2f(x0), c = h2f(x1);
+  if (s.mode == TQ_SIDE_INT8) {
+    // absmax: one signed byte a coordinate (byte j of the row), the scale
+    // max |x| / 127 in the norm slot
+    float m = fmaxf(fabsf(a), fabsf(c));
+    for (int k = 32; k >= 1; k >>= 1) m = fmaxf(m, __shfl_xor(m, k));
+    uint8_t *b8 = reinterpret_cast<uint8_t *>(s.codes + row * s.words);
+    b8[lane] = static_cast<uint8_t>(m > 0.0f ? int8_code(a, m) : 0);
+    b8[lane + 64] = static_cast<uint8_t>(m > 0.0f ? int8_code(c, m) : 0);
+    if (lane == 0) s.norms[row] = m / 127.0f;
+    return;
+  }
   float ss = a * a + c * c;
   for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
   const float n = sqrtf(ss);
@@ -1726,9 +1738,9 @@ void launch_sc(const DecodeParams &p, dim3 grid, hipStream_t stream) {
 template <int KB, int VB, int GP>
 void launch_gp(const DecodeParams &p, dim3 grid, hipStream_t stream) {
   if (p.ap_split >= 0) {
-    // fused append: exact decode, no scores (the host checks both; INT8 and
-    // delegated sides take the two separate calls instead)
-    if constexpr (KB != kInt8) launch_sp<KB, VB, GP, false, false, true>(p, grid, stream);
+    // fused append: exact decode, no scores (the host checks both; delegated
+    // sides take the two separate calls instead)
+    launch_sp<KB, VB, GP, false, false, true>(p, grid, stream);
     return;
   }
   if (p.scores) {

@@ -90,20 +90,7 @@ __device__ __forceinline__ void encode_int8(const float (&x)[4], int t, bool wri
   uint32_t w = 0;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    int c = 0;
-    if (a > 0.0f) {
-      const float y2 = 254.0f * x[e];  // 2 (127 x), exact
-      float k = rintf(0.5f * y2 / a);
-      const float up = fmaf(-(2.0f * k + 1.0f), a, y2);  // sign of 127 x / a - (k + 1/2)
-      const float dn = fmaf(-(2.0f * k - 1.0f), a, y2);  // sign of 127 x / a - (k - 1/2)
-      const bool odd = (static_cast<int>(k) & 1) != 0;
-      if (up > 0.0f || (up == 0.0f && odd)) {
-        k += 1.0f;
-      } else if (dn < 0.0f || (dn == 0.0f && odd)) {
-        k -= 1.0f;
-      }
-      c = min(127, max(-127, static_cast<int>(k)));
-    }
+    const int c = a > 0.0f ? int8_code(x[e], a) : 0;
     w |= (static_cast<uint32_t>(c) & 0xffu) << (8 * e);
   }
   if (write) {

@@ -83,6 +83,25 @@ __device__ __forceinline__ int count_below(const float *thr, int bits, float y) 
   return code;
 }
 
+// INT8 absmax code of x in a row whose largest magnitude is a > 0:
+// round(127 x / a) to nearest, ties to even, decided exactly.  2 (127 x) =
+// 254 x is exact in float; a first guess k from the rounded division is
+// moved by one where the exact signs of 127 x / a - (k +- 1/2), taken by
+// fused multiply-adds, say it lies past a half step.
+__device__ __forceinline__ int int8_code(float x, float a) {
+  const float y2 = 254.0f * x;  // 2 (127 x), exact
+  float k = rintf(0.5f * y2 / a);
+  const float up = fmaf(-(2.0f * k + 1.0f), a, y2);  // sign of 127 x / a - (k + 1/2)
+  const float dn = fmaf(-(2.0f * k - 1.0f), a, y2);  // sign of 127 x / a - (k - 1/2)
+  const bool odd = (static_cast<int>(k) & 1) != 0;
+  if (up > 0.0f || (up == 0.0f && odd)) {
+    k += 1.0f;
+  } else if (dn < 0.0f || (dn == 0.0f && odd)) {
+    k -= 1.0f;
+  }
+  return min(127, max(-127, static_cast<int>(k)));
+}
+
 // Extract code j (bits wide) from a packed LSB-first row.
 __device__ __forceinline__ uint32_t extract_code(const uint32_t *row, int bits, int j) {
   const int o = bits * j;

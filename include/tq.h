@@ -266,16 +266,16 @@ int tq_decode_attention_sparse(const tq_cache *cache, const void *q, int q_heads
  *   k_new, v_new: device fp16 [B][Hkv][1][d], the new position of every
  *                 sequence; written at row `offset` (0 <= offset < capacity).
  *   the rest: as tq_decode_attention (the same workspace size).
- * Where the matrix-core decode takes the shape, both sides are fp16 or
- * packed, offset < length and `scores` is NULL, this is one launch: in the
+ * Where the matrix-core decode takes the shape, no side is delegated,
+ * offset < length and `scores` is NULL, this is one launch: in the
  * split that holds `offset`, the wave that reads the position's chunk
  * encodes and writes the new rows first, so the step pays no separate
- * launch.  Otherwise (delegated or INT8 sides, other shapes, offset >=
- * length, scores requested) it makes the two calls in order on
- * `hip_stream`.  The rows written are those tq_quantize_append defines, up
- * to rounding: the one-launch path sums the norm and the rotation in another
- * order, so a norm may differ in its last bits and a coordinate within
- * rounding of a threshold may take the neighbouring code.
+ * launch.  Otherwise (delegated V, other shapes, offset >= length, scores
+ * requested) it makes the two calls in order on `hip_stream`.  The rows written are those tq_quantize_append defines, up
+ * to rounding: the one-launch path sums the norm and the rotation of packed
+ * rows in another order, so a norm may differ in its last bits and a
+ * coordinate within rounding of a threshold may take the neighbouring code
+ * (fp16 and INT8 rows are the same).
  * Errors: as tq_quantize_append (with n_new = 1) and tq_decode_attention,
  * all checked before anything is launched. */
 int tq_decode_attention_append(const tq_cache *cache, const void *k_new, const void *v_new,

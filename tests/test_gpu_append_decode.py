@@ -3,16 +3,16 @@ oracle and against the two separate calls it stands for.
 
 Each case fills a cache with quantize_append, then writes one new position
 per sequence at `offset` and attends over [0, length) in one call.  Checked:
-* the rows written at `offset`: fp16 rows exactly; packed codes equal the
-  oracle's quantization of the new rows except within 1e-6 of a threshold,
-  norms within 1e-6;
+* the rows written at `offset`: fp16 rows exactly; INT8 codes and scales
+  equal the exact definition; packed codes equal the oracle's quantization
+  of the new rows except within 1e-6 of a threshold, norms within 1e-6;
 * scores and outputs against the oracle's attention over the rows the GPU
   wrote, within 2e-3 of each row's largest magnitude;
 * the separate calls (tq_quantize_append, then tq_decode_attention) on a
   second cache filled the same way: outputs within the same tolerance, and
-  bit-identical where the call makes those two calls itself (delegated and
-  INT8 sides, head_dim 64, an offset past the attended range, and any call
-  that asks for scores).
+  bit-identical where the call makes those two calls itself (delegated
+  sides, head_dim 64, an offset past the attended range, and any call that
+  asks for scores).
 """
 import numpy as np
 import pytest
@@ -38,7 +38,8 @@ CASES = [
     ("mid_offset", 1, 2, 8, 128, 1024, 1000, 517, 1000, S("packed", 3), S("packed", 4), 0, 2, True),
     ("asym_paged", 2, 2, 8, 128, 640, 600, 600, 601, S("fp16", 0), S("packed", 4), 64, 0, True),
     ("delegated", 1, 2, 16, 128, 960, 899, 899, 900, S("fp16", 0), S("delegated", 4, 64), 0, 0, False),
-    ("int8", 1, 2, 8, 128, 704, 699, 699, 700, S("int8", 0), S("int8", 0), 0, 0, False),
+    ("int8", 1, 2, 8, 128, 704, 699, 699, 700, S("int8", 0), S("int8", 0), 0, 0, True),
+    ("int8_g12_paged", 1, 2, 24, 128, 640, 600, 600, 601, S("int8", 0), S("int8", 0), 64, 0, True),
     ("d64", 1, 2, 4, 64, 300, 255, 255, 256, S("packed", 3), S("packed", 4), 0, 0, False),
     ("past_length", 1, 2, 8, 128, 800, 700, 750, 700, S("packed", 3), S("packed", 4), 0, 0, False),
 ]
@@ -95,6 +96,11 @@ def _check_row(cache, side, spec, x, offset):
     if spec.mode == "fp16":
         got = _view(cache, side + "_fp16")[:, :, offset:offset + 1].cpu().numpy()
         assert np.array_equal(got, x), side
+    elif spec.mode == "int8":
+        c = _view(cache, side + "_codes")[:, :, offset:offset + 1].cpu().numpy().view(np.int8)
+        s = _view(cache, side + "_norms")[:, :, offset:offset + 1].cpu().numpy()
+        c_o, s_o = oracle.int8_quantize(x)
+        assert np.array_equal(c, c_o) and np.array_equal(s, s_o), side
     elif spec.mode == "packed":
         R = oracle.rotation_matrix(cache.seed, d)
         _, t = oracle.lloyd_max(d, spec.bits)
