@@ -755,16 +755,25 @@ struct Wave {
   // and every other weight is below 2^-30 of them; a row whose V norm is
   // tiny next to others does not force the scale down unless its weight is
   // large too.
-  template <bool TAIL, bool SCALED>
+  // HMAX: every chunk's maximum per head is needed (sparse-V); otherwise
+  // the head's maximum is only formed when some lane's values outgrow the
+  // running maximum by the rescale margin (the same decisions: a head's
+  // maximum grows past it exactly when one of its lanes' does).
+  template <bool TAIL, bool SCALED, bool HMAX>
   __device__ __forceinline__ half8_t softmax(const float (&c)[NV], const float (&n)[NV]) {
     // c holds the logits before the query's power-of-two scale qinv (> 0),
     // which commutes with the maximum and enters the exponent by an fma
     float cmax = c[0];
 #pragma unroll
     for (int j = 1; j < NV; ++j) cmax = fmaxf(cmax, c[j]);
-    cmax = head_max<GP>(cmax) * qinv;
+    cmax *= qinv;  // exact (a power of two), so it commutes with the maximum
+    if (HMAX) cmax = head_max<GP>(cmax);
+    bool grow = cmax > m_run + kRescale;
+    if (!HMAX && __ballot(grow)) {
+      cmax = head_max<GP>(cmax);
+      grow = cmax > m_run + kRescale;
+    }
     chunk_max = cmax;
-    const bool grow = cmax > m_run + kRescale;
     if (__ballot(grow)) {
       const float m_new = grow ? cmax : m_run;
       const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
@@ -966,7 +975,7 @@ struct Wave {
       if (TAIL && t0 + cpos + j >= we) cs[j] = -INFINITY;
     }
     if (scores) store_scores<TAIL>(t0, we, cs, scores, score_row0, length);
-    const half8_t ap = softmax<TAIL, true>(cs, c.vn);
+    const half8_t ap = softmax<TAIL, true, SP>(cs, c.vn);
     if (!SP) {
       // exact decode: a threshold never set (kept as a runtime test: the
       // branch keeps the value phase out of the score phase's schedule)
@@ -1037,7 +1046,7 @@ struct Wave {
         if (t >= wb && t < we) scores[(score_row0 + col % GP) * length + t] = cs[j] * qinv * kLn2;
       }
     }
-    const half8_t ap = softmax<true, false>(cs, vn);
+    const half8_t ap = softmax<true, false, false>(cs, vn);
     // fp16 ring rows: tile q covers coordinates 16 q + col
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
