@@ -1168,10 +1168,11 @@ __device__ __forceinline__ void set_priority(int k) {
 // Wave balancing.  The instruction arbiter of a SIMD favours the oldest of
 // its waves, so with equal shares of chunks the oldest wave finishes far
 // ahead and the youngest runs alone at the end, without other waves to hide
-// its latencies.  Each wave therefore publishes how many chunks it has done
-// and runs at a priority equal to how far it lags the leading wave of the
-// block.  Only the issue order changes: which wave takes which chunk, and so
-// every sum, stays the same.
+// its latencies.  Each wave therefore publishes how many chunks (fp16 K) or
+// pairs of chunks (packed and INT8 K) it has done and runs at a priority
+// equal to how far it lags the leading wave of the block.  Only the issue
+// order changes: which wave takes which chunk, and so every sum, stays the
+// same.
 // The counters live at LDS byte address PROG (the kernel's only LDS array
 // starts at address 0); volatile LDS-space accesses, so every step reads
 // the other waves' current counts with ds_read.
@@ -1551,7 +1552,7 @@ __global__ __launch_bounds__(64 * waves_of<KB>(), 1) void decode_mfma_kernel(con
       nblk = nblk2;
       asm volatile("" ::: "memory");
       W.template cold_chunk<false, SP>(s0 + c * kChunk, s1, B, scores, hq0, p.length);
-      bal.step(wave, lane);
+      // (balanced once per two chunks here: measured faster for these shapes)
       c = cn;
     }
     if (c < n_chunks) {
