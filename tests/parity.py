@@ -27,10 +27,15 @@ def words_to_codes(words_i32, bits, d):
     return oracle.unpack_codes(np.asarray(words_i32).view(np.uint32), bits, d)
 
 
-def rows_close(got, ref, rel=REL):
+def rows_close(got, ref, rel=REL, floor=None):
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     err = np.max(np.abs(got - ref), axis=-1)
     scale = np.max(np.abs(ref), axis=-1)
+    if floor is not None:
+        # a row whose values all cancel to near zero (a one-position decode
+        # holds a single score) is judged against the scale of the terms
+        # summed instead of its own magnitude
+        scale = np.maximum(scale, np.asarray(floor, np.float64))
     worst = float(np.max(err / np.where(scale > 0, scale, 1.0)))
     return bool(np.all(err <= rel * scale + 1e-30)), worst

@@ -14,7 +14,9 @@ Checks, as in the fixed-case parity tests:
   there); norms within 1e-6; INT8 sides: codes and scales equal the exact
   definition; fp16 sides: the rows themselves;
 * decode (both kernels): scores and outputs against the oracle's attention
-  over the rows the GPU wrote, within 2e-3 of each row's largest magnitude;
+  over the rows the GPU wrote, within 2e-3 of each row's largest magnitude
+  (for scores, at least 1e-3 of the row's Cauchy-Schwarz bound: a
+  one-position row can cancel to near zero);
 * sparse-V (both kernels, a threshold per case): within the oracle's bound
   of the exact output;
 * the allocation-free entry point: the same output as the workspace call;
@@ -177,6 +179,12 @@ def test_random_configuration(seed):
     q = synth.q_numpy(9000 + seed, B, Hq, d)
     kr, vr = _rows(cache, "k", c["k"], T), _rows(cache, "v", c["v"], T)
     o_ref, s_ref = oracle.decode_attention(q, kr, vr)
+    # scores: a row's scale is at least 1e-3 of the Cauchy-Schwarz bound
+    # |q_h| max_i |k_i| / sqrt(d) of its dot products (the scale of the terms
+    # each sums), so a short row that cancels to near zero is not judged by
+    # its own magnitude alone
+    kmax = np.max(np.linalg.norm(kr, axis=-1), axis=-1) if T else np.zeros((B, H))
+    s_floor = 1e-3 * np.linalg.norm(q.astype(np.float64), axis=-1) * np.repeat(kmax, G, axis=1) / np.sqrt(d)
     tau = (1e-4, 1e-3, 1e-2)[seed % 3]
     bound = oracle.sparse_v_bound(q, kr, vr, tau)
     qd = torch.from_numpy(q).cuda()
@@ -187,7 +195,7 @@ def test_random_configuration(seed):
             out, sc = cache.decode_attention(qd, T, n_splits=c["splits"], scores=True)
             sparse = cache.decode_attention(qd, T, n_splits=c["splits"], sparse_v=tau)
             torch.cuda.synchronize()
-            ok_s, worst_s = rows_close(sc.cpu().numpy(), s_ref)
+            ok_s, worst_s = rows_close(sc.cpu().numpy(), s_ref, floor=s_floor)
             ok_o, worst_o = rows_close(out.cpu().numpy(), o_ref)
             print(f"  {variant}: scores {worst_s:.2e}, out {worst_o:.2e}", flush=True)
             assert ok_s, f"{desc} [{variant}]: scores worst {worst_s}"
